@@ -1,0 +1,9 @@
+"""CPU oracle of the fine-grained MoE layer (test infrastructure only).
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import
+this package; the product path never does.
+"""
+from .moe_oracle import (LayerSpec, SOFTMAX, SIGMOID, round_bf16, silu, sigmoid,  # noqa: F401
+                         router_logits, router_scores, select_topk, token_gates,
+                         dispatch, swiglu, lowrank_apply, lowrank_swiglu, Experts,
+                         aux_statistic, route, layer_forward)

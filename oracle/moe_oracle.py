@@ -1,0 +1,360 @@
+"""Plain, slow CPU oracle of the fine-grained MoE feed-forward layer.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module. The product path
+(the HIP library and its Python binding) never imports, links or calls it, and
+this module imports nothing from the product path.
+
+Everything is evaluated in float64 on the exact input values. The layer is a
+per-token definition; the GPU reaches the same result by regrouping tokens by
+expert, so this oracle simply evaluates the definition token by token over the
+experts each token selected.
+
+Sources (pages as cited; the formulas not printed on any page are readings,
+listed in the design notes of this repository):
+  * Router with top-k of E routed experts plus always-on shared experts: Vertex
+    AGI research page, Architecture ("Router", "Routed experts", "Shared
+    experts"); Quartz Micro Preview Base model card, Architecture table; Moonfrost
+    site, MoE card (top 3 of 32 plus one shared expert, so 4 of 33 run).
+  * Sigmoid scoring with a bias used for balancing: Sutra-1.3B site, "48 + 1
+    experts" card; dormouse site, stack list ("dropless MoE + LFB": balancing by a
+    router bias rather than an auxiliary loss).
+  * 0.01-weighted load-balancing loss: research page Architecture, model card
+    Architecture table. Its form E * sum_i f_i * P_i is the reading used here.
+  * Capacity-based routing over stacked (E, hidden, ffn) expert tensors: Moonfrost
+    site, stacking card. Dropless routing (every token keeps every expert it
+    chose, capacity 0 meaning dropless): dormouse site, "dropless MoE" card and
+    terminal block.
+  * Low-rank experts, each matrix U diag(s) V^T of rank 64: dormouse site, "TSCT
+    low-rank experts" card.
+  * Gated (three-matrix) experts of width F: consistent with the parameter totals
+    on the research page and model card (see tests/golden).
+
+Readings where the pages are silent: SwiGLU experts without biases; softmax
+ranking by logit with ties to the lower expert id; gates renormalised over the
+top-k when the workload says so; sigmoid gates are the selected sigmoid scores
+normalised to sum 1 and the selection bias moves selection only; capacity queues
+are in token order; the bf16 rounding points rho are the SwiGLU product h and the
+rank-r intermediates z (identity for float32 workloads).
+
+Parity unpinned: no page prints layer inputs or outputs, so no function here is
+checked against page values; every function is pinned by brute force on tiny
+inputs, closed forms, invariants and textbook reductions instead (tests/).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+SOFTMAX = "softmax"
+SIGMOID = "sigmoid"
+
+
+@dataclass(frozen=True)
+class LayerSpec:
+    """The layer's hyper-parameters, as the pages state a model's MoE block."""
+
+    hidden: int          # d
+    n_routed: int        # E
+    top_k: int           # k
+    n_shared: int        # S
+    ffn: int             # F
+    rank: int = 0        # 0: dense experts
+    score: str = SOFTMAX
+    renorm: bool = True  # softmax: divide the selected probabilities by their sum
+    capacity: int = 0    # 0: dropless
+    aux_coef: float = 0.01
+    bf16: bool = True    # rho rounds to bf16 (bf16 workloads); identity for float32
+
+
+# ---------------------------------------------------------------------------
+# rho: round to the nearest bf16 value, ties to even, from float64 directly.
+# bf16 keeps 8 significant bits and float32's exponent range.
+# ---------------------------------------------------------------------------
+_BF16_MAX = float.fromhex("0x1.fep127")
+_BF16_MIN_NORMAL = 2.0 ** -126
+
+
+def round_bf16(a) -> np.ndarray:
+    a = np.asarray(a, dtype=np.float64)
+    out = np.empty_like(a)
+    fin = np.isfinite(a)
+    mant, expo = np.frexp(np.where(fin, a, 0.0))         # a = mant * 2**expo, |mant| in [0.5, 1)
+    normal = np.abs(a) >= _BF16_MIN_NORMAL
+    # normal range: 8 significant bits -> mant * 256 rounded half-to-even
+    rn = np.ldexp(np.rint(mant * 256.0), expo - 8)
+    # subnormal range: fixed spacing 2**-133
+    rs = np.ldexp(np.rint(np.ldexp(np.where(fin, a, 0.0), 133)), -133)
+    out[...] = np.where(normal, rn, rs)
+    # anything that rounds beyond the largest finite bf16 overflows
+    big = np.abs(out) > _BF16_MAX
+    out[big] = np.copysign(np.inf, a[big])
+    out[~fin] = a[~fin]
+    return out
+
+
+def _rho(spec: LayerSpec):
+    return round_bf16 if spec.bf16 else (lambda v: np.asarray(v, dtype=np.float64))
+
+
+def silu(z):
+    """SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def sigmoid(z):
+    z = np.asarray(z, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+# ---------------------------------------------------------------------------
+# Router: projection, scores, top-k selection, gates
+# ---------------------------------------------------------------------------
+def router_logits(x, w_router, logit_bias=None) -> np.ndarray:
+    """l[t, i] = sum_c x[t, c] * W_r[c, i] + logit_bias[i]   (float64)."""
+    l = np.asarray(x, np.float64) @ np.asarray(w_router, np.float64)
+    if logit_bias is not None:
+        l = l + np.asarray(logit_bias, np.float64)[None, :]
+    return l
+
+
+def router_scores(l, spec: LayerSpec, select_bias=None):
+    """Returns (key, prob, sig).
+
+    key  -- what top-k ranks by: the logit (softmax rule), or sigmoid + selection
+            bias (sigmoid rule);
+    prob -- the full per-token distribution over experts used by the aux
+            statistic: softmax(l), or s / sum(s) for the sigmoid rule;
+    sig  -- sigmoid scores (sigmoid rule) or None.
+    """
+    l = np.asarray(l, np.float64)
+    if spec.score == SOFTMAX:
+        m = l.max(axis=1, keepdims=True)
+        ex = np.exp(l - m)
+        prob = ex / ex.sum(axis=1, keepdims=True)
+        return l.copy(), prob, None
+    if spec.score == SIGMOID:
+        s = sigmoid(l)
+        key = s + (0.0 if select_bias is None else np.asarray(select_bias, np.float64)[None, :])
+        prob = s / s.sum(axis=1, keepdims=True)
+        return key, prob, s
+    raise ValueError(spec.score)
+
+
+def select_topk(key, k):
+    """Experts ordered by descending key, equal keys to the lower id first.
+
+    Returns idx [T, k] and margin [T] = key of the k-th minus key of the
+    (k+1)-th expert (+inf when k == E).
+    """
+    key = np.asarray(key, np.float64)
+    T, E = key.shape
+    order = np.argsort(-key, axis=1, kind="stable")
+    idx = order[:, :k].astype(np.int64)
+    if k < E:
+        rows = np.arange(T)
+        margin = key[rows, order[:, k - 1]] - key[rows, order[:, k]]
+    else:
+        margin = np.full(T, np.inf)
+    return idx, margin
+
+
+def token_gates(t, sel, prob, sig, spec: LayerSpec) -> np.ndarray:
+    """Gate weights of token t's selected experts, in selection order."""
+    sel = np.asarray(sel)
+    if spec.score == SOFTMAX:
+        g = prob[t, sel].astype(np.float64)
+        if spec.renorm:
+            g = g / g.sum()
+        return g
+    s = sig[t, sel].astype(np.float64)
+    return s / s.sum()
+
+
+# ---------------------------------------------------------------------------
+# Dispatch: histogram, capacity, prefix sum, permutation
+# ---------------------------------------------------------------------------
+def dispatch(idx, n_routed, capacity):
+    """Group the T*k slots by expert in token order.
+
+    Visiting tokens in ascending order (and each token's k choices in list
+    order), a slot's position is the number of earlier slots on the same
+    expert. With capacity C > 0 a slot is kept iff its position is below C;
+    capacity 0 keeps every slot. Kept slots of expert e occupy rows
+    offsets[e] + position, offsets being the exclusive prefix sum of the kept
+    counts.
+    """
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    E = n_routed
+    running = [0] * E
+    pos = np.zeros((T, k), np.int64)
+    keep = np.zeros((T, k), bool)
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            p = running[e]
+            running[e] = p + 1
+            pos[t, j] = p
+            keep[t, j] = capacity == 0 or p < capacity
+    counts = np.array(running, np.int64)
+    kept = np.minimum(counts, capacity) if capacity > 0 else counts.copy()
+    offsets = np.zeros(E + 1, np.int64)
+    offsets[1:] = np.cumsum(kept)
+    row_of_slot = np.full((T, k), -1, np.int64)
+    sorted_token = np.full(int(offsets[E]), -1, np.int64)
+    for t in range(T):
+        for j in range(k):
+            if keep[t, j]:
+                row = int(offsets[idx[t, j]] + pos[t, j])
+                row_of_slot[t, j] = row
+                sorted_token[row] = t
+    dropped = ~keep
+    return dict(counts=counts, kept=kept, offsets=offsets, pos=pos,
+                row_of_slot=row_of_slot, sorted_token=sorted_token,
+                dropped=dropped, n_dropped=int(dropped.sum()))
+
+
+# ---------------------------------------------------------------------------
+# Experts
+# ---------------------------------------------------------------------------
+class _Bank:
+    """float64 views of one expert bank, converted lazily per expert."""
+
+    def __init__(self, arr):
+        self.arr = arr
+        self.cache = {}
+
+    def __getitem__(self, e):
+        m = self.cache.get(e)
+        if m is None:
+            m = np.asarray(self.arr[e], np.float64)
+            self.cache[e] = m
+        return m
+
+
+def swiglu(xrow, w_gate, w_up, w_down, rho):
+    """W_down^T applied to rho(SiLU(x W_gate) * (x W_up)) for one token row."""
+    a = xrow @ w_gate
+    b = xrow @ w_up
+    h = rho(silu(a) * b)
+    return h @ w_down
+
+
+def lowrank_apply(v, u, s, vmat, rho):
+    """v W with W = U diag(s) V^T: z = rho((v U) * s), then z V^T."""
+    z = rho((v @ u) * s)
+    return z @ vmat.T
+
+
+def lowrank_swiglu(xrow, f, rho):
+    """SwiGLU expert whose three matrices are each rank-r factorised."""
+    a = lowrank_apply(xrow, f["u_gate"], f["s_gate"], f["v_gate"], rho)
+    b = lowrank_apply(xrow, f["u_up"], f["s_up"], f["v_up"], rho)
+    h = rho(silu(a) * b)
+    return lowrank_apply(h, f["u_down"], f["s_down"], f["v_down"], rho)
+
+
+class Experts:
+    """Routed and shared expert weights of one layer in float64."""
+
+    def __init__(self, weights: dict, spec: LayerSpec):
+        self.spec = spec
+        self.rho = _rho(spec)
+        if spec.rank == 0:
+            self.gate = _Bank(weights["w_gate"])
+            self.up = _Bank(weights["w_up"])
+            self.down = _Bank(weights["w_down"])
+        else:
+            self.lr = {n: _Bank(weights[n]) for n in (
+                "u_gate", "s_gate", "v_gate", "u_up", "s_up", "v_up",
+                "u_down", "s_down", "v_down")}
+        self.S = spec.n_shared
+        if self.S > 0:
+            self.sh = [_Bank(weights["sh_gate"]), _Bank(weights["sh_up"]),
+                       _Bank(weights["sh_down"])]
+
+    def routed(self, xrow, e):
+        if self.spec.rank == 0:
+            return swiglu(xrow, self.gate[e], self.up[e], self.down[e], self.rho)
+        f = {n: b[e] for n, b in self.lr.items()}
+        return lowrank_swiglu(xrow, f, self.rho)
+
+    def shared(self, xrow):
+        out = np.zeros(self.spec.hidden)
+        for s in range(self.S):
+            out = out + swiglu(xrow, self.sh[0][s], self.sh[1][s], self.sh[2][s], self.rho)
+        return out
+
+
+# ---------------------------------------------------------------------------
+# Aux load-balancing statistic
+# ---------------------------------------------------------------------------
+def aux_statistic(counts, prob, T, k, spec: LayerSpec):
+    """f_i = counts_i / (T k) (pre-drop), P_i = mean_t prob[t, i],
+    aux_raw = E * sum_i f_i P_i, aux = aux_coef * aux_raw."""
+    f = np.asarray(counts, np.float64) / float(T * k)
+    P = np.asarray(prob, np.float64).sum(axis=0) / float(T)
+    aux_raw = spec.n_routed * float(np.sum(f * P))
+    return dict(f=f, P=P, aux_raw=aux_raw, aux=spec.aux_coef * aux_raw)
+
+
+# ---------------------------------------------------------------------------
+# The layer
+# ---------------------------------------------------------------------------
+def route(x, w_router, spec: LayerSpec, logit_bias=None, select_bias=None,
+          override_idx=None, override_mask=None):
+    """Router projection, scores, top-k and gates for every token.
+
+    override_idx/override_mask force the selection of the masked tokens (used
+    for near-tie tokens, where either choice is correct); their gates are then
+    computed by the same formulas from the forced set.
+    """
+    l = router_logits(x, w_router, logit_bias)
+    key, prob, sig = router_scores(l, spec, select_bias)
+    idx, margin = select_topk(key, spec.top_k)
+    if override_mask is not None:
+        mask = np.asarray(override_mask, bool)
+        idx = idx.copy()
+        idx[mask] = np.asarray(override_idx)[mask]
+    T = idx.shape[0]
+    gates = np.zeros(idx.shape)
+    for t in range(T):
+        gates[t] = token_gates(t, idx[t], prob, sig, spec)
+    return dict(logits=l, key=key, prob=prob, sig=sig, idx=idx, margin=margin,
+                gates=gates)
+
+
+def layer_forward(x, weights: dict, spec: LayerSpec, tokens=None,
+                  override_idx=None, override_mask=None):
+    """The whole layer. y is evaluated for ``tokens`` (default: all tokens),
+    routing and dispatch for every token (capacity decisions need them all).
+
+    Returns a dict with the router outputs, the dispatch tables, the aux
+    statistic and ``y`` [len(tokens), d] in float64.
+    """
+    x = np.asarray(x)
+    T = x.shape[0]
+    r = route(x, weights["w_router"], spec, weights.get("logit_bias"),
+              weights.get("select_bias"), override_idx, override_mask)
+    dsp = dispatch(r["idx"], spec.n_routed, spec.capacity)
+    aux = aux_statistic(dsp["counts"], r["prob"], T, spec.top_k, spec)
+    experts = Experts(weights, spec)
+    toks = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
+    y = np.zeros((len(toks), spec.hidden))
+    for n, t in enumerate(toks):
+        xrow = np.asarray(x[t], np.float64)
+        acc = experts.shared(xrow) if spec.n_shared > 0 else np.zeros(spec.hidden)
+        for j in range(spec.top_k):
+            if dsp["row_of_slot"][t, j] < 0:
+                continue                      # dropped slot contributes nothing
+            acc = acc + r["gates"][t, j] * experts.routed(xrow, int(r["idx"][t, j]))
+        y[n] = acc
+    out = dict(r)
+    out.update(dsp)
+    out.update(aux)
+    out["tokens"] = toks
+    out["y"] = y
+    return out
