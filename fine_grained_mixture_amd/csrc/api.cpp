@@ -1,0 +1,534 @@
+// C ABI of the MoE layer: argument validation, workspace layout and the
+// sequence of kernel launches. This file launches through the kernel files'
+// launch_* helpers and performs no device-to-host transfer of any kind: every
+// data-dependent size (expert row counts, tile lists) stays on the device.
+
+#include <hip/hip_runtime.h>
+
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+thread_local std::string g_last_error;
+thread_local const char* g_stage_names[64];
+thread_local int g_n_stages = 0;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool valid_config(const moe_config* c) {
+  if (!c) return false;
+  if (c->hidden <= 0 || c->hidden % 64) return false;
+  if (c->ffn <= 0 || c->ffn % 64) return false;
+  if (c->top_k < 1 || c->top_k > 15) return false;
+  if (c->n_routed < c->top_k || c->n_routed > 4096) return false;
+  if (c->n_shared < 0 || c->n_shared > 64) return false;
+  if (c->rank < 0) return false;
+  if (c->score != MOE_SOFTMAX && c->score != MOE_SIGMOID) return false;
+  if (c->score == MOE_SIGMOID && c->renorm_topk != 1) return false;
+  if (c->renorm_topk != 0 && c->renorm_topk != 1) return false;
+  if (c->capacity < 0) return false;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return false;
+  return true;
+}
+
+bool supported_config(const moe_config* c) {
+  if (c->rank != 0) return false;   // low-rank experts: fused kernel below
+  return true;
+}
+
+size_t elem_size(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
+
+int plan_bm(const moe_config* c) { return c->dtype == MOE_F32 ? kGemmBM_F32 : kGemmBM; }
+
+struct Layout {
+  int64_t T = 0, R = 0, nblk = 0, max_tiles = 0;
+  size_t logits = 0, blk_counts = 0, blk_base = 0, blk_psum = 0, plan = 0;
+  size_t h = 0, h_sh = 0, y_perm = 0, y_sh = 0, total = 0;
+};
+
+int64_t max_rows(const moe_config* c, int64_t T) {
+  const int64_t tk = T * c->top_k;
+  if (c->capacity > 0) return std::min<int64_t>(tk, (int64_t)c->n_routed * c->capacity);
+  return tk;
+}
+
+Layout make_layout(const moe_config* c, int64_t T) {
+  Layout L;
+  const int64_t E = c->n_routed, d = c->hidden, F = c->ffn, S = c->n_shared;
+  const size_t es = elem_size(c);
+  L.T = T;
+  L.R = max_rows(c, T);
+  L.nblk = ceil_div(T, kRouteBlock);
+  L.max_tiles = ceil_div(L.R, plan_bm(c)) + E;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.logits = take((size_t)T * E * 4);
+  L.blk_counts = take((size_t)L.nblk * E * 4);
+  L.blk_base = take((size_t)L.nblk * E * 4);
+  L.blk_psum = take((size_t)L.nblk * E * 4);
+  L.plan = take((size_t)(1 + 2 * L.max_tiles) * 4);
+  L.h = take((size_t)L.R * F * es);
+  L.h_sh = take((size_t)T * S * F * es);
+  L.y_perm = take((size_t)L.R * d * 4);
+  L.y_sh = take(S > 0 ? (size_t)T * d * 4 : 0);
+  L.total = off;
+  return L;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<unsigned char*>(ws) + off);
+}
+
+// Launch bookkeeping: optional events before every launch, names for
+// moe_stage_name().
+struct Runner {
+  hipStream_t stream;
+  void** events = nullptr;
+  int n_events = 0;
+  int n = 0;
+  hipError_t err = hipSuccess;
+
+  void stage(const char* name) {
+    if (events && n < n_events) hipEventRecord(static_cast<hipEvent_t>(events[n]), stream);
+    if (n < 64) g_stage_names[n] = name;
+    ++n;
+  }
+  bool check(hipError_t e) {
+    if (e != hipSuccess && err == hipSuccess) err = e;
+    return e == hipSuccess;
+  }
+  void finish() {
+    if (events && n < n_events) hipEventRecord(static_cast<hipEvent_t>(events[n]), stream);
+    g_n_stages = n;
+  }
+};
+
+int hip_fail(hipError_t e) {
+  g_last_error = hipGetErrorString(e);
+  return MOE_EHIP;
+}
+
+int check_ws(const moe_config* c, int64_t T, void* ws, size_t ws_bytes, Layout& L) {
+  L = make_layout(c, T);
+  if (L.total > 0 && !ws) return MOE_EWORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOE_EWORKSPACE;
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  return MOE_OK;
+}
+
+int check_common(const moe_config* c, int64_t T) {
+  if (!valid_config(c)) return MOE_EINVAL;
+  if (T < 0 || T * c->top_k >= ((int64_t)1 << 31)) return MOE_EINVAL;
+  if (max_rows(c, T) * std::max(c->hidden, c->ffn) >= ((int64_t)1 << 40)) return MOE_EINVAL;
+  if (!supported_config(c)) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+// Per-token arrays may be NULL when T == 0 (empty tensors have no storage).
+bool route_outputs_ok(const moe_outputs* o, int64_t T) {
+  return o && o->counts && o->kept && o->offsets && o->n_dropped && o->aux &&
+         (T == 0 || (o->topk_idx && o->topk_gate));
+}
+bool permute_outputs_ok(const moe_outputs* o, int64_t T) {
+  return o && (T == 0 || (o->row_of_slot && o->sorted_token));
+}
+bool expert_weights_ok(const moe_config* c, const moe_weights* w, bool routed, bool shared) {
+  if (!w) return false;
+  if (routed) {
+    if (c->rank == 0) {
+      if (!w->w_gate || !w->w_up || !w->w_down) return false;
+    } else {
+      if (!w->u_gate || !w->s_gate || !w->v_gate || !w->u_up || !w->s_up || !w->v_up ||
+          !w->u_down || !w->s_down || !w->v_down)
+        return false;
+    }
+  }
+  if (shared && c->n_shared > 0 && (!w->sh_gate || !w->sh_up || !w->sh_down)) return false;
+  return true;
+}
+
+// ---- stage bodies (no validation) ------------------------------------------
+void run_route(Runner& R, const moe_config* c, const Layout& L, const void* x,
+               const moe_weights* w, moe_outputs* o, void* ws, bool with_plan) {
+  const int64_t T = L.T;
+  const int E = c->n_routed;
+  float* logits = at<float>(ws, L.logits);
+  if (T > 0) {
+    GemmLaunch G{};
+    GemmProblem& p = G.p[0];
+    p.A = x;
+    p.lda = c->hidden;
+    p.B0 = w->w_router;
+    p.ldb = E;
+    p.C = logits;
+    p.ldc = E;
+    p.col_bias = w->logit_bias;
+    p.M = (int32_t)T;
+    p.N = E;
+    p.K = c->hidden;
+    p.G = 1;
+    const int bn = c->dtype == MOE_BF16 ? 128 : 64;
+    const int bm = c->dtype == MOE_BF16 ? kGemmBM : kGemmBM_F32;
+    p.n_tiles_n = (int32_t)ceil_div(E, bn);
+    p.max_m_tiles = (int32_t)ceil_div(T, bm);
+    G.n_problems = 1;
+    G.tiles0 = p.max_m_tiles * p.n_tiles_n;
+    R.stage("router_gemm");
+    R.check(c->dtype == MOE_BF16 ? launch_gemm_bf16(G, kEpiStoreF32, R.stream)
+                                 : launch_gemm_f32(G, kEpiStoreF32, R.stream));
+
+    TopkArgs t{};
+    t.logits = logits;
+    t.select_bias = c->score == MOE_SIGMOID ? w->select_bias : nullptr;
+    t.topk_idx = o->topk_idx;
+    t.topk_gate = o->topk_gate;
+    t.topk_margin = o->topk_margin;
+    t.blk_counts = at<int32_t>(ws, L.blk_counts);
+    t.blk_psum = at<float>(ws, L.blk_psum);
+    t.T = T;
+    t.E = E;
+    t.k = c->top_k;
+    t.score = c->score;
+    t.renorm = c->renorm_topk;
+    R.stage("topk");
+    R.check(launch_topk(t, R.stream));
+  }
+  ScanArgs s{};
+  s.blk_counts = at<int32_t>(ws, L.blk_counts);
+  s.blk_psum = at<float>(ws, L.blk_psum);
+  s.blk_base = at<int32_t>(ws, L.blk_base);
+  s.counts = o->counts;
+  s.kept = o->kept;
+  s.offsets = o->offsets;
+  s.n_dropped = o->n_dropped;
+  s.aux = o->aux;
+  s.f = o->f;
+  s.P = o->P;
+  s.plan = with_plan ? at<int32_t>(ws, L.plan) : nullptr;
+  s.plan_bm = plan_bm(c);
+  s.nblk = (int32_t)L.nblk;
+  s.E = E;
+  s.k = c->top_k;
+  s.capacity = c->capacity;
+  s.T = T;
+  s.aux_coef = c->aux_coef;
+  R.stage("scan");
+  R.check(launch_scan(s, R.stream));
+}
+
+void run_rank(Runner& R, const moe_config* c, const Layout& L, moe_outputs* o, void* ws) {
+  if (L.T == 0) return;
+  RankArgs r{};
+  r.topk_idx = o->topk_idx;
+  r.blk_base = at<int32_t>(ws, L.blk_base);
+  r.offsets = o->offsets;
+  r.row_of_slot = o->row_of_slot;
+  r.sorted_token = o->sorted_token;
+  r.dropped = o->dropped;
+  r.T = L.T;
+  r.E = c->n_routed;
+  r.k = c->top_k;
+  r.capacity = c->capacity;
+  r.nblk = (int32_t)L.nblk;
+  R.stage("rank");
+  R.check(launch_rank(r, R.stream));
+}
+
+// Expert FFN launches. Routed rows: A = a_routed with optional row gather;
+// shared rows: A = a_shared (T rows).
+void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool shared,
+             const void* a_routed, const int32_t* a_rows, const int32_t* offsets,
+             const void* a_shared, const moe_weights* w, float* y_routed, float* y_shared,
+             void* ws) {
+  const int64_t T = L.T, d = c->hidden, F = c->ffn, S = c->n_shared;
+  const bool bf = c->dtype == MOE_BF16;
+  const int bm = plan_bm(c);
+  const int bn_dual = 64, bn = bf ? 128 : 64;
+  shared = shared && S > 0 && T > 0;
+  routed = routed && L.R > 0;
+  if (!routed && !shared) return;
+  void* h = at<void>(ws, L.h);
+  void* h_sh = at<void>(ws, L.h_sh);
+  const int32_t* plan = at<int32_t>(ws, L.plan);
+
+  auto launch = [&](const GemmLaunch& G, int epi, const char* name) {
+    R.stage(name);
+    R.check(bf ? launch_gemm_bf16(G, epi, R.stream) : launch_gemm_f32(G, epi, R.stream));
+  };
+
+  // gate/up with fused SiLU * up
+  {
+    GemmLaunch G{};
+    int np = 0;
+    if (shared) {
+      GemmProblem& p = G.p[np++];
+      p.A = a_shared;
+      p.lda = d;
+      p.B0 = w->sh_gate;
+      p.B1 = w->sh_up;
+      p.b_group_stride = d * F;
+      p.ldb = F;
+      p.C = h_sh;
+      p.ldc = S * F;
+      p.c_group_col = F;
+      p.M = (int32_t)T;
+      p.N = (int32_t)F;
+      p.K = (int32_t)d;
+      p.G = (int32_t)S;
+      p.n_tiles_n = (int32_t)(F / (bf ? bn_dual : 64));
+      p.max_m_tiles = (int32_t)(S * ceil_div(T, bm));
+    }
+    if (routed) {
+      GemmProblem& p = G.p[np++];
+      p.A = a_routed;
+      p.a_rows = a_rows;
+      p.lda = d;
+      p.B0 = w->w_gate;
+      p.B1 = w->w_up;
+      p.b_group_stride = d * F;
+      p.ldb = F;
+      p.C = h;
+      p.ldc = F;
+      p.row_off = offsets;
+      p.plan = plan;
+      p.N = (int32_t)F;
+      p.K = (int32_t)d;
+      p.G = c->n_routed;
+      p.n_tiles_n = (int32_t)(F / (bf ? bn_dual : 64));
+      p.max_m_tiles = (int32_t)L.max_tiles;
+    }
+    G.n_problems = np;
+    G.tiles0 = G.p[0].max_m_tiles * G.p[0].n_tiles_n;
+    launch(G, kEpiSwiGLU, "gate_up_gemm");
+  }
+  // down projection
+  {
+    GemmLaunch G{};
+    int np = 0;
+    if (shared) {
+      GemmProblem& p = G.p[np++];
+      p.A = h_sh;
+      p.lda = S * F;
+      p.B0 = w->sh_down;        // [S, F, d] read as [S*F, d]: the S experts summed
+      p.ldb = d;
+      p.C = y_shared;
+      p.ldc = d;
+      p.M = (int32_t)T;
+      p.N = (int32_t)d;
+      p.K = (int32_t)(S * F);
+      p.G = 1;
+      p.n_tiles_n = (int32_t)ceil_div(d, bn);
+      p.max_m_tiles = (int32_t)ceil_div(T, bm);
+    }
+    if (routed) {
+      GemmProblem& p = G.p[np++];
+      p.A = h;
+      p.lda = F;
+      p.B0 = w->w_down;
+      p.b_group_stride = F * d;
+      p.ldb = d;
+      p.C = y_routed;
+      p.ldc = d;
+      p.row_off = offsets;
+      p.plan = plan;
+      p.N = (int32_t)d;
+      p.K = (int32_t)F;
+      p.G = c->n_routed;
+      p.n_tiles_n = (int32_t)ceil_div(d, bn);
+      p.max_m_tiles = (int32_t)L.max_tiles;
+    }
+    G.n_problems = np;
+    G.tiles0 = G.p[0].max_m_tiles * G.p[0].n_tiles_n;
+    launch(G, kEpiStoreF32, "down_gemm");
+  }
+}
+
+void run_combine(Runner& R, const moe_config* c, int64_t T, const float* y_routed,
+                 const float* y_shared, moe_outputs* o) {
+  if (T == 0) return;
+  CombineArgs a{};
+  a.y_routed = y_routed;
+  a.y_shared = y_shared;
+  a.row_of_slot = o->row_of_slot;
+  a.topk_gate = o->topk_gate;
+  a.y = o->y;
+  a.y_lowp = o->y_lowp;
+  a.T = T;
+  a.d = c->hidden;
+  a.k = c->top_k;
+  a.dtype = c->dtype;
+  R.stage("combine");
+  R.check(launch_combine(a, R.stream));
+}
+
+int finish(Runner& R) {
+  R.finish();
+  if (R.err != hipSuccess) return hip_fail(R.err);
+  return MOE_OK;
+}
+
+int layer_forward(const moe_config* c, int64_t T, const void* x, const moe_weights* w,
+                  moe_outputs* o, void* ws, size_t ws_bytes, void* stream, void** events,
+                  int n_events) {
+  int st = check_common(c, T);
+  if (st) return st;
+  if (!x && T > 0) return MOE_EINVAL;
+  if (!w || !w->w_router || !expert_weights_ok(c, w, true, true)) return MOE_EINVAL;
+  if (c->score == MOE_SOFTMAX && w->select_bias) return MOE_EINVAL;
+  if (!route_outputs_ok(o, T) || !permute_outputs_ok(o, T) || (T > 0 && !o->y))
+    return MOE_EINVAL;
+  Layout L;
+  if ((st = check_ws(c, T, ws, ws_bytes, L))) return st;
+  Runner R{static_cast<hipStream_t>(stream), events, n_events};
+  run_route(R, c, L, x, w, o, ws, true);
+  run_rank(R, c, L, o, ws);
+  float* y_perm = at<float>(ws, L.y_perm);
+  float* y_sh = c->n_shared > 0 ? at<float>(ws, L.y_sh) : nullptr;
+  run_ffn(R, c, L, true, true, x, o->sorted_token, o->offsets, x, w, y_perm, y_sh, ws);
+  run_combine(R, c, T, y_perm, y_sh, o);
+  st = finish(R);
+  return st ? st : R.n;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int32_t moe_capacity(int64_t num, int64_t den, int64_t T, int32_t k, int32_t E) {
+  if (num <= 0 || den <= 0 || T < 0 || k <= 0 || E <= 0) return -1;
+  const __int128 n = (__int128)num * T * k;
+  const __int128 q = (__int128)den * E;
+  const __int128 c = (n + q - 1) / q;
+  if (c > INT32_MAX) return -1;
+  return (int32_t)c;
+}
+
+int64_t moe_max_rows(const moe_config* cfg, int64_t T) {
+  if (!valid_config(cfg) || T < 0) return -1;
+  return max_rows(cfg, T);
+}
+
+size_t moe_workspace_bytes(const moe_config* cfg, int64_t T) {
+  if (!valid_config(cfg) || T < 0) return 0;
+  return make_layout(cfg, T).total;
+}
+
+int moe_route(const moe_config* c, int64_t T, const void* x, const moe_weights* w,
+              moe_outputs* o, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_common(c, T);
+  if (st) return st;
+  if ((!x && T > 0) || !w || !w->w_router || !route_outputs_ok(o, T)) return MOE_EINVAL;
+  if (c->score == MOE_SOFTMAX && w->select_bias) return MOE_EINVAL;
+  Layout L;
+  if ((st = check_ws(c, T, ws, ws_bytes, L))) return st;
+  Runner R{static_cast<hipStream_t>(stream)};
+  run_route(R, c, L, x, w, o, ws, false);
+  return finish(R);
+}
+
+int moe_permute(const moe_config* c, int64_t T, const void* x, moe_outputs* o, void* x_perm,
+                void* ws, size_t ws_bytes, void* stream) {
+  int st = check_common(c, T);
+  if (st) return st;
+  if (!o || !o->offsets || !permute_outputs_ok(o, T) || (T > 0 && !o->topk_idx))
+    return MOE_EINVAL;
+  if (x_perm && !x && T > 0) return MOE_EINVAL;
+  Layout L;
+  if ((st = check_ws(c, T, ws, ws_bytes, L))) return st;
+  Runner R{static_cast<hipStream_t>(stream)};
+  run_rank(R, c, L, o, ws);
+  if (x_perm && L.R > 0) {
+    R.stage("gather");
+    R.check(launch_gather(x, o->sorted_token, o->offsets, c->n_routed, L.R,
+                          (int64_t)c->hidden * elem_size(c), x_perm, R.stream));
+  }
+  return finish(R);
+}
+
+int moe_grouped_ffn(const moe_config* c, int64_t T, int32_t groups, const void* x_perm,
+                    const int32_t* offsets, const void* x_shared, const moe_weights* w,
+                    float* y_routed, float* y_shared, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_common(c, T);
+  if (st) return st;
+  if (groups & ~(MOE_GROUPS_ROUTED | MOE_GROUPS_SHARED)) return MOE_EINVAL;
+  const bool routed = groups & MOE_GROUPS_ROUTED;
+  const bool shared = (groups & MOE_GROUPS_SHARED) && c->n_shared > 0;
+  if (!expert_weights_ok(c, w, routed, shared)) return MOE_EINVAL;
+  if (routed && (!x_perm || !offsets || !y_routed)) return MOE_EINVAL;
+  if (shared && T > 0 && (!x_shared || !y_shared)) return MOE_EINVAL;
+  Layout L;
+  if ((st = check_ws(c, T, ws, ws_bytes, L))) return st;
+  Runner R{static_cast<hipStream_t>(stream)};
+  if (routed && L.R > 0) {
+    R.stage("plan");
+    R.check(launch_plan(offsets, c->n_routed, plan_bm(c), at<int32_t>(ws, L.plan), R.stream));
+  }
+  run_ffn(R, c, L, routed, shared, x_perm, nullptr, offsets, x_shared, w, y_routed, y_shared,
+          ws);
+  return finish(R);
+}
+
+int moe_combine(const moe_config* c, int64_t T, const float* y_routed, const float* y_shared,
+                moe_outputs* o, void* stream) {
+  int st = check_common(c, T);
+  if (st) return st;
+  if (!o || (T > 0 && (!o->row_of_slot || !o->topk_gate || !o->y))) return MOE_EINVAL;
+  if (T > 0 && !y_routed) return MOE_EINVAL;
+  if (c->n_shared > 0 && T > 0 && !y_shared) return MOE_EINVAL;
+  Runner R{static_cast<hipStream_t>(stream)};
+  run_combine(R, c, T, y_routed, c->n_shared > 0 ? y_shared : nullptr, o);
+  return finish(R);
+}
+
+int moe_layer_forward(const moe_config* c, int64_t T, const void* x, const moe_weights* w,
+                      moe_outputs* o, void* ws, size_t ws_bytes, void* stream) {
+  const int r = layer_forward(c, T, x, w, o, ws, ws_bytes, stream, nullptr, 0);
+  return r < 0 ? r : MOE_OK;
+}
+
+int moe_layer_forward_timed(const moe_config* c, int64_t T, const void* x, const moe_weights* w,
+                            moe_outputs* o, void* ws, size_t ws_bytes, void* stream,
+                            void** events, int n_events) {
+  if (n_events < 0 || (n_events > 0 && !events)) return MOE_EINVAL;
+  return layer_forward(c, T, x, w, o, ws, ws_bytes, stream, events, n_events);
+}
+
+const char* moe_stage_name(int i) {
+  if (i < 0 || i >= g_n_stages || i >= 64) return nullptr;
+  return g_stage_names[i];
+}
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "configuration not supported by this build";
+    case MOE_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case MOE_EHIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// Device-side helpers for the MoE kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // raw bf16 bits in memory
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// Round-to-nearest-even float32 -> bf16 (NaN kept quiet).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float load_elem(const float* p) { return *p; }
+__device__ __forceinline__ float load_elem(const bf16_t* p) { return bf16_to_f32(*p); }
+
+__device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_elem(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+// Monotone map of a float onto uint32 (larger float -> larger integer).
+__device__ __forceinline__ uint32_t float_orderable(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float orderable_float(uint32_t o) {
+  uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+  return __uint_as_float(u);
+}
+
+// (key, id) packed into one integer: a larger packed value means a larger key,
+// and among equal keys the lower expert id.
+__device__ __forceinline__ uint64_t pack_key_id(float key, int id) {
+  return (static_cast<uint64_t>(float_orderable(key)) << 32) |
+         static_cast<uint64_t>(0xffffffffu - static_cast<uint32_t>(id));
+}
+__device__ __forceinline__ int packed_id(uint64_t p) {
+  return static_cast<int>(0xffffffffu - static_cast<uint32_t>(p & 0xffffffffu));
+}
+__device__ __forceinline__ float packed_key(uint64_t p) {
+  return orderable_float(static_cast<uint32_t>(p >> 32));
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+  lo = __shfl_xor(lo, mask, kWave);
+  hi = __shfl_xor(hi, mask, kWave);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    uint64_t o = shfl_xor_u64(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Butterfly sums: every lane ends with the same value, combined in a fixed
+// order, so the result does not depend on scheduling.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Bits of a wave ballot below this lane.
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+}  // namespace moe

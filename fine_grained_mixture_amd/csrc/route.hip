@@ -1,0 +1,473 @@
+// Routing and dispatch kernels of the MoE layer on gfx950.
+//
+//   topk   : scores, top-k selection, gates, per-block expert histogram and
+//            per-block sums of the routing probabilities (router top-k of the
+//            Quartz model card Architecture table; sigmoid scoring with a
+//            balancing bias on the Sutra-1.3B "48 + 1 experts" card)
+//   scan   : per-expert totals, capacity, exclusive prefix sums (dropless or
+//            capacity routing: dormouse "dropless MoE" card, Moonfrost stacking
+//            card), aux statistic (0.01-weighted balancing loss, research page
+//            Architecture), and the grouped-GEMM tile list
+//   rank   : each slot's position in its expert's token-ordered queue, drops,
+//            row_of_slot and sorted_token
+//   gather : x_perm[row] = x[sorted_token[row]]
+//
+// Nothing here uses floating-point atomics: every sum is taken in a fixed
+// order, so routing outputs and the aux statistic are bitwise reproducible.
+
+#include <float.h>
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+// ---------------------------------------------------------------------------
+// top-k: one wave per token (16 tokens per wave, 4 waves = one 64-token block
+// per workgroup). Lane l owns experts l, l + 64, ...; each lane keeps its best
+// KMAX (key, id) pairs, then k+1 rounds of a wave-wide maximum pick the
+// winners in descending key order (equal keys: lower id first).
+// ---------------------------------------------------------------------------
+template <int EPL, int KMAX>
+__global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  int* s_cnt = reinterpret_cast<int*>(smem_raw);                 // [E]
+  float* s_ps = reinterpret_cast<float*>(smem_raw) + a.E;        // [E]
+
+  const int E = a.E, k = a.k;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int blk = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    s_cnt[e] = 0;
+    s_ps[e] = 0.f;
+  }
+  __syncthreads();
+
+  float psum[EPL];
+#pragma unroll
+  for (int m = 0; m < EPL; ++m) psum[m] = 0.f;
+
+  const int rounds = min(k + 1, E);
+  const int64_t t_begin = (int64_t)blk * kRouteBlock + wave * (kRouteBlock / 4);
+  for (int it = 0; it < kRouteBlock / 4; ++it) {
+    const int64_t t = t_begin + it;
+    if (t >= a.T) break;
+    const float* lrow = a.logits + t * E;
+
+    float l[EPL], key[EPL], sg[EPL];
+#pragma unroll
+    for (int m = 0; m < EPL; ++m) {
+      const int e = lane + 64 * m;
+      const bool ok = e < E;
+      l[m] = ok ? lrow[e] : -FLT_MAX;
+      if (a.score == MOE_SOFTMAX) {
+        key[m] = l[m];
+        sg[m] = 0.f;
+      } else {
+        sg[m] = ok ? 1.0f / (1.0f + __expf(-l[m])) : 0.f;
+        key[m] = sg[m] + ((ok && a.select_bias) ? a.select_bias[e] : 0.f);
+      }
+    }
+
+    // lane-local best KMAX candidates, descending
+    uint64_t cand[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) cand[i] = 0;
+#pragma unroll
+    for (int m = 0; m < EPL; ++m) {
+      const int e = lane + 64 * m;
+      if (e < E) {
+        uint64_t c = pack_key_id(key[m], e);
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i) {
+          const uint64_t hi = cand[i] > c ? cand[i] : c;
+          c = cand[i] > c ? c : cand[i];
+          cand[i] = hi;
+        }
+      }
+    }
+    // k+1 rounds of wave-wide maximum
+    int sel_id[KMAX];
+    float sel_key[KMAX];
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r) {
+      sel_id[r] = 0;
+      sel_key[r] = 0.f;
+      if (r < rounds) {
+        const uint64_t mx = wave_max_u64(cand[0]);
+        if (cand[0] == mx) {
+#pragma unroll
+          for (int i = 0; i < KMAX - 1; ++i) cand[i] = cand[i + 1];
+          cand[KMAX - 1] = 0;
+        }
+        sel_id[r] = packed_id(mx);
+        sel_key[r] = packed_key(mx);
+      }
+    }
+
+    // gates and routing probabilities
+    float my_gate = 0.f;
+    int my_id = 0;
+    if (a.score == MOE_SOFTMAX) {
+      const float mxl = sel_key[0];
+      float se = 0.f;
+#pragma unroll
+      for (int m = 0; m < EPL; ++m) se += (lane + 64 * m < E) ? __expf(l[m] - mxl) : 0.f;
+      se = wave_sum(se);
+      const float inv = 1.0f / se;
+#pragma unroll
+      for (int m = 0; m < EPL; ++m)
+        if (lane + 64 * m < E) psum[m] += __expf(l[m] - mxl) * inv;
+      float ssel = 0.f;
+#pragma unroll
+      for (int r = 0; r < KMAX; ++r)
+        if (r < k) ssel += __expf(sel_key[r] - mxl);
+      const float denom = a.renorm ? ssel : se;
+#pragma unroll
+      for (int r = 0; r < KMAX; ++r)
+        if (r < k && lane == r) {
+          my_id = sel_id[r];
+          my_gate = __expf(sel_key[r] - mxl) / denom;
+        }
+    } else {
+      float ss = 0.f;
+#pragma unroll
+      for (int m = 0; m < EPL; ++m) ss += sg[m];
+      ss = wave_sum(ss);
+      const float inv = 1.0f / ss;
+#pragma unroll
+      for (int m = 0; m < EPL; ++m)
+        if (lane + 64 * m < E) psum[m] += sg[m] * inv;
+      // sigmoid scores of the winners, recomputed from their logits (the key
+      // also carries the selection bias, which must not reach the gates)
+      float ssel = 0.f, mine = 0.f;
+#pragma unroll
+      for (int r = 0; r < KMAX; ++r)
+        if (r < k) {
+          const float s = 1.0f / (1.0f + __expf(-lrow[sel_id[r]]));
+          ssel += s;
+          if (lane == r) {
+            mine = s;
+            my_id = sel_id[r];
+          }
+        }
+      my_gate = mine / ssel;
+    }
+    if (lane < k) {
+      a.topk_idx[t * k + lane] = my_id;
+      a.topk_gate[t * k + lane] = my_gate;
+      atomicAdd(&s_cnt[my_id], 1);
+    }
+    if (lane == 0 && a.topk_margin) {
+      float mg = FLT_MAX;
+#pragma unroll
+      for (int r = 1; r < KMAX; ++r)
+        if (r == k && k < E) mg = sel_key[r - 1] - sel_key[r];
+      a.topk_margin[t] = k < E ? mg : __int_as_float(0x7f800000);
+    }
+  }
+
+  // per-block probability sums: waves add into LDS one after another
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int m = 0; m < EPL; ++m) {
+        const int e = lane + 64 * m;
+        if (e < E) s_ps[e] += psum[m];
+      }
+    }
+    __syncthreads();
+  }
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    a.blk_counts[(int64_t)blk * E + e] = s_cnt[e];
+    a.blk_psum[(int64_t)blk * E + e] = s_ps[e];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// scan: one workgroup of 1024 threads.
+// ---------------------------------------------------------------------------
+__device__ int block_scan_excl(int v, int* smem, int& total) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += n;
+  }
+  if (lane == 63) smem[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    const int w = lane < nw ? smem[lane] : 0;
+    int wi = w;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int n = __shfl_up(wi, o, 64);
+      if (lane >= o) wi += n;
+    }
+    if (lane < nw) smem[lane] = wi;
+  }
+  __syncthreads();
+  const int base = wave > 0 ? smem[wave - 1] : 0;
+  total = smem[nw - 1];
+  __syncthreads();
+  return base + incl - v;
+}
+
+// Sum over the workgroup in a fixed order (lane butterfly, then waves in order).
+__device__ double block_sum_fixed(double v, double* smem) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  if (lane == 0) smem[wave] = v;
+  __syncthreads();
+  double tot = 0.0;
+  for (int w = 0; w < nw; ++w) tot += smem[w];
+  __syncthreads();
+  return tot;
+}
+
+constexpr int kScanRG = 16;   // row groups (block ranges) per 64-expert column chunk
+
+__global__ void __launch_bounds__(1024) scan_kernel(ScanArgs a) {
+  __shared__ int s_part[kScanRG][64];
+  __shared__ float s_fpart[kScanRG][64];
+  __shared__ int s_i[16];
+  __shared__ double s_d[16];
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  int* s_cnt = reinterpret_cast<int*>(smem_raw);                  // [E]
+  float* s_P = reinterpret_cast<float*>(smem_raw) + a.E;          // [E]
+
+  const int E = a.E, nblk = a.nblk;
+  const int tid = threadIdx.x;
+  const int rg = tid >> 6, cl = tid & 63;
+  const int per = (nblk + kScanRG - 1) / kScanRG;
+  const int b0 = rg * per, b1 = min(nblk, b0 + per);
+
+  // 1) per-expert totals and block prefix (token order across blocks)
+  for (int c0 = 0; c0 < E; c0 += 64) {
+    const int e = c0 + cl;
+    int cs = 0;
+    float ps = 0.f;
+    if (e < E) {
+      for (int b = b0; b < b1; ++b) {
+        cs += a.blk_counts[(int64_t)b * E + e];
+        ps += a.blk_psum[(int64_t)b * E + e];
+      }
+    }
+    s_part[rg][cl] = cs;
+    s_fpart[rg][cl] = ps;
+    __syncthreads();
+    if (rg == 0 && e < E) {
+      int run = 0;
+      float pr = 0.f;
+      for (int g = 0; g < kScanRG; ++g) {
+        const int c = s_part[g][cl];
+        s_part[g][cl] = run;
+        run += c;
+        pr += s_fpart[g][cl];
+      }
+      s_cnt[e] = run;
+      s_P[e] = pr;
+    }
+    __syncthreads();
+    if (e < E) {
+      int run = s_part[rg][cl];
+      for (int b = b0; b < b1; ++b) {
+        a.blk_base[(int64_t)b * E + e] = run;
+        run += a.blk_counts[(int64_t)b * E + e];
+      }
+    }
+    __syncthreads();
+  }
+
+  // 2) capacity, prefix sum of kept counts, drops
+  const int epT = (E + blockDim.x - 1) / blockDim.x;
+  const int e0 = tid * epT;
+  int local_kept = 0, local_drop = 0;
+  for (int e = e0; e < min(E, e0 + epT); ++e) {
+    const int c = s_cnt[e];
+    const int kp = a.capacity > 0 ? min(c, a.capacity) : c;
+    local_kept += kp;
+    local_drop += c - kp;
+  }
+  int total_kept;
+  const int row_start = block_scan_excl(local_kept, s_i, total_kept);
+  int total_drop;
+  (void)block_scan_excl(local_drop, s_i, total_drop);
+  int pos = row_start;
+  for (int e = e0; e < min(E, e0 + epT); ++e) {
+    const int c = s_cnt[e];
+    const int kp = a.capacity > 0 ? min(c, a.capacity) : c;
+    a.counts[e] = c;
+    a.kept[e] = kp;
+    a.offsets[e] = pos;
+    pos += kp;
+  }
+  if (tid == 0) {
+    a.offsets[E] = total_kept;
+    a.n_dropped[0] = total_drop;
+  }
+
+  // 3) aux statistic: f_i = counts_i / (T k), P_i = psum_i / T
+  const double Tk = (double)a.T * a.k;
+  double part = 0.0;
+  for (int e = e0; e < min(E, e0 + epT); ++e) {
+    const double fe = a.T > 0 ? (double)s_cnt[e] / Tk : 0.0;
+    const double Pe = a.T > 0 ? (double)s_P[e] / (double)a.T : 0.0;
+    part += fe * Pe;
+    if (a.f) a.f[e] = (float)fe;
+    if (a.P) a.P[e] = (float)Pe;
+  }
+  const double tot = block_sum_fixed(part, s_d);
+  if (tid == 0) {
+    const double raw = (double)E * tot;
+    a.aux[0] = (float)raw;
+    a.aux[1] = (float)(a.aux_coef * raw);
+  }
+
+  // 4) tile list of the routed grouped GEMM: ceil(kept / plan_bm) M-tiles per
+  //    expert, (expert, first row) in expert order
+  if (a.plan) {
+    int local = 0;
+    for (int e = e0; e < min(E, e0 + epT); ++e) {
+      const int c = s_cnt[e];
+      const int kp = a.capacity > 0 ? min(c, a.capacity) : c;
+      local += (kp + a.plan_bm - 1) / a.plan_bm;
+    }
+    int total;
+    int tp = block_scan_excl(local, s_i, total);
+    int row = row_start;
+    for (int e = e0; e < min(E, e0 + epT); ++e) {
+      const int c = s_cnt[e];
+      const int kp = a.capacity > 0 ? min(c, a.capacity) : c;
+      for (int r = 0; r < kp; r += a.plan_bm) {
+        a.plan[1 + 2 * tp] = e;
+        a.plan[2 + 2 * tp] = row + r;
+        ++tp;
+      }
+      row += kp;
+    }
+    if (tid == 0) a.plan[0] = total;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// rank: one wave per 64-token block, 4 blocks per workgroup. Slots are visited
+// in token order (t, then j) 64 at a time; lanes holding the same expert are
+// found with ballots over the id bits, and each lane's position is the
+// expert's running count plus the number of lower lanes with that expert.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) rank_kernel(RankArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  const int E = a.E, k = a.k;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  int* cnt = reinterpret_cast<int*>(smem_raw) + wave * E;
+  const int b = blockIdx.x * 4 + wave;
+  if (b >= a.nblk) return;
+  for (int e = lane; e < E; e += 64) cnt[e] = a.blk_base[(int64_t)b * E + e];
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+
+  const int64_t s_begin = (int64_t)b * kRouteBlock * k;
+  const int64_t s_end = min(a.T, (int64_t)(b + 1) * kRouteBlock) * k;
+  const uint64_t lt = lanemask_lt();
+  for (int64_t base = s_begin; base < s_end; base += 64) {
+    const int64_t s = base + lane;
+    const bool valid = s < s_end;
+    const int e = valid ? a.topk_idx[s] : 0;
+    uint64_t match = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool on = (e >> bit) & 1;
+      const uint64_t bb = __ballot(valid && on);
+      match &= on ? bb : ~bb;
+    }
+    const int rank = __popcll(match & lt);
+    const int total = __popcll(match);
+    int pos = 0;
+    if (valid) pos = cnt[e] + rank;
+    __builtin_amdgcn_wave_barrier();
+    if (valid && rank == 0) cnt[e] = pos + total;
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      const bool keep = a.capacity == 0 || pos < a.capacity;
+      const int row = keep ? a.offsets[e] + pos : -1;
+      a.row_of_slot[s] = row;
+      if (keep) a.sorted_token[row] = (int32_t)(s / k);
+      if (a.dropped) a.dropped[s] = keep ? 0 : 1;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// gather: one wave per row, 16-byte lane copies.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) gather_kernel(const unsigned char* x,
+                                                     const int32_t* sorted_token,
+                                                     const int32_t* offsets, int E,
+                                                     int64_t row_bytes, unsigned char* out) {
+  const int64_t rows = offsets[E];
+  const int lane = lane_id();
+  const int64_t nchunk = row_bytes >> 4;
+  for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < rows;
+       r += (int64_t)gridDim.x * 4) {
+    const int64_t t = sorted_token[r];
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + t * row_bytes);
+    u32x4* dst = reinterpret_cast<u32x4*>(out + r * row_bytes);
+    for (int64_t c = lane; c < nchunk; c += 64) dst[c] = src[c];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
+  const int nblk = (int)((a.T + kRouteBlock - 1) / kRouteBlock);
+  if (nblk == 0) return hipSuccess;
+  const size_t shm = (size_t)a.E * 8;
+  const int epl = (a.E + 63) / 64;
+  const int k1 = a.k + 1;
+#define MOE_TOPK(EPLV, KM)                                                                  \
+  hipLaunchKernelGGL((topk_kernel<EPLV, KM>), dim3(nblk), dim3(256), shm, s, a)
+#define MOE_TOPK_K(EPLV)                \
+  do {                                  \
+    if (k1 <= 4) MOE_TOPK(EPLV, 4);     \
+    else if (k1 <= 8) MOE_TOPK(EPLV, 8); \
+    else MOE_TOPK(EPLV, 16);            \
+  } while (0)
+  if (epl <= 1) MOE_TOPK_K(1);
+  else if (epl <= 2) MOE_TOPK_K(2);
+  else if (epl <= 4) MOE_TOPK_K(4);
+  else if (epl <= 8) MOE_TOPK_K(8);
+  else if (epl <= 16) MOE_TOPK_K(16);
+  else if (epl <= 32) MOE_TOPK_K(32);
+  else MOE_TOPK_K(64);
+#undef MOE_TOPK_K
+#undef MOE_TOPK
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), (size_t)a.E * 8, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rank(const RankArgs& a, hipStream_t s) {
+  if (a.nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL(rank_kernel, dim3((a.nblk + 3) / 4), dim3(256), (size_t)a.E * 16, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const void* x, const int32_t* sorted_token, const int32_t* offsets,
+                         int32_t E, int64_t r_max, int64_t row_bytes, void* x_perm,
+                         hipStream_t s) {
+  if (r_max == 0) return hipSuccess;
+  int64_t grid = (r_max + 3) / 4;
+  if (grid > 8192) grid = 8192;
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)grid), dim3(256), 0, s,
+                     static_cast<const unsigned char*>(x), sorted_token, offsets, E, row_bytes,
+                     static_cast<unsigned char*>(x_perm));
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,195 @@
+/*
+ * moe.h -- C ABI of the fine-grained mixture-of-experts feed-forward layer,
+ * built from hand-written HIP kernels for MI355X (gfx950, CDNA4).
+ *
+ * The layer (DeepSeek-style fine-grained MoE, as on the Vertex AGI research
+ * page "Architecture" section, the Quartz Micro Preview Base model card
+ * "Architecture" table, the Moonfrost site MoE and stacking cards, the
+ * Sutra-1.3B "48 + 1 experts" card and the dormouse "dropless MoE" and
+ * "TSCT low-rank experts" cards), for T tokens x[T,d]:
+ *
+ *   l    = x W_r + logit_bias                       router projection
+ *   key  = l (softmax rule)  |  sigmoid(l) + select_bias (sigmoid rule)
+ *   idx  = the k experts of largest key, equal keys -> lower id first
+ *   gate = softmax(l)[idx] (optionally / their sum)  |  sigmoid(l)[idx] / their sum
+ *   dispatch: each expert's slots in token order; with capacity C > 0 only the
+ *             first C slots of an expert are kept (the rest are dropped)
+ *   y[t] = sum_{s<S} SwiGLU_s(x[t]) + sum_{kept j} gate[t,j] SwiGLU_{idx[t,j]}(x[t])
+ *   SwiGLU(v) = (SiLU(v W_gate) * (v W_up)) W_down,  h = SiLU(.)*(.) rounded to
+ *             the storage type before W_down; low-rank experts use
+ *             W = U diag(s) V^T for each of the three matrices
+ *   aux_raw = E * sum_i f_i P_i,  f_i = counts_i/(T k),  P_i = mean_t prob[t,i]
+ *             (prob = full softmax, or sigmoid / row sum); aux = aux_coef * aux_raw
+ *
+ * Conventions for every entry point
+ *   - Pointers named "device" are HIP device pointers; every array is dense
+ *     row-major with the shape given. The caller owns and allocates all of them
+ *     and the workspace; the library never allocates or frees device memory and
+ *     keeps nothing between calls.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *     enqueues work on it and returns; results are valid after the stream
+ *     synchronises. No call reads device memory from the host.
+ *   - Errors are returned as moe_status codes; arguments are validated before
+ *     anything is enqueued, so an error return means nothing was launched
+ *     (except MOE_EHIP, reported when a launch itself fails).
+ *   - Calls that share a workspace on different streams race; calls on one
+ *     stream are ordered.
+ *   - Limits of this build: 1 <= k <= 15, k <= E <= 4096; d and F multiples of
+ *     64; T*k < 2^31; rank is 0 or 64 with bf16 (low-rank float32 experts are
+ *     MOE_EUNSUPPORTED); sigmoid scoring requires renorm_topk == 1.
+ */
+#ifndef FGM_MOE_H
+#define FGM_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,        /* NULL required pointer or a size/setting out of range   */
+  MOE_EUNSUPPORTED = -2,  /* legal layer this build does not implement (see limits) */
+  MOE_EWORKSPACE = -3,    /* ws is NULL/misaligned or ws_bytes < moe_workspace_bytes */
+  MOE_EHIP = -4           /* a HIP call failed; moe_last_error() holds its text      */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;        /* type of x and weights */
+typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score;  /* router scoring rule   */
+
+/* moe_grouped_ffn `groups` bits */
+enum { MOE_GROUPS_ROUTED = 1, MOE_GROUPS_SHARED = 2 };
+
+typedef struct {
+  int32_t hidden;       /* d, multiple of 64                                       */
+  int32_t n_routed;     /* E, routed experts                                       */
+  int32_t top_k;        /* k, active routed experts per token                      */
+  int32_t n_shared;     /* S, always-on ungated shared experts (0 allowed)         */
+  int32_t ffn;          /* F, width of every expert, multiple of 64                */
+  int32_t rank;         /* 0: dense experts; r > 0: U diag(s) V^T factors of rank r */
+  int32_t score;        /* moe_score                                               */
+  int32_t renorm_topk;  /* softmax: 1 = gates divided by their top-k sum, 0 = raw
+                           probabilities; sigmoid: must be 1                       */
+  int32_t capacity;     /* 0: dropless; C > 0: at most C slots per expert, later
+                           tokens' slots dropped (see moe_capacity)               */
+  float   aux_coef;     /* alpha of the aux statistic (0.01 for Quartz)            */
+  int32_t dtype;        /* moe_dtype of x, every weight and the x_perm/h buffers   */
+} moe_config;
+
+/* Device pointers to one layer's weights, element type = cfg.dtype unless noted.
+   All read-only. */
+typedef struct {
+  const void  *w_router;     /* [d, E]                                              */
+  const float *logit_bias;   /* [E] float32 or NULL; added to the logits (moves gates) */
+  const float *select_bias;  /* [E] float32 or NULL; sigmoid rule only: added to the
+                                selection key, never to the gates                   */
+  /* dense experts (rank == 0): stacked expert tensors                              */
+  const void *w_gate;        /* [E, d, F] */
+  const void *w_up;          /* [E, d, F] */
+  const void *w_down;        /* [E, F, d] */
+  /* low-rank experts (rank == r > 0): W[in,out] = U[in,r] diag(s[r]) V[out,r]^T    */
+  const void *u_gate, *s_gate, *v_gate;   /* [E,d,r], [E,r], [E,F,r] */
+  const void *u_up,   *s_up,   *v_up;     /* [E,d,r], [E,r], [E,F,r] */
+  const void *u_down, *s_down, *v_down;   /* [E,F,r], [E,r], [E,d,r] */
+  /* shared experts (S > 0), NULL when S == 0                                      */
+  const void *sh_gate;       /* [S, d, F] */
+  const void *sh_up;         /* [S, d, F] */
+  const void *sh_down;       /* [S, F, d] */
+} moe_weights;
+
+/* Device output buffers, caller-allocated. R_max = T*k (dropless) or
+   min(T*k, E*C). "optional" pointers may be NULL. */
+typedef struct {
+  int32_t *topk_idx;      /* [T, k] selected expert ids, descending key          */
+  float   *topk_gate;     /* [T, k] gate weights                                  */
+  float   *topk_margin;   /* [T] optional: key of k-th minus key of (k+1)-th
+                             expert (+inf when k == E)                            */
+  int32_t *counts;        /* [E] slots per expert before capacity                 */
+  int32_t *kept;          /* [E] min(counts, C) (counts when dropless)             */
+  int32_t *offsets;       /* [E+1] exclusive prefix sum of kept; offsets[E] = rows  */
+  int32_t *sorted_token;  /* [R_max] token of each dispatched row, rows grouped by
+                             expert, ascending token within an expert; entries at
+                             and beyond offsets[E] are left untouched              */
+  int32_t *row_of_slot;   /* [T, k] dispatched row of slot (t, j), -1 if dropped  */
+  uint8_t *dropped;       /* [T, k] optional: 1 if slot dropped by capacity       */
+  int32_t *n_dropped;     /* [1] number of dropped slots                          */
+  float   *aux;           /* [2] {aux_raw, aux_coef * aux_raw}                    */
+  float   *f;             /* [E] optional: counts / (T k)                          */
+  float   *P;             /* [E] optional: mean routing probability per expert    */
+  float   *y;             /* [T, d] float32 layer output                          */
+  void    *y_lowp;        /* [T, d] optional copy of y in cfg.dtype               */
+} moe_outputs;
+
+/* Capacity C = ceil(num * T * k / (den * E)) in exact integer arithmetic, as for
+   a capacity factor num/den (Moonfrost stacking card: capacity-based routing;
+   factor 5/4 gives C = 1920 at T = 16384, k = 3, E = 32). Returns -1 on bad input. */
+int32_t moe_capacity(int64_t num, int64_t den, int64_t T, int32_t k, int32_t E);
+
+/* Largest number of dispatched rows: T*k dropless, else min(T*k, E*C). */
+int64_t moe_max_rows(const moe_config *cfg, int64_t T);
+
+/* Workspace bytes every entry point below needs for this config and T (the same
+   workspace serves all of them). 0 if cfg is invalid. */
+size_t moe_workspace_bytes(const moe_config *cfg, int64_t T);
+
+/* Router projection, scores, top-k, gates, per-expert histogram, capacity,
+   prefix sum and aux statistic.
+   In:  x [T,d] device; w->w_router, w->logit_bias, w->select_bias.
+   Out: o->topk_idx, topk_gate, (topk_margin), counts, kept, offsets, n_dropped,
+        aux, (f), (P); per-block tables kept in ws for moe_permute.           */
+int moe_route(const moe_config *cfg, int64_t T, const void *x, const moe_weights *w,
+              moe_outputs *o, void *ws, size_t ws_bytes, void *stream);
+
+/* Token permutation: each kept slot's row in token order per expert, drops,
+   and optionally the gathered rows x_perm[row] = x[sorted_token[row]].
+   Must follow moe_route with the same cfg, T, outputs and ws on the same stream.
+   In:  x [T,d] device (read only if x_perm != NULL).
+   Out: o->row_of_slot, sorted_token, (dropped); x_perm [R_max, d] cfg.dtype or NULL. */
+int moe_permute(const moe_config *cfg, int64_t T, const void *x, moe_outputs *o,
+                void *x_perm, void *ws, size_t ws_bytes, void *stream);
+
+/* Grouped SwiGLU expert FFN.
+   groups & MOE_GROUPS_ROUTED: for every routed expert e, the rows
+     x_perm[offsets[e] : offsets[e+1]] of x_or_xperm ([R_max, d]) go through
+     expert e; result rows written to y_routed [R_max, d] float32 (rows at and
+     beyond offsets[E] untouched). offsets [E+1] device, as from moe_route.
+   groups & MOE_GROUPS_SHARED: every row of x_shared [T, d] goes through all S
+     shared experts, summed, into y_shared [T, d] float32.
+   Unused inputs/outputs may be NULL.                                         */
+int moe_grouped_ffn(const moe_config *cfg, int64_t T, int32_t groups,
+                    const void *x_perm, const int32_t *offsets, const void *x_shared,
+                    const moe_weights *w, float *y_routed, float *y_shared,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/* Gate-weighted combine: y[t] = y_shared[t] + sum_{j kept, ascending j}
+   topk_gate[t,j] * y_routed[row_of_slot[t,j]], in float32 in that order.
+   y_shared may be NULL (S == 0). Writes o->y and (o->y_lowp).               */
+int moe_combine(const moe_config *cfg, int64_t T, const float *y_routed,
+                const float *y_shared, moe_outputs *o, void *stream);
+
+/* The whole layer forward (route, permute, grouped FFN for routed and shared
+   experts, combine). Intermediates live in ws; fills every output of o.       */
+int moe_layer_forward(const moe_config *cfg, int64_t T, const void *x,
+                      const moe_weights *w, moe_outputs *o, void *ws, size_t ws_bytes,
+                      void *stream);
+
+/* Same as moe_layer_forward, and records events[i] (hipEvent_t, caller-created)
+   on `stream` before the i-th kernel launch, plus one after the last, for
+   i < n_events; returns the number of kernels launched (>= 0) or a moe_status.
+   moe_stage_name(i) names the i-th kernel of the last such call.             */
+int moe_layer_forward_timed(const moe_config *cfg, int64_t T, const void *x,
+                            const moe_weights *w, moe_outputs *o, void *ws,
+                            size_t ws_bytes, void *stream, void **events, int n_events);
+const char *moe_stage_name(int i);
+
+/* Static text for a status code, and the text of the last MOE_EHIP error of the
+   calling thread. */
+const char *moe_status_str(int status);
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FGM_MOE_H */

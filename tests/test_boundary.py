@@ -1,0 +1,139 @@
+"""The C ABI library loads, exports every function include/moe.h declares, and
+its host-side logic (capacity, sizes, argument validation) behaves as
+documented. Nothing here launches a kernel, so it runs without a GPU: every
+invalid call must return before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from fine_grained_mixture_amd import _lib
+from fine_grained_mixture_amd.synth import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__  # noqa: F401
+        from fine_grained_mixture_amd import build
+        build.build()
+    return _lib.load()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
+              "moe_workspace_bytes", "moe_status_str", "moe_capacity"):
+        assert n in names
+    assert set(names) == set(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+    for n in declared_functions():
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def test_capacity_exact_ceiling(lib):
+    # capacity factor 5/4 at the Moonfrost shape gives exactly 1920 slots
+    assert _lib.moe_capacity(5, 4, 16384, 3, 32) == 1920
+    assert _lib.moe_capacity(5, 4, 16385, 3, 32) == 1921
+    assert _lib.moe_capacity(1, 1, 10, 2, 4) == 5
+    assert _lib.moe_capacity(1, 1, 11, 2, 4) == 6
+    assert _lib.moe_capacity(5, 4, 1000, 3, 32) == WORKLOADS["moonfrost"].replace(T=1000).capacity
+    assert _lib.moe_capacity(0, 1, 10, 2, 4) == -1
+
+
+def test_max_rows_and_workspace(lib):
+    from fine_grained_mixture_amd.layer import config_from_workload
+    for wl in WORKLOADS.values():
+        cfg = config_from_workload(wl)
+        r = _lib.moe_max_rows(cfg, wl.T)
+        want = wl.T * wl.top_k if wl.capacity == 0 else min(wl.T * wl.top_k,
+                                                            wl.n_routed * wl.capacity)
+        assert r == want
+        ws = _lib.moe_workspace_bytes(cfg, wl.T)
+        es = 2 if wl.dtype == "bf16" else 4
+        # at least the routed intermediates and the fp32 routed outputs
+        assert ws >= r * wl.ffn * es + r * wl.hidden * 4
+        assert ws % 256 == 0 or ws > 0
+
+
+def _cfg(**kw):
+    from fine_grained_mixture_amd.layer import make_config
+    base = dict(hidden=128, n_routed=8, top_k=2, n_shared=1, ffn=64)
+    base.update(kw)
+    return make_config(**base)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(hidden=100), dict(ffn=48), dict(top_k=0), dict(top_k=9), dict(top_k=16, n_routed=32),
+    dict(n_routed=5000), dict(score="sigmoid", renorm=False), dict(capacity=-1),
+    dict(n_shared=-1),
+])
+def test_invalid_config_rejected(lib, bad):
+    cfg = _cfg(**bad)
+    assert _lib.moe_workspace_bytes(cfg, 64) == 0
+    w = _lib.MoeWeights(w_router=0x1000)
+    o = _lib.MoeOutputs(**{n: 0x1000 for n in _lib.OUTPUT_FIELDS})
+    st = lib.moe_layer_forward(ctypes.byref(cfg), 64, 0x1000, ctypes.byref(w), ctypes.byref(o),
+                               0x1000, 1 << 30, None)
+    assert st == _lib.MOE_EINVAL
+
+
+def test_null_pointers_and_workspace_rejected(lib):
+    cfg = _cfg()
+    full_w = _lib.MoeWeights(**{n: 0x1000 for n in ("w_router", "w_gate", "w_up", "w_down",
+                                                      "sh_gate", "sh_up", "sh_down")})
+    full_o = _lib.MoeOutputs(**{n: 0x1000 for n in _lib.OUTPUT_FIELDS})
+    need = _lib.moe_workspace_bytes(cfg, 64)
+
+    def call(w=full_w, o=full_o, x=0x1000, ws=0x1000, nbytes=need, T=64):
+        return lib.moe_layer_forward(ctypes.byref(cfg), T, x, ctypes.byref(w), ctypes.byref(o),
+                                     ws, nbytes, None)
+
+    assert call(x=0) == _lib.MOE_EINVAL
+    w = _lib.MoeWeights.from_buffer_copy(full_w)
+    w.w_up = None
+    assert call(w=w) == _lib.MOE_EINVAL
+    w = _lib.MoeWeights.from_buffer_copy(full_w)
+    w.sh_down = None
+    assert call(w=w) == _lib.MOE_EINVAL
+    w = _lib.MoeWeights.from_buffer_copy(full_w)
+    w.select_bias = 0x1000          # selection bias only exists for the sigmoid rule
+    assert call(w=w) == _lib.MOE_EINVAL
+    o = _lib.MoeOutputs.from_buffer_copy(full_o)
+    o.row_of_slot = None
+    assert call(o=o) == _lib.MOE_EINVAL
+    assert call(nbytes=need - 1) == _lib.MOE_EWORKSPACE
+    assert call(ws=0) == _lib.MOE_EWORKSPACE
+    assert call(ws=0x1001) == _lib.MOE_EWORKSPACE
+    assert call(T=-1) == _lib.MOE_EINVAL
+    # grouped FFN: unknown group bits, routed without offsets
+    st = lib.moe_grouped_ffn(ctypes.byref(cfg), 64, 4, 0x1000, 0x1000, 0x1000,
+                             ctypes.byref(full_w), 0x1000, 0x1000, 0x1000, need, None)
+    assert st == _lib.MOE_EINVAL
+    st = lib.moe_grouped_ffn(ctypes.byref(cfg), 64, _lib.MOE_GROUPS_ROUTED, 0x1000, None, None,
+                             ctypes.byref(full_w), 0x1000, None, 0x1000, need, None)
+    assert st == _lib.MOE_EINVAL
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4):
+        assert lib.moe_status_str(st)
+    assert lib.moe_stage_name(0) is None or isinstance(lib.moe_stage_name(0), bytes)

@@ -1,0 +1,142 @@
+"""HIP path vs the CPU oracle on the same seeded inputs, through the C ABI.
+
+Small shapes (every token checked, several tiles and ragged tails), the five
+workloads at full size (routing checked on every token, y on sampled tokens),
+edge cases, determinism, and the stage entry points against the whole-layer
+entry point.
+"""
+import numpy as np
+import pytest
+import torch
+
+from fine_grained_mixture_amd import layer as L
+from fine_grained_mixture_amd import synth
+from fine_grained_mixture_amd._lib import MOE_GROUPS_ROUTED, MOE_GROUPS_SHARED
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_and_check(wl, tokens=None, **kw):
+    print(f"\n[case] {wl}", flush=True)
+    inp = synth.make_inputs(wl)
+    g = P.run_gpu(wl, inp)
+    rep = P.check_parity(wl, inp, g, tokens, **kw)
+    print(f"[report] {wl.name} T={wl.T}: {rep}", flush=True)
+    return rep
+
+
+SMALL = {
+    "tiny": synth.TINY,
+    "tiny_ragged": synth.TINY.replace(T=77, seed=1),
+    "quartz_small": synth.QUARTZ.replace(T=517, hidden=256, ffn=128),
+    "moonfrost_small": synth.MOONFROST.replace(T=1000, hidden=256, ffn=128),
+    "moonfrost_small_renorm": synth.MOONFROST.replace(T=1000, hidden=256, ffn=128, renorm=1),
+    "sutra_small": synth.SUTRA.replace(T=700, hidden=384, ffn=192),
+    "dormouse_small": synth.DORMOUSE.replace(T=600, hidden=256, ffn=128),
+    "dormouse_small_renorm": synth.DORMOUSE.replace(T=600, hidden=256, ffn=128, renorm=1),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_parity(name):
+    _run_and_check(SMALL[name])
+
+
+EDGE = {
+    "single_expert": synth.Workload("e1", T=130, hidden=128, n_routed=1, top_k=1, n_shared=0,
+                                    ffn=64),
+    "all_experts_active": synth.Workload("ek", T=150, hidden=128, n_routed=4, top_k=4,
+                                         n_shared=1, ffn=64, renorm=0),
+    "capacity_one": synth.QUARTZ.replace(T=200, hidden=128, ffn=64, capacity_factor="1/200"),
+    "capacity_large": synth.MOONFROST.replace(T=300, hidden=128, ffn=64, capacity_factor="10"),
+    "no_shared_sigmoid": synth.SUTRA.replace(T=333, hidden=128, ffn=64, n_shared=0),
+    "one_token": synth.QUARTZ.replace(T=1, hidden=128, ffn=64),
+    "odd_experts": synth.Workload("odd", T=257, hidden=192, n_routed=13, top_k=3, n_shared=3,
+                                  ffn=192, logit_offset_std=0.3),
+    "many_experts_k8": synth.Workload("k8", T=190, hidden=128, n_routed=300, top_k=8,
+                                      n_shared=1, ffn=64, renorm=0),
+    "tiny_f32_capacity": synth.TINY.replace(T=200, capacity_factor="1/2", seed=3),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_edge_parity(name):
+    wl = EDGE[name]
+    rep = _run_and_check(wl)
+    if name == "capacity_one":
+        assert wl.capacity == 1 and rep["rows"] <= wl.n_routed
+
+
+def test_empty_batch():
+    wl = synth.QUARTZ.replace(T=0, hidden=128, ffn=64)
+    cfg = L.config_from_workload(wl)
+    x = torch.empty((0, wl.hidden), dtype=torch.bfloat16, device="cuda")
+    inp = synth.make_inputs(wl.replace(T=1))
+    w = L.DeviceWeights.from_numpy(inp, cfg, "cuda")
+    out = L.allocate_outputs(cfg, 0, "cuda")
+    ws = L.allocate_workspace(cfg, 0, "cuda")
+    L.layer_forward(cfg, x, w, out, ws)
+    torch.cuda.synchronize()
+    assert out["counts"].sum().item() == 0
+    assert out["offsets"].sum().item() == 0
+    assert out["n_dropped"].item() == 0
+
+
+FULL = {
+    "tiny": (synth.TINY, None),
+    "quartz": (synth.QUARTZ, 40),
+    "moonfrost": (synth.MOONFROST, 40),
+    "moonfrost_renorm": (synth.MOONFROST.replace(renorm=1), 24),
+    "sutra": (synth.SUTRA, 24),
+    "dormouse": (synth.DORMOUSE, 40),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_parity(name):
+    wl, n = FULL[name]
+    toks = None if n is None else P.sample_tokens(wl.T, n, seed=1)
+    _run_and_check(wl, toks)
+
+
+def test_determinism_bitwise():
+    wl = synth.MOONFROST.replace(T=3000, hidden=256, ffn=128)
+    inp = synth.make_inputs(wl)
+    a = P.run_gpu(wl, inp)
+    b = P.run_gpu(wl, inp)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+@pytest.mark.parametrize("base", ["quartz", "tiny"])
+def test_stage_entry_points_match_layer(base):
+    wl = (synth.QUARTZ.replace(T=700, hidden=256, ffn=128) if base == "quartz"
+          else synth.TINY.replace(T=150))
+    inp = synth.make_inputs(wl)
+    whole = P.run_gpu(wl, inp, y_lowp=True)
+    cfg, x, w = P.upload(wl, inp)
+    T = wl.T
+    out = L.allocate_outputs(cfg, T, x.device, y_lowp=True)
+    ws = L.allocate_workspace(cfg, T, x.device)
+    R = max(1, int(L._lib.moe_max_rows(cfg, T)))
+    x_perm = torch.empty((R, wl.hidden), dtype=x.dtype, device=x.device)
+    y_routed = torch.empty((R, wl.hidden), dtype=torch.float32, device=x.device)
+    y_shared = torch.empty((T, wl.hidden), dtype=torch.float32, device=x.device)
+    L.route(cfg, x, w, out, ws)
+    L.permute(cfg, x, out, ws, x_perm)
+    L.grouped_ffn(cfg, T, MOE_GROUPS_ROUTED, w, ws, x_perm=x_perm, offsets=out["offsets"],
+                  y_routed=y_routed)
+    L.grouped_ffn(cfg, T, MOE_GROUPS_SHARED, w, ws, x_shared=x, y_shared=y_shared)
+    L.combine(cfg, T, y_routed, y_shared, out)
+    torch.cuda.synchronize()
+    staged = P.to_numpy(out)
+    for k in whole:
+        np.testing.assert_array_equal(staged[k], whole[k], err_msg=k)
+    # the gathered rows are the token rows
+    rows = int(staged["offsets"][-1])
+    st = torch.from_numpy(staged["sorted_token"][:rows]).long().to(x.device)
+    assert torch.equal(x_perm[:rows], x[st])
+    # y_lowp is y rounded to the storage type
+    yl = torch.from_numpy(whole["y"]).to(x.dtype).float().numpy()
+    np.testing.assert_array_equal(whole["y_lowp"], yl)
