@@ -1,0 +1,219 @@
+"""MoE layer forward throughput on one MI355X, Quartz shape.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload quartz] [--no-cpu]
+
+One step is one call of moe_layer_forward (router GEMM, top-k, scan, rank,
+fused gate/up grouped GEMM, down grouped GEMM, combine) over one batch of
+synthetic inputs already resident in device memory. Prints one JSON line.
+
+Per-kernel durations come from HIP events that the library records on the
+launch stream between its kernels (moe_layer_forward_timed); the dominant
+kernel's roofline is its algorithmic FLOPs per launch over its mean duration.
+The CPU baseline is the float64 oracle timed on a bounded sample of the same
+workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="quartz")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=1536,
+                    help="tokens of the workload the CPU oracle processes")
+    return ap.parse_args()
+
+
+def algorithmic(wl, rows):
+    """Algorithmic FLOPs and bytes of each stage for `rows` dispatched rows."""
+    T, d, E, k, S, F, r = wl.T, wl.hidden, wl.n_routed, wl.top_k, wl.n_shared, wl.ffn, wl.rank
+    b = 2 if wl.dtype == "bf16" else 4
+    if r == 0:
+        gate_up = 4.0 * d * F * (rows + S * T)
+        down = 2.0 * d * F * (rows + S * T)
+    else:
+        per = 2.0 * (2 * (d * r + r * F) + (F * r + r * d))
+        gate_up = rows * 2.0 * 2 * (d * r + r * F) + 4.0 * d * F * S * T
+        down = rows * 2.0 * (F * r + r * d) + 2.0 * d * F * S * T
+        del per
+    return dict(
+        router_flops=2.0 * T * d * E,
+        gate_up_flops=gate_up,
+        down_flops=down,
+        route_bytes=T * d * b + d * E * b + T * E * 4,
+        topk_bytes=T * E * 4 + 8 * T * k,
+        combine_bytes=rows * d * 4 + (T * d * 4 if S > 0 else 0) + T * d * 4 + 8 * T * k,
+    )
+
+
+def traffic_from_profile(kernel_src: str):
+    """HBM bytes per launch of the gate/up kernel from the committed counter
+    summary, if it was taken from the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "gate_up_gemm_quartz_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source sha256:\s*([0-9a-f]{64})", text)
+    t = re.search(r"hbm bytes per launch:\s*([0-9.eE+]+)", text)
+    if not m or not t:
+        return None
+    cur = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    return float(t.group(1)) if m.group(1) == cur else None
+
+
+def cpu_baseline(wl, inp, n_tokens):
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    sub = wl.replace(T=min(n_tokens, wl.T))
+    spec = oracle.LayerSpec(hidden=wl.hidden, n_routed=wl.n_routed, top_k=wl.top_k,
+                            n_shared=wl.n_shared, ffn=wl.ffn, rank=wl.rank, score=wl.score,
+                            renorm=bool(wl.renorm), capacity=sub.capacity,
+                            aux_coef=wl.aux_coef, bf16=wl.dtype == "bf16")
+    sinp = dict(inp)
+    sinp["x"] = np.ascontiguousarray(inp["x"][: sub.T])
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.layer_forward(sinp["x"], sinp, spec)
+        dt = time.perf_counter() - t0
+    return {"value": sub.T / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the first {sub.T} of the {wl.T} tokens as one batch (full layer: routing, "
+                      f"dispatch, every expert output), float64 NumPy, 1 BLAS thread, "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this MoE layer build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from fine_grained_mixture_amd import _lib, synth
+    from fine_grained_mixture_amd.layer import (DeviceWeights, allocate_outputs,
+                                                allocate_workspace, config_from_workload,
+                                                current_stream)
+
+    wl = synth.WORKLOADS[args.workload]
+    inp = synth.make_inputs(wl)
+    cfg = config_from_workload(wl)
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    x = torch.from_numpy(inp["x"]).to(device=dev, dtype=dt)
+    w = DeviceWeights.from_numpy(inp, cfg, dev)
+    out = allocate_outputs(cfg, wl.T, dev)
+    ws = allocate_workspace(cfg, wl.T, dev)
+    stream = current_stream()
+
+    def step(events=None):
+        if events is None:
+            _lib.moe_layer_forward(cfg, wl.T, x.data_ptr(), w.struct, out.struct, ws.data_ptr(),
+                                   ws.numel(), stream)
+            return 0
+        return _lib.moe_layer_forward_timed(cfg, wl.T, x.data_ptr(), w.struct, out.struct,
+                                            ws.data_ptr(), ws.numel(), stream,
+                                            [e.cuda_event for e in events])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K whole-layer steps back to back
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for _ in range(args.steps):
+        step()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / args.steps
+
+    # per-kernel durations: the same steps with events between the kernels
+    n_ev = 16
+    ev_sets = []
+    for _ in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+        for e in evs:
+            e.record()          # materialise the underlying hipEvent
+        ev_sets.append(evs)
+    torch.cuda.synchronize()
+    n_k = 0
+    for evs in ev_sets:
+        n_k = step(evs)
+    torch.cuda.synchronize()
+    names = [_lib.moe_stage_name(i) for i in range(n_k)]
+    dur = {n: [] for n in names}
+    for evs in ev_sets:
+        for i, n in enumerate(names):
+            dur[n].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)   # us
+    stage_us = {n: float(np.mean(v)) for n, v in dur.items()}
+    stage_us_med = {n: float(np.median(v)) for n, v in dur.items()}
+
+    rows = int(out["offsets"][-1].item())
+    alg = algorithmic(wl, rows)
+    gu_us = stage_us["gate_up_gemm"]
+    dn_us = stage_us["down_gemm"]
+    gu_tflops = alg["gate_up_flops"] / (gu_us * 1e-6) / 1e12
+    expert_tflops = (alg["gate_up_flops"] + alg["down_flops"]) / ((gu_us + dn_us) * 1e-6) / 1e12
+    kernel_src = os.path.join(ROOT, "fine_grained_mixture_amd", "csrc", "gemm.hip")
+    result = {
+        "metric": "MoE layer fwd tokens/s + expert-GEMM TFLOP/s (% MFMA peak), Quartz shape",
+        "value": wl.T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}-shape MoE layer forward", "tokens": wl.T,
+                   "hidden": wl.hidden, "routed_experts": wl.n_routed, "top_k": wl.top_k,
+                   "shared_experts": wl.n_shared, "expert_ffn": wl.ffn, "rank": wl.rank,
+                   "score": wl.score, "capacity": wl.capacity, "rows": rows,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "gate_up_gemm", "achieved": gu_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": gu_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": traffic_from_profile(kernel_src)},
+        "expert_gemm_tflops": expert_tflops,
+        "expert_gemm_frac_of_peak": expert_tflops / PEAK_BF16_TFLOPS,
+        "stage_us_mean": stage_us,
+        "stage_us_median": stage_us_med,
+        "combine_gbs": alg["combine_bytes"] / (stage_us["combine"] * 1e-6) / 1e9,
+        "layer_flops": alg["router_flops"] + alg["gate_up_flops"] + alg["down_flops"],
+        "wall_s_timed_region": wall,
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_tokens)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -43,17 +43,28 @@ bool valid_config(const moe_config* c) {
   return true;
 }
 
+// Low-rank experts: rank 64 with bf16 (the fused kernel's shape).
 bool supported_config(const moe_config* c) {
-  if (c->rank != 0) return false;   // low-rank experts: fused kernel below
+  if (c->rank != 0 && (c->rank != 64 || c->dtype != MOE_BF16)) return false;
   return true;
 }
 
 size_t elem_size(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
 
-int plan_bm(const moe_config* c) { return c->dtype == MOE_F32 ? kGemmBM_F32 : kGemmBM; }
+int plan_bm(const moe_config* c) {
+  if (c->dtype == MOE_F32) return kGemmBM_F32;
+  return c->rank > 0 ? kLowRankBM : kGemmBM;
+}
+
+// bf16 layers with few experts use the fused router (16-token blocks).
+bool fused_router(const moe_config* c) {
+  return c->dtype == MOE_BF16 && c->n_routed <= kRouteSmallMaxE;
+}
+int route_tb(const moe_config* c) { return fused_router(c) ? kRouteBlockSmall : kRouteBlock; }
 
 struct Layout {
   int64_t T = 0, R = 0, nblk = 0, max_tiles = 0;
+  int tb = kRouteBlock;
   size_t logits = 0, blk_counts = 0, blk_base = 0, blk_psum = 0, plan = 0;
   size_t h = 0, h_sh = 0, y_perm = 0, y_sh = 0, total = 0;
 };
@@ -70,7 +81,8 @@ Layout make_layout(const moe_config* c, int64_t T) {
   const size_t es = elem_size(c);
   L.T = T;
   L.R = max_rows(c, T);
-  L.nblk = ceil_div(T, kRouteBlock);
+  L.tb = route_tb(c);
+  L.nblk = ceil_div(T, L.tb);
   L.max_tiles = ceil_div(L.R, plan_bm(c)) + E;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -78,7 +90,7 @@ Layout make_layout(const moe_config* c, int64_t T) {
     off = align_up(off + bytes);
     return at;
   };
-  L.logits = take((size_t)T * E * 4);
+  L.logits = take(fused_router(c) ? 0 : (size_t)T * E * 4);
   L.blk_counts = take((size_t)L.nblk * E * 4);
   L.blk_base = take((size_t)L.nblk * E * 4);
   L.blk_psum = take((size_t)L.nblk * E * 4);
@@ -170,7 +182,26 @@ void run_route(Runner& R, const moe_config* c, const Layout& L, const void* x,
   const int64_t T = L.T;
   const int E = c->n_routed;
   float* logits = at<float>(ws, L.logits);
-  if (T > 0) {
+  if (T > 0 && fused_router(c)) {
+    RouteSmallArgs r{};
+    r.x = x;
+    r.w_router = w->w_router;
+    r.logit_bias = w->logit_bias;
+    r.select_bias = c->score == MOE_SIGMOID ? w->select_bias : nullptr;
+    r.topk_idx = o->topk_idx;
+    r.topk_gate = o->topk_gate;
+    r.topk_margin = o->topk_margin;
+    r.blk_counts = at<int32_t>(ws, L.blk_counts);
+    r.blk_psum = at<float>(ws, L.blk_psum);
+    r.T = T;
+    r.d = c->hidden;
+    r.E = E;
+    r.k = c->top_k;
+    r.score = c->score;
+    r.renorm = c->renorm_topk;
+    R.stage("route");
+    R.check(launch_route_small(r, R.stream));
+  } else if (T > 0) {
     GemmLaunch G{};
     GemmProblem& p = G.p[0];
     p.A = x;
@@ -207,6 +238,7 @@ void run_route(Runner& R, const moe_config* c, const Layout& L, const void* x,
     t.k = c->top_k;
     t.score = c->score;
     t.renorm = c->renorm_topk;
+    t.tb = L.tb;
     R.stage("topk");
     R.check(launch_topk(t, R.stream));
   }
@@ -247,6 +279,7 @@ void run_rank(Runner& R, const moe_config* c, const Layout& L, moe_outputs* o, v
   r.k = c->top_k;
   r.capacity = c->capacity;
   r.nblk = (int32_t)L.nblk;
+  r.tb = L.tb;
   R.stage("rank");
   R.check(launch_rank(r, R.stream));
 }
@@ -273,6 +306,32 @@ void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool 
     R.check(bf ? launch_gemm_bf16(G, epi, R.stream) : launch_gemm_f32(G, epi, R.stream));
   };
 
+  if (routed && c->rank > 0) {
+    LowRankArgs lr{};
+    lr.A = a_routed;
+    lr.a_rows = a_rows;
+    lr.lda = d;
+    lr.u_gate = w->u_gate;
+    lr.s_gate = w->s_gate;
+    lr.v_gate = w->v_gate;
+    lr.u_up = w->u_up;
+    lr.s_up = w->s_up;
+    lr.v_up = w->v_up;
+    lr.u_down = w->u_down;
+    lr.s_down = w->s_down;
+    lr.v_down = w->v_down;
+    lr.offsets = offsets;
+    lr.plan = plan;
+    lr.y = y_routed;
+    lr.d = (int32_t)d;
+    lr.F = (int32_t)F;
+    lr.E = c->n_routed;
+    lr.max_tiles = (int32_t)L.max_tiles;
+    R.stage("lowrank_experts");
+    R.check(launch_lowrank(lr, R.stream));
+    routed = false;                 // the dense launches below serve the shared experts
+    if (!shared) return;
+  }
   // gate/up with fused SiLU * up
   {
     GemmLaunch G{};

@@ -1,0 +1,233 @@
+// Fused low-rank SwiGLU experts on gfx950 (bf16, rank 64).
+//
+// Each expert matrix is W = U diag(s) V^T of rank r (dormouse site, "TSCT
+// low-rank experts" card: rank 64, which is what lets a 1.07B-parameter bank
+// fit a 16 GB card). For the rows routed to expert e:
+//   zg = rho((A U_gate) * s_gate),  zu = rho((A U_up) * s_up)        [rows, r]
+//   h  = rho(SiLU(zg V_gate^T) * (zu V_up^T))                       [rows, F]
+//   zd = rho((h U_down) * s_down)                                    [rows, r]
+//   y  = zd V_down^T                                                 [rows, d]
+// with rho = round to bf16 and every product accumulated in fp32 by
+// v_mfma_f32_16x16x32_bf16.
+//
+// One workgroup per (expert, chunk of up to 64 rows), from the device tile
+// list. The rank-r intermediates and h never leave the CU: zg|zu and zd live in
+// LDS, and h is produced 64 columns at a time and immediately folded into the
+// zd accumulators, so HBM traffic is the expert weights (streamed once per
+// chunk), the token rows and the fp32 output rows. U matrices arrive [in, r]
+// (r contiguous) and are transposed on their way into LDS; V matrices arrive
+// [out, r], which is already the k-contiguous order the MFMA B operand needs,
+// so they are read straight from memory.
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kR = 64;          // rank
+constexpr int kBM = kLowRankBM; // 64 rows per workgroup
+constexpr int kLd = 72;         // padded LDS row for 64-wide k tiles
+constexpr int kLdZ = 136;       // padded LDS row for the [rows, 2r] zg|zu tile
+
+__device__ __forceinline__ void load_b_pair(const bf16_t* src, int64_t ldb, uint32_t* reg) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) reg[i] = *reinterpret_cast<const uint32_t*>(src + i * ldb);
+}
+
+// Two adjacent columns x 8 consecutive k (as loaded by load_b_pair) written as
+// two k-contiguous 16-byte runs: rows `row` and `row + 1` of a [n][k] tile.
+__device__ __forceinline__ void store_b_pair(bf16_t* lds, int row, int kq, const uint32_t* reg) {
+  u32x4 lo, hi;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t x0 = reg[2 * m], x1 = reg[2 * m + 1];
+    lo[m] = (x0 & 0xffffu) | (x1 << 16);
+    hi[m] = (x0 >> 16) | (x1 & 0xffff0000u);
+  }
+  *reinterpret_cast<u32x4*>(&lds[row * kLd + 8 * kq]) = lo;
+  *reinterpret_cast<u32x4*>(&lds[(row + 1) * kLd + 8 * kq]) = hi;
+}
+
+__device__ __forceinline__ floatx4 mfma(const bf16x8& a, const bf16x8& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[kBM * kLd];        // A k-chunk
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2 * kR * kLd];     // U_gate|U_up chunk, [n][k]
+  __shared__ __attribute__((aligned(16))) bf16_t Zs[kBM * kLdZ];       // zg | zu
+  __shared__ __attribute__((aligned(16))) bf16_t Hs[kBM * kLd];        // 64-column chunk of h
+  __shared__ __attribute__((aligned(16))) bf16_t Bd[kR * kLd];         // U_down chunk, [n][k]
+  __shared__ __attribute__((aligned(16))) bf16_t Zd[kBM * kLd];        // zd
+
+  const int tile = blockIdx.x;
+  if (tile >= a.plan[0]) return;
+  const int e = a.plan[1 + 2 * tile];
+  const int r0 = a.plan[2 + 2 * tile];
+  const int r_end = min(a.offsets[e + 1], r0 + kBM);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lk = 8 * (lane >> 4);
+  const int d = a.d, F = a.F;
+
+  const bf16_t* A = static_cast<const bf16_t*>(a.A);
+  const bf16_t* Ug = static_cast<const bf16_t*>(a.u_gate) + (int64_t)e * d * kR;
+  const bf16_t* Uu = static_cast<const bf16_t*>(a.u_up) + (int64_t)e * d * kR;
+  const bf16_t* Vg = static_cast<const bf16_t*>(a.v_gate) + (int64_t)e * F * kR;
+  const bf16_t* Vu = static_cast<const bf16_t*>(a.v_up) + (int64_t)e * F * kR;
+  const bf16_t* Ud = static_cast<const bf16_t*>(a.u_down) + (int64_t)e * F * kR;
+  const bf16_t* Vd = static_cast<const bf16_t*>(a.v_down) + (int64_t)e * d * kR;
+  const bf16_t* sg = static_cast<const bf16_t*>(a.s_gate) + (int64_t)e * kR;
+  const bf16_t* su = static_cast<const bf16_t*>(a.s_up) + (int64_t)e * kR;
+  const bf16_t* sd = static_cast<const bf16_t*>(a.s_down) + (int64_t)e * kR;
+
+  // A rows of this chunk (clamped: rows past r_end are computed, never stored)
+  const int a_c = tid & 7, a_rb = tid >> 3;
+  const bf16_t* a_src[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = min(r0 + a_rb + 32 * i, r_end - 1);
+    const int64_t arow = a.a_rows ? a.a_rows[r] : r;
+    a_src[i] = A + arow * a.lda + 8 * a_c;
+  }
+  // B transposing loader: unit (column pair p, k-group q)
+  const int bp = tid & 31, bq = tid >> 5;
+
+  // ---- stage 1: zg | zu = A [U_gate | U_up]; wave w owns columns 32w..32w+31
+  floatx4 acc1[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc1[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < d; k0 += 64) {
+    u32x4 ar[2];
+    uint32_t br[2][8];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ar[i] = *reinterpret_cast<const u32x4*>(a_src[i] + k0);
+    load_b_pair(Ug + (int64_t)(k0 + 8 * bq) * kR + 2 * bp, kR, br[0]);
+    load_b_pair(Uu + (int64_t)(k0 + 8 * bq) * kR + 2 * bp, kR, br[1]);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<u32x4*>(&As[(a_rb + 32 * i) * kLd + 8 * a_c]) = ar[i];
+    store_b_pair(Bs, 2 * bp, bq, br[0]);
+    store_b_pair(Bs, kR + 2 * bp, bq, br[1]);
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 av[4], bv[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        av[i] = *reinterpret_cast<const bf16x8*>(&As[(16 * i + lr) * kLd + 32 * kk + lk]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bv[j] = *reinterpret_cast<const bf16x8*>(&Bs[(32 * wave + 16 * j + lr) * kLd + 32 * kk + lk]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc1[i][j] = mfma(av[i], bv[j], acc1[i][j]);
+    }
+  }
+  // scale by s and round: column c < r is gate, c >= r is up
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = 32 * wave + 16 * j + lr;
+    const float sc = col < kR ? bf16_to_f32(sg[col]) : bf16_to_f32(su[col - kR]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        Zs[(16 * i + 4 * (lane >> 4) + q) * kLdZ + col] = f32_to_bf16(acc1[i][j][q] * sc);
+  }
+  __syncthreads();
+
+  // ---- stages 2-3: per 64 columns of F, h chunk then zd += h U_down
+  floatx4 accd[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) accd[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int f0 = 0; f0 < F; f0 += 64) {
+    // U_down rows f0..f0+63 (transposing load into registers early)
+    uint32_t bd[8];
+    load_b_pair(Ud + (int64_t)(f0 + 8 * bq) * kR + 2 * bp, kR, bd);
+    floatx4 accg[4], accu[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) accg[i] = accu[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const int n = f0 + 16 * wave + lr;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 bg = *reinterpret_cast<const bf16x8*>(Vg + (int64_t)n * kR + 32 * kk + lk);
+      const bf16x8 bu = *reinterpret_cast<const bf16x8*>(Vu + (int64_t)n * kR + 32 * kk + lk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 ag = *reinterpret_cast<const bf16x8*>(&Zs[(16 * i + lr) * kLdZ + 32 * kk + lk]);
+        const bf16x8 au = *reinterpret_cast<const bf16x8*>(&Zs[(16 * i + lr) * kLdZ + kR + 32 * kk + lk]);
+        accg[i] = mfma(ag, bg, accg[i]);
+        accu[i] = mfma(au, bu, accu[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        Hs[(16 * i + 4 * (lane >> 4) + q) * kLd + 16 * wave + lr] =
+            f32_to_bf16(silu_f32(accg[i][q]) * accu[i][q]);
+    store_b_pair(Bd, 2 * bp, bq, bd);
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&Bd[(16 * wave + lr) * kLd + 32 * kk + lk]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Hs[(16 * i + lr) * kLd + 32 * kk + lk]);
+        accd[i] = mfma(av, bv, accd[i]);
+      }
+    }
+    __syncthreads();
+  }
+  {
+    const int col = 16 * wave + lr;
+    const float sc = bf16_to_f32(sd[col]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        Zd[(16 * i + 4 * (lane >> 4) + q) * kLd + col] = f32_to_bf16(accd[i][q] * sc);
+  }
+  __syncthreads();
+
+  // ---- stage 4: y = zd V_down^T, 64 output columns per pass
+  float* Y = a.y;
+  for (int n0 = 0; n0 < d; n0 += 64) {
+    floatx4 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const int n = n0 + 16 * wave + lr;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(Vd + (int64_t)n * kR + 32 * kk + lk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Zd[(16 * i + lr) * kLd + 32 * kk + lk]);
+        acc[i] = mfma(av, bv, acc[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = r0 + 16 * i + 4 * (lane >> 4) + q;
+        if (row < r_end) Y[(int64_t)row * d + n] = acc[i][q];
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_lowrank(const LowRankArgs& a, hipStream_t s) {
+  if (a.max_tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL(lowrank_kernel, dim3((unsigned)a.max_tiles), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -9,9 +9,13 @@
 
 namespace moe {
 
-// Tokens per routing block: the top-k kernel histograms, and the rank kernel
-// ranks, one block of this many consecutive tokens per workgroup / wave.
+// Tokens per routing block: the top-k kernels histogram, and the rank kernel
+// ranks, blocks of this many consecutive tokens (one workgroup / one wave
+// each). The fused small-E router uses 16-token blocks, the generic one 64.
+constexpr int kRouteBlockSmall = 16;
 constexpr int kRouteBlock = 64;
+// Largest expert count the fused small-E router handles.
+constexpr int kRouteSmallMaxE = 64;
 // Rows per M-tile of the grouped GEMMs.
 constexpr int kGemmBM = 128;
 constexpr int kGemmBM_F32 = 64;
@@ -73,8 +77,26 @@ struct TopkArgs {
   float* blk_psum;           // [nblk, E]
   int64_t T;
   int32_t E, k, score, renorm;
+  int32_t tb;                // tokens per block (multiple of 4)
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+// Fused router for E <= kRouteSmallMaxE, bf16: logits by MFMA, top-k, gates,
+// block histogram and probability sums, kRouteBlockSmall tokens per block.
+struct RouteSmallArgs {
+  const void* x;             // [T, d] bf16
+  const void* w_router;      // [d, E] bf16
+  const float* logit_bias;   // [E] or null
+  const float* select_bias;  // [E] or null
+  int32_t* topk_idx;
+  float* topk_gate;
+  float* topk_margin;        // or null
+  int32_t* blk_counts;       // [nblk, E]
+  float* blk_psum;           // [nblk, E]
+  int64_t T;
+  int32_t d, E, k, score, renorm;
+};
+hipError_t launch_route_small(const RouteSmallArgs& a, hipStream_t s);
 
 struct ScanArgs {
   const int32_t* blk_counts;  // [nblk, E]
@@ -104,6 +126,7 @@ struct RankArgs {
   uint8_t* dropped;          // [T, k] or null
   int64_t T;
   int32_t E, k, capacity, nblk;
+  int32_t tb;                // tokens per block, as for the top-k tables
 };
 hipError_t launch_rank(const RankArgs& a, hipStream_t s);
 
@@ -123,5 +146,19 @@ struct CombineArgs {
   int32_t d, k, dtype;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+// Fused low-rank (rank 64) SwiGLU experts, bf16. Rows of expert e are
+// [offsets[e], offsets[e+1]); A row of dispatched row r is a_rows[r] (or r).
+struct LowRankArgs {
+  const void* A;             // [*, d] bf16 token rows
+  const int32_t* a_rows;     // [R_max] or null
+  int64_t lda;
+  const void *u_gate, *s_gate, *v_gate, *u_up, *s_up, *v_up, *u_down, *s_down, *v_down;
+  const int32_t* offsets;    // [E+1]
+  const int32_t* plan;       // tile list with kLowRankBM rows per tile
+  float* y;                  // [R_max, d]
+  int32_t d, F, E, max_tiles;
+};
+hipError_t launch_lowrank(const LowRankArgs& a, hipStream_t s);
 
 }  // namespace moe

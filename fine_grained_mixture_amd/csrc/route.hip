@@ -24,8 +24,8 @@ namespace moe {
 namespace {
 
 // ---------------------------------------------------------------------------
-// top-k: one wave per token (16 tokens per wave, 4 waves = one 64-token block
-// per workgroup). Lane l owns experts l, l + 64, ...; each lane keeps its best
+// top-k: one wave per token (tb/4 tokens per wave, 4 waves = one tb-token
+// block per workgroup). Lane l owns experts l, l + 64, ...; each lane keeps its best
 // KMAX (key, id) pairs, then k+1 rounds of a wave-wide maximum pick the
 // winners in descending key order (equal keys: lower id first).
 // ---------------------------------------------------------------------------
@@ -49,8 +49,9 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
   for (int m = 0; m < EPL; ++m) psum[m] = 0.f;
 
   const int rounds = min(k + 1, E);
-  const int64_t t_begin = (int64_t)blk * kRouteBlock + wave * (kRouteBlock / 4);
-  for (int it = 0; it < kRouteBlock / 4; ++it) {
+  const int per_wave = a.tb >> 2;
+  const int64_t t_begin = (int64_t)blk * a.tb + wave * per_wave;
+  for (int it = 0; it < per_wave; ++it) {
     const int64_t t = t_begin + it;
     if (t >= a.T) break;
     const float* lrow = a.logits + t * E;
@@ -370,8 +371,8 @@ __global__ void __launch_bounds__(256) rank_kernel(RankArgs a) {
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
 
-  const int64_t s_begin = (int64_t)b * kRouteBlock * k;
-  const int64_t s_end = min(a.T, (int64_t)(b + 1) * kRouteBlock) * k;
+  const int64_t s_begin = (int64_t)b * a.tb * k;
+  const int64_t s_end = min(a.T, (int64_t)(b + 1) * a.tb) * k;
   const uint64_t lt = lanemask_lt();
   for (int64_t base = s_begin; base < s_end; base += 64) {
     const int64_t s = base + lane;
@@ -422,7 +423,7 @@ __global__ void __launch_bounds__(256) gather_kernel(const unsigned char* x,
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
-  const int nblk = (int)((a.T + kRouteBlock - 1) / kRouteBlock);
+  const int nblk = (int)((a.T + a.tb - 1) / a.tb);
   if (nblk == 0) return hipSuccess;
   const size_t shm = (size_t)a.E * 8;
   const int epl = (a.E + 63) / 64;
