@@ -53,7 +53,7 @@ size_t elem_size(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
 
 int plan_bm(const moe_config* c) {
   if (c->dtype == MOE_F32) return kGemmBM_F32;
-  return c->rank > 0 ? kLowRankBM : kGemmBM;
+  return c->rank > 0 ? kLowRankBM : kGemmBigBM;
 }
 
 // bf16 layers with few experts use the fused router (16-token blocks).
@@ -292,7 +292,8 @@ void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool 
              void* ws) {
   const int64_t T = L.T, d = c->hidden, F = c->ffn, S = c->n_shared;
   const bool bf = c->dtype == MOE_BF16;
-  const int bm = plan_bm(c);
+  // tile shapes: bf16 256 x 128 (gate/up: 256 x (64 + 64)); fp32 64 x 64
+  const int bm = bf ? kGemmBigBM : kGemmBM_F32;
   const int bn_dual = 64, bn = bf ? 128 : 64;
   shared = shared && S > 0 && T > 0;
   routed = routed && L.R > 0;
@@ -303,7 +304,7 @@ void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool 
 
   auto launch = [&](const GemmLaunch& G, int epi, const char* name) {
     R.stage(name);
-    R.check(bf ? launch_gemm_bf16(G, epi, R.stream) : launch_gemm_f32(G, epi, R.stream));
+    R.check(bf ? launch_gemm_big(G, epi, R.stream) : launch_gemm_f32(G, epi, R.stream));
   };
 
   if (routed && c->rank > 0) {
@@ -351,7 +352,7 @@ void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool 
       p.N = (int32_t)F;
       p.K = (int32_t)d;
       p.G = (int32_t)S;
-      p.n_tiles_n = (int32_t)(F / (bf ? bn_dual : 64));
+      p.n_tiles_n = (int32_t)ceil_div(F, bn_dual);
       p.max_m_tiles = (int32_t)(S * ceil_div(T, bm));
     }
     if (routed) {
@@ -370,7 +371,7 @@ void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool 
       p.N = (int32_t)F;
       p.K = (int32_t)d;
       p.G = c->n_routed;
-      p.n_tiles_n = (int32_t)(F / (bf ? bn_dual : 64));
+      p.n_tiles_n = (int32_t)ceil_div(F, bn_dual);
       p.max_m_tiles = (int32_t)L.max_tiles;
     }
     G.n_problems = np;

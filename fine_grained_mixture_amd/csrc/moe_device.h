@@ -19,12 +19,9 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
-// Round-to-nearest-even float32 -> bf16 (NaN kept quiet).
+// float32 -> bf16, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
 __device__ __forceinline__ float load_elem(const float* p) { return *p; }
@@ -33,7 +30,10 @@ __device__ __forceinline__ float load_elem(const bf16_t* p) { return bf16_to_f32
 __device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_elem(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU(z) = z * sigmoid(z), with the hardware reciprocal (v_rcp_f32).
+__device__ __forceinline__ float silu_f32(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // Monotone map of a float onto uint32 (larger float -> larger integer).
 __device__ __forceinline__ uint32_t float_orderable(float f) {

@@ -18,6 +18,8 @@ constexpr int kRouteBlock = 64;
 constexpr int kRouteSmallMaxE = 64;
 // Rows per M-tile of the grouped GEMMs.
 constexpr int kGemmBM = 128;
+// Rows per tile of the large-tile expert GEMM (256 x 128 output tiles).
+constexpr int kGemmBigBM = 256;
 constexpr int kGemmBM_F32 = 64;
 // Rows per workgroup of the fused low-rank expert kernel.
 constexpr int kLowRankBM = 64;
@@ -62,6 +64,8 @@ struct GemmLaunch {
 
 hipError_t launch_gemm_bf16(const GemmLaunch& L, int epilogue, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmLaunch& L, int epilogue, hipStream_t s);
+// 256 x 128 tiles (dual: 256 x (64 + 64)); N multiple of 8, K of 32.
+hipError_t launch_gemm_big(const GemmLaunch& L, int epilogue, hipStream_t s);
 // Tile list of a row_off problem from offsets[0..G] (one workgroup).
 hipError_t launch_plan(const int32_t* offsets, int32_t G, int32_t bm, int32_t* plan,
                        hipStream_t s);
