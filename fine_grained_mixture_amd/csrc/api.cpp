@@ -65,7 +65,7 @@ int route_tb(const moe_config* c) { return fused_router(c) ? kRouteBlockSmall : 
 struct Layout {
   int64_t T = 0, R = 0, nblk = 0, max_tiles = 0;
   int tb = kRouteBlock;
-  size_t logits = 0, blk_counts = 0, blk_base = 0, blk_psum = 0, plan = 0;
+  size_t logits = 0, blk_counts = 0, blk_base = 0, blk_psum = 0, psum_tot = 0, plan = 0;
   size_t h = 0, h_sh = 0, y_perm = 0, y_sh = 0, total = 0;
 };
 
@@ -94,6 +94,7 @@ Layout make_layout(const moe_config* c, int64_t T) {
   L.blk_counts = take((size_t)L.nblk * E * 4);
   L.blk_base = take((size_t)L.nblk * E * 4);
   L.blk_psum = take((size_t)L.nblk * E * 4);
+  L.psum_tot = take((size_t)E * 4);
   L.plan = take((size_t)(1 + 2 * L.max_tiles) * 4);
   L.h = take((size_t)L.R * F * es);
   L.h_sh = take((size_t)T * S * F * es);
@@ -222,8 +223,16 @@ void run_route(Runner& R, const moe_config* c, const Layout& L, const void* x,
     G.n_problems = 1;
     G.tiles0 = p.max_m_tiles * p.n_tiles_n;
     R.stage("router_gemm");
-    R.check(c->dtype == MOE_BF16 ? launch_gemm_bf16(G, kEpiStoreF32, R.stream)
-                                 : launch_gemm_f32(G, kEpiStoreF32, R.stream));
+    if (c->dtype == MOE_BF16 && E % 8 == 0) {
+      // many experts: the large-tile kernel (256 x 128 tiles)
+      p.n_tiles_n = (int32_t)ceil_div(E, 128);
+      p.max_m_tiles = (int32_t)ceil_div(T, kGemmBigBM);
+      G.tiles0 = p.max_m_tiles * p.n_tiles_n;
+      R.check(launch_gemm_big(G, kEpiStoreF32, R.stream));
+    } else {
+      R.check(c->dtype == MOE_BF16 ? launch_gemm_bf16(G, kEpiStoreF32, R.stream)
+                                   : launch_gemm_f32(G, kEpiStoreF32, R.stream));
+    }
 
     TopkArgs t{};
     t.logits = logits;
@@ -253,6 +262,7 @@ void run_route(Runner& R, const moe_config* c, const Layout& L, const void* x,
   s.aux = o->aux;
   s.f = o->f;
   s.P = o->P;
+  s.psum_tot = at<float>(ws, L.psum_tot);
   s.plan = with_plan ? at<int32_t>(ws, L.plan) : nullptr;
   s.plan_bm = plan_bm(c);
   s.nblk = (int32_t)L.nblk;

@@ -65,25 +65,60 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+// Intra-row (16-lane) exchanges on the DPP path: after the quad_perm steps a
+// quad holds one value, row_half_mirror pairs quad q with quad 1 - q of each
+// 8, row_mirror pairs the two 8-lane halves of each row.
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = dpp_u32<CTRL>(static_cast<uint32_t>(v));
+  const uint32_t hi = dpp_u32<CTRL>(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    uint64_t o = shfl_xor_u64(v, m);
-    v = o > v ? o : v;
-  }
+  v = max_u64(v, dpp_u64<kDppQuadXor1>(v));
+  v = max_u64(v, dpp_u64<kDppQuadXor2>(v));
+  v = max_u64(v, dpp_u64<kDppRowHalfMirror>(v));
+  v = max_u64(v, dpp_u64<kDppRowMirror>(v));
+  v = max_u64(v, shfl_xor_u64(v, 16));
+  v = max_u64(v, shfl_xor_u64(v, 32));
   return v;
 }
 
-// Butterfly sums: every lane ends with the same value, combined in a fixed
+// Sums and maxima: every lane ends with the same value, combined in a fixed
 // order, so the result does not depend on scheduling.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  v += dpp_f32<kDppQuadXor1>(v);
+  v += dpp_f32<kDppQuadXor2>(v);
+  v += dpp_f32<kDppRowHalfMirror>(v);
+  v += dpp_f32<kDppRowMirror>(v);
+  v += __shfl_xor(v, 16, kWave);
+  v += __shfl_xor(v, 32, kWave);
   return v;
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  v = fmaxf(v, dpp_f32<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
+  v = fmaxf(v, __shfl_xor(v, 16, kWave));
+  v = fmaxf(v, __shfl_xor(v, 32, kWave));
   return v;
 }
 

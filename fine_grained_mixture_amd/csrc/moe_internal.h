@@ -113,6 +113,7 @@ struct ScanArgs {
   float* aux;                 // [2]
   float* f;                   // [E] or null
   float* P;                   // [E] or null
+  float* psum_tot;            // [E] scratch: per-expert probability sums (E > 64)
   int32_t* plan;              // routed tile list (rows per tile plan_bm) or null
   int32_t plan_bm;
   int32_t nblk, E, k, capacity;

@@ -24,13 +24,21 @@ namespace moe {
 namespace {
 
 // ---------------------------------------------------------------------------
-// top-k: one wave per token (tb/4 tokens per wave, 4 waves = one tb-token
-// block per workgroup). Lane l owns experts l, l + 64, ...; each lane keeps its best
+// top-k: one wave per token (16 waves of a 1024-thread workgroup share one
+// tb-token block, tb/16 tokens per wave; the next token's logits are loaded
+// while the current one is reduced). Lane l owns experts l, l + 64, ...; each lane keeps its best
 // KMAX (key, id) pairs, then k+1 rounds of a wave-wide maximum pick the
 // winners in descending key order (equal keys: lower id first).
 // ---------------------------------------------------------------------------
+// Threads per workgroup: as many waves as the per-lane registers allow
+// (EPL logits, keys and sums plus the KMAX-entry candidate list).
 template <int EPL, int KMAX>
-__global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
+constexpr int topk_threads() {
+  return (EPL <= 4 && KMAX <= 8) ? 1024 : (EPL <= 16 ? 512 : 256);
+}
+
+template <int EPL, int KMAX>
+__global__ void __launch_bounds__((topk_threads<EPL, KMAX>())) topk_kernel(TopkArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   int* s_cnt = reinterpret_cast<int*>(smem_raw);                 // [E]
   float* s_ps = reinterpret_cast<float*>(smem_raw) + a.E;        // [E]
@@ -49,19 +57,34 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
   for (int m = 0; m < EPL; ++m) psum[m] = 0.f;
 
   const int rounds = min(k + 1, E);
-  const int per_wave = a.tb >> 2;
+  const int nwaves = blockDim.x >> 6;
+  const int per_wave = a.tb / nwaves;
   const int64_t t_begin = (int64_t)blk * a.tb + wave * per_wave;
-  for (int it = 0; it < per_wave; ++it) {
-    const int64_t t = t_begin + it;
-    if (t >= a.T) break;
+  const int64_t t_end = min(a.T, t_begin + per_wave);
+  float nxt[EPL];
+  if (t_begin < t_end) {
+#pragma unroll
+    for (int m = 0; m < EPL; ++m) {
+      const int e = lane + 64 * m;
+      nxt[m] = e < E ? a.logits[t_begin * E + e] : -FLT_MAX;
+    }
+  }
+  for (int64_t t = t_begin; t < t_end; ++t) {
     const float* lrow = a.logits + t * E;
-
     float l[EPL], key[EPL], sg[EPL];
+#pragma unroll
+    for (int m = 0; m < EPL; ++m) l[m] = nxt[m];
+    if (t + 1 < t_end) {
+#pragma unroll
+      for (int m = 0; m < EPL; ++m) {
+        const int e = lane + 64 * m;
+        nxt[m] = e < E ? lrow[E + e] : -FLT_MAX;
+      }
+    }
 #pragma unroll
     for (int m = 0; m < EPL; ++m) {
       const int e = lane + 64 * m;
       const bool ok = e < E;
-      l[m] = ok ? lrow[e] : -FLT_MAX;
       if (a.score == MOE_SOFTMAX) {
         key[m] = l[m];
         sg[m] = 0.f;
@@ -170,7 +193,7 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
   }
 
   // per-block probability sums: waves add into LDS one after another
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < nwaves; ++w) {
     if (wave == w) {
 #pragma unroll
       for (int m = 0; m < EPL; ++m) {
@@ -229,56 +252,86 @@ __device__ double block_sum_fixed(double v, double* smem) {
   return tot;
 }
 
-constexpr int kScanRG = 16;   // row groups (block ranges) per 64-expert column chunk
+// Column pass of the scan for experts [c0, c0 + CW): per-expert totals of the
+// block tables and each block's exclusive prefix (slots of the expert in
+// earlier blocks, i.e. earlier tokens). 1024 threads: the blocks are split
+// over 1024 / CW row groups, each summing its consecutive blocks.
+__device__ void scan_columns(const ScanArgs& a, int c0, int CW, int* s_part, float* s_fpart,
+                             int* cnt_out, float* psum_out) {
+  const int E = a.E, nblk = a.nblk;
+  const int tid = threadIdx.x;
+  const int RG = 1024 / CW;
+  const int rg = tid / CW, cl = tid - rg * CW;
+  const int per = (nblk + RG - 1) / RG;
+  const int b0 = min(nblk, rg * per), b1 = min(nblk, b0 + per);
+  const int e = c0 + cl;
+  int cs = 0;
+  float ps = 0.f;
+  if (e < E) {
+#pragma unroll 8
+    for (int b = b0; b < b1; ++b) {
+      cs += a.blk_counts[(int64_t)b * E + e];
+      ps += a.blk_psum[(int64_t)b * E + e];
+    }
+  }
+  s_part[tid] = cs;
+  s_fpart[tid] = ps;
+  __syncthreads();
+  if (rg == 0 && e < E) {
+    int run = 0;
+    float pr = 0.f;
+    for (int g = 0; g < RG; ++g) {
+      const int c = s_part[g * CW + cl];
+      s_part[g * CW + cl] = run;
+      run += c;
+      pr += s_fpart[g * CW + cl];
+    }
+    cnt_out[e] = run;
+    psum_out[e] = pr;
+  }
+  __syncthreads();
+  if (e < E) {
+    int run = s_part[tid];
+#pragma unroll 8
+    for (int b = b0; b < b1; ++b) {
+      a.blk_base[(int64_t)b * E + e] = run;
+      run += a.blk_counts[(int64_t)b * E + e];
+    }
+  }
+  __syncthreads();
+}
 
+__device__ __forceinline__ int scan_cw(int E) { return E <= 16 ? 16 : (E <= 32 ? 32 : 64); }
+
+// Many experts: one workgroup per 64-expert column, totals to global memory.
+__global__ void __launch_bounds__(1024) scan_cols_kernel(ScanArgs a) {
+  __shared__ int s_part[1024];
+  __shared__ float s_fpart[1024];
+  scan_columns(a, blockIdx.x * 64, 64, s_part, s_fpart, a.counts, a.psum_tot);
+}
+
+// FUSED: the column pass runs here (few experts); otherwise the totals come
+// from scan_cols_kernel.
+template <bool FUSED>
 __global__ void __launch_bounds__(1024) scan_kernel(ScanArgs a) {
-  __shared__ int s_part[kScanRG][64];
-  __shared__ float s_fpart[kScanRG][64];
+  __shared__ int s_part[1024];
+  __shared__ float s_fpart[1024];
   __shared__ int s_i[16];
   __shared__ double s_d[16];
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   int* s_cnt = reinterpret_cast<int*>(smem_raw);                  // [E]
   float* s_P = reinterpret_cast<float*>(smem_raw) + a.E;          // [E]
 
-  const int E = a.E, nblk = a.nblk;
+  const int E = a.E;
   const int tid = threadIdx.x;
-  const int rg = tid >> 6, cl = tid & 63;
-  const int per = (nblk + kScanRG - 1) / kScanRG;
-  const int b0 = rg * per, b1 = min(nblk, b0 + per);
-
-  // 1) per-expert totals and block prefix (token order across blocks)
-  for (int c0 = 0; c0 < E; c0 += 64) {
-    const int e = c0 + cl;
-    int cs = 0;
-    float ps = 0.f;
-    if (e < E) {
-      for (int b = b0; b < b1; ++b) {
-        cs += a.blk_counts[(int64_t)b * E + e];
-        ps += a.blk_psum[(int64_t)b * E + e];
-      }
-    }
-    s_part[rg][cl] = cs;
-    s_fpart[rg][cl] = ps;
-    __syncthreads();
-    if (rg == 0 && e < E) {
-      int run = 0;
-      float pr = 0.f;
-      for (int g = 0; g < kScanRG; ++g) {
-        const int c = s_part[g][cl];
-        s_part[g][cl] = run;
-        run += c;
-        pr += s_fpart[g][cl];
-      }
-      s_cnt[e] = run;
-      s_P[e] = pr;
-    }
-    __syncthreads();
-    if (e < E) {
-      int run = s_part[rg][cl];
-      for (int b = b0; b < b1; ++b) {
-        a.blk_base[(int64_t)b * E + e] = run;
-        run += a.blk_counts[(int64_t)b * E + e];
-      }
+  // 1) per-expert totals and the block prefix
+  if (FUSED) {
+    const int CW = scan_cw(E);
+    for (int c0 = 0; c0 < E; c0 += CW) scan_columns(a, c0, CW, s_part, s_fpart, s_cnt, s_P);
+  } else {
+    for (int e = tid; e < E; e += blockDim.x) {
+      s_cnt[e] = a.counts[e];
+      s_P[e] = a.psum_tot[e];
     }
     __syncthreads();
   }
@@ -429,7 +482,8 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   const int epl = (a.E + 63) / 64;
   const int k1 = a.k + 1;
 #define MOE_TOPK(EPLV, KM)                                                                  \
-  hipLaunchKernelGGL((topk_kernel<EPLV, KM>), dim3(nblk), dim3(256), shm, s, a)
+  hipLaunchKernelGGL((topk_kernel<EPLV, KM>), dim3(nblk), dim3(topk_threads<EPLV, KM>()), shm, s, \
+                     a)
 #define MOE_TOPK_K(EPLV)                \
   do {                                  \
     if (k1 <= 4) MOE_TOPK(EPLV, 4);     \
@@ -449,7 +503,12 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), (size_t)a.E * 8, s, a);
+  if (a.E <= 64 || !a.psum_tot) {
+    hipLaunchKernelGGL(scan_kernel<true>, dim3(1), dim3(1024), (size_t)a.E * 8, s, a);
+  } else {
+    hipLaunchKernelGGL(scan_cols_kernel, dim3((a.E + 63) / 64), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(scan_kernel<false>, dim3(1), dim3(1024), (size_t)a.E * 8, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -5,10 +5,12 @@
 // One workgroup per 16 tokens:
 //   1. logits[16, E] = x[16, d] W_r[d, E] + logit_bias with
 //      v_mfma_f32_16x16x32_bf16: the token rows are the A operand loaded
-//      straight from memory (8 consecutive k per lane); W_r is staged through
-//      LDS in 256-row chunks, transposed so each lane reads 8 consecutive k of
-//      one expert; the four waves take the k32 steps round-robin and their
-//      partial sums are added in a fixed order;
+//      straight from memory (8 consecutive k per lane); W_r is copied into LDS
+//      in 256-row chunks in its own [k][e] layout and the B operand is read
+//      with ds_read_b64_tr_b16 (lane group of 16: source lane s addresses row
+//      k0 + s/4, experts e0 + 4 (s%4); output lane j gets 4 consecutive k of
+//      expert e0 + j); the four waves take the k32 steps round-robin and
+//      their partial sums are added in a fixed order;
 //   2. one lane per token walks its E scores and keeps the best k+1 in a
 //      register list (strictly larger keys move ahead, so equal keys keep the
 //      lower expert id first), then computes gates and the routing
@@ -27,16 +29,18 @@ namespace {
 
 constexpr int kTB = kRouteBlockSmall;   // tokens per workgroup
 constexpr int kKC = 256;                // rows of W_r per LDS chunk
-constexpr int kLdsW = kKC + 8;          // padded LDS row (elements)
 
-template <int EP, int KMAX>
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef short shortx8 __attribute__((ext_vector_type(8)));
+
+template <int EP, int KMAX, bool VEC>
 __global__ void __launch_bounds__(256) route_small_kernel(RouteSmallArgs a) {
   constexpr int NS = EP / 16;
-  __shared__ __attribute__((aligned(16))) bf16_t Ws[EP * kLdsW];
+  __shared__ __attribute__((aligned(16))) bf16_t Ws[kKC * EP];   // [k][e], row EP
   __shared__ float s_part[4][kTB][EP + 1];
   __shared__ float s_log[kTB][EP + 1];
   __shared__ float s_p[kTB][EP + 1];
-  __shared__ int s_ids[kTB][KMAX];
+  __shared__ int s_cnt[EP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, d = a.d, k = a.k;
@@ -44,8 +48,10 @@ __global__ void __launch_bounds__(256) route_small_kernel(RouteSmallArgs a) {
   const bf16_t* x = static_cast<const bf16_t*>(a.x);
   const bf16_t* W = static_cast<const bf16_t*>(a.w_router);
 
-  // padded expert rows stay zero
-  for (int i = tid; i < (EP - E) * kLdsW; i += 256) Ws[E * kLdsW + i] = 0;
+  if (tid < EP) s_cnt[tid] = 0;
+  // padded expert columns: their logits are never read, but keep them finite
+  if (EP > E)
+    for (int i = tid; i < kKC * (EP - E); i += 256) Ws[(i / (EP - E)) * EP + E + i % (EP - E)] = 0;
 
   floatx4 acc[NS];
 #pragma unroll
@@ -55,22 +61,47 @@ __global__ void __launch_bounds__(256) route_small_kernel(RouteSmallArgs a) {
 
   for (int kc0 = 0; kc0 < d; kc0 += kKC) {
     const int kcn = min(kKC, d - kc0);
-    __syncthreads();
-    const int nel = kcn * E;
-    const bf16_t* wsrc = W + (int64_t)kc0 * E;
-    for (int i = tid; i < nel; i += 256) {
-      const int kk = i / E;
-      const int e = i - kk * E;
-      Ws[e * kLdsW + kk] = wsrc[i];
+    // this wave's token-row fragments of the chunk (k32 steps wave, wave + 4),
+    // requested before the weight staging so their latency overlaps it
+    bf16x8 av[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int ks = wave + 4 * q;
+      if (ks < kcn / 32) av[q] = *reinterpret_cast<const bf16x8*>(xr + kc0 + ks * 32);
     }
     __syncthreads();
-    for (int ks = wave; ks < kcn / 32; ks += 4) {
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(xr + kc0 + ks * 32);
+    const bf16_t* wsrc = W + (int64_t)kc0 * E;
+    if (VEC) {
+      // E % 8 == 0: 16-byte pieces, E / 8 per row
+      const int cpr = E >> 3;
+      for (int i = tid; i < kcn * cpr; i += 256) {
+        const int kk = i / cpr, c = i - kk * cpr;
+        *reinterpret_cast<u32x4*>(&Ws[kk * EP + 8 * c]) =
+            *reinterpret_cast<const u32x4*>(wsrc + (int64_t)kk * E + 8 * c);
+      }
+    } else {
+      for (int i = tid; i < kcn * E; i += 256) {
+        const int kk = i / E, e = i - kk * E;
+        Ws[kk * EP + e] = wsrc[i];
+      }
+    }
+    __syncthreads();
+    const int g16 = lane >> 4, s16 = lane & 15;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int ks = wave + 4 * q;
+      if (ks >= kcn / 32) break;
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(
-            &Ws[(16 * j + (lane & 15)) * kLdsW + ks * 32 + 8 * (lane >> 4)]);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[j], 0, 0, 0);
+        // B operand: 8 consecutive k (32 ks + 8 g16 ..) of expert 16 j + s16
+        const bf16_t* p0 = &Ws[(ks * 32 + 8 * g16 + (s16 >> 2)) * EP + 16 * j + 4 * (s16 & 3)];
+        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) shortx4*)p0);
+        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) shortx4*)(p0 + 4 * EP));
+        const shortx8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[q], __builtin_bit_cast(bf16x8, v),
+                                                         acc[j], 0, 0, 0);
       }
     }
   }
@@ -151,12 +182,10 @@ __global__ void __launch_bounds__(256) route_small_kernel(RouteSmallArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
-      if (j < k) {
-        s_ids[lane][j] = valid ? ki[j] : -1;
-        if (valid) {
-          a.topk_idx[t * k + j] = ki[j];
-          a.topk_gate[t * k + j] = gates[j];
-        }
+      if (j < k && valid) {
+        a.topk_idx[t * k + j] = ki[j];
+        a.topk_gate[t * k + j] = gates[j];
+        atomicAdd(&s_cnt[ki[j]], 1);   // integer counts: order-independent
       }
     }
     if (valid && a.topk_margin) {
@@ -170,13 +199,10 @@ __global__ void __launch_bounds__(256) route_small_kernel(RouteSmallArgs a) {
   __syncthreads();
 
   for (int e = tid; e < E; e += 256) {
-    int c = 0;
     float ps = 0.f;
-    for (int t = 0; t < kTB; ++t) {
-      ps += s_p[t][e];
-      for (int j = 0; j < k; ++j) c += s_ids[t][j] == e;
-    }
-    a.blk_counts[(int64_t)blockIdx.x * E + e] = c;
+#pragma unroll
+    for (int t = 0; t < kTB; ++t) ps += s_p[t][e];
+    a.blk_counts[(int64_t)blockIdx.x * E + e] = s_cnt[e];
     a.blk_psum[(int64_t)blockIdx.x * E + e] = ps;
   }
 }
@@ -189,8 +215,15 @@ hipError_t launch_route_small(const RouteSmallArgs& a, hipStream_t s) {
   if (a.E > kRouteSmallMaxE || a.k + 1 > 16) return hipErrorInvalidValue;
   const int ep = (a.E + 15) / 16 * 16;
   const int k1 = a.k + 1;
-#define MOE_RS(EPV, KM) \
-  hipLaunchKernelGGL((route_small_kernel<EPV, KM>), dim3((unsigned)nblk), dim3(256), 0, s, a)
+#define MOE_RS(EPV, KM)                                                                      \
+  do {                                                                                       \
+    if (a.E % 8 == 0)                                                                        \
+      hipLaunchKernelGGL((route_small_kernel<EPV, KM, true>), dim3((unsigned)nblk), dim3(256), 0, \
+                         s, a);                                                              \
+    else                                                                                     \
+      hipLaunchKernelGGL((route_small_kernel<EPV, KM, false>), dim3((unsigned)nblk), dim3(256), \
+                         0, s, a);                                                           \
+  } while (0)
 #define MOE_RS_K(EPV)                \
   do {                               \
     if (k1 <= 4) MOE_RS(EPV, 4);     \
