@@ -38,7 +38,25 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=1536,
                     help="tokens of the workload the CPU oracle processes")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of the layer, run 3 plain device copies of this many MiB "
+                         "(calibrates the HBM byte counters of a profiler run)")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int):
+    """Three launches of a plain elementwise copy (y = x * 1) of `mib` MiB of
+    float32: each reads and writes exactly mib MiB."""
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, device="cuda:0", dtype=torch.float32)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4,
+                      "launches": 3}))
 
 
 def algorithmic(wl, rows):
@@ -106,6 +124,9 @@ def main():
         print("bench.py measures one GPU only: this MoE layer build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_mib > 0:
+        copy_calibration(args.copy_mib)
+        return
     import numpy as np
     import torch
 
