@@ -21,7 +21,8 @@
 // tiles; the swizzle is applied by choosing which global chunk each lane
 // fetches. A three-stage ring keeps two K-steps in flight: each wave waits for
 // its own loads of the step (vmcnt), one workgroup barrier per step publishes
-// it and releases the stage the next loads overwrite.
+// it and releases the stage the next loads overwrite. The loads of a step are
+// interleaved with the MFMAs of the step two behind it.
 //
 // The epilogue stages each wave's results through a private LDS slice and
 // writes whole 16-byte pieces of rows (fp32 rows, or bf16 h = SiLU(gate) * up).
@@ -185,15 +186,25 @@ gemm_big_kernel(GemmLaunch L) {
   for (int j = 0; j < 2; ++j) bcol[j] = (DUAL ? 64 * j + 32 * wn : 64 * wn + 32 * j) + bn_lane;
 
   typedef short shortx8 __attribute__((ext_vector_type(8)));
-  auto compute = [&](int st) {
+  const int nk = K / kBK;
+  // One K-step: the fragments of both k16 halves are requested first; the six
+  // direct-to-LDS loads of step kt_next go out one after each of the first six
+  // MFMAs. A load whose issue stalls (the CU's load path is shared by eight
+  // waves) then waits behind MFMAs already in flight instead of in front of
+  // them.
+  auto step = [&](int st, int kt_next) {
     const unsigned char* As = smem + st * kStageBytes;
     const unsigned char* Bs = As + kAStage * 2;
+    const uint32_t Asn = smem_base + (kt_next % kStages) * kStageBytes;
+    const uint32_t Bsn = Asn + kAStage * 2;
+    const int k0n = kt_next * kBK;
+    const bool do_issue = kt_next < nk;
+    bf16x8 a[2][4], b[2][2];
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8 a[4], b[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(As + a_off(128 * wm + 32 * i + l32, 2 * ks + lhi));
+        a[ks][i] = *reinterpret_cast<const bf16x8*>(As + a_off(128 * wm + 32 * i + l32, 2 * ks + lhi));
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int k = 16 * ks + bk_lane;
@@ -205,19 +216,25 @@ gemm_big_kernel(GemmLaunch L) {
         const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) shortx4*)(Bs + o1));
         const shortx8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        b[j] = __builtin_bit_cast(bf16x8, v);
+        b[ks][j] = __builtin_bit_cast(bf16x8, v);
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int q = 0; q < 16; ++q) {
+      const int ks = q >> 3, i = (q >> 1) & 3, j = q & 1;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0);
+      if (do_issue && q < 6) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (q < 4) dma16(a_src[q] + k0n, Asn + (4 * wave_u + q) * 1024);
+        else dma16(b_src + (int64_t)(k0n + 4 * (q - 4)) * ldb, Bsn + (2 * wave_u + q - 4) * 1024);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
   constexpr int kWaitVm6 = 6 | (7 << 4) | (15 << 8);
   constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
-  const int nk = K / kBK;
   issue(0);
   if (nk > 1) issue(1);
   for (int kt = 0; kt < nk; ++kt) {
@@ -226,8 +243,7 @@ gemm_big_kernel(GemmLaunch L) {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();   // stage kt published; stage (kt - 1) % 3 released
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + 2 < nk) issue(kt + 2);
-    compute(kt % kStages);
+    step(kt % kStages, kt + 2);
     __builtin_amdgcn_sched_barrier(0);
   }
 
