@@ -64,17 +64,17 @@ def algorithmic(wl, rows):
     T, d, E, k, S, F, r = wl.T, wl.hidden, wl.n_routed, wl.top_k, wl.n_shared, wl.ffn, wl.rank
     b = 2 if wl.dtype == "bf16" else 4
     if r == 0:
-        gate_up = 4.0 * d * F * (rows + S * T)
-        down = 2.0 * d * F * (rows + S * T)
+        gate_up = 4.0 * d * F * rows
+        down = 2.0 * d * F * rows
     else:
-        per = 2.0 * (2 * (d * r + r * F) + (F * r + r * d))
-        gate_up = rows * 2.0 * 2 * (d * r + r * F) + 4.0 * d * F * S * T
-        down = rows * 2.0 * (F * r + r * d) + 2.0 * d * F * S * T
-        del per
+        gate_up = rows * 2.0 * 2 * (d * r + r * F)
+        down = rows * 2.0 * (F * r + r * d)
     return dict(
         router_flops=2.0 * T * d * E,
         gate_up_flops=gate_up,
         down_flops=down,
+        shared_gate_up_flops=4.0 * d * F * S * T,
+        shared_down_flops=2.0 * d * F * S * T,
         route_bytes=T * d * b + d * E * b + T * E * 4,
         topk_bytes=T * E * 4 + 8 * T * k,
         combine_bytes=rows * d * 4 + (T * d * 4 if S > 0 else 0) + T * d * 4 + 8 * T * k,
@@ -173,8 +173,9 @@ def main():
     ms_total = t_start.elapsed_time(t_end)
     ms_per_step = ms_total / args.steps
 
-    # per-kernel durations: the same steps with events between the kernels
-    n_ev = 16
+    # per-kernel durations: the same steps with a start and an end event
+    # around every kernel, on the stream it runs on
+    n_ev = 32
     ev_sets = []
     for _ in range(args.steps):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
@@ -190,22 +191,33 @@ def main():
     dur = {n: [] for n in names}
     for evs in ev_sets:
         for i, n in enumerate(names):
-            dur[n].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)   # us
+            dur[n].append(evs[2 * i].elapsed_time(evs[2 * i + 1]) * 1e3)   # us
     stage_us = {n: float(np.mean(v)) for n, v in dur.items()}
     stage_us_med = {n: float(np.median(v)) for n, v in dur.items()}
 
     rows = int(out["offsets"][-1].item())
     alg = algorithmic(wl, rows)
     kernel_src = os.path.join(ROOT, "fine_grained_mixture_amd", "csrc", "gemm_big.hip")
+    # every expert GEMM stage present and its algorithmic FLOPs
+    gemm_stages = {"gate_up_gemm": alg["gate_up_flops"], "down_gemm": alg["down_flops"],
+                   "lowrank_experts": alg["gate_up_flops"] + alg["down_flops"],
+                   "shared_gate_up_gemm": alg["shared_gate_up_flops"],
+                   "shared_down_gemm": alg["shared_down_flops"]}
+    if "shared_gate_up_gemm" not in stage_us:
+        # the shared experts run inside the routed launches
+        gemm_stages["gate_up_gemm"] += alg["shared_gate_up_flops"]
+        gemm_stages["down_gemm"] += alg["shared_down_flops"]
+    present = {n: f for n, f in gemm_stages.items() if n in stage_us}
+    expert_tflops = sum(present.values()) / (sum(stage_us[n] for n in present) * 1e-6) / 1e12
     if wl.rank == 0 and wl.dtype == "bf16":
-        # dominant kernel: the fused gate/up grouped GEMM (MFMA bound)
+        # dominant kernel: the fused gate/up grouped GEMM of the routed experts
+        # (MFMA bound)
         dom = "gate_up_gemm"
-        gu_us, dn_us = stage_us["gate_up_gemm"], stage_us["down_gemm"]
-        achieved = alg["gate_up_flops"] / (gu_us * 1e-6) / 1e12
+        gu_us = stage_us["gate_up_gemm"]
+        achieved = gemm_stages["gate_up_gemm"] / (gu_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                 "traffic": traffic_from_profile(kernel_src)}
-        expert_tflops = (alg["gate_up_flops"] + alg["down_flops"]) / ((gu_us + dn_us) * 1e-6) / 1e12
     elif wl.rank > 0:
         # dominant kernel: the fused low-rank experts, bound by streaming the
         # factor weights of every expert that received rows
@@ -220,14 +232,12 @@ def main():
         roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
                 "algorithmic_bytes": wbytes + io}
-        expert_tflops = (alg["gate_up_flops"] + alg["down_flops"]) / (us * 1e-6) / 1e12
     else:
         dom = "gate_up_gemm"
-        gu_us, dn_us = stage_us["gate_up_gemm"], stage_us["down_gemm"]
-        achieved = alg["gate_up_flops"] / (gu_us * 1e-6) / 1e12
+        gu_us = stage_us["gate_up_gemm"]
+        achieved = gemm_stages["gate_up_gemm"] / (gu_us * 1e-6) / 1e12
         roof = {"bound": "alu", "kernel": dom, "achieved": achieved, "peak": 157.3,
                 "unit": "TFLOP/s", "frac": achieved / 157.3, "traffic": None}
-        expert_tflops = (alg["gate_up_flops"] + alg["down_flops"]) / ((gu_us + dn_us) * 1e-6) / 1e12
     result = {
         "metric": "MoE layer fwd tokens/s + expert-GEMM TFLOP/s (% MFMA peak), Quartz shape",
         "value": wl.T / (ms_per_step * 1e-3),
@@ -252,7 +262,8 @@ def main():
         "stage_us_mean": stage_us,
         "stage_us_median": stage_us_med,
         "combine_gbs": alg["combine_bytes"] / (stage_us["combine"] * 1e-6) / 1e9,
-        "layer_flops": alg["router_flops"] + alg["gate_up_flops"] + alg["down_flops"],
+        "layer_flops": alg["router_flops"] + alg["gate_up_flops"] + alg["down_flops"]
+        + alg["shared_gate_up_flops"] + alg["shared_down_flops"],
         "wall_s_timed_region": wall,
     }
     if not args.no_cpu:

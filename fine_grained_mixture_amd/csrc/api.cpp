@@ -109,27 +109,34 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<unsigned char*>(ws) + off);
 }
 
-// Launch bookkeeping: optional events before every launch, names for
-// moe_stage_name().
-struct Runner {
-  hipStream_t stream;
+// Launch bookkeeping shared by the streams of one call: stage names for
+// moe_stage_name() and, when timing, a start and an end event per stage
+// recorded on the stream the stage runs on.
+struct Timeline {
   void** events = nullptr;
   int n_events = 0;
   int n = 0;
   hipError_t err = hipSuccess;
+};
 
-  void stage(const char* name) {
-    if (events && n < n_events) hipEventRecord(static_cast<hipEvent_t>(events[n]), stream);
-    if (n < 64) g_stage_names[n] = name;
-    ++n;
+struct Runner {
+  hipStream_t stream;
+  Timeline* tl;
+
+  // Launches one kernel (launch() returns its hipError_t) as stage `name`.
+  template <class F>
+  void run(const char* name, F&& launch) {
+    const int i = tl->n++;
+    if (i < 64) g_stage_names[i] = name;
+    hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(tl->events);
+    const bool timed = ev && 2 * i + 1 < tl->n_events;
+    if (timed) check(hipEventRecord(ev[2 * i], stream));
+    check(launch());
+    if (timed) check(hipEventRecord(ev[2 * i + 1], stream));
   }
   bool check(hipError_t e) {
-    if (e != hipSuccess && err == hipSuccess) err = e;
+    if (e != hipSuccess && tl->err == hipSuccess) tl->err = e;
     return e == hipSuccess;
-  }
-  void finish() {
-    if (events && n < n_events) hipEventRecord(static_cast<hipEvent_t>(events[n]), stream);
-    g_n_stages = n;
   }
 };
 
@@ -200,8 +207,7 @@ void run_route(Runner& R, const moe_config* c, const Layout& L, const void* x,
     r.k = c->top_k;
     r.score = c->score;
     r.renorm = c->renorm_topk;
-    R.stage("route");
-    R.check(launch_route_small(r, R.stream));
+    R.run("route", [&] { return launch_route_small(r, R.stream); });
   } else if (T > 0) {
     GemmLaunch G{};
     GemmProblem& p = G.p[0];
@@ -222,16 +228,17 @@ void run_route(Runner& R, const moe_config* c, const Layout& L, const void* x,
     p.max_m_tiles = (int32_t)ceil_div(T, bm);
     G.n_problems = 1;
     G.tiles0 = p.max_m_tiles * p.n_tiles_n;
-    R.stage("router_gemm");
     if (c->dtype == MOE_BF16 && E % 8 == 0) {
       // many experts: the large-tile kernel (256 x 128 tiles)
       p.n_tiles_n = (int32_t)ceil_div(E, 128);
       p.max_m_tiles = (int32_t)ceil_div(T, kGemmBigBM);
       G.tiles0 = p.max_m_tiles * p.n_tiles_n;
-      R.check(launch_gemm_big(G, kEpiStoreF32, R.stream));
+      R.run("router_gemm", [&] { return launch_gemm_big(G, kEpiStoreF32, R.stream); });
     } else {
-      R.check(c->dtype == MOE_BF16 ? launch_gemm_bf16(G, kEpiStoreF32, R.stream)
-                                   : launch_gemm_f32(G, kEpiStoreF32, R.stream));
+      R.run("router_gemm", [&] {
+        return c->dtype == MOE_BF16 ? launch_gemm_bf16(G, kEpiStoreF32, R.stream)
+                                    : launch_gemm_f32(G, kEpiStoreF32, R.stream);
+      });
     }
 
     TopkArgs t{};
@@ -248,8 +255,7 @@ void run_route(Runner& R, const moe_config* c, const Layout& L, const void* x,
     t.score = c->score;
     t.renorm = c->renorm_topk;
     t.tb = L.tb;
-    R.stage("topk");
-    R.check(launch_topk(t, R.stream));
+    R.run("topk", [&] { return launch_topk(t, R.stream); });
   }
   ScanArgs s{};
   s.blk_counts = at<int32_t>(ws, L.blk_counts);
@@ -271,8 +277,7 @@ void run_route(Runner& R, const moe_config* c, const Layout& L, const void* x,
   s.capacity = c->capacity;
   s.T = T;
   s.aux_coef = c->aux_coef;
-  R.stage("scan");
-  R.check(launch_scan(s, R.stream));
+  R.run("scan", [&] { return launch_scan(s, R.stream); });
 }
 
 void run_rank(Runner& R, const moe_config* c, const Layout& L, moe_outputs* o, void* ws) {
@@ -290,8 +295,7 @@ void run_rank(Runner& R, const moe_config* c, const Layout& L, moe_outputs* o, v
   r.capacity = c->capacity;
   r.nblk = (int32_t)L.nblk;
   r.tb = L.tb;
-  R.stage("rank");
-  R.check(launch_rank(r, R.stream));
+  R.run("rank", [&] { return launch_rank(r, R.stream); });
 }
 
 // Expert FFN launches. Routed rows: A = a_routed with optional row gather;
@@ -313,8 +317,9 @@ void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool 
   const int32_t* plan = at<int32_t>(ws, L.plan);
 
   auto launch = [&](const GemmLaunch& G, int epi, const char* name) {
-    R.stage(name);
-    R.check(bf ? launch_gemm_big(G, epi, R.stream) : launch_gemm_f32(G, epi, R.stream));
+    R.run(name, [&] {
+      return bf ? launch_gemm_big(G, epi, R.stream) : launch_gemm_f32(G, epi, R.stream);
+    });
   };
 
   if (routed && c->rank > 0) {
@@ -338,11 +343,13 @@ void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool 
     lr.F = (int32_t)F;
     lr.E = c->n_routed;
     lr.max_tiles = (int32_t)L.max_tiles;
-    R.stage("lowrank_experts");
-    R.check(launch_lowrank(lr, R.stream));
-    routed = false;                 // the dense launches below serve the shared experts
-    if (!shared) return;
+    R.run("lowrank_experts", [&] { return launch_lowrank(lr, R.stream); });
   }
+  if (c->rank > 0) routed = false;   // the dense launches below serve the shared experts
+  if (!routed && !shared) return;
+  // stage names: routed and shared launches are told apart when only one
+  // group is present
+  const bool both = routed && shared;
   // gate/up with fused SiLU * up
   {
     GemmLaunch G{};
@@ -386,7 +393,7 @@ void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool 
     }
     G.n_problems = np;
     G.tiles0 = G.p[0].max_m_tiles * G.p[0].n_tiles_n;
-    launch(G, kEpiSwiGLU, "gate_up_gemm");
+    launch(G, kEpiSwiGLU, both || routed ? "gate_up_gemm" : "shared_gate_up_gemm");
   }
   // down projection
   {
@@ -426,7 +433,7 @@ void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool 
     }
     G.n_problems = np;
     G.tiles0 = G.p[0].max_m_tiles * G.p[0].n_tiles_n;
-    launch(G, kEpiStoreF32, "down_gemm");
+    launch(G, kEpiStoreF32, both || routed ? "down_gemm" : "shared_down_gemm");
   }
 }
 
@@ -444,13 +451,12 @@ void run_combine(Runner& R, const moe_config* c, int64_t T, const float* y_route
   a.d = c->hidden;
   a.k = c->top_k;
   a.dtype = c->dtype;
-  R.stage("combine");
-  R.check(launch_combine(a, R.stream));
+  R.run("combine", [&] { return launch_combine(a, R.stream); });
 }
 
-int finish(Runner& R) {
-  R.finish();
-  if (R.err != hipSuccess) return hip_fail(R.err);
+int finish(Timeline& tl) {
+  g_n_stages = tl.n;
+  if (tl.err != hipSuccess) return hip_fail(tl.err);
   return MOE_OK;
 }
 
@@ -466,15 +472,16 @@ int layer_forward(const moe_config* c, int64_t T, const void* x, const moe_weigh
     return MOE_EINVAL;
   Layout L;
   if ((st = check_ws(c, T, ws, ws_bytes, L))) return st;
-  Runner R{static_cast<hipStream_t>(stream), events, n_events};
-  run_route(R, c, L, x, w, o, ws, true);
-  run_rank(R, c, L, o, ws);
+  Timeline tl{events, n_events};
+  Runner R{static_cast<hipStream_t>(stream), &tl};
   float* y_perm = at<float>(ws, L.y_perm);
   float* y_sh = c->n_shared > 0 ? at<float>(ws, L.y_sh) : nullptr;
+  run_route(R, c, L, x, w, o, ws, true);
+  run_rank(R, c, L, o, ws);
   run_ffn(R, c, L, true, true, x, o->sorted_token, o->offsets, x, w, y_perm, y_sh, ws);
   run_combine(R, c, T, y_perm, y_sh, o);
-  st = finish(R);
-  return st ? st : R.n;
+  st = finish(tl);
+  return st ? st : tl.n;
 }
 
 }  // namespace
@@ -511,9 +518,10 @@ int moe_route(const moe_config* c, int64_t T, const void* x, const moe_weights* 
   if (c->score == MOE_SOFTMAX && w->select_bias) return MOE_EINVAL;
   Layout L;
   if ((st = check_ws(c, T, ws, ws_bytes, L))) return st;
-  Runner R{static_cast<hipStream_t>(stream)};
+  Timeline tl;
+  Runner R{static_cast<hipStream_t>(stream), &tl};
   run_route(R, c, L, x, w, o, ws, false);
-  return finish(R);
+  return finish(tl);
 }
 
 int moe_permute(const moe_config* c, int64_t T, const void* x, moe_outputs* o, void* x_perm,
@@ -525,14 +533,16 @@ int moe_permute(const moe_config* c, int64_t T, const void* x, moe_outputs* o, v
   if (x_perm && !x && T > 0) return MOE_EINVAL;
   Layout L;
   if ((st = check_ws(c, T, ws, ws_bytes, L))) return st;
-  Runner R{static_cast<hipStream_t>(stream)};
+  Timeline tl;
+  Runner R{static_cast<hipStream_t>(stream), &tl};
   run_rank(R, c, L, o, ws);
   if (x_perm && L.R > 0) {
-    R.stage("gather");
-    R.check(launch_gather(x, o->sorted_token, o->offsets, c->n_routed, L.R,
-                          (int64_t)c->hidden * elem_size(c), x_perm, R.stream));
+    R.run("gather", [&] {
+      return launch_gather(x, o->sorted_token, o->offsets, c->n_routed, L.R,
+                           (int64_t)c->hidden * elem_size(c), x_perm, R.stream);
+    });
   }
-  return finish(R);
+  return finish(tl);
 }
 
 int moe_grouped_ffn(const moe_config* c, int64_t T, int32_t groups, const void* x_perm,
@@ -548,14 +558,16 @@ int moe_grouped_ffn(const moe_config* c, int64_t T, int32_t groups, const void* 
   if (shared && T > 0 && (!x_shared || !y_shared)) return MOE_EINVAL;
   Layout L;
   if ((st = check_ws(c, T, ws, ws_bytes, L))) return st;
-  Runner R{static_cast<hipStream_t>(stream)};
+  Timeline tl;
+  Runner R{static_cast<hipStream_t>(stream), &tl};
   if (routed && L.R > 0) {
-    R.stage("plan");
-    R.check(launch_plan(offsets, c->n_routed, plan_bm(c), at<int32_t>(ws, L.plan), R.stream));
+    R.run("plan", [&] {
+      return launch_plan(offsets, c->n_routed, plan_bm(c), at<int32_t>(ws, L.plan), R.stream);
+    });
   }
   run_ffn(R, c, L, routed, shared, x_perm, nullptr, offsets, x_shared, w, y_routed, y_shared,
           ws);
-  return finish(R);
+  return finish(tl);
 }
 
 int moe_combine(const moe_config* c, int64_t T, const float* y_routed, const float* y_shared,
@@ -565,9 +577,10 @@ int moe_combine(const moe_config* c, int64_t T, const float* y_routed, const flo
   if (!o || (T > 0 && (!o->row_of_slot || !o->topk_gate || !o->y))) return MOE_EINVAL;
   if (T > 0 && !y_routed) return MOE_EINVAL;
   if (c->n_shared > 0 && T > 0 && !y_shared) return MOE_EINVAL;
-  Runner R{static_cast<hipStream_t>(stream)};
+  Timeline tl;
+  Runner R{static_cast<hipStream_t>(stream), &tl};
   run_combine(R, c, T, y_routed, c->n_shared > 0 ? y_shared : nullptr, o);
-  return finish(R);
+  return finish(tl);
 }
 
 int moe_layer_forward(const moe_config* c, int64_t T, const void* x, const moe_weights* w,

@@ -407,6 +407,135 @@ __global__ void __launch_bounds__(1024) scan_kernel(ScanArgs a) {
   }
 }
 
+// Few experts (E <= 64): the blocks are split into 16 contiguous parts, one
+// wave each, lane e summing expert e over its part; after one workgroup
+// barrier every wave writes the block prefix of its part and wave 0 alone
+// derives the per-expert outputs with wave-wide scans, so the kernel is two
+// rounds of global loads and no further synchronisation.
+constexpr int kScanParts = 16;
+constexpr int kScanReg = 16;   // a part of at most this many blocks stays in registers
+
+__global__ void __launch_bounds__(1024) scan_small_kernel(ScanArgs a) {
+  __shared__ int s_c[kScanParts][64];
+  __shared__ float s_p[kScanParts][64];
+  const int E = a.E, nblk = a.nblk;
+  const int e = lane_id(), part = threadIdx.x >> 6;
+  const bool ve = e < E;
+  const int b0 = (int)((int64_t)part * nblk / kScanParts);
+  const int b1 = (int)((int64_t)(part + 1) * nblk / kScanParts);
+  const bool in_reg = b1 - b0 <= kScanReg;
+
+  // 1) this part's totals, blocks in order
+  int creg[kScanReg];
+  int cs = 0;
+  float ps = 0.f;
+  if (ve && in_reg) {
+    float preg[kScanReg];
+#pragma unroll
+    for (int i = 0; i < kScanReg; ++i) {
+      const bool in = b0 + i < b1;
+      creg[i] = in ? a.blk_counts[(int64_t)(b0 + i) * E + e] : 0;
+      preg[i] = in ? a.blk_psum[(int64_t)(b0 + i) * E + e] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kScanReg; ++i) {
+      cs += creg[i];
+      ps += preg[i];
+    }
+  } else if (ve) {
+#pragma unroll 8
+    for (int b = b0; b < b1; ++b) {
+      cs += a.blk_counts[(int64_t)b * E + e];
+      ps += a.blk_psum[(int64_t)b * E + e];
+    }
+  }
+  s_c[part][e] = cs;
+  s_p[part][e] = ps;
+  __syncthreads();
+
+  // 2) block prefix: slots of expert e in the blocks before each block
+  if (ve) {
+    int base = 0;
+    for (int q = 0; q < part; ++q) base += s_c[q][e];
+    if (in_reg) {
+#pragma unroll
+      for (int i = 0; i < kScanReg; ++i) {
+        if (b0 + i < b1) a.blk_base[(int64_t)(b0 + i) * E + e] = base;
+        base += creg[i];
+      }
+    } else {
+      for (int b = b0; b < b1; ++b) {
+        a.blk_base[(int64_t)b * E + e] = base;
+        base += a.blk_counts[(int64_t)b * E + e];
+      }
+    }
+  }
+  if (part != 0) return;
+
+  // 3) wave 0: totals, capacity, offsets, drops
+  int c = 0;
+  float P = 0.f;
+  if (ve) {
+    for (int q = 0; q < kScanParts; ++q) {
+      c += s_c[q][e];
+      P += s_p[q][e];
+    }
+  }
+  const int kp = ve ? (a.capacity > 0 ? min(c, a.capacity) : c) : 0;
+  int incl = kp;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(incl, o, 64);
+    if (e >= o) incl += n;
+  }
+  const int excl = incl - kp;
+  const int total_kept = __shfl(incl, 63, 64);
+  int drop = c - kp;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) drop += __shfl_xor(drop, m, 64);
+  if (ve) {
+    a.counts[e] = c;
+    a.kept[e] = kp;
+    a.offsets[e] = excl;
+  }
+  if (e == 0) {
+    a.offsets[E] = total_kept;
+    a.n_dropped[0] = drop;
+  }
+
+  // 4) aux statistic: f_e = counts_e / (T k), P_e = psum_e / T
+  const double fe = ve && a.T > 0 ? (double)c / ((double)a.T * a.k) : 0.0;
+  const double Pe = ve && a.T > 0 ? (double)P / (double)a.T : 0.0;
+  if (ve && a.f) a.f[e] = (float)fe;
+  if (ve && a.P) a.P[e] = (float)Pe;
+  double prod = fe * Pe;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) prod += __shfl_xor(prod, m, 64);
+  if (e == 0) {
+    const double raw = (double)E * prod;
+    a.aux[0] = (float)raw;
+    a.aux[1] = (float)(a.aux_coef * raw);
+  }
+
+  // 5) tile list of the routed grouped GEMM, (expert, first row) in expert order
+  if (a.plan) {
+    const int nt = (kp + a.plan_bm - 1) / a.plan_bm;
+    int ti = nt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int n = __shfl_up(ti, o, 64);
+      if (e >= o) ti += n;
+    }
+    const int total = __shfl(ti, 63, 64);
+    int tp = ti - nt;
+    for (int r = 0; r < kp; r += a.plan_bm, ++tp) {
+      a.plan[1 + 2 * tp] = e;
+      a.plan[2 + 2 * tp] = excl + r;
+    }
+    if (e == 0) a.plan[0] = total;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // rank: one wave per 64-token block, 4 blocks per workgroup. Slots are visited
 // in token order (t, then j) 64 at a time; lanes holding the same expert are
@@ -415,22 +544,37 @@ __global__ void __launch_bounds__(1024) scan_kernel(ScanArgs a) {
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) rank_kernel(RankArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  constexpr int kMaxChunks = 15;   // tb * k / 64 with tb = 64, k <= 15
   const int E = a.E, k = a.k;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-  int* cnt = reinterpret_cast<int*>(smem_raw) + wave * E;
+  int* cnt = reinterpret_cast<int*>(smem_raw) + wave * 2 * E;
+  int* offs = cnt + E;
   const int b = blockIdx.x * 4 + wave;
   if (b >= a.nblk) return;
-  for (int e = lane; e < E; e += 64) cnt[e] = a.blk_base[(int64_t)b * E + e];
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
 
   const int64_t s_begin = (int64_t)b * a.tb * k;
   const int64_t s_end = min(a.T, (int64_t)(b + 1) * a.tb) * k;
+  // every expert id of the block and its base counts, requested at once
+  int ids[kMaxChunks];
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const int64_t s = s_begin + 64 * c + lane;
+    ids[c] = s < s_end ? a.topk_idx[s] : -1;
+  }
+  for (int e = lane; e < E; e += 64) {
+    cnt[e] = a.blk_base[(int64_t)b * E + e];
+    offs[e] = a.offsets[e];
+  }
+  __builtin_amdgcn_wave_barrier();
   const uint64_t lt = lanemask_lt();
-  for (int64_t base = s_begin; base < s_end; base += 64) {
-    const int64_t s = base + lane;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const int64_t s = s_begin + 64 * c + lane;
+    if (s_begin + 64 * c >= s_end) break;
     const bool valid = s < s_end;
-    const int e = valid ? a.topk_idx[s] : 0;
+    const int e = valid ? ids[c] : 0;
     uint64_t match = __ballot(valid);
     for (int bit = 0; bit < nbits; ++bit) {
       const bool on = (e >> bit) & 1;
@@ -446,7 +590,7 @@ __global__ void __launch_bounds__(256) rank_kernel(RankArgs a) {
     __builtin_amdgcn_wave_barrier();
     if (valid) {
       const bool keep = a.capacity == 0 || pos < a.capacity;
-      const int row = keep ? a.offsets[e] + pos : -1;
+      const int row = keep ? offs[e] + pos : -1;
       a.row_of_slot[s] = row;
       if (keep) a.sorted_token[row] = (int32_t)(s / k);
       if (a.dropped) a.dropped[s] = keep ? 0 : 1;
@@ -503,7 +647,9 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
-  if (a.E <= 64 || !a.psum_tot) {
+  if (a.E <= 64) {
+    hipLaunchKernelGGL(scan_small_kernel, dim3(1), dim3(1024), 0, s, a);
+  } else if (!a.psum_tot) {
     hipLaunchKernelGGL(scan_kernel<true>, dim3(1), dim3(1024), (size_t)a.E * 8, s, a);
   } else {
     hipLaunchKernelGGL(scan_cols_kernel, dim3((a.E + 63) / 64), dim3(1024), 0, s, a);
@@ -514,7 +660,8 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
 
 hipError_t launch_rank(const RankArgs& a, hipStream_t s) {
   if (a.nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL(rank_kernel, dim3((a.nblk + 3) / 4), dim3(256), (size_t)a.E * 16, s, a);
+  if ((int64_t)a.tb * a.k > 64 * 15) return hipErrorInvalidValue;   // ids held in registers
+  hipLaunchKernelGGL(rank_kernel, dim3((a.nblk + 3) / 4), dim3(256), (size_t)a.E * 32, s, a);
   return hipGetLastError();
 }
 

@@ -170,15 +170,16 @@ int moe_combine(const moe_config *cfg, int64_t T, const float *y_routed,
                 const float *y_shared, moe_outputs *o, void *stream);
 
 /* The whole layer forward (route, permute, grouped FFN for routed and shared
-   experts, combine). Intermediates live in ws; fills every output of o.       */
+   experts, combine). Intermediates live in ws; fills every output of o.     */
 int moe_layer_forward(const moe_config *cfg, int64_t T, const void *x,
                       const moe_weights *w, moe_outputs *o, void *ws, size_t ws_bytes,
                       void *stream);
 
-/* Same as moe_layer_forward, and records events[i] (hipEvent_t, caller-created)
-   on `stream` before the i-th kernel launch, plus one after the last, for
-   i < n_events; returns the number of kernels launched (>= 0) or a moe_status.
-   moe_stage_name(i) names the i-th kernel of the last such call.             */
+/* Same as moe_layer_forward, and records events[2i] and events[2i+1]
+   (hipEvent_t, caller-created) immediately before and after the launch of
+   kernel i, on the stream that kernel runs on, for 2i+1 < n_events; returns
+   the number of kernels launched (>= 0) or a moe_status. moe_stage_name(i)
+   names kernel i of the last such call.                                     */
 int moe_layer_forward_timed(const moe_config *cfg, int64_t T, const void *x,
                             const moe_weights *w, moe_outputs *o, void *ws,
                             size_t ws_bytes, void *stream, void **events, int n_events);
