@@ -60,7 +60,9 @@ int plan_bm(const moe_config* c) {
 bool fused_router(const moe_config* c) {
   return c->dtype == MOE_BF16 && c->n_routed <= kRouteSmallMaxE;
 }
-int route_tb(const moe_config* c) { return fused_router(c) ? kRouteBlockSmall : kRouteBlock; }
+int route_tb(const moe_config* c, int64_t T) {
+  return fused_router(c) ? kRouteBlockSmall * route_small_groups(T, c->top_k) : kRouteBlock;
+}
 
 struct Layout {
   int64_t T = 0, R = 0, nblk = 0, max_tiles = 0;
@@ -81,7 +83,7 @@ Layout make_layout(const moe_config* c, int64_t T) {
   const size_t es = elem_size(c);
   L.T = T;
   L.R = max_rows(c, T);
-  L.tb = route_tb(c);
+  L.tb = route_tb(c, T);
   L.nblk = ceil_div(T, L.tb);
   L.max_tiles = ceil_div(L.R, plan_bm(c)) + E;
   size_t off = 0;
@@ -207,7 +209,9 @@ void run_route(Runner& R, const moe_config* c, const Layout& L, const void* x,
     r.k = c->top_k;
     r.score = c->score;
     r.renorm = c->renorm_topk;
-    R.run("route", [&] { return launch_route_small(r, R.stream); });
+    R.run("route", [&] {
+      return launch_route_small(r, L.tb / kRouteBlockSmall, R.stream);
+    });
   } else if (T > 0) {
     GemmLaunch G{};
     GemmProblem& p = G.p[0];

@@ -100,7 +100,11 @@ struct RouteSmallArgs {
   int64_t T;
   int32_t d, E, k, score, renorm;
 };
-hipError_t launch_route_small(const RouteSmallArgs& a, hipStream_t s);
+// Groups of kRouteBlockSmall tokens each workgroup of the fused router
+// handles for T tokens; its routing blocks are kRouteBlockSmall * groups
+// tokens long.
+int route_small_groups(int64_t T, int k);
+hipError_t launch_route_small(const RouteSmallArgs& a, int groups, hipStream_t s);
 
 struct ScanArgs {
   const int32_t* blk_counts;  // [nblk, E]

@@ -28,14 +28,15 @@
 #include "moe_device.h"
 #include "moe_internal.h"
 
+#include <algorithm>
+
 
 namespace moe {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kTB = kRouteBlockSmall;    // tokens per workgroup
-static_assert(kTB == 16, "one MFMA row block per workgroup");
-constexpr int kWsPerNs = 8 * 1024;        // LDS per wave slice of W_r rows, per 16 experts
+constexpr int kTB = kRouteBlockSmall;    // tokens per group
+static_assert(kTB == 16, "one MFMA row block per group");
 constexpr int kWsPad = 256;               // reads of padding columns past a slice's last row
 constexpr int XB = 16;                    // k steps of token-row fragments in flight
 
@@ -64,10 +65,23 @@ __device__ __forceinline__ float row_sum(float v) {
 }
 __device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
-template <int NS, int KMAX, bool DMA>
-__global__ void __launch_bounds__(256) route_small_kernel(RouteSmallArgs a) {
+// LDS of the kernel: four W_r slices (one per wave), the partial logits and
+// the per-wave block statistics, filling the 160 KiB of a CU.
+template <int NS>
+constexpr int part_bytes() { return kWaves * kTB * (16 * NS + 1) * 4; }
+template <int NS>
+constexpr int stat_bytes() { return 2 * kWaves * 16 * NS * 4; }
+template <int NS>
+constexpr int slice_bytes() {
+  return ((160 * 1024 - part_bytes<NS>() - stat_bytes<NS>()) / kWaves - kWsPad) & ~1023;
+}
+
+// RES: every wave's K range fits its LDS slice and the fragment registers, so
+// W_r is staged once and each group only loads token rows.
+template <int NS, int KMAX, bool DMA, bool RES>
+__global__ void __launch_bounds__(256) route_small_kernel(RouteSmallArgs a, int groups) {
   constexpr int EP = 16 * NS;
-  constexpr int ws_slice = kWsPerNs * NS;
+  constexpr int ws_slice = slice_bytes<NS>();
   __shared__ __attribute__((aligned(16))) unsigned char s_w[kWaves][ws_slice + kWsPad];
   __shared__ float s_part[kWaves * kTB * (EP + 1)];   // [wave][token][expert] partial logits
   __shared__ float s_ps[kWaves][EP];
@@ -77,28 +91,21 @@ __global__ void __launch_bounds__(256) route_small_kernel(RouteSmallArgs a) {
   const int E = a.E, d = a.d, k = a.k;
   const int pitch = DMA ? E : EP;
   const int l16 = lane & 15, g = lane >> 4;
-  const int64_t t0 = (int64_t)blockIdx.x * kTB;
   const bf16_t* x = static_cast<const bf16_t*>(a.x);
   const bf16_t* W = static_cast<const bf16_t*>(a.w_router);
-  const bf16_t* xr = x + min(t0 + l16, a.T - 1) * d + 8 * g;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   unsigned char* Ws = s_w[wave_u];
   const uint32_t ws_base =
       (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)Ws);
+  const bool sig = a.score == MOE_SIGMOID;
 
-  // this wave's k steps: [s_lo, s_hi) of d / 32
+  // this wave's k steps: [s_lo, s_hi) of d / 32; KC of them fit in its slice
   const int ns = d / 32;
   const int s_lo = wave * ns / kWaves, s_hi = (wave + 1) * ns / kWaves;
-  const int KC = ws_slice / (64 * pitch);   // k steps per LDS chunk (>= 8)
+  const int KC = ws_slice / (64 * pitch);
 
-  floatx4 acc[NS];
-#pragma unroll
-  for (int j = 0; j < NS; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  bf16x8 xf[XB];
-
-  for (int c0 = s_lo; c0 < s_hi; c0 += KC) {
-    const int cn = min(KC, s_hi - c0);
-    // stage rows [32 c0, 32 (c0 + cn)) of W_r in this wave's slice
+  // copies W_r rows [32 c0, 32 (c0 + cn)) into this wave's slice
+  auto stage = [&](int c0, int cn) {
     if (DMA) {
       const unsigned char* src = reinterpret_cast<const unsigned char*>(W + (int64_t)32 * c0 * E);
       const int nbytes = 32 * cn * E * 2;
@@ -111,19 +118,23 @@ __global__ void __launch_bounds__(256) route_small_kernel(RouteSmallArgs a) {
         wl[kk * EP + e] = W[(int64_t)(32 * c0 + kk) * E + e];
       }
     }
-    for (int b0 = 0; b0 < cn; b0 += XB) {
-      const int bn = min(XB, cn - b0);
+  };
+  bf16x8 xf[XB];
+  // token-row fragments of steps [c0 + b0, c0 + b0 + bn), all requested at once
+  auto load_x = [&](const bf16_t* xr, int c0b0, int bn) {
 #pragma unroll
-      for (int u = 0; u < XB; ++u)
-        xf[u] = *reinterpret_cast<const bf16x8*>(xr + 32 * (c0 + b0 + min(u, bn - 1)));
-      __builtin_amdgcn_s_waitcnt(0);   // W slice and fragments landed (this wave only)
-      __builtin_amdgcn_sched_barrier(0);
+    for (int u = 0; u < XB; ++u)
+      if (u < bn) xf[u] = *reinterpret_cast<const bf16x8*>(xr + 32 * (c0b0 + u));
+  };
+  // MFMAs of bn steps whose B rows start at row kl0 of the slice (a guarded
+  // body rather than an early exit, so that xf stays in registers)
+  auto mfma = [&](floatx4* acc, int kl0, int bn) {
 #pragma unroll
-      for (int u = 0; u < XB; ++u) {
-        if (u >= bn) break;
+    for (int u = 0; u < XB; ++u) {
+      if (u < bn) {
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-          const int kk = 32 * (b0 + u) + 8 * g + (l16 >> 2);
+          const int kk = kl0 + 32 * u + 8 * g + (l16 >> 2);
           const int col = 16 * j + 4 * (l16 & 3);
           const unsigned char* p0 = Ws + 2 * (kk * pitch + col);
           const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -135,132 +146,209 @@ __global__ void __launch_bounds__(256) route_small_kernel(RouteSmallArgs a) {
                                                            acc[j], 0, 0, 0);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
-  }
-  // partial logits of this wave: token row 4 g + i, expert 16 j + l16
-#pragma unroll
-  for (int j = 0; j < NS; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_part[(wave * kTB + 4 * g + i) * (EP + 1) + 16 * j + l16] = acc[j][i];
-  __syncthreads();
+  };
 
-  // ---- wave w scores tokens 4 w + g (one per 16-lane row); lane holds experts 16 j + l16
-  const int tk = 4 * wave + g;
-  const int64_t t = t0 + tk;
-  const bool tval = t < a.T;
-  const bool sig = a.score == MOE_SIGMOID;
-  float key[NS], lg[NS];
+  const int64_t blk_t0 = (int64_t)blockIdx.x * groups * kTB;
+  auto x_row = [&](int64_t t0) { return x + min(t0 + l16, a.T - 1) * d + 8 * g; };
+  if (RES) {
+    // the whole K range of the wave stays in LDS for every group
+    load_x(x_row(blk_t0), s_lo, s_hi - s_lo);
+    stage(s_lo, s_hi - s_lo);
+  }
+  // block statistics of this lane's expert slots, accumulated over the groups
+  int st_cnt[NS];
+  float st_ps[NS];
   int eid[NS];
+  float lbias[NS], sbias[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
+    st_cnt[j] = 0;
+    st_ps[j] = 0.f;
     eid[j] = 16 * j + l16;
     const bool ve = eid[j] < E;
-    float v = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) v += s_part[(w * kTB + tk) * (EP + 1) + eid[j]];
-    if (ve && a.logit_bias) v += a.logit_bias[eid[j]];
-    lg[j] = v;
-    const float sb = ve && sig && a.select_bias ? a.select_bias[eid[j]] : 0.f;
-    key[j] = !ve ? -INFINITY : (sig ? sigmoid_f32(v) + sb : v);
+    lbias[j] = ve && a.logit_bias ? a.logit_bias[eid[j]] : 0.f;
+    sbias[j] = ve && sig && a.select_bias ? a.select_bias[eid[j]] : 0.f;
   }
-  const int rounds = min(k + 1, E);
-  uint64_t sel[KMAX];
+  // A group's outputs are stored after the next group's fragments have
+  // landed: stores count in vmcnt, so storing before that wait would make it
+  // wait for them too. Lane l16 holds selection l16 (< k) of its row's token.
+  int64_t out_t = -1;
+  int out_idx = 0;
+  float out_gate = 0.f, out_margin = 0.f;
+  auto store_out = [&]() {
+    if (out_t >= 0) {
+      if (l16 < k) {
+        a.topk_idx[out_t * k + l16] = out_idx;
+        a.topk_gate[out_t * k + l16] = out_gate;
+      }
+      if (a.topk_margin && l16 == 15) a.topk_margin[out_t] = out_margin;
+    }
+  };
+
+  for (int grp = 0; grp < groups; ++grp) {
+    const int64_t t0 = blk_t0 + (int64_t)grp * kTB;
+    if (t0 >= a.T) break;
+    const bf16_t* xr = x_row(t0);
+    floatx4 acc[NS];
 #pragma unroll
-  for (int r = 0; r < KMAX; ++r) sel[r] = 0;
-#pragma unroll
-  for (int r = 0; r < KMAX; ++r) {
-    if (r >= rounds) break;
-    uint64_t best = 0;
-#pragma unroll
-    for (int j = 0; j < NS; ++j) best = max_u64(best, pack_key_id(key[j], eid[j]));
-    best = row_max_u64(best);
-    sel[r] = best;
-    const int id = packed_id(best);
+    for (int j = 0; j < NS; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (RES) {
+      __builtin_amdgcn_s_waitcnt(0);   // slice (first group) and fragments landed
+      __builtin_amdgcn_sched_barrier(0);
+      store_out();
+      mfma(acc, 0, s_hi - s_lo);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      store_out();
+      for (int c0 = s_lo; c0 < s_hi; c0 += KC) {
+        const int cn = min(KC, s_hi - c0);
+        stage(c0, cn);
+        for (int b0 = 0; b0 < cn; b0 += XB) {
+          const int bn = min(XB, cn - b0);
+          load_x(xr, c0 + b0, bn);
+          __builtin_amdgcn_s_waitcnt(0);   // slice chunk and fragments landed
+          __builtin_amdgcn_sched_barrier(0);
+          mfma(acc, 32 * b0, bn);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    // partial logits of this wave: token row 4 g + i, expert 16 j + l16
 #pragma unroll
     for (int j = 0; j < NS; ++j)
-      if (eid[j] == id) key[j] = -INFINITY;
-  }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        s_part[(wave * kTB + 4 * g + i) * (EP + 1) + 16 * j + l16] = acc[j][i];
+    // next group's fragments travel while this group is scored (rows are
+    // clamped to the last token, so the load after the last group is a
+    // harmless re-read; no data-dependent branch around the loads keeps them
+    // back to back)
+    if (RES) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_x(x_row(t0 + kTB), s_lo, s_hi - s_lo);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
 
-  float gate[KMAX], prob[NS];
-  float tot = 0.f;
-  if (!sig) {
-    const float m = packed_key(sel[0]);
+    // ---- wave w scores tokens 4 w + g (one per 16-lane row); lane holds experts 16 j + l16
+    const int tk = 4 * wave + g;
+    const int64_t t = t0 + tk;
+    const bool tval = t < a.T;
+    float key[NS], lg[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-      prob[j] = eid[j] < E ? __expf(lg[j] - m) : 0.f;
-      tot += prob[j];
+      const bool ve = eid[j] < E;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) v += s_part[(w * kTB + tk) * (EP + 1) + eid[j]];
+      v += lbias[j];
+      lg[j] = v;
+      key[j] = !ve ? -INFINITY : (sig ? sigmoid_f32(v) + sbias[j] : v);
     }
-    tot = row_sum(tot);
-    float ssel = 0.f;
-#pragma unroll
-    for (int r = 0; r < KMAX; ++r) {
-      gate[r] = r < k ? __expf(packed_key(sel[r]) - m) : 0.f;
-      ssel += gate[r];
-    }
-    const float den = a.renorm ? ssel : tot;
-#pragma unroll
-    for (int r = 0; r < KMAX; ++r) gate[r] /= den;
-  } else {
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      prob[j] = eid[j] < E ? sigmoid_f32(lg[j]) : 0.f;
-      tot += prob[j];
-    }
-    tot = row_sum(tot);
-    float ssel = 0.f;
-#pragma unroll
-    for (int r = 0; r < KMAX; ++r) {
-      float s = 0.f;
-      if (r < k) {
-        const int id = packed_id(sel[r]);
-#pragma unroll
-        for (int j = 0; j < NS; ++j) s += eid[j] == id ? prob[j] : 0.f;
-        s = row_sum(s);
-      }
-      gate[r] = s;
-      ssel += s;
-    }
-#pragma unroll
-    for (int r = 0; r < KMAX; ++r) gate[r] /= ssel;
-  }
-  const float inv = 1.0f / tot;
-#pragma unroll
-  for (int j = 0; j < NS; ++j) prob[j] = tval ? prob[j] * inv : 0.f;
+    __syncthreads();   // s_part is free for the next group
 
-  if (tval) {
+    const int rounds = min(k + 1, E);
+    uint64_t sel[KMAX];
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r) sel[r] = 0;
 #pragma unroll
     for (int r = 0; r < KMAX; ++r) {
-      if (r < k && l16 == r) {
-        a.topk_idx[t * k + r] = packed_id(sel[r]);
-        a.topk_gate[t * k + r] = gate[r];
+      if (r >= rounds) break;
+      uint64_t best = 0;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) best = max_u64(best, pack_key_id(key[j], eid[j]));
+      best = row_max_u64(best);
+      sel[r] = best;
+      const int id = packed_id(best);
+#pragma unroll
+      for (int j = 0; j < NS; ++j)
+        if (eid[j] == id) key[j] = -INFINITY;
+    }
+
+    float gate[KMAX], prob[NS];
+    float tot = 0.f;
+    if (!sig) {
+      const float m = packed_key(sel[0]);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        prob[j] = eid[j] < E ? __expf(lg[j] - m) : 0.f;
+        tot += prob[j];
+      }
+      tot = row_sum(tot);
+      float ssel = 0.f;
+#pragma unroll
+      for (int r = 0; r < KMAX; ++r) {
+        gate[r] = r < k ? __expf(packed_key(sel[r]) - m) : 0.f;
+        ssel += gate[r];
+      }
+      const float den = a.renorm ? ssel : tot;
+#pragma unroll
+      for (int r = 0; r < KMAX; ++r) gate[r] /= den;
+    } else {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        prob[j] = eid[j] < E ? sigmoid_f32(lg[j]) : 0.f;
+        tot += prob[j];
+      }
+      tot = row_sum(tot);
+      // sigmoid score of each selected expert, taken from the lane holding it
+      float ssel = 0.f;
+#pragma unroll
+      for (int r = 0; r < KMAX; ++r) {
+        float sc = 0.f;
+        if (r < k) {
+          const int id = packed_id(sel[r]);
+#pragma unroll
+          for (int j = 0; j < NS; ++j) sc += eid[j] == id ? prob[j] : 0.f;
+          sc = row_sum(sc);   // one non-zero term
+        }
+        gate[r] = sc;
+        ssel += sc;
+      }
+#pragma unroll
+      for (int r = 0; r < KMAX; ++r) gate[r] /= ssel;
+    }
+    const float inv = 1.0f / tot;
+
+    out_t = tval ? t : -1;
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r) {
+      if (l16 == r) {
+        out_idx = packed_id(sel[r]);
+        out_gate = gate[r];
       }
     }
-    if (a.topk_margin && l16 == 15) {
-      float mg = INFINITY;
+    out_margin = INFINITY;
 #pragma unroll
-      for (int r = 1; r < KMAX; ++r)
-        if (r == k && k < E) mg = packed_key(sel[r - 1]) - packed_key(sel[r]);
-      a.topk_margin[t] = mg;
-    }
-  }
-  // block statistics: the wave's 4 tokens (rows), then the waves in order
-#pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    int cnt = 0;
+    for (int r = 1; r < KMAX; ++r)
+      if (r == k && k < E) out_margin = packed_key(sel[r - 1]) - packed_key(sel[r]);
     if (tval) {
 #pragma unroll
-      for (int r = 0; r < KMAX; ++r)
-        if (r < k && packed_id(sel[r]) == eid[j]) ++cnt;
+      for (int j = 0; j < NS; ++j) {
+#pragma unroll
+        for (int r = 0; r < KMAX; ++r)
+          if (r < k && packed_id(sel[r]) == eid[j]) ++st_cnt[j];
+        st_ps[j] += prob[j] * inv;
+      }
     }
-    float ps = prob[j];
+  }
+
+  store_out();
+
+  // ---- block statistics: the wave's rows in a fixed pairing order, then the
+  // waves in order
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    int cnt = st_cnt[j];
+    float ps = st_ps[j];
     cnt += __shfl_xor(cnt, 16, 64);
     cnt += __shfl_xor(cnt, 32, 64);
     ps += __shfl_xor(ps, 16, 64);
     ps += __shfl_xor(ps, 32, 64);
     if (g == 0) {
-      s_ct[wave][eid[j]] = cnt;
-      s_ps[wave][eid[j]] = ps;
+      s_ct[wave][16 * j + l16] = cnt;
+      s_ps[wave][16 * j + l16] = ps;
     }
   }
   __syncthreads();
@@ -279,21 +367,55 @@ __global__ void __launch_bounds__(256) route_small_kernel(RouteSmallArgs a) {
 
 }  // namespace
 
-hipError_t launch_route_small(const RouteSmallArgs& a, hipStream_t s) {
-  const int64_t nblk = (a.T + kTB - 1) / kTB;
+int route_small_groups(int64_t T, int k) {
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      n_cu = n;
+    else
+      n_cu = 256;
+  }
+  // about one workgroup per CU; a block of 16 G tokens keeps its k-slot ids
+  // within the rank kernel's registers (16 G k <= 64 * 15)
+  const int64_t n16 = (T + kTB - 1) / kTB;
+  int64_t G = (n16 + n_cu - 1) / n_cu;
+  G = std::min<int64_t>(G, 60 / k);
+  return (int)std::max<int64_t>(G, 1);
+}
+
+hipError_t launch_route_small(const RouteSmallArgs& a, int groups, hipStream_t s) {
+  const int64_t nblk = (a.T + (int64_t)kTB * groups - 1) / ((int64_t)kTB * groups);
   if (nblk == 0) return hipSuccess;
-  if (a.E > kRouteSmallMaxE || a.k + 1 > 16 || a.d % 32) return hipErrorInvalidValue;
+  if (a.E > kRouteSmallMaxE || a.k + 1 > 16 || a.d % 32 || groups < 1) return hipErrorInvalidValue;
   const int ns = (a.E + 15) / 16;
   const int k1 = a.k + 1;
   const bool dma = a.E % 4 == 0;
-#define MOE_RS(NSV, KM)                                                                      \
-  do {                                                                                       \
-    if (dma)                                                                                 \
-      hipLaunchKernelGGL((route_small_kernel<NSV, KM, true>), dim3((unsigned)nblk), dim3(256), \
-                         0, s, a);                                                           \
-    else                                                                                     \
-      hipLaunchKernelGGL((route_small_kernel<NSV, KM, false>), dim3((unsigned)nblk), dim3(256), \
-                         0, s, a);                                                           \
+  // the largest K range of a wave against its slice and the fragment registers
+  const int pitch = dma ? a.E : 16 * ns;
+  const int steps_w = (a.d / 32 + kWaves - 1) / kWaves;
+  int slice = 0;
+  switch (ns) {
+    case 1: slice = slice_bytes<1>(); break;
+    case 2: slice = slice_bytes<2>(); break;
+    case 3: slice = slice_bytes<3>(); break;
+    default: slice = slice_bytes<4>(); break;
+  }
+  const bool res = steps_w <= XB && steps_w * 64 * pitch <= slice;
+#define MOE_RS3(NSV, KM, DM)                                                              \
+  do {                                                                                    \
+    if (res)                                                                              \
+      hipLaunchKernelGGL((route_small_kernel<NSV, KM, DM, true>), dim3((unsigned)nblk),   \
+                         dim3(256), 0, s, a, groups);                                     \
+    else                                                                                  \
+      hipLaunchKernelGGL((route_small_kernel<NSV, KM, DM, false>), dim3((unsigned)nblk),  \
+                         dim3(256), 0, s, a, groups);                                     \
+  } while (0)
+#define MOE_RS(NSV, KM)                   \
+  do {                                    \
+    if (dma) MOE_RS3(NSV, KM, true);      \
+    else MOE_RS3(NSV, KM, false);         \
   } while (0)
 #define MOE_RS_K(NSV)                 \
   do {                                \
@@ -309,6 +431,7 @@ hipError_t launch_route_small(const RouteSmallArgs& a, hipStream_t s) {
   }
 #undef MOE_RS_K
 #undef MOE_RS
+#undef MOE_RS3
   return hipGetLastError();
 }
 
