@@ -61,26 +61,33 @@ __global__ void __launch_bounds__((topk_threads<EPL, KMAX>())) topk_kernel(TopkA
   const int per_wave = a.tb / nwaves;
   const int64_t t_begin = (int64_t)blk * a.tb + wave * per_wave;
   const int64_t t_end = min(a.T, t_begin + per_wave);
+  // Logit rows are read one token ahead with unconditional loads (lanes past
+  // E re-read element E - 1 and mask it), and a token's outputs are stored
+  // only after the next token's loads are issued: stores count in vmcnt, so
+  // storing them earlier would make the wait for the next row wait for them.
   float nxt[EPL];
-  if (t_begin < t_end) {
+  auto load_row = [&](int64_t t) {
+    const float* row = a.logits + t * E;
 #pragma unroll
-    for (int m = 0; m < EPL; ++m) {
-      const int e = lane + 64 * m;
-      nxt[m] = e < E ? a.logits[t_begin * E + e] : -FLT_MAX;
-    }
-  }
+    for (int m = 0; m < EPL; ++m) nxt[m] = row[min(lane + 64 * m, E - 1)];
+  };
+  if (t_begin < t_end) load_row(t_begin);
+  int64_t out_t = -1;
+  int out_id = 0;
+  float out_gate = 0.f, out_margin = 0.f;
   for (int64_t t = t_begin; t < t_end; ++t) {
     const float* lrow = a.logits + t * E;
     float l[EPL], key[EPL], sg[EPL];
 #pragma unroll
-    for (int m = 0; m < EPL; ++m) l[m] = nxt[m];
-    if (t + 1 < t_end) {
-#pragma unroll
-      for (int m = 0; m < EPL; ++m) {
-        const int e = lane + 64 * m;
-        nxt[m] = e < E ? lrow[E + e] : -FLT_MAX;
+    for (int m = 0; m < EPL; ++m) l[m] = lane + 64 * m < E ? nxt[m] : -FLT_MAX;
+    if (out_t >= 0) {
+      if (lane < k) {
+        a.topk_idx[out_t * k + lane] = out_id;
+        a.topk_gate[out_t * k + lane] = out_gate;
       }
+      if (lane == 0 && a.topk_margin) a.topk_margin[out_t] = out_margin;
     }
+    load_row(min(t + 1, t_end - 1));
 #pragma unroll
     for (int m = 0; m < EPL; ++m) {
       const int e = lane + 64 * m;
@@ -135,14 +142,17 @@ __global__ void __launch_bounds__((topk_threads<EPL, KMAX>())) topk_kernel(TopkA
     int my_id = 0;
     if (a.score == MOE_SOFTMAX) {
       const float mxl = sel_key[0];
+      float ex[EPL];
       float se = 0.f;
 #pragma unroll
-      for (int m = 0; m < EPL; ++m) se += (lane + 64 * m < E) ? __expf(l[m] - mxl) : 0.f;
+      for (int m = 0; m < EPL; ++m) {
+        ex[m] = (lane + 64 * m < E) ? __expf(l[m] - mxl) : 0.f;
+        se += ex[m];
+      }
       se = wave_sum(se);
       const float inv = 1.0f / se;
 #pragma unroll
-      for (int m = 0; m < EPL; ++m)
-        if (lane + 64 * m < E) psum[m] += __expf(l[m] - mxl) * inv;
+      for (int m = 0; m < EPL; ++m) psum[m] += ex[m] * inv;
       float ssel = 0.f;
 #pragma unroll
       for (int r = 0; r < KMAX; ++r)
@@ -178,18 +188,22 @@ __global__ void __launch_bounds__((topk_threads<EPL, KMAX>())) topk_kernel(TopkA
         }
       my_gate = mine / ssel;
     }
-    if (lane < k) {
-      a.topk_idx[t * k + lane] = my_id;
-      a.topk_gate[t * k + lane] = my_gate;
-      atomicAdd(&s_cnt[my_id], 1);
-    }
-    if (lane == 0 && a.topk_margin) {
-      float mg = FLT_MAX;
+    if (lane < k) atomicAdd(&s_cnt[my_id], 1);   // integer counts: order-independent
+    float mg = FLT_MAX;
 #pragma unroll
-      for (int r = 1; r < KMAX; ++r)
-        if (r == k && k < E) mg = sel_key[r - 1] - sel_key[r];
-      a.topk_margin[t] = k < E ? mg : __int_as_float(0x7f800000);
+    for (int r = 1; r < KMAX; ++r)
+      if (r == k && k < E) mg = sel_key[r - 1] - sel_key[r];
+    out_t = t;
+    out_id = my_id;
+    out_gate = my_gate;
+    out_margin = k < E ? mg : __int_as_float(0x7f800000);
+  }
+  if (out_t >= 0) {
+    if (lane < k) {
+      a.topk_idx[out_t * k + lane] = out_id;
+      a.topk_gate[out_t * k + lane] = out_gate;
     }
+    if (lane == 0 && a.topk_margin) a.topk_margin[out_t] = out_margin;
   }
 
   // per-block probability sums: waves add into LDS one after another
