@@ -24,21 +24,26 @@ namespace moe {
 namespace {
 
 // ---------------------------------------------------------------------------
-// top-k: one wave per token (16 waves of a 1024-thread workgroup share one
-// tb-token block, tb/16 tokens per wave; the next token's logits are loaded
-// while the current one is reduced). Lane l owns experts l, l + 64, ...; each lane keeps its best
-// KMAX (key, id) pairs, then k+1 rounds of a wave-wide maximum pick the
-// winners in descending key order (equal keys: lower id first).
+// top-k (many experts): one wave per token, the waves of a workgroup sharing
+// one tb-token block, tb / nwaves consecutive tokens per wave. Lane l owns
+// experts l, l + 64, ...; each lane keeps its best R (key, id) pairs packed so
+// that a larger integer is a larger key or, for equal keys, the lower id;
+// then R rounds of a wave-wide maximum pick the winners in descending key
+// order, the winning lane advancing its list. Everything per token is
+// branch-free apart from wave-uniform control flow: experts past E carry key
+// -inf. The next token's logit row is loaded while the current one is
+// reduced, and a token's outputs are stored after that load is issued
+// (stores count in vmcnt, so earlier stores would hold up the wait for it).
 // ---------------------------------------------------------------------------
 // Threads per workgroup: as many waves as the per-lane registers allow
-// (EPL logits, keys and sums plus the KMAX-entry candidate list).
-template <int EPL, int KMAX>
+// (EPL logits, scores and sums plus the R-entry candidate list).
+template <int EPL, int R>
 constexpr int topk_threads() {
-  return (EPL <= 4 && KMAX <= 8) ? 1024 : (EPL <= 16 ? 512 : 256);
+  return (EPL <= 4 && R <= 8) ? 1024 : (EPL <= 16 ? 512 : 256);
 }
 
-template <int EPL, int KMAX>
-__global__ void __launch_bounds__((topk_threads<EPL, KMAX>())) topk_kernel(TopkArgs a) {
+template <int EPL, int R, bool SIG>
+__global__ void __launch_bounds__((topk_threads<EPL, R>())) topk_kernel(TopkArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   int* s_cnt = reinterpret_cast<int*>(smem_raw);                 // [E]
   float* s_ps = reinterpret_cast<float*>(smem_raw) + a.E;        // [E]
@@ -52,19 +57,20 @@ __global__ void __launch_bounds__((topk_threads<EPL, KMAX>())) topk_kernel(TopkA
   }
   __syncthreads();
 
-  float psum[EPL];
+  float psum[EPL], sbias[EPL];
 #pragma unroll
-  for (int m = 0; m < EPL; ++m) psum[m] = 0.f;
+  for (int m = 0; m < EPL; ++m) {
+    psum[m] = 0.f;
+    const int e = lane + 64 * m;
+    sbias[m] = SIG && a.select_bias && e < E ? a.select_bias[e] : 0.f;
+  }
 
   const int rounds = min(k + 1, E);
   const int nwaves = blockDim.x >> 6;
   const int per_wave = a.tb / nwaves;
   const int64_t t_begin = (int64_t)blk * a.tb + wave * per_wave;
   const int64_t t_end = min(a.T, t_begin + per_wave);
-  // Logit rows are read one token ahead with unconditional loads (lanes past
-  // E re-read element E - 1 and mask it), and a token's outputs are stored
-  // only after the next token's loads are issued: stores count in vmcnt, so
-  // storing them earlier would make the wait for the next row wait for them.
+
   float nxt[EPL];
   auto load_row = [&](int64_t t) {
     const float* row = a.logits + t * E;
@@ -75,11 +81,7 @@ __global__ void __launch_bounds__((topk_threads<EPL, KMAX>())) topk_kernel(TopkA
   int64_t out_t = -1;
   int out_id = 0;
   float out_gate = 0.f, out_margin = 0.f;
-  for (int64_t t = t_begin; t < t_end; ++t) {
-    const float* lrow = a.logits + t * E;
-    float l[EPL], key[EPL], sg[EPL];
-#pragma unroll
-    for (int m = 0; m < EPL; ++m) l[m] = lane + 64 * m < E ? nxt[m] : -FLT_MAX;
+  auto store_out = [&]() {
     if (out_t >= 0) {
       if (lane < k) {
         a.topk_idx[out_t * k + lane] = out_id;
@@ -87,50 +89,46 @@ __global__ void __launch_bounds__((topk_threads<EPL, KMAX>())) topk_kernel(TopkA
       }
       if (lane == 0 && a.topk_margin) a.topk_margin[out_t] = out_margin;
     }
-    load_row(min(t + 1, t_end - 1));
-#pragma unroll
-    for (int m = 0; m < EPL; ++m) {
-      const int e = lane + 64 * m;
-      const bool ok = e < E;
-      if (a.score == MOE_SOFTMAX) {
-        key[m] = l[m];
-        sg[m] = 0.f;
-      } else {
-        sg[m] = ok ? 1.0f / (1.0f + __expf(-l[m])) : 0.f;
-        key[m] = sg[m] + ((ok && a.select_bias) ? a.select_bias[e] : 0.f);
-      }
-    }
+  };
 
-    // lane-local best KMAX candidates, descending
-    uint64_t cand[KMAX];
+  for (int64_t t = t_begin; t < t_end; ++t) {
+    // scores of this lane's experts (SIG: sigmoid(l), else the logit)
+    float sc[EPL];
+    uint64_t cand[R];
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) cand[i] = 0;
+    for (int i = 0; i < R; ++i) cand[i] = 0;
 #pragma unroll
     for (int m = 0; m < EPL; ++m) {
-      const int e = lane + 64 * m;
-      if (e < E) {
-        uint64_t c = pack_key_id(key[m], e);
+      const bool ok = lane + 64 * m < E;
+      const float l = nxt[m];
+      sc[m] = SIG ? 1.0f / (1.0f + __expf(-l)) : l;
+      const float key = ok ? (SIG ? sc[m] + sbias[m] : l) : -INFINITY;
+      // insert into the descending list
+      uint64_t c = pack_key_id(key, lane + 64 * m);
 #pragma unroll
-        for (int i = 0; i < KMAX; ++i) {
-          const uint64_t hi = cand[i] > c ? cand[i] : c;
-          c = cand[i] > c ? c : cand[i];
-          cand[i] = hi;
-        }
+      for (int i = 0; i < R; ++i) {
+        const bool gt = c > cand[i];
+        const uint64_t hi = gt ? c : cand[i];
+        c = gt ? cand[i] : c;
+        cand[i] = hi;
       }
     }
-    // k+1 rounds of wave-wide maximum
-    int sel_id[KMAX];
-    float sel_key[KMAX];
+    store_out();
+    load_row(min(t + 1, t_end - 1));
+
+    // R rounds of the wave-wide maximum
+    int sel_id[R];
+    float sel_key[R];
 #pragma unroll
-    for (int r = 0; r < KMAX; ++r) {
+    for (int r = 0; r < R; ++r) {
       sel_id[r] = 0;
       sel_key[r] = 0.f;
       if (r < rounds) {
         const uint64_t mx = wave_max_u64(cand[0]);
         if (cand[0] == mx) {
 #pragma unroll
-          for (int i = 0; i < KMAX - 1; ++i) cand[i] = cand[i + 1];
-          cand[KMAX - 1] = 0;
+          for (int i = 0; i < R - 1; ++i) cand[i] = cand[i + 1];
+          cand[R - 1] = 0;
         }
         sel_id[r] = packed_id(mx);
         sel_key[r] = packed_key(mx);
@@ -140,71 +138,71 @@ __global__ void __launch_bounds__((topk_threads<EPL, KMAX>())) topk_kernel(TopkA
     // gates and routing probabilities
     float my_gate = 0.f;
     int my_id = 0;
-    if (a.score == MOE_SOFTMAX) {
+    if (!SIG) {
       const float mxl = sel_key[0];
-      float ex[EPL];
       float se = 0.f;
 #pragma unroll
       for (int m = 0; m < EPL; ++m) {
-        ex[m] = (lane + 64 * m < E) ? __expf(l[m] - mxl) : 0.f;
-        se += ex[m];
+        sc[m] = lane + 64 * m < E ? __expf(sc[m] - mxl) : 0.f;
+        se += sc[m];
       }
       se = wave_sum(se);
       const float inv = 1.0f / se;
 #pragma unroll
-      for (int m = 0; m < EPL; ++m) psum[m] += ex[m] * inv;
+      for (int m = 0; m < EPL; ++m) psum[m] += sc[m] * inv;
       float ssel = 0.f;
 #pragma unroll
-      for (int r = 0; r < KMAX; ++r)
-        if (r < k) ssel += __expf(sel_key[r] - mxl);
-      const float denom = a.renorm ? ssel : se;
-#pragma unroll
-      for (int r = 0; r < KMAX; ++r)
-        if (r < k && lane == r) {
+      for (int r = 0; r < R; ++r) {
+        const float g = r < k ? __expf(sel_key[r] - mxl) : 0.f;
+        ssel += g;
+        if (lane == r) {
           my_id = sel_id[r];
-          my_gate = __expf(sel_key[r] - mxl) / denom;
+          my_gate = g;
         }
+      }
+      my_gate /= a.renorm ? ssel : se;
     } else {
       float ss = 0.f;
 #pragma unroll
-      for (int m = 0; m < EPL; ++m) ss += sg[m];
+      for (int m = 0; m < EPL; ++m) {
+        if (lane + 64 * m >= E) sc[m] = 0.f;
+        ss += sc[m];
+      }
       ss = wave_sum(ss);
       const float inv = 1.0f / ss;
 #pragma unroll
-      for (int m = 0; m < EPL; ++m)
-        if (lane + 64 * m < E) psum[m] += sg[m] * inv;
-      // sigmoid scores of the winners, recomputed from their logits (the key
-      // also carries the selection bias, which must not reach the gates)
-      float ssel = 0.f, mine = 0.f;
+      for (int m = 0; m < EPL; ++m) psum[m] += sc[m] * inv;
+      // sigmoid score of each winner, from the lane holding it (the key also
+      // carries the selection bias, which must not reach the gates)
+      float ssel = 0.f;
 #pragma unroll
-      for (int r = 0; r < KMAX; ++r)
+      for (int r = 0; r < R; ++r) {
         if (r < k) {
-          const float s = 1.0f / (1.0f + __expf(-lrow[sel_id[r]]));
-          ssel += s;
+          const int id = sel_id[r];
+          float mine = 0.f;
+#pragma unroll
+          for (int m = 0; m < EPL; ++m) mine = id == lane + 64 * m ? sc[m] : mine;
+          const float g = __shfl(mine, id & 63, 64);
+          ssel += g;
           if (lane == r) {
-            mine = s;
-            my_id = sel_id[r];
+            my_id = id;
+            my_gate = g;
           }
         }
-      my_gate = mine / ssel;
+      }
+      my_gate /= ssel;
     }
     if (lane < k) atomicAdd(&s_cnt[my_id], 1);   // integer counts: order-independent
-    float mg = FLT_MAX;
+    float mg = INFINITY;
 #pragma unroll
-    for (int r = 1; r < KMAX; ++r)
+    for (int r = 1; r < R; ++r)
       if (r == k && k < E) mg = sel_key[r - 1] - sel_key[r];
     out_t = t;
     out_id = my_id;
     out_gate = my_gate;
-    out_margin = k < E ? mg : __int_as_float(0x7f800000);
+    out_margin = mg;
   }
-  if (out_t >= 0) {
-    if (lane < k) {
-      a.topk_idx[out_t * k + lane] = out_id;
-      a.topk_gate[out_t * k + lane] = out_gate;
-    }
-    if (lane == 0 && a.topk_margin) a.topk_margin[out_t] = out_margin;
-  }
+  store_out();
 
   // per-block probability sums: waves add into LDS one after another
   for (int w = 0; w < nwaves; ++w) {
@@ -639,9 +637,15 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   const size_t shm = (size_t)a.E * 8;
   const int epl = (a.E + 63) / 64;
   const int k1 = a.k + 1;
-#define MOE_TOPK(EPLV, KM)                                                                  \
-  hipLaunchKernelGGL((topk_kernel<EPLV, KM>), dim3(nblk), dim3(topk_threads<EPLV, KM>()), shm, s, \
-                     a)
+#define MOE_TOPK(EPLV, KM)                                                                   \
+  do {                                                                                       \
+    if (a.score == MOE_SIGMOID)                                                              \
+      hipLaunchKernelGGL((topk_kernel<EPLV, KM, true>), dim3(nblk),                          \
+                         dim3(topk_threads<EPLV, KM>()), shm, s, a);                         \
+    else                                                                                     \
+      hipLaunchKernelGGL((topk_kernel<EPLV, KM, false>), dim3(nblk),                         \
+                         dim3(topk_threads<EPLV, KM>()), shm, s, a);                         \
+  } while (0)
 #define MOE_TOPK_K(EPLV)                \
   do {                                  \
     if (k1 <= 4) MOE_TOPK(EPLV, 4);     \
