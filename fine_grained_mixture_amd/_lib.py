@@ -19,8 +19,8 @@ MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_GROUPS_ROUTED, MOE_GROUPS_SHARED = 1, 2
 
 EXPORTED = ("moe_capacity", "moe_max_rows", "moe_workspace_bytes", "moe_route", "moe_permute",
-            "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_layer_forward_timed",
-            "moe_stage_name", "moe_status_str", "moe_last_error")
+            "moe_grouped_ffn", "moe_combine", "moe_bias_update", "moe_layer_forward",
+            "moe_layer_forward_timed", "moe_stage_name", "moe_status_str", "moe_last_error")
 
 
 class MoeConfig(ctypes.Structure):
@@ -79,6 +79,7 @@ def load():
         "moe_grouped_ffn": (c_int, [cfgp, c_int64, c_int32, c_void_p, c_void_p, c_void_p, wp,
                                     c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "moe_combine": (c_int, [cfgp, c_int64, c_void_p, c_void_p, op, c_void_p]),
+        "moe_bias_update": (c_int, [cfgp, c_int64, c_void_p, c_void_p, c_float, c_void_p]),
         "moe_layer_forward": (c_int, [cfgp, c_int64, c_void_p, wp, op, c_void_p, c_size_t,
                                       c_void_p]),
         "moe_layer_forward_timed": (c_int, [cfgp, c_int64, c_void_p, wp, op, c_void_p,
@@ -128,6 +129,11 @@ def moe_grouped_ffn(cfg, T, groups, x_perm, offsets, x_shared, w, y_routed, y_sh
     _check(load().moe_grouped_ffn(ctypes.byref(cfg), T, groups, x_perm, offsets, x_shared,
                                   ctypes.byref(w), y_routed, y_shared, ws, ws_bytes, stream),
            "moe_grouped_ffn")
+
+
+def moe_bias_update(cfg, T, counts, select_bias, gamma, stream) -> None:
+    _check(load().moe_bias_update(ctypes.byref(cfg), T, counts, select_bias, gamma, stream),
+           "moe_bias_update")
 
 
 def moe_combine(cfg, T, y_routed, y_shared, o, stream) -> None:

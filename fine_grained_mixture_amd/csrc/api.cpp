@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <math.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -585,6 +586,15 @@ int moe_combine(const moe_config* c, int64_t T, const float* y_routed, const flo
   Runner R{static_cast<hipStream_t>(stream), &tl};
   run_combine(R, c, T, y_routed, c->n_shared > 0 ? y_shared : nullptr, o);
   return finish(tl);
+}
+
+int moe_bias_update(const moe_config* c, int64_t T, const int32_t* counts, float* select_bias,
+                    float gamma, void* stream) {
+  if (!valid_config(c) || T < 0 || !isfinite(gamma)) return MOE_EINVAL;
+  if (!counts || !select_bias) return MOE_EINVAL;
+  const hipError_t e = launch_bias_update(counts, select_bias, c->n_routed, T * c->top_k, gamma,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
 int moe_layer_forward(const moe_config* c, int64_t T, const void* x, const moe_weights* w,

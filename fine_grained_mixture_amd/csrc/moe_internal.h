@@ -126,6 +126,10 @@ struct ScanArgs {
 };
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
 
+// select_bias[e] += gamma * sign(Tk - E counts[e]) for e < E.
+hipError_t launch_bias_update(const int32_t* counts, float* bias, int E, int64_t Tk, float gamma,
+                              hipStream_t s);
+
 struct RankArgs {
   const int32_t* topk_idx;   // [T, k]
   const int32_t* blk_base;   // [nblk, E]

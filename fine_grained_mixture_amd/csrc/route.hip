@@ -611,6 +611,20 @@ __global__ void __launch_bounds__(256) rank_kernel(RankArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bias update (loss-free balancing): select_bias[e] += gamma * sign(T k - E
+// counts[e]), the integer comparison of expert e's pre-drop slot count with
+// the mean, one float32 addition per expert.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) bias_update_kernel(const int32_t* counts, float* bias,
+                                                          int E, int64_t Tk, float gamma) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  const int64_t diff = Tk - (int64_t)E * counts[e];
+  const float step = diff > 0 ? gamma : (diff < 0 ? -gamma : 0.f);
+  bias[e] = bias[e] + step;
+}
+
+// ---------------------------------------------------------------------------
 // gather: one wave per row, 16-byte lane copies.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) gather_kernel(const unsigned char* x,
@@ -680,6 +694,14 @@ hipError_t launch_rank(const RankArgs& a, hipStream_t s) {
   if (a.nblk == 0) return hipSuccess;
   if ((int64_t)a.tb * a.k > 64 * 15) return hipErrorInvalidValue;   // ids held in registers
   hipLaunchKernelGGL(rank_kernel, dim3((a.nblk + 3) / 4), dim3(256), (size_t)a.E * 32, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_update(const int32_t* counts, float* bias, int E, int64_t Tk, float gamma,
+                              hipStream_t s) {
+  if (E <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bias_update_kernel, dim3((E + 255) / 256), dim3(256), 0, s, counts, bias, E,
+                     Tk, gamma);
   return hipGetLastError();
 }
 

@@ -138,3 +138,10 @@ def grouped_ffn(cfg, T, groups, w, ws, *, x_perm=None, offsets=None, x_shared=No
 
 def combine(cfg, T, y_routed, y_shared, out):
     _lib.moe_combine(cfg, T, _ptr(y_routed), _ptr(y_shared), out.struct, current_stream())
+
+
+def bias_update(cfg, T, counts: torch.Tensor, select_bias: torch.Tensor, gamma: float):
+    """select_bias += gamma * sign(T k - E counts), in place on the device."""
+    if counts.dtype != torch.int32 or select_bias.dtype != torch.float32:
+        raise TypeError("counts must be int32 and select_bias float32")
+    _lib.moe_bias_update(cfg, T, _ptr(counts), _ptr(select_bias), float(gamma), current_stream())

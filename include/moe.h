@@ -169,6 +169,20 @@ int moe_grouped_ffn(const moe_config *cfg, int64_t T, int32_t groups,
 int moe_combine(const moe_config *cfg, int64_t T, const float *y_routed,
                 const float *y_shared, moe_outputs *o, void *stream);
 
+/* Loss-free balancing step (dormouse site, stack list "dropless MoE + LFB":
+   balancing by a router bias instead of an auxiliary loss; Sutra-1.3B site,
+   "48 + 1 experts" card: bias-based load balancing). For every routed expert e:
+     select_bias[e] += gamma * sign(T * top_k - n_routed * counts[e])
+   i.e. the bias of an expert with fewer pre-drop slots than the mean T k / E
+   rises by gamma, above the mean it falls by gamma, at the mean it stays; one
+   float32 addition per expert. counts [E] int32 device (o->counts of the
+   routing call, before capacity); select_bias [E] float32 device, updated in
+   place (the array moe_route reads for the sigmoid rule). gamma must be
+   finite. Enqueued on `stream`; returns MOE_EINVAL for a bad configuration,
+   T < 0, a null pointer or a non-finite gamma.                              */
+int moe_bias_update(const moe_config *cfg, int64_t T, const int32_t *counts,
+                    float *select_bias, float gamma, void *stream);
+
 /* The whole layer forward (route, permute, grouped FFN for routed and shared
    experts, combine). Intermediates live in ws; fills every output of o.     */
 int moe_layer_forward(const moe_config *cfg, int64_t T, const void *x,

@@ -302,6 +302,30 @@ def aux_statistic(counts, prob, T, k, spec: LayerSpec):
 
 
 # ---------------------------------------------------------------------------
+# Loss-free balancing: one update of the selection bias
+# ---------------------------------------------------------------------------
+def bias_update(select_bias, counts, T, k, gamma):
+    """Bias-based balancing in place of an auxiliary loss (dormouse site, stack
+    list "dropless MoE + LFB", which points to the auxiliary-loss-free balancing
+    method; Sutra-1.3B site, "48 + 1 experts" card: bias-based load balancing).
+
+    Each expert's selection bias moves by gamma toward balance: up when its
+    pre-drop slot count is below the mean T k / E, down when above, unchanged
+    when equal. The comparison is made in integers (T k against E counts_i).
+    The new bias is the float32 value nearest to b_i + gamma sign(T k - E c_i);
+    with float32 inputs the float64 sum is exact whenever the binary exponents
+    of b_i and gamma differ by at most 29, so that single rounding is the float32
+    addition's own.
+    """
+    b = np.asarray(select_bias, np.float32).astype(np.float64)
+    c = np.asarray(counts, np.int64)
+    n_routed = c.shape[0]
+    direction = np.sign(int(T) * int(k) - n_routed * c).astype(np.float64)
+    g = float(np.float32(gamma))
+    return (b + g * direction).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
 # The layer
 # ---------------------------------------------------------------------------
 def route(x, w_router, spec: LayerSpec, logit_bias=None, select_bias=None,

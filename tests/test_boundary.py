@@ -133,6 +133,20 @@ def test_null_pointers_and_workspace_rejected(lib):
     assert st == _lib.MOE_EINVAL
 
 
+def test_bias_update_validation(lib):
+    cfg = _cfg()
+    call = lambda T=64, c=0x1000, b=0x1000, g=0.01: lib.moe_bias_update(  # noqa: E731
+        ctypes.byref(cfg), T, c, b, g, None)
+    assert call(c=None) == _lib.MOE_EINVAL
+    assert call(b=None) == _lib.MOE_EINVAL
+    assert call(T=-1) == _lib.MOE_EINVAL
+    assert call(g=float("nan")) == _lib.MOE_EINVAL
+    assert call(g=float("inf")) == _lib.MOE_EINVAL
+    bad = _cfg()
+    bad.top_k = 0
+    assert lib.moe_bias_update(ctypes.byref(bad), 64, 0x1000, 0x1000, 0.01, None) == _lib.MOE_EINVAL
+
+
 def test_status_strings(lib):
     for st in (0, -1, -2, -3, -4):
         assert lib.moe_status_str(st)

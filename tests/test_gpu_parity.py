@@ -140,3 +140,45 @@ def test_stage_entry_points_match_layer(base):
     # y_lowp is y rounded to the storage type
     yl = torch.from_numpy(whole["y"]).to(x.dtype).float().numpy()
     np.testing.assert_array_equal(whole["y_lowp"], yl)
+
+
+def test_bias_update_matches_oracle():
+    """moe_bias_update against the oracle, bit for bit: counts from a real
+    routing call on the GPU (Sutra-shaped skew), then hand-made patterns with
+    experts exactly at the mean, an empty expert, and signed zeros."""
+    import oracle
+    wl = SMALL["sutra_small"]
+    print(f"\n[case] bias update after {wl}", flush=True)
+    inp = synth.make_inputs(wl)
+    cfg, x, w = P.upload(wl, inp)
+    out = L.allocate_outputs(cfg, wl.T, x.device)
+    ws = L.allocate_workspace(cfg, wl.T, x.device)
+    L.layer_forward(cfg, x, w, out, ws)
+    torch.cuda.synchronize()
+    counts = out.t["counts"].clone()
+    E = wl.n_routed
+    cases = [(wl.T, wl.top_k, counts, w.t["select_bias"].clone(), 1e-3)]
+    # T k / E = 2 exactly: experts at, above and below the mean, one empty
+    hand = torch.tensor([2, 5, 0, 2, 1, 2, 3, 1], dtype=torch.int32, device=x.device)
+    bias = torch.tensor([0.5, -0.0, 0.0, -0.25, 3.0, -1e-8, 7.5, 1e-3], dtype=torch.float32,
+                        device=x.device)
+    cfg8 = L.make_config(hidden=128, n_routed=8, top_k=2, n_shared=0, ffn=64, score="sigmoid")
+    for T, k, c, b, g in cases + [(8, 2, hand, bias, 0.0625)]:
+        cf = cfg if c.numel() == E else cfg8
+        want = oracle.bias_update(b.cpu().numpy(), c.cpu().numpy(), T, k, g)
+        got = b.clone()
+        L.bias_update(cf, T, c, got, g)
+        torch.cuda.synchronize()
+        got = got.cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (got, want)
+    # repeated on the device: the largest load falls toward the mean
+    sb = w.t["select_bias"]
+    first = int(counts.max())
+    for _ in range(60):
+        L.layer_forward(cfg, x, w, out, ws)
+        L.bias_update(cfg, wl.T, out.t["counts"], sb, 0.05)
+    torch.cuda.synchronize()
+    last = int(out.t["counts"].max())
+    print(f"[report] bias update: max count {first} -> {last} (mean {wl.T * wl.top_k / E:.1f})",
+          flush=True)
+    assert last < first

@@ -374,3 +374,64 @@ def test_quartz_parameter_totals_pin_gated_experts():
     assert round(active / 1e6, 1) == P["active_params_per_token_millions"]
     two = common + n_moe * ((P["routed_experts"] + P["shared_experts"]) * 2 * d * F + router)
     assert round(two / 1e6, 1) != P["total_params_millions"]
+
+
+# ---------------------------------------------------------------- bias update
+def test_bias_update_closed_forms():
+    """Balanced counts leave the bias unchanged; above-mean experts move down
+    by exactly gamma, below-mean up, at-mean not at all (integer comparison:
+    here T k / E = 3 exactly)."""
+    T, k, E = 12, 2, 8                    # mean slots per expert: 3
+    b = np.array([0.25, -0.5, 0.0, 1.0, 0.125, -2.0, 0.75, 3.0], np.float32)
+    g = np.float32(0.03125)               # a power of two: every result is exact
+    same = oracle.bias_update(b, np.full(E, 3), T, k, g)
+    np.testing.assert_array_equal(same, b)
+    counts = np.array([9, 0, 3, 4, 2, 3, 1, 2])
+    assert counts.sum() == T * k
+    out = oracle.bias_update(b, counts, T, k, g)
+    want = b + g * np.array([-1, 1, 0, -1, 1, 0, 1, 1], np.float32)
+    np.testing.assert_array_equal(out, want)
+    assert out.dtype == np.float32
+
+
+def test_bias_update_rounds_once_in_float32():
+    """The result is the float32 addition b + gamma (or b - gamma)."""
+    rng = np.random.default_rng(1)
+    b = rng.standard_normal(64).astype(np.float32)
+    counts = rng.integers(0, 40, 64)
+    T, k = 100, 8
+    g = np.float32(1e-3)
+    out = oracle.bias_update(b, counts, T, k, g)
+    d = np.sign(T * k - 64 * counts.astype(np.int64))
+    want = np.where(d > 0, b + g, np.where(d < 0, b - g, b)).astype(np.float32)
+    np.testing.assert_array_equal(out, want)
+
+
+def test_bias_update_balances_a_skewed_router():
+    """Repeated updates on a router with a strong per-expert offset drive the
+    per-expert loads toward the mean; the reverse sign would drive them apart."""
+    T, d, E, k = 256, 16, 8, 2
+    w = _inputs(T, d, E, k, 0, 8, seed=11, score="sigmoid")
+    spec = _spec(d, E, k, 0, 8, score="sigmoid", bf16=False)
+    logit_bias = -1.5 * np.log(np.arange(E) + 1.0)      # Zipf-like skew by expert id
+
+    def max_over_mean(bias):
+        r = oracle.route(w["x"], w["w_router"], spec, logit_bias, bias)
+        c = np.bincount(r["idx"].ravel(), minlength=E)
+        return c.max() / (T * k / E), c
+
+    bias = np.zeros(E, np.float32)
+    start, _ = max_over_mean(bias)
+    for _ in range(150):
+        _, c = max_over_mean(bias)
+        bias = oracle.bias_update(bias, c, T, k, 0.02)
+    end, _ = max_over_mean(bias)
+    assert start > 2.5
+    assert end < 1.4, (start, end)
+
+    flipped = np.zeros(E, np.float32)
+    for _ in range(20):
+        _, c = max_over_mean(flipped)
+        flipped = 2 * flipped - oracle.bias_update(flipped, c, T, k, 0.02)   # opposite sign
+    worse, _ = max_over_mean(flipped)
+    assert worse >= start
