@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=1536,
                     help="tokens of the workload the CPU oracle processes")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="override the workload's token count T (e.g. decode-sized batches)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the layer, run 3 plain device copies of this many MiB "
                          "(calibrates the HBM byte counters of a profiler run)")
@@ -136,6 +138,8 @@ def main():
                                                 current_stream)
 
     wl = synth.WORKLOADS[args.workload]
+    if args.tokens > 0:
+        wl = wl.replace(T=args.tokens)
     inp = synth.make_inputs(wl)
     cfg = config_from_workload(wl)
     dev = torch.device("cuda:0")
@@ -251,7 +255,8 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}-shape MoE layer forward", "tokens": wl.T,
+        "config": {"workload": f"{wl.name}-shape MoE layer forward"
+                   + (f", T={wl.T}" if args.tokens > 0 else ""), "tokens": wl.T,
                    "hidden": wl.hidden, "routed_experts": wl.n_routed, "top_k": wl.top_k,
                    "shared_experts": wl.n_shared, "expert_ffn": wl.ffn, "rank": wl.rank,
                    "score": wl.score, "capacity": wl.capacity, "rows": rows,
@@ -266,6 +271,19 @@ def main():
         + alg["shared_gate_up_flops"] + alg["shared_down_flops"],
         "wall_s_timed_region": wall,
     }
+    if wl.score == "sigmoid":
+        # loss-free balancing step on this call's counts (the bias is restored)
+        sb = w.t["select_bias"]
+        saved = sb.clone()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            _lib.moe_bias_update(cfg, wl.T, out["counts"].data_ptr(), sb.data_ptr(), 1e-3, stream)
+        e1.record()
+        torch.cuda.synchronize()
+        result["bias_update_us"] = e0.elapsed_time(e1) * 1e3 / args.steps
+        sb.copy_(saved)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_tokens)
     print(json.dumps(result))

@@ -321,8 +321,11 @@ void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool 
   void* h_sh = at<void>(ws, L.h_sh);
   const int32_t* plan = at<int32_t>(ws, L.plan);
 
+  // decode-sized batches: the weight-streaming skinny kernel
+  const bool skinny = bf && T <= kSkinnyMaxT;
   auto launch = [&](const GemmLaunch& G, int epi, const char* name) {
     R.run(name, [&] {
+      if (skinny) return launch_gemm_skinny(G, epi, R.stream);
       return bf ? launch_gemm_big(G, epi, R.stream) : launch_gemm_f32(G, epi, R.stream);
     });
   };

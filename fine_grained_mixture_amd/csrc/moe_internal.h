@@ -55,6 +55,10 @@ enum GemmEpilogue : int {
   kEpiSwiGLU = 1,     // dual: C (dtype) = round(SiLU(acc_gate) * acc_up)
 };
 
+// Batches of at most this many tokens run the expert GEMMs with the skinny
+// kernel (few rows per expert: weight-bandwidth bound).
+constexpr int kSkinnyMaxT = 4;
+
 // Up to two problems share one launch: tiles of p[0] come first, then p[1].
 struct GemmLaunch {
   GemmProblem p[2];
@@ -67,6 +71,9 @@ hipError_t launch_gemm_f32(const GemmLaunch& L, int epilogue, hipStream_t s);
 // 256 x 128 tiles (dual: 256 x (64 + 64)); N multiple of 8, K of 32.
 hipError_t launch_gemm_big(const GemmLaunch& L, int epilogue, hipStream_t s);
 // Tile list of a row_off problem from offsets[0..G] (one workgroup).
+// Few rows per group (bf16): one workgroup per (group, 64 columns), weights
+// streamed once per pass of 4 rows; row_off groups or uniform groups of M rows.
+hipError_t launch_gemm_skinny(const GemmLaunch& L, int epilogue, hipStream_t s);
 hipError_t launch_plan(const int32_t* offsets, int32_t G, int32_t bm, int32_t* plan,
                        hipStream_t s);
 

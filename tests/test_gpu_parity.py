@@ -60,6 +60,24 @@ EDGE = {
 }
 
 
+# decode-sized batches (T <= 4 take the weight-streaming skinny expert kernel;
+# the larger ones check the tile kernel at few rows per expert)
+DECODE = {
+    "quartz_t2": synth.QUARTZ.replace(T=2, seed=5),
+    "quartz_t4": synth.QUARTZ.replace(T=4, seed=10),
+    "quartz_t17": synth.QUARTZ.replace(T=17, seed=6),
+    "quartz_t64": synth.QUARTZ.replace(T=64, seed=7),
+    "sutra_t3": synth.SUTRA.replace(T=3, seed=8),
+    "sutra_t9": synth.SUTRA.replace(T=9, seed=8),
+    "moonfrost_t40_capacity": synth.MOONFROST.replace(T=40, seed=9),
+}
+
+
+@pytest.mark.parametrize("name", list(DECODE))
+def test_decode_parity(name):
+    _run_and_check(DECODE[name])
+
+
 @pytest.mark.parametrize("name", list(EDGE))
 def test_edge_parity(name):
     wl = EDGE[name]
