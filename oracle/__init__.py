@@ -6,4 +6,5 @@ this package; the product path never does.
 from .moe_oracle import (LayerSpec, SOFTMAX, SIGMOID, round_bf16, silu, sigmoid,  # noqa: F401
                          router_logits, router_scores, select_topk, token_gates,
                          dispatch, swiglu, lowrank_apply, lowrank_swiglu, Experts,
-                         aux_statistic, bias_update, route, layer_forward)
+                         aux_statistic, bias_update, route, layer_forward, dsilu,
+                         layer_backward)

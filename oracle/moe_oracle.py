@@ -382,3 +382,116 @@ def layer_forward(x, weights: dict, spec: LayerSpec, tokens=None,
     out["tokens"] = toks
     out["y"] = y
     return out
+
+
+# ---------------------------------------------------------------------------
+# Backward of the layer
+# ---------------------------------------------------------------------------
+def dsilu(z):
+    """d/dz of z * sigmoid(z)."""
+    s = sigmoid(z)
+    return s * (1.0 + z * (1.0 - s))
+
+
+def _expert_backward(xrow, wg, wu, wd, dyrow, rho, grads, key):
+    """One SwiGLU expert on one token: y = rho(SiLU(x Wg) * (x Wu)) Wd with the
+    upstream gradient dyrow (already rounded where the layer rounds it).
+    Adds to grads[key] = [dWg, dWu, dWd] and returns dx. rho is straight-through
+    on h; the gradients entering the two gate/up products, da and db, are
+    rounded with rho (they are the bf16 operands of those products)."""
+    a = xrow @ wg
+    b = xrow @ wu
+    h = rho(silu(a) * b)
+    dWg, dWu, dWd = grads[key]
+    dWd += np.outer(h, dyrow)
+    dh = wd @ dyrow
+    da = rho(dh * b * dsilu(a))
+    db = rho(dh * silu(a))
+    dWg += np.outer(xrow, da)
+    dWu += np.outer(xrow, db)
+    return wg @ da + wu @ db
+
+
+def layer_backward(x, weights: dict, spec: LayerSpec, dy, aux_grad=0.0, fwd=None):
+    """Gradients of L = sum(dy * y) + aux_grad * aux with respect to x, the
+    router weight and every expert weight (dense experts).
+
+    Readings (the pages train the layer but print no backward): the top-k
+    choice and the capacity drops are held fixed (no gradient through the
+    selection), as are the counts in f; rho on h is straight-through; the
+    selection bias of the sigmoid rule receives no gradient. Where the layer
+    works in bf16 the gradients entering the expert products are rounded with
+    rho at the points the GPU path rounds them: the routed upstream rows
+    rho(g * dy), the shared upstream rows rho(dy), and da, db. Everything else
+    is float64.
+
+    Returns dict dx [T, d], dw_router [d, E], dw_gate/up/down [E, ...] and
+    dsh_gate/up/down [S, ...].
+    """
+    if spec.rank != 0:
+        raise NotImplementedError("backward of low-rank experts")
+    x = np.asarray(x)
+    T, d = x.shape
+    E, k, S, F = spec.n_routed, spec.top_k, spec.n_shared, spec.ffn
+    rho = _rho(spec)
+    if fwd is None:
+        fwd = layer_forward(x, weights, spec)
+    dy = np.asarray(dy, np.float64)
+    ex = Experts(weights, spec)
+    grads = {("r", e): [np.zeros((d, F)), np.zeros((d, F)), np.zeros((F, d))] for e in range(E)}
+    for s in range(S):
+        grads[("s", s)] = [np.zeros((d, F)), np.zeros((d, F)), np.zeros((F, d))]
+    dx = np.zeros((T, d))
+    dg = np.zeros((T, k))
+    idx, gates, rows = fwd["idx"], fwd["gates"], fwd["row_of_slot"]
+    for t in range(T):
+        xrow = np.asarray(x[t], np.float64)
+        for s in range(S):
+            dx[t] += _expert_backward(xrow, ex.sh[0][s], ex.sh[1][s], ex.sh[2][s], rho(dy[t]),
+                                      rho, grads, ("s", s))
+        for j in range(k):
+            if rows[t, j] < 0:
+                continue                      # dropped slot: no gradient
+            e = int(idx[t, j])
+            dg[t, j] = float(dy[t] @ ex.routed(xrow, e))
+            dx[t] += _expert_backward(xrow, ex.gate[e], ex.up[e], ex.down[e],
+                                      rho(gates[t, j] * dy[t]), rho, grads, ("r", e))
+
+    # router: gates -> logits, plus the aux statistic's dependence on the
+    # routing distribution (f held fixed)
+    l = router_logits(x, weights["w_router"], weights.get("logit_bias"))
+    _, prob, sig = router_scores(l, spec)
+    dl = np.zeros((T, E))
+    f = np.asarray(fwd["f"], np.float64)
+    c = aux_grad * spec.aux_coef * E / T
+    for t in range(T):
+        sel = idx[t]
+        g = gates[t]
+        if spec.score == SOFTMAX and spec.renorm:
+            dl[t, sel] += g * (dg[t] - np.dot(g, dg[t]))
+        elif spec.score == SOFTMAX:
+            p = prob[t]
+            dl[t] += -p * np.dot(p[sel], dg[t])
+            dl[t, sel] += p[sel] * dg[t]
+        else:
+            st = sig[t, sel]
+            dsig = (dg[t] - np.dot(g, dg[t])) / st.sum()
+            dl[t, sel] += dsig * st * (1.0 - st)
+        if spec.score == SOFTMAX:
+            p = prob[t]
+            dl[t] += c * p * (f - np.dot(f, p))
+        else:
+            st = sig[t]
+            pr = prob[t]
+            dl[t] += c * (f - np.dot(f, pr)) / st.sum() * st * (1.0 - st)
+    wr = np.asarray(weights["w_router"], np.float64)
+    dx += dl @ wr.T
+    out = dict(dx=dx, dw_router=np.asarray(x, np.float64).T @ dl, dl=dl, dg=dg)
+    out["dw_gate"] = np.stack([grads[("r", e)][0] for e in range(E)])
+    out["dw_up"] = np.stack([grads[("r", e)][1] for e in range(E)])
+    out["dw_down"] = np.stack([grads[("r", e)][2] for e in range(E)])
+    if S > 0:
+        out["dsh_gate"] = np.stack([grads[("s", s)][0] for s in range(S)])
+        out["dsh_up"] = np.stack([grads[("s", s)][1] for s in range(S)])
+        out["dsh_down"] = np.stack([grads[("s", s)][2] for s in range(S)])
+    return out

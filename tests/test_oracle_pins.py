@@ -435,3 +435,124 @@ def test_bias_update_balances_a_skewed_router():
         flipped = 2 * flipped - oracle.bias_update(flipped, c, T, k, 0.02)   # opposite sign
     worse, _ = max_over_mean(flipped)
     assert worse >= start
+
+
+# ---------------------------------------------------------------- backward
+def _f64(w):
+    return {n: (None if v is None else np.asarray(v, np.float64)) for n, v in w.items()}
+
+
+def _loss(x, w, spec, dy, aux_grad, idx):
+    """sum(dy * y) + aux_grad * aux with the selection held at idx."""
+    T = x.shape[0]
+    f = oracle.layer_forward(x, w, spec, override_idx=idx, override_mask=np.ones(T, bool))
+    return float(np.sum(dy * f["y"])) + aux_grad * f["aux"]
+
+
+def _fd_grad(fn, arr, h=1e-6):
+    g = np.zeros(arr.shape)
+    it = np.nditer(arr, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        keep = arr[i]
+        arr[i] = keep + h
+        lp = fn()
+        arr[i] = keep - h
+        lm = fn()
+        arr[i] = keep
+        g[i] = (lp - lm) / (2 * h)
+    return g
+
+
+BWD_CASES = [
+    # T, d, E, k, S, F, score, renorm, capacity
+    (5, 6, 4, 2, 1, 3, "softmax", True, 0),
+    (6, 5, 5, 3, 0, 4, "softmax", False, 0),
+    (5, 4, 6, 2, 2, 3, "sigmoid", True, 0),
+    (8, 4, 3, 2, 1, 3, "softmax", True, 3),     # capacity drops some slots
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES)
+def test_backward_matches_finite_differences(case):
+    """Every gradient the backward returns agrees with central differences of
+    the forward oracle, selection held fixed, in float64 (rho = identity)."""
+    T, d, E, k, S, F, score, renorm, cap = case
+    w = _inputs(T, d, E, k, S, F, seed=40 + T, score=score, logit_std=0.5,
+                select_std=0.2 if score == "sigmoid" else 0.0)
+    w = _f64(w)
+    spec = _spec(d, E, k, S, F, score=score, renorm=renorm, capacity=cap, bf16=False,
+                 aux_coef=0.05)
+    x = w.pop("x")
+    rng = np.random.default_rng(7)
+    dy = rng.standard_normal((T, d))
+    aux_grad = 1.7
+    base = oracle.layer_forward(x, w, spec)
+    if cap:
+        assert base["n_dropped"] > 0
+    idx = base["idx"]
+    g = oracle.layer_backward(x, w, spec, dy, aux_grad=aux_grad)
+    fn = lambda: _loss(x, w, spec, dy, aux_grad, idx)
+    assert _rel(g["dx"], _fd_grad(fn, x)) < 1e-7
+    assert _rel(g["dw_router"], _fd_grad(fn, w["w_router"])) < 1e-7
+    for name, key in (("dw_gate", "w_gate"), ("dw_up", "w_up"), ("dw_down", "w_down")):
+        assert _rel(g[name], _fd_grad(fn, w[key])) < 1e-7, name
+    if S:
+        for name, key in (("dsh_gate", "sh_gate"), ("dsh_up", "sh_up"), ("dsh_down", "sh_down")):
+            assert _rel(g[name], _fd_grad(fn, w[key])) < 1e-7, name
+
+
+def test_backward_aux_term_alone():
+    """With dy = 0 only the aux statistic carries gradient: the expert weights
+    get none, and the router gradient matches differences of aux alone."""
+    T, d, E, k, S, F = 7, 5, 4, 2, 1, 3
+    w = _f64(_inputs(T, d, E, k, S, F, seed=3, logit_std=0.4))
+    spec = _spec(d, E, k, S, F, bf16=False, aux_coef=0.1)
+    x = w.pop("x")
+    dy = np.zeros((T, d))
+    g = oracle.layer_backward(x, w, spec, dy, aux_grad=1.0)
+    for name in ("dw_gate", "dw_up", "dw_down", "dsh_gate", "dsh_up", "dsh_down"):
+        assert not np.any(g[name]), name
+    assert np.any(g["dw_router"])
+    idx = oracle.layer_forward(x, w, spec)["idx"]
+    fn = lambda: _loss(x, w, spec, dy, 1.0, idx)
+    assert _rel(g["dw_router"], _fd_grad(fn, w["w_router"])) < 1e-7
+
+
+def test_backward_single_expert_is_textbook_swiglu():
+    """E = 1, k = 1, no shared expert, no aux: the layer is one SwiGLU MLP with
+    gate one, so its gradients are those torch autograd gives for
+    SiLU(x Wg) * (x Wu) Wd, and the router gets none."""
+    T, d, F = 6, 5, 7
+    w = _f64(_inputs(T, d, 1, 1, 0, F, seed=11))
+    spec = _spec(d, 1, 1, 0, F, bf16=False)
+    x = w.pop("x")
+    dy = np.random.default_rng(1).standard_normal((T, d))
+    g = oracle.layer_backward(x, w, spec, dy, aux_grad=0.0)
+    xt = torch.tensor(x, requires_grad=True)
+    wg = torch.tensor(w["w_gate"][0], requires_grad=True)
+    wu = torch.tensor(w["w_up"][0], requires_grad=True)
+    wd = torch.tensor(w["w_down"][0], requires_grad=True)
+    y = (torch.nn.functional.silu(xt @ wg) * (xt @ wu)) @ wd
+    (y * torch.tensor(dy)).sum().backward()
+    assert _rel(g["dx"], xt.grad.numpy()) < 1e-12
+    assert _rel(g["dw_gate"][0], wg.grad.numpy()) < 1e-12
+    assert _rel(g["dw_up"][0], wu.grad.numpy()) < 1e-12
+    assert _rel(g["dw_down"][0], wd.grad.numpy()) < 1e-12
+    assert not np.any(g["dw_router"])
+
+
+def test_backward_bf16_rounding_points_are_small_perturbations():
+    """Rounding the expert-product operands to bf16 moves each gradient by
+    rounding-level amounts only (a misplaced rho on a whole tensor, or a
+    missing gate, would move it by O(1))."""
+    T, d, E, k, S, F = 12, 16, 6, 2, 1, 8
+    w = _f64(_inputs(T, d, E, k, S, F, seed=5, logit_std=0.5))
+    x = w.pop("x")
+    dy = np.random.default_rng(2).standard_normal((T, d))
+    g64 = oracle.layer_backward(x, w, _spec(d, E, k, S, F, bf16=False), dy, aux_grad=0.3)
+    g16 = oracle.layer_backward(x, w, _spec(d, E, k, S, F, bf16=True), dy, aux_grad=0.3)
+    for name in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dsh_gate", "dsh_up",
+                 "dsh_down"):
+        r = _rel(g16[name], g64[name])
+        assert 0 < r < 3e-2, (name, r)
