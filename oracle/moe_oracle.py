@@ -421,9 +421,9 @@ def layer_backward(x, weights: dict, spec: LayerSpec, dy, aux_grad=0.0, fwd=None
     selection), as are the counts in f; rho on h is straight-through; the
     selection bias of the sigmoid rule receives no gradient. Where the layer
     works in bf16 the gradients entering the expert products are rounded with
-    rho at the points the GPU path rounds them: the routed upstream rows
-    rho(g * dy), the shared upstream rows rho(dy), and da, db. Everything else
-    is float64.
+    rho at the points where the products take bf16 operands: the routed
+    upstream rows rho(g * dy), the shared upstream rows rho(dy), da and db, and
+    the router-logit gradient rho(dl). Everything else is float64.
 
     Returns dict dx [T, d], dw_router [d, E], dw_gate/up/down [E, ...] and
     dsh_gate/up/down [S, ...].
@@ -485,6 +485,7 @@ def layer_backward(x, weights: dict, spec: LayerSpec, dy, aux_grad=0.0, fwd=None
             pr = prob[t]
             dl[t] += c * (f - np.dot(f, pr)) / st.sum() * st * (1.0 - st)
     wr = np.asarray(weights["w_router"], np.float64)
+    dl = rho(dl)            # the operand of the two router products
     dx += dl @ wr.T
     out = dict(dx=dx, dw_router=np.asarray(x, np.float64).T @ dl, dl=dl, dg=dg)
     out["dw_gate"] = np.stack([grads[("r", e)][0] for e in range(E)])
