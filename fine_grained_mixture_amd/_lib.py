@@ -20,7 +20,8 @@ MOE_GROUPS_ROUTED, MOE_GROUPS_SHARED = 1, 2
 
 EXPORTED = ("moe_capacity", "moe_max_rows", "moe_workspace_bytes", "moe_route", "moe_permute",
             "moe_grouped_ffn", "moe_combine", "moe_bias_update", "moe_layer_forward",
-            "moe_layer_forward_timed", "moe_stage_name", "moe_status_str", "moe_last_error")
+            "moe_layer_forward_timed", "moe_backward_workspace_bytes", "moe_layer_backward",
+            "moe_layer_backward_timed", "moe_stage_name", "moe_status_str", "moe_last_error")
 
 
 class MoeConfig(ctypes.Structure):
@@ -46,6 +47,14 @@ class MoeOutputs(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in OUTPUT_FIELDS]
 
 
+GRAD_FIELDS = ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dsh_gate", "dsh_up",
+               "dsh_down")
+
+
+class MoeGrads(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in GRAD_FIELDS]
+
+
 class MoeError(RuntimeError):
     def __init__(self, status: int, where: str):
         lib = load()
@@ -69,6 +78,7 @@ def load():
                            "`python -m fine_grained_mixture_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
     cfgp, wp, op = POINTER(MoeConfig), POINTER(MoeWeights), POINTER(MoeOutputs)
+    gp = POINTER(MoeGrads)
     sig = {
         "moe_capacity": (c_int32, [c_int64, c_int64, c_int64, c_int32, c_int32]),
         "moe_max_rows": (c_int64, [cfgp, c_int64]),
@@ -84,6 +94,12 @@ def load():
                                       c_void_p]),
         "moe_layer_forward_timed": (c_int, [cfgp, c_int64, c_void_p, wp, op, c_void_p,
                                             c_size_t, c_void_p, POINTER(c_void_p), c_int]),
+        "moe_backward_workspace_bytes": (c_size_t, [cfgp, c_int64]),
+        "moe_layer_backward": (c_int, [cfgp, c_int64, c_void_p, wp, op, c_void_p, c_float, gp,
+                                       c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]),
+        "moe_layer_backward_timed": (c_int, [cfgp, c_int64, c_void_p, wp, op, c_void_p, c_float,
+                                             gp, c_void_p, c_size_t, c_void_p, c_size_t,
+                                             c_void_p, POINTER(c_void_p), c_int]),
         "moe_stage_name": (c_char_p, [c_int]),
         "moe_status_str": (c_char_p, [c_int]),
         "moe_last_error": (c_char_p, []),
@@ -152,6 +168,26 @@ def moe_layer_forward_timed(cfg, T, x, w, o, ws, ws_bytes, stream, events) -> in
     n = load().moe_layer_forward_timed(ctypes.byref(cfg), T, x, ctypes.byref(w),
                                        ctypes.byref(o), ws, ws_bytes, stream, arr, len(events))
     return _check(n, "moe_layer_forward_timed")
+
+
+def moe_backward_workspace_bytes(cfg: MoeConfig, T: int) -> int:
+    return load().moe_backward_workspace_bytes(ctypes.byref(cfg), T)
+
+
+def moe_layer_backward(cfg, T, x, w, o, dy, aux_grad, g, ws, ws_bytes, bws, bws_bytes,
+                       stream) -> None:
+    _check(load().moe_layer_backward(ctypes.byref(cfg), T, x, ctypes.byref(w), ctypes.byref(o),
+                                     dy, aux_grad, ctypes.byref(g), ws, ws_bytes, bws, bws_bytes,
+                                     stream), "moe_layer_backward")
+
+
+def moe_layer_backward_timed(cfg, T, x, w, o, dy, aux_grad, g, ws, ws_bytes, bws, bws_bytes,
+                             stream, events) -> int:
+    arr = (c_void_p * max(1, len(events)))(*events)
+    n = load().moe_layer_backward_timed(ctypes.byref(cfg), T, x, ctypes.byref(w),
+                                        ctypes.byref(o), dy, aux_grad, ctypes.byref(g), ws,
+                                        ws_bytes, bws, bws_bytes, stream, arr, len(events))
+    return _check(n, "moe_layer_backward_timed")
 
 
 def moe_stage_name(i: int) -> str | None:

@@ -492,6 +492,412 @@ int layer_forward(const moe_config* c, int64_t T, const void* x, const moe_weigh
   return st ? st : tl.n;
 }
 
+
+// ---- backward ---------------------------------------------------------------
+// Rows of the split-K chunks of the products summed over all tokens.
+constexpr int kRouterKChunk = 512;
+constexpr int kSharedKChunk = 2048;
+
+bool backward_supported(const moe_config* c) {
+  return c->dtype == MOE_BF16 && c->rank == 0 && c->n_routed % 8 == 0;
+}
+
+struct BwdLayout {
+  int64_t T = 0, R = 0, nch_r = 1, nch_s = 1;
+  size_t dyr = 0, dysh = 0, dg = 0, logits = 0, dl = 0, dab = 0, dabsh = 0, xperm = 0, dxp = 0,
+         dxsh = 0, plan = 0, part_r = 0, part_g = 0, part_u = 0, part_d = 0, total = 0;
+};
+
+BwdLayout make_bwd_layout(const moe_config* c, int64_t T) {
+  BwdLayout B;
+  const int64_t E = c->n_routed, d = c->hidden, F = c->ffn, S = c->n_shared, k = c->top_k;
+  B.T = T;
+  B.R = max_rows(c, T);
+  B.nch_r = std::max<int64_t>(1, ceil_div(T, kRouterKChunk));
+  B.nch_s = std::max<int64_t>(1, ceil_div(T, kSharedKChunk));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  B.dyr = take((size_t)B.R * d * 2);
+  B.dysh = take((size_t)T * d * 2 * (S > 0));
+  B.dg = take((size_t)T * k * 4);
+  B.logits = take(fused_router(c) ? (size_t)T * E * 4 : 0);
+  B.dl = take((size_t)T * E * 2);
+  B.dab = take((size_t)B.R * 2 * F * 2);
+  B.dabsh = take((size_t)T * S * 2 * F * 2);
+  B.xperm = take((size_t)B.R * d * 2);
+  B.dxp = take((size_t)B.R * d * 4);
+  B.dxsh = take((size_t)T * d * 4 * (S > 0));
+  B.plan = take((size_t)(1 + 2 * (ceil_div(B.R, kSwigluBwdBM) + E)) * 4);
+  B.part_r = take(B.nch_r > 1 ? (size_t)B.nch_r * d * E * 4 : 0);
+  const size_t shp = (S > 0 && B.nch_s > 1) ? (size_t)S * B.nch_s * d * F * 4 : 0;
+  B.part_g = take(shp);
+  B.part_u = take(shp);
+  B.part_d = take(shp);
+  B.total = off;
+  return B;
+}
+
+BwdGemm bwd_problem() {
+  BwdGemm p{};
+  p.n_chunks = 1;
+  p.G = 1;
+  p.c_split = INT32_MAX;
+  return p;
+}
+
+int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weights* w,
+                   const moe_outputs* o, const float* dy, float aux_grad, moe_grads* g,
+                   const void* ws, size_t ws_bytes, void* bws, size_t bws_bytes, void* stream,
+                   void** events, int n_events) {
+  int st = check_common(c, T);
+  if (st) return st;
+  if (!backward_supported(c)) return MOE_EUNSUPPORTED;
+  if (!isfinite(aux_grad)) return MOE_EINVAL;
+  if (!w || !w->w_router || !expert_weights_ok(c, w, true, true)) return MOE_EINVAL;
+  if (!o || !o->counts || !o->offsets) return MOE_EINVAL;
+  if (T > 0 && (!x || !dy || !o->topk_idx || !o->topk_gate || !o->row_of_slot ||
+                !o->sorted_token))
+    return MOE_EINVAL;
+  if (!g || !g->dw_router || !g->dw_gate || !g->dw_up || !g->dw_down || (T > 0 && !g->dx))
+    return MOE_EINVAL;
+  if (c->n_shared > 0 && (!g->dsh_gate || !g->dsh_up || !g->dsh_down)) return MOE_EINVAL;
+  Layout L;
+  if ((st = check_ws(c, T, const_cast<void*>(ws), ws_bytes, L))) return st;
+  const BwdLayout B = make_bwd_layout(c, T);
+  if (B.total > 0 && !bws) return MOE_EWORKSPACE;
+  if (reinterpret_cast<uintptr_t>(bws) % kAlign || bws_bytes < B.total) return MOE_EWORKSPACE;
+
+  void* fws = const_cast<void*>(ws);
+  const int64_t E = c->n_routed, d = c->hidden, F = c->ffn, S = c->n_shared, k = c->top_k;
+  const int64_t R = B.R;
+  Timeline tl{events, n_events};
+  Runner Rn{static_cast<hipStream_t>(stream), &tl};
+  uint16_t* dyr = at<uint16_t>(bws, B.dyr);
+  uint16_t* dysh = S > 0 ? at<uint16_t>(bws, B.dysh) : nullptr;
+  float* dg = at<float>(bws, B.dg);
+  float* logits = fused_router(c) ? at<float>(bws, B.logits) : at<float>(fws, L.logits);
+  uint16_t* dl = at<uint16_t>(bws, B.dl);
+  void* dab = at<void>(bws, B.dab);
+  void* dabsh = at<void>(bws, B.dabsh);
+  void* xperm = at<void>(bws, B.xperm);
+  float* dxp = at<float>(bws, B.dxp);
+  float* dxsh = S > 0 ? at<float>(bws, B.dxsh) : nullptr;
+  int32_t* plan128 = at<int32_t>(bws, B.plan);
+  const float* y_perm = at<float>(fws, L.y_perm);
+  const void* h = at<void>(fws, L.h);
+  const void* h_sh = at<void>(fws, L.h_sh);
+  const int32_t* plan256 = at<int32_t>(fws, L.plan);
+
+  if (T > 0) {
+    // upstream rows of the expert products and the gate gradients
+    CombineBwdArgs cb{};
+    cb.dy = dy;
+    cb.y_routed = y_perm;
+    cb.row_of_slot = o->row_of_slot;
+    cb.topk_gate = o->topk_gate;
+    cb.dy_routed = dyr;
+    cb.dy_shared = dysh;
+    cb.dgate = dg;
+    cb.T = T;
+    cb.d = (int32_t)d;
+    cb.k = (int32_t)k;
+    Rn.run("combine_bwd", [&] { return launch_combine_bwd(cb, Rn.stream); });
+
+    // router logits (the fused forward router keeps none)
+    if (fused_router(c)) {
+      GemmLaunch G{};
+      GemmProblem& p = G.p[0];
+      p.A = x;
+      p.lda = d;
+      p.B0 = w->w_router;
+      p.ldb = E;
+      p.C = logits;
+      p.ldc = E;
+      p.col_bias = w->logit_bias;
+      p.M = (int32_t)T;
+      p.N = (int32_t)E;
+      p.K = (int32_t)d;
+      p.G = 1;
+      p.n_tiles_n = (int32_t)ceil_div(E, 128);
+      p.max_m_tiles = (int32_t)ceil_div(T, kGemmBigBM);
+      G.n_problems = 1;
+      G.tiles0 = p.max_m_tiles * p.n_tiles_n;
+      Rn.run("router_logits", [&] { return launch_gemm_big(G, kEpiStoreF32, Rn.stream); });
+    }
+    RouterBwdArgs rb{};
+    rb.logits = logits;
+    rb.topk_idx = o->topk_idx;
+    rb.topk_gate = o->topk_gate;
+    rb.dgate = dg;
+    rb.counts = o->counts;
+    rb.dl = dl;
+    rb.T = T;
+    rb.E = (int32_t)E;
+    rb.k = (int32_t)k;
+    rb.score = c->score;
+    rb.renorm = c->renorm_topk;
+    rb.aux_scale = (float)((double)aux_grad * c->aux_coef * (double)E / (double)T);
+    Rn.run("router_bwd", [&] { return launch_router_bwd(rb, Rn.stream); });
+
+    Rn.run("gather", [&] {
+      return launch_gather(x, o->sorted_token, o->offsets, (int32_t)E, R, d * 2, xperm, Rn.stream);
+    });
+    Rn.run("plan", [&] {
+      return launch_plan(o->offsets, (int32_t)E, kSwigluBwdBM, plan128, Rn.stream);
+    });
+
+    // SwiGLU backward (shared experts, then routed)
+    {
+      SwigluBwdLaunch SL{};
+      int np = 0;
+      if (S > 0) {
+        SwigluBwdProblem& p = SL.p[np++];
+        p.X = x;
+        p.ldx = d;
+        p.DY = dysh;
+        p.ldy = d;
+        p.Wg = w->sh_gate;
+        p.Wu = w->sh_up;
+        p.Wd = w->sh_down;
+        p.w_group = d * F;
+        p.DAB = dabsh;
+        p.ldab = S * 2 * F;
+        p.ab_group = 2 * F;
+        p.M = (int32_t)T;
+        p.d = (int32_t)d;
+        p.F = (int32_t)F;
+        p.G = (int32_t)S;
+        p.n_tiles_n = (int32_t)(F / 64);
+      }
+      {
+        SwigluBwdProblem& p = SL.p[np++];
+        p.X = xperm;
+        p.ldx = d;
+        p.DY = dyr;
+        p.ldy = d;
+        p.Wg = w->w_gate;
+        p.Wu = w->w_up;
+        p.Wd = w->w_down;
+        p.w_group = d * F;
+        p.DAB = dab;
+        p.ldab = 2 * F;
+        p.m_off = o->offsets;
+        p.plan = plan128;
+        p.d = (int32_t)d;
+        p.F = (int32_t)F;
+        p.G = (int32_t)E;
+        p.n_tiles_n = (int32_t)(F / 64);
+        p.max_m_tiles = (int32_t)(ceil_div(R, kSwigluBwdBM) + E);
+      }
+      SL.n = np;
+      const SwigluBwdProblem& p0 = SL.p[0];
+      SL.tiles0 = p0.plan ? p0.max_m_tiles * p0.n_tiles_n
+                          : p0.G * (int32_t)ceil_div(p0.M, kSwigluBwdBM) * p0.n_tiles_n;
+      Rn.run("swiglu_bwd", [&] { return launch_swiglu_bwd(SL, Rn.stream); });
+    }
+
+    // input gradient products: shared experts, router, routed experts
+    {
+      BwdLaunch BL{};
+      int np = 0;
+      const int32_t ntn = (int32_t)ceil_div(d, 128), ntm = (int32_t)ceil_div(T, kGemmBigBM);
+      if (S > 0) {
+        BwdGemm& p = BL.p[np++] = bwd_problem();
+        p.A = dabsh;
+        p.lda = S * 2 * F;
+        p.B0 = w->sh_gate;
+        p.B1 = w->sh_up;
+        p.ldb = F;
+        p.k_seg = (int32_t)F;
+        p.b_seg = d * F;
+        p.C0 = dxsh;
+        p.ldc = d;
+        p.M = (int32_t)T;
+        p.N = (int32_t)d;
+        p.K = (int32_t)(S * 2 * F);
+        p.k_chunk = p.K;
+        p.n_tiles_m = ntm;
+        p.n_tiles_n = ntn;
+      }
+      {
+        BwdGemm& p = BL.p[np++] = bwd_problem();
+        p.A = dl;
+        p.lda = E;
+        p.B0 = w->w_router;
+        p.ldb = E;
+        p.C0 = g->dx;
+        p.ldc = d;
+        p.M = (int32_t)T;
+        p.N = (int32_t)d;
+        p.K = (int32_t)E;
+        p.k_chunk = p.K;
+        p.n_tiles_m = ntm;
+        p.n_tiles_n = ntn;
+      }
+      {
+        BwdGemm& p = BL.p[np++] = bwd_problem();
+        p.A = dab;
+        p.lda = 2 * F;
+        p.B0 = w->w_gate;
+        p.B1 = w->w_up;
+        p.ldb = F;
+        p.b_group = d * F;
+        p.k_seg = (int32_t)F;
+        p.C0 = dxp;
+        p.ldc = d;
+        p.m_off = o->offsets;
+        p.plan = plan256;
+        p.N = (int32_t)d;
+        p.K = (int32_t)(2 * F);
+        p.G = (int32_t)E;
+        p.n_tiles_n = ntn;
+        p.max_m_tiles = (int32_t)L.max_tiles;
+      }
+      BL.n = np;
+      Rn.run("dgrad_gemm", [&] { return launch_gemm_bwd(BL, true, true, Rn.stream); });
+    }
+    DxGatherArgs dx{};
+    dx.dx_rows = dxp;
+    dx.dx_shared = dxsh;
+    dx.row_of_slot = o->row_of_slot;
+    dx.dx = g->dx;
+    dx.T = T;
+    dx.d = (int32_t)d;
+    dx.k = (int32_t)k;
+    Rn.run("dx_gather", [&] { return launch_dx_gather(dx, Rn.stream); });
+  }
+
+  // weight gradient products: shared experts (split over tokens), routed
+  // experts (their own rows), router (split over tokens)
+  {
+    BwdLaunch BL{};
+    int np = 0;
+    const bool split_s = S > 0 && B.nch_s > 1;
+    const int32_t kch_s = (int32_t)(split_s ? kSharedKChunk : std::max<int64_t>(T, 1));
+    if (S > 0) {
+      BwdGemm& p = BL.p[np++] = bwd_problem();
+      p.A = h_sh;
+      p.lda = S * F;
+      p.a_group = F;
+      p.B0 = dysh;
+      p.ldb = d;
+      p.C0 = split_s ? at<float>(bws, B.part_d) : g->dsh_down;
+      p.ldc = d;
+      p.c_group = (int64_t)B.nch_s * F * d;
+      p.c_chunk = F * d;
+      p.M = (int32_t)F;
+      p.N = (int32_t)d;
+      p.K = (int32_t)T;
+      p.G = (int32_t)S;
+      p.k_chunk = kch_s;
+      p.n_chunks = (int32_t)B.nch_s;
+      p.n_tiles_m = (int32_t)ceil_div(F, kGemmBigBM);
+      p.n_tiles_n = (int32_t)ceil_div(d, 128);
+    }
+    if (S > 0) {
+      BwdGemm& p = BL.p[np++] = bwd_problem();
+      p.A = x;
+      p.lda = d;
+      p.B0 = dabsh;
+      p.ldb = S * 2 * F;
+      p.b_group = 2 * F;
+      p.C0 = split_s ? at<float>(bws, B.part_g) : g->dsh_gate;
+      p.C1 = split_s ? at<float>(bws, B.part_u) : g->dsh_up;
+      p.c_split = (int32_t)F;
+      p.ldc = F;
+      p.c_group = (int64_t)B.nch_s * d * F;
+      p.c_chunk = d * F;
+      p.M = (int32_t)d;
+      p.N = (int32_t)(2 * F);
+      p.K = (int32_t)T;
+      p.G = (int32_t)S;
+      p.k_chunk = kch_s;
+      p.n_chunks = (int32_t)B.nch_s;
+      p.n_tiles_m = (int32_t)ceil_div(d, kGemmBigBM);
+      p.n_tiles_n = (int32_t)ceil_div(2 * F, 128);
+    }
+    {
+      BwdGemm& p = BL.p[np++] = bwd_problem();
+      p.A = h;
+      p.lda = F;
+      p.B0 = dyr;
+      p.ldb = d;
+      p.C0 = g->dw_down;
+      p.ldc = d;
+      p.c_group = F * d;
+      p.k_off = o->offsets;
+      p.M = (int32_t)F;
+      p.N = (int32_t)d;
+      p.K = (int32_t)R;
+      p.G = (int32_t)E;
+      p.n_tiles_m = (int32_t)ceil_div(F, kGemmBigBM);
+      p.n_tiles_n = (int32_t)ceil_div(d, 128);
+    }
+    {
+      BwdGemm& p = BL.p[np++] = bwd_problem();
+      p.A = xperm;
+      p.lda = d;
+      p.B0 = dab;
+      p.ldb = 2 * F;
+      p.C0 = g->dw_gate;
+      p.C1 = g->dw_up;
+      p.c_split = (int32_t)F;
+      p.ldc = F;
+      p.c_group = d * F;
+      p.k_off = o->offsets;
+      p.M = (int32_t)d;
+      p.N = (int32_t)(2 * F);
+      p.K = (int32_t)R;
+      p.G = (int32_t)E;
+      p.n_tiles_m = (int32_t)ceil_div(d, kGemmBigBM);
+      p.n_tiles_n = (int32_t)ceil_div(2 * F, 128);
+    }
+    {
+      BwdGemm& p = BL.p[np++] = bwd_problem();
+      p.A = x;
+      p.lda = d;
+      p.B0 = dl;
+      p.ldb = E;
+      p.C0 = B.nch_r > 1 ? at<float>(bws, B.part_r) : g->dw_router;
+      p.ldc = E;
+      p.c_chunk = d * E;
+      p.M = (int32_t)d;
+      p.N = (int32_t)E;
+      p.K = (int32_t)T;
+      p.k_chunk = B.nch_r > 1 ? kRouterKChunk : (int32_t)std::max<int64_t>(T, 1);
+      p.n_chunks = (int32_t)B.nch_r;
+      p.n_tiles_m = (int32_t)ceil_div(d, kGemmBigBM);
+      p.n_tiles_n = (int32_t)ceil_div(E, 128);
+    }
+    BL.n = np;
+    Rn.run("wgrad_gemm", [&] { return launch_gemm_bwd(BL, false, false, Rn.stream); });
+    if (B.nch_r > 1) {
+      Rn.run("reduce_router", [&] {
+        return launch_reduce_chunks(at<float>(bws, B.part_r), g->dw_router, 1, B.nch_r, d * E,
+                                    Rn.stream);
+      });
+    }
+    if (split_s) {
+      Rn.run("reduce_shared", [&] {
+        hipError_t e = launch_reduce_chunks(at<float>(bws, B.part_g), g->dsh_gate, S, B.nch_s,
+                                            d * F, Rn.stream);
+        if (e == hipSuccess)
+          e = launch_reduce_chunks(at<float>(bws, B.part_u), g->dsh_up, S, B.nch_s, d * F,
+                                   Rn.stream);
+        if (e == hipSuccess)
+          e = launch_reduce_chunks(at<float>(bws, B.part_d), g->dsh_down, S, B.nch_s, F * d,
+                                   Rn.stream);
+        return e;
+      });
+    }
+  }
+  st = finish(tl);
+  return st ? st : tl.n;
+}
 }  // namespace
 }  // namespace moe
 
@@ -611,6 +1017,29 @@ int moe_layer_forward_timed(const moe_config* c, int64_t T, const void* x, const
                             void** events, int n_events) {
   if (n_events < 0 || (n_events > 0 && !events)) return MOE_EINVAL;
   return layer_forward(c, T, x, w, o, ws, ws_bytes, stream, events, n_events);
+}
+
+size_t moe_backward_workspace_bytes(const moe_config* cfg, int64_t T) {
+  if (!valid_config(cfg) || T < 0) return 0;
+  return make_bwd_layout(cfg, T).total;
+}
+
+int moe_layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weights* w,
+                       const moe_outputs* o, const float* dy, float aux_grad, moe_grads* g,
+                       const void* ws, size_t ws_bytes, void* bwd_ws, size_t bwd_ws_bytes,
+                       void* stream) {
+  const int r = layer_backward(c, T, x, w, o, dy, aux_grad, g, ws, ws_bytes, bwd_ws,
+                               bwd_ws_bytes, stream, nullptr, 0);
+  return r < 0 ? r : MOE_OK;
+}
+
+int moe_layer_backward_timed(const moe_config* c, int64_t T, const void* x, const moe_weights* w,
+                             const moe_outputs* o, const float* dy, float aux_grad, moe_grads* g,
+                             const void* ws, size_t ws_bytes, void* bwd_ws, size_t bwd_ws_bytes,
+                             void* stream, void** events, int n_events) {
+  if (n_events < 0 || (n_events > 0 && !events)) return MOE_EINVAL;
+  return layer_backward(c, T, x, w, o, dy, aux_grad, g, ws, ws_bytes, bwd_ws, bwd_ws_bytes,
+                        stream, events, n_events);
 }
 
 const char* moe_stage_name(int i) {

@@ -181,4 +181,133 @@ struct LowRankArgs {
 };
 hipError_t launch_lowrank(const LowRankArgs& a, hipStream_t s);
 
+
+// ---- backward --------------------------------------------------------------
+
+// One product of the backward: C[m, n] = sum over the work item's k range of
+// A(m, k) B(k, n), bf16 operands, fp32 result. Tiles are kGemmBigBM x 128.
+//   A(m, k), k-contiguous:  A[(a_gather ? a_gather[m] : m) * lda + k]
+//            k-strided:     A[k * lda + m]
+//            (group s adds s * a_group elements)
+//   B(k, n), k-strided:     B0[k * ldb + n]  (+ s * b_group)
+//            k-contiguous:  K is cut in segments of k_seg (one segment when
+//                           k_seg == 0); segment q reads (q odd ? B1 : B0)
+//                           + s * b_group + (q / 2) * b_seg at
+//                           [n * ldb + k - q * k_seg]
+//   Work items:
+//     plan != null: M-ragged groups, rows of group s are [m_off[s], m_off[s+1])
+//       in the plan's kGemmBigBM-row tiles; k in [0, K)
+//     otherwise: groups s < G of rows [0, M); k in [k_off[s], k_off[s+1]) when
+//       k_off, else chunk c < n_chunks covers [c k_chunk, min(K, (c+1) k_chunk))
+//   Output: column n < c_split goes to C0, n >= c_split to C1 at n - c_split;
+//     element offset s * c_group + c * c_chunk + row * ldc. An empty k range
+//     writes zeros.
+struct BwdGemm {
+  const void* A;
+  const int32_t* a_gather;   // k-contiguous A only
+  int64_t lda, a_group;
+  const void* B0;
+  const void* B1;
+  int64_t ldb, b_group, b_seg;
+  int32_t k_seg;
+  float* C0;
+  float* C1;
+  int64_t ldc, c_group, c_chunk;
+  int32_t c_split;
+  const int32_t* m_off;
+  const int32_t* plan;
+  const int32_t* k_off;
+  int32_t k_chunk, n_chunks;
+  int32_t M, N, K, G;
+  int32_t n_tiles_m, n_tiles_n, max_m_tiles;
+};
+constexpr int kBwdMaxProblems = 5;
+// Problems of one launch share the operand layouts; tiles of p[i] are
+// [start[i], start[i + 1]).
+struct BwdLaunch {
+  BwdGemm p[kBwdMaxProblems];
+  int32_t start[kBwdMaxProblems + 1];
+  int32_t n;
+};
+// Work items (workgroups) of one problem.
+int64_t bwd_tiles(const BwdGemm& P);
+hipError_t launch_gemm_bwd(BwdLaunch& L, bool a_kcontig, bool b_kcontig, hipStream_t s);
+
+// SwiGLU backward of one expert group, fused with the recomputation of its
+// gate and up products: for rows r of group s and columns f < F
+//   a = X[xrow(r)] Wg_s[:, f],  b = X[xrow(r)] Wu_s[:, f],  dh = DY[r] Wd_s[f, :]^T
+//   DAB[r, f] = bf16(dh b SiLU'(a)),  DAB[r, F + f] = bf16(dh SiLU(a))
+// (+ s * ab_group). Rows: plan tiles of kSwigluBwdBM rows over m_off, or
+// rows [0, M) of each group s < G.
+constexpr int kSwigluBwdBM = 128;
+struct SwigluBwdProblem {
+  const void* X;
+  const int32_t* x_rows;
+  int64_t ldx;
+  const void* DY;
+  int64_t ldy;
+  const void* Wg;
+  const void* Wu;
+  const void* Wd;
+  int64_t w_group;
+  void* DAB;
+  int64_t ldab, ab_group;
+  const int32_t* m_off;
+  const int32_t* plan;
+  int32_t M, d, F, G, n_tiles_n, max_m_tiles;
+};
+struct SwigluBwdLaunch {
+  SwigluBwdProblem p[2];
+  int32_t n, tiles0;
+};
+hipError_t launch_swiglu_bwd(const SwigluBwdLaunch& L, hipStream_t s);
+
+// Upstream rows of the expert products and the gate gradients, one token per
+// wave: for kept slots j of token t (row = row_of_slot[t, j])
+//   dy_routed[row] = bf16(gate[t, j] dy[t]),  dgate[t, j] = <dy[t], y_routed[row]>
+// (dgate 0 for dropped slots), and dy_shared[t] = bf16(dy[t]) when non-null.
+struct CombineBwdArgs {
+  const float* dy;
+  const float* y_routed;
+  const int32_t* row_of_slot;
+  const float* topk_gate;
+  uint16_t* dy_routed;
+  uint16_t* dy_shared;
+  float* dgate;
+  int64_t T;
+  int32_t d, k;
+};
+hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t s);
+
+// Gradient of the router logits, one token per wave, rounded to bf16.
+struct RouterBwdArgs {
+  const float* logits;       // [T, E], logit_bias included
+  const int32_t* topk_idx;   // [T, k]
+  const float* topk_gate;    // [T, k]
+  const float* dgate;        // [T, k]
+  const int32_t* counts;     // [E] pre-drop slot counts
+  uint16_t* dl;            // [T, E] out
+  int64_t T;
+  int32_t E, k, score, renorm;
+  float aux_scale;           // d(loss)/d(aux) * aux_coef * E / T
+};
+hipError_t launch_router_bwd(const RouterBwdArgs& a, hipStream_t s);
+
+// dx[t] = (dx[t] + dx_shared[t]) + sum over kept slots j, ascending, of
+// dx_rows[row_of_slot[t, j]]; dx_shared may be null.
+struct DxGatherArgs {
+  const float* dx_rows;
+  const float* dx_shared;
+  const int32_t* row_of_slot;
+  float* dx;
+  int64_t T;
+  int32_t d, k;
+};
+hipError_t launch_dx_gather(const DxGatherArgs& a, hipStream_t s);
+
+// out[g * n + i] = sum over c < chunks, ascending, of part[(g * chunks + c) * n + i]
+// for g < groups, i < n (n multiple of 4).
+hipError_t launch_reduce_chunks(const float* part, float* out, int64_t groups, int64_t chunks,
+                                int64_t n, hipStream_t s);
+
 }  // namespace moe

@@ -145,3 +145,48 @@ def bias_update(cfg, T, counts: torch.Tensor, select_bias: torch.Tensor, gamma: 
     if counts.dtype != torch.int32 or select_bias.dtype != torch.float32:
         raise TypeError("counts must be int32 and select_bias float32")
     _lib.moe_bias_update(cfg, T, _ptr(counts), _ptr(select_bias), float(gamma), current_stream())
+
+
+@dataclass
+class Grads:
+    t: dict
+    struct: _lib.MoeGrads
+
+    def __getitem__(self, k):
+        return self.t[k]
+
+
+def allocate_grads(cfg: MoeConfig, T: int, device="cuda") -> Grads:
+    E, d, F, S = cfg.n_routed, cfg.hidden, cfg.ffn, cfg.n_shared
+    f32 = dict(dtype=torch.float32, device=device)
+    t = {
+        "dx": torch.empty((T, d), **f32),
+        "dw_router": torch.empty((d, E), **f32),
+        "dw_gate": torch.empty((E, d, F), **f32),
+        "dw_up": torch.empty((E, d, F), **f32),
+        "dw_down": torch.empty((E, F, d), **f32),
+        "dsh_gate": torch.empty((S, d, F), **f32) if S else None,
+        "dsh_up": torch.empty((S, d, F), **f32) if S else None,
+        "dsh_down": torch.empty((S, F, d), **f32) if S else None,
+    }
+    return Grads(t, _lib.MoeGrads(**{n: _ptr(t[n]) for n in _lib.GRAD_FIELDS}))
+
+
+def allocate_backward_workspace(cfg: MoeConfig, T: int, device="cuda") -> torch.Tensor:
+    n = _lib.moe_backward_workspace_bytes(cfg, T)
+    return torch.empty((max(n, 256),), dtype=torch.uint8, device=device)
+
+
+def layer_backward(cfg: MoeConfig, x: torch.Tensor, w: DeviceWeights, out: Outputs,
+                   ws: torch.Tensor, dy: torch.Tensor, aux_grad: float = 0.0,
+                   grads: Grads | None = None, bws: torch.Tensor | None = None) -> Grads:
+    """Gradients of sum(dy * y) + aux_grad * aux after layer_forward(cfg, x, w, out, ws)."""
+    T = x.shape[0]
+    if dy.dtype != torch.float32 or tuple(dy.shape) != (T, cfg.hidden) or not dy.is_contiguous():
+        raise TypeError("dy must be a contiguous float32 [T, d] tensor")
+    grads = grads or allocate_grads(cfg, T, x.device)
+    bws = bws if bws is not None else allocate_backward_workspace(cfg, T, x.device)
+    _lib.moe_layer_backward(cfg, T, x.data_ptr(), w.struct, out.struct, dy.data_ptr(),
+                            float(aux_grad), grads.struct, ws.data_ptr(), ws.numel(),
+                            bws.data_ptr(), bws.numel(), current_stream())
+    return grads

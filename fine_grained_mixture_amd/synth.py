@@ -160,3 +160,11 @@ def make_inputs(wl: Workload) -> dict:
 def small_variant(wl: Workload, **kw) -> Workload:
     """A reduced-size copy of a workload for oracle-speed parity tests."""
     return wl.replace(**kw)
+
+
+def make_upstream(wl: Workload, seed_offset: int = 1000) -> np.ndarray:
+    """The loss gradient of the layer output for a backward call: float32
+    standard normal [T, d] from ``default_rng(seed + seed_offset)`` (float32,
+    like the layer output it stands for; not rounded)."""
+    rng = np.random.default_rng(wl.seed + seed_offset)
+    return rng.standard_normal(size=(wl.T, wl.hidden), dtype=np.float32)

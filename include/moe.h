@@ -199,6 +199,53 @@ int moe_layer_forward_timed(const moe_config *cfg, int64_t T, const void *x,
                             size_t ws_bytes, void *stream, void **events, int n_events);
 const char *moe_stage_name(int i);
 
+/* ---- backward --------------------------------------------------------------
+   Gradients of  L = sum(dy * y) + aux_grad * aux  for the layer above (every
+   page trains it: the Quartz card's training setup, the Moonfrost stacking and
+   training cards, the Sutra-1.3B and dormouse training notes). The top-k
+   choice, the capacity drops and the counts in f are held fixed (they carry
+   no gradient); the selection bias of the sigmoid rule gets none. h is taken
+   as rounded in the forward (straight through). In bf16 layers the operands
+   of the backward products are rounded to bf16 where they are formed: the
+   routed upstream rows gate * dy, the shared upstream rows dy, the SwiGLU
+   gradients da = dh * b * SiLU'(a) and db = dh * SiLU(a), and the router-logit
+   gradient; every sum is float32.
+   Outputs, float32 device arrays, overwritten (not accumulated):            */
+typedef struct {
+  float *dx;          /* [T, d]                                              */
+  float *dw_router;   /* [d, E]                                              */
+  float *dw_gate;     /* [E, d, F]                                           */
+  float *dw_up;       /* [E, d, F]                                           */
+  float *dw_down;     /* [E, F, d]                                           */
+  float *dsh_gate;    /* [S, d, F]  (NULL allowed when S == 0)               */
+  float *dsh_up;      /* [S, d, F]                                           */
+  float *dsh_down;    /* [S, F, d]                                           */
+} moe_grads;
+
+/* Bytes of the backward's own workspace for this config and T (0 if cfg is
+   invalid). */
+size_t moe_backward_workspace_bytes(const moe_config *cfg, int64_t T);
+
+/* Layer backward. Must follow moe_layer_forward on the same stream with the
+   same cfg, T, x and w; o and ws are that call's outputs and workspace, read
+   here and not modified (h, the shared h and the expert output rows of the
+   forward live in ws). dy [T, d] float32 device: the loss gradient of o->y;
+   aux_grad: the loss gradient of aux (o->aux[1]), finite. bwd_ws: device,
+   256-byte aligned, at least moe_backward_workspace_bytes. This build: bf16
+   dense experts with n_routed a multiple of 8, otherwise MOE_EUNSUPPORTED.
+   The result does not depend on scheduling (fixed summation orders, no
+   atomics).                                                                 */
+int moe_layer_backward(const moe_config *cfg, int64_t T, const void *x, const moe_weights *w,
+                       const moe_outputs *o, const float *dy, float aux_grad, moe_grads *g,
+                       const void *ws, size_t ws_bytes, void *bwd_ws, size_t bwd_ws_bytes,
+                       void *stream);
+/* Same, recording events around each kernel as moe_layer_forward_timed does. */
+int moe_layer_backward_timed(const moe_config *cfg, int64_t T, const void *x,
+                             const moe_weights *w, const moe_outputs *o, const float *dy,
+                             float aux_grad, moe_grads *g, const void *ws, size_t ws_bytes,
+                             void *bwd_ws, size_t bwd_ws_bytes, void *stream, void **events,
+                             int n_events);
+
 /* Static text for a status code, and the text of the last MOE_EHIP error of the
    calling thread. */
 const char *moe_status_str(int status);

@@ -393,12 +393,16 @@ def dsilu(z):
     return s * (1.0 + z * (1.0 - s))
 
 
-def _expert_backward(xrow, wg, wu, wd, dyrow, rho, grads, key):
+def _expert_backward(xrow, wg, wu, wd, dyrow, rho, grads, key, scales=None):
     """One SwiGLU expert on one token: y = rho(SiLU(x Wg) * (x Wu)) Wd with the
     upstream gradient dyrow (already rounded where the layer rounds it).
     Adds to grads[key] = [dWg, dWu, dWd] and returns dx. rho is straight-through
     on h; the gradients entering the two gate/up products, da and db, are
-    rounded with rho (they are the bf16 operands of those products)."""
+    rounded with rho (they are the bf16 operands of those products).
+
+    With ``scales`` (a dict), also accumulates for every gradient element the
+    largest single product term and the sum of the terms' magnitudes, in
+    scales[key] = [(M, S) for dWg, dWu, dWd], and returns (dx, M_dx, S_dx)."""
     a = xrow @ wg
     b = xrow @ wu
     h = rho(silu(a) * b)
@@ -409,10 +413,22 @@ def _expert_backward(xrow, wg, wu, wd, dyrow, rho, grads, key):
     db = rho(dh * silu(a))
     dWg += np.outer(xrow, da)
     dWu += np.outer(xrow, db)
-    return wg @ da + wu @ db
+    dx = wg @ da + wu @ db
+    if scales is None:
+        return dx
+    ax = np.abs(xrow)
+    for (M, S), (u, v) in zip(scales[key], ((ax, np.abs(da)), (ax, np.abs(db)),
+                                             (np.abs(h), np.abs(dyrow)))):
+        t = np.outer(u, v)
+        np.maximum(M, t, out=M)
+        S += t
+    tg = np.abs(wg) * np.abs(da)
+    tu = np.abs(wu) * np.abs(db)
+    return dx, np.maximum(tg.max(axis=1), tu.max(axis=1)), tg.sum(axis=1) + tu.sum(axis=1)
 
 
-def layer_backward(x, weights: dict, spec: LayerSpec, dy, aux_grad=0.0, fwd=None):
+def layer_backward(x, weights: dict, spec: LayerSpec, dy, aux_grad=0.0, fwd=None,
+                   scales=False):
     """Gradients of L = sum(dy * y) + aux_grad * aux with respect to x, the
     router weight and every expert weight (dense experts).
 
@@ -426,7 +442,11 @@ def layer_backward(x, weights: dict, spec: LayerSpec, dy, aux_grad=0.0, fwd=None
     the router-logit gradient rho(dl). Everything else is float64.
 
     Returns dict dx [T, d], dw_router [d, E], dw_gate/up/down [E, ...] and
-    dsh_gate/up/down [S, ...].
+    dsh_gate/up/down [S, ...]. With ``scales``, also M_<name> and S_<name> for
+    each of them: per element, the largest magnitude of a single product term
+    of its sums, and the sum of those magnitudes (error scales of a result
+    formed from rounded operands; the terms of dx are its products' terms
+    with the weights).
     """
     if spec.rank != 0:
         raise NotImplementedError("backward of low-rank experts")
@@ -443,19 +463,33 @@ def layer_backward(x, weights: dict, spec: LayerSpec, dy, aux_grad=0.0, fwd=None
         grads[("s", s)] = [np.zeros((d, F)), np.zeros((d, F)), np.zeros((F, d))]
     dx = np.zeros((T, d))
     dg = np.zeros((T, k))
+    sc = None
+    if scales:
+        sc = {key: [(np.zeros_like(m), np.zeros_like(m)) for m in mats]
+              for key, mats in grads.items()}
+        mdx, sdx = np.zeros((T, d)), np.zeros((T, d))
+
+    def run_expert(t, xrow, w3, dyrow, key):
+        r = _expert_backward(xrow, *w3, dyrow, rho, grads, key, sc)
+        if sc is None:
+            dx[t] += r
+        else:
+            dx[t] += r[0]
+            np.maximum(mdx[t], r[1], out=mdx[t])
+            sdx[t] += r[2]
+
     idx, gates, rows = fwd["idx"], fwd["gates"], fwd["row_of_slot"]
     for t in range(T):
         xrow = np.asarray(x[t], np.float64)
         for s in range(S):
-            dx[t] += _expert_backward(xrow, ex.sh[0][s], ex.sh[1][s], ex.sh[2][s], rho(dy[t]),
-                                      rho, grads, ("s", s))
+            run_expert(t, xrow, (ex.sh[0][s], ex.sh[1][s], ex.sh[2][s]), rho(dy[t]), ("s", s))
         for j in range(k):
             if rows[t, j] < 0:
                 continue                      # dropped slot: no gradient
             e = int(idx[t, j])
             dg[t, j] = float(dy[t] @ ex.routed(xrow, e))
-            dx[t] += _expert_backward(xrow, ex.gate[e], ex.up[e], ex.down[e],
-                                      rho(gates[t, j] * dy[t]), rho, grads, ("r", e))
+            run_expert(t, xrow, (ex.gate[e], ex.up[e], ex.down[e]), rho(gates[t, j] * dy[t]),
+                       ("r", e))
 
     # router: gates -> logits, plus the aux statistic's dependence on the
     # routing distribution (f held fixed)
@@ -488,11 +522,19 @@ def layer_backward(x, weights: dict, spec: LayerSpec, dy, aux_grad=0.0, fwd=None
     dl = rho(dl)            # the operand of the two router products
     dx += dl @ wr.T
     out = dict(dx=dx, dw_router=np.asarray(x, np.float64).T @ dl, dl=dl, dg=dg)
-    out["dw_gate"] = np.stack([grads[("r", e)][0] for e in range(E)])
-    out["dw_up"] = np.stack([grads[("r", e)][1] for e in range(E)])
-    out["dw_down"] = np.stack([grads[("r", e)][2] for e in range(E)])
+    names = [("dw_gate", "r", E, 0), ("dw_up", "r", E, 1), ("dw_down", "r", E, 2)]
     if S > 0:
-        out["dsh_gate"] = np.stack([grads[("s", s)][0] for s in range(S)])
-        out["dsh_up"] = np.stack([grads[("s", s)][1] for s in range(S)])
-        out["dsh_down"] = np.stack([grads[("s", s)][2] for s in range(S)])
+        names += [("dsh_gate", "s", S, 0), ("dsh_up", "s", S, 1), ("dsh_down", "s", S, 2)]
+    for name, kind, n, i in names:
+        out[name] = np.stack([grads[(kind, g)][i] for g in range(n)])
+        if scales:
+            out["M_" + name] = np.stack([sc[(kind, g)][i][0] for g in range(n)])
+            out["S_" + name] = np.stack([sc[(kind, g)][i][1] for g in range(n)])
+    if scales:
+        ax, adl, awr = np.abs(np.asarray(x, np.float64)), np.abs(dl), np.abs(wr)
+        tr = adl[:, None, :] * awr[None, :, :]          # [T, d, E] router terms of dx
+        out["M_dx"] = np.maximum(mdx, tr.max(axis=2))
+        out["S_dx"] = sdx + tr.sum(axis=2)
+        out["M_dw_router"] = (ax[:, :, None] * adl[:, None, :]).max(axis=0)
+        out["S_dw_router"] = ax.T @ adl
     return out

@@ -151,3 +151,41 @@ def test_status_strings(lib):
     for st in (0, -1, -2, -3, -4):
         assert lib.moe_status_str(st)
     assert lib.moe_stage_name(0) is None or isinstance(lib.moe_stage_name(0), bytes)
+
+
+def test_backward_validation(lib):
+    cfg = _cfg(dtype="bf16")
+    T = 64
+    full_w = _lib.MoeWeights(**{n: 0x1000 for n in ("w_router", "w_gate", "w_up", "w_down",
+                                                      "sh_gate", "sh_up", "sh_down")})
+    full_o = _lib.MoeOutputs(**{n: 0x1000 for n in _lib.OUTPUT_FIELDS})
+    full_g = _lib.MoeGrads(**{n: 0x1000 for n in _lib.GRAD_FIELDS})
+    need = _lib.moe_workspace_bytes(cfg, T)
+    bneed = _lib.moe_backward_workspace_bytes(cfg, T)
+    assert bneed > 0 and bneed % 256 == 0
+
+    def call(c=cfg, w=full_w, o=full_o, g=full_g, x=0x1000, dy=0x1000, aux=1.0, ws=0x1000,
+             nbytes=need, bws=0x1000, bbytes=bneed, T=T):
+        return lib.moe_layer_backward(ctypes.byref(c), T, x, ctypes.byref(w), ctypes.byref(o),
+                                      dy, aux, ctypes.byref(g), ws, nbytes, bws, bbytes, None)
+
+    assert call(x=0) == _lib.MOE_EINVAL
+    assert call(dy=0) == _lib.MOE_EINVAL
+    assert call(aux=float("nan")) == _lib.MOE_EINVAL
+    for field in ("dx", "dw_router", "dw_gate", "dsh_down"):
+        g = _lib.MoeGrads.from_buffer_copy(full_g)
+        setattr(g, field, None)
+        assert call(g=g) == _lib.MOE_EINVAL, field
+    o = _lib.MoeOutputs.from_buffer_copy(full_o)
+    o.sorted_token = None
+    assert call(o=o) == _lib.MOE_EINVAL
+    assert call(nbytes=need - 1) == _lib.MOE_EWORKSPACE
+    assert call(bbytes=bneed - 1) == _lib.MOE_EWORKSPACE
+    assert call(bws=0) == _lib.MOE_EWORKSPACE
+    assert call(bws=0x1001) == _lib.MOE_EWORKSPACE
+    assert call(T=-1) == _lib.MOE_EINVAL
+    # this build's backward: bf16 dense experts, expert count a multiple of 8
+    for bad in (_cfg(dtype="f32"), _cfg(n_routed=12), _cfg(rank=64)):
+        nb = _lib.moe_backward_workspace_bytes(bad, T)
+        st = call(c=bad, nbytes=_lib.moe_workspace_bytes(bad, T), bbytes=nb)
+        assert st == _lib.MOE_EUNSUPPORTED

@@ -1,0 +1,131 @@
+"""Layer backward on the GPU against the oracle's backward, through the C ABI.
+
+The forward runs first (its workspace holds what the backward reads); the
+oracle's backward then takes the GPU's expert selection for every token (it is
+the oracle's own for tokens away from near-ties, and either choice is correct
+within them) and the same upstream gradient.
+
+Tolerance, per element of every gradient tensor. Each element is a sum of
+products whose bf16 operands both sides round at the same points; the GPU
+forms the unrounded operand in float32, the oracle in float64, so an operand
+lying within that difference of a bf16 rounding boundary rounds one ulp apart
+on the two sides (a change of at most 2^-7 of the operand). Allowing four such
+operands per sum, plus float32 summation:
+    |gpu - oracle| <= 2^-5 M + 2^-16 S,
+M the largest single term's magnitude and S the sum of the terms' magnitudes,
+both computed by the oracle. The error relative to the tensor's RMS is
+reported as well.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fine_grained_mixture_amd import layer as L
+from fine_grained_mixture_amd import synth
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dsh_gate", "dsh_up", "dsh_down")
+
+
+def _gpu_fwd_bwd(wl, inp, dy, aux_grad):
+    cfg, x, w = P.upload(wl, inp)
+    out = L.allocate_outputs(cfg, wl.T, x.device)
+    ws = L.allocate_workspace(cfg, wl.T, x.device)
+    L.layer_forward(cfg, x, w, out, ws)
+    dyt = torch.from_numpy(dy).to(x.device)
+    g = L.layer_backward(cfg, x, w, out, ws, dyt, aux_grad)
+    torch.cuda.synchronize()
+    fwd = P.to_numpy(out)
+    grads = {n: v.cpu().numpy() for n, v in g.t.items() if v is not None}
+    return fwd, grads
+
+
+def _check(wl, *, aux_grad=1.0, zero_dy=False):
+    print(f"\n[case] {wl} aux_grad={aux_grad} zero_dy={zero_dy}", flush=True)
+    inp = synth.make_inputs(wl)
+    dy = np.zeros((wl.T, wl.hidden), np.float32) if zero_dy else synth.make_upstream(wl)
+    fwd, g = _gpu_fwd_bwd(wl, inp, dy, aux_grad)
+    P.check_parity(wl, inp, fwd, tokens=[], check_y=False)
+    spec = P.spec_of(wl)
+    gi = fwd["topk_idx"].astype(np.int64)
+    ref_f = oracle.layer_forward(inp["x"], inp, spec, tokens=[], override_idx=gi,
+                                 override_mask=np.ones(wl.T, bool))
+    ref = oracle.layer_backward(inp["x"], inp, spec, dy, aux_grad=aux_grad, fwd=ref_f,
+                                scales=True)
+    rep = {}
+    for n in NAMES:
+        if n not in ref:
+            continue
+        r, v = ref[n], g[n].astype(np.float64)
+        assert v.shape == r.shape, n
+        assert np.all(np.isfinite(v)), n
+        rms = float(np.sqrt(np.mean(r ** 2)))
+        err = np.abs(v - r)
+        tol = 2.0 ** -5 * ref["M_" + n] + 2.0 ** -16 * ref["S_" + n]
+        worst = float(np.max(err / np.maximum(tol, 1e-300))) if r.size else 0.0
+        rep[n] = (float(err.max()) / rms if rms else float(err.max(initial=0.0)), worst)
+        bad = err > tol
+        if bad.any():
+            i = np.unravel_index(int(np.argmax(err - tol)), err.shape)
+            raise AssertionError(f"{n}: {int(bad.sum())} elements beyond 2^-5 M + 2^-16 S, "
+                                 f"e.g. {i}: gpu {v[i]:.6e} oracle {r[i]:.6e} tol {tol[i]:.3e}")
+    print(f"[report] {wl.name} T={wl.T}: " + ", ".join(
+        f"{k}: {a:.2e} rms, {b:.2f} tol" for k, (a, b) in rep.items()), flush=True)
+    return rep
+
+
+CASES = {
+    "quartz_small": synth.QUARTZ.replace(T=517, hidden=256, ffn=128),
+    "moonfrost_small_capacity": synth.MOONFROST.replace(T=1000, hidden=256, ffn=128),
+    "sutra_small_sigmoid": synth.SUTRA.replace(T=700, hidden=384, ffn=192),
+    "quartz_no_shared": synth.QUARTZ.replace(T=300, hidden=128, ffn=64, n_shared=0, seed=2),
+    "split_k_tokens": synth.Workload("sk", T=2500, hidden=128, n_routed=8, top_k=2,
+                                     n_shared=1, ffn=64, logit_offset_std=0.5, seed=4),
+    "one_token": synth.QUARTZ.replace(T=1, hidden=128, ffn=64),
+    "wide_ffn_k1": synth.Workload("wk", T=260, hidden=192, n_routed=8, top_k=1, n_shared=3,
+                                  ffn=320, seed=6),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_backward_parity(name):
+    _check(CASES[name])
+
+
+def test_backward_aux_only():
+    """dy = 0: only the aux statistic's gradient reaches the router and x."""
+    rep = _check(synth.QUARTZ.replace(T=400, hidden=128, ffn=64, logit_offset_std=0.5, seed=3),
+                 aux_grad=3.0, zero_dy=True)
+    assert rep["dw_gate"][0] == 0.0
+
+
+def test_backward_empty_batch_zeroes_weight_grads():
+    wl = synth.QUARTZ.replace(T=0, hidden=128, ffn=64)
+    inp = synth.make_inputs(wl)
+    cfg, x, w = P.upload(wl, inp)
+    out = L.allocate_outputs(cfg, 0, x.device)
+    ws = L.allocate_workspace(cfg, 0, x.device)
+    L.layer_forward(cfg, x, w, out, ws)
+    grads = L.allocate_grads(cfg, 0, x.device)
+    for n, v in grads.t.items():
+        if v is not None:
+            v.fill_(7.0)
+    L.layer_backward(cfg, x, w, out, ws, torch.zeros((0, wl.hidden), device=x.device),
+                     1.0, grads)
+    torch.cuda.synchronize()
+    for n, v in grads.t.items():
+        if v is not None and v.numel():
+            assert float(v.abs().max()) == 0.0, n
+
+
+def test_backward_deterministic():
+    wl = synth.QUARTZ.replace(T=700, hidden=256, ffn=128, seed=9)
+    inp = synth.make_inputs(wl)
+    dy = synth.make_upstream(wl)
+    _, g1 = _gpu_fwd_bwd(wl, inp, dy, 1.0)
+    _, g2 = _gpu_fwd_bwd(wl, inp, dy, 1.0)
+    for n in g1:
+        assert np.array_equal(g1[n], g2[n]), n

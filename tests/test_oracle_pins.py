@@ -556,3 +556,27 @@ def test_backward_bf16_rounding_points_are_small_perturbations():
                  "dsh_down"):
         r = _rel(g16[name], g64[name])
         assert 0 < r < 3e-2, (name, r)
+
+
+def test_backward_error_scales_bound_the_gradients():
+    """M (largest term) and S (sum of term magnitudes) satisfy
+    |C| <= S, M <= S <= n M for a sum of n terms; a one-token, one-expert layer
+    has single-term weight gradients, where M = S = |C|."""
+    T, d, E, k, S_, F = 9, 6, 4, 2, 1, 5
+    w = _f64(_inputs(T, d, E, k, S_, F, seed=21, logit_std=0.3))
+    x = w.pop("x")
+    spec = _spec(d, E, k, S_, F, bf16=True)
+    dy = np.random.default_rng(4).standard_normal((T, d))
+    g = oracle.layer_backward(x, w, spec, dy, aux_grad=0.5, scales=True)
+    for name in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dsh_gate", "dsh_up",
+                 "dsh_down"):
+        c, m, s = g[name], g["M_" + name], g["S_" + name]
+        assert np.all(np.abs(c) <= s * (1 + 1e-12) + 1e-300), name
+        assert np.all(m <= s * (1 + 1e-12)), name
+        assert np.all(s <= T * 64 * m + 1e-300), name
+    w1 = _f64(_inputs(1, d, 1, 1, 0, F, seed=22))
+    x1 = w1.pop("x")
+    g1 = oracle.layer_backward(x1, w1, _spec(d, 1, 1, 0, F, bf16=False), dy[:1], scales=True)
+    for name in ("dw_gate", "dw_up", "dw_down"):
+        np.testing.assert_allclose(g1["M_" + name], np.abs(g1[name]), rtol=1e-12)
+        np.testing.assert_allclose(g1["S_" + name], np.abs(g1[name]), rtol=1e-12)
