@@ -5,6 +5,10 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload quartz] [--no-cp
 One step is one call of moe_layer_forward (router GEMM, top-k, scan, rank,
 fused gate/up grouped GEMM, down grouped GEMM, combine) over one batch of
 synthetic inputs already resident in device memory. Prints one JSON line.
+For bf16 dense layers the line also carries the training pair under
+"backward": the forward that keeps its gate and up products, the
+moe_layer_backward call after it, forward + backward tokens/s, and the
+backward products' TFLOP/s.
 
 Per-kernel durations come from HIP events that the library records on the
 launch stream between its kernels (moe_layer_forward_timed); the dominant
@@ -36,6 +40,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="quartz")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the layer backward")
     ap.add_argument("--cpu-tokens", type=int, default=1536,
                     help="tokens of the workload the CPU oracle processes")
     ap.add_argument("--tokens", type=int, default=0,
@@ -81,6 +86,91 @@ def algorithmic(wl, rows):
         topk_bytes=T * E * 4 + 8 * T * k,
         combine_bytes=rows * d * 4 + (T * d * 4 if S > 0 else 0) + T * d * 4 + 8 * T * k,
     )
+
+
+def backward_flops(wl, rows):
+    """Algorithmic FLOPs of the layer backward's products for `rows` dispatched
+    rows, with the forward's gate and up products saved: dh = dy W_down^T, the
+    input-gradient products (experts and router) and the weight-gradient
+    products (experts and router)."""
+    T, d, E, S, F = wl.T, wl.hidden, wl.n_routed, wl.n_shared, wl.ffn
+    ex = rows + S * T
+    return dict(dh_gemm=2.0 * d * F * ex, dgrad_gemm=4.0 * d * F * ex + 2.0 * d * E * T,
+                wgrad_gemm=6.0 * d * F * ex + 2.0 * d * E * T)
+
+
+def time_backward(wl, cfg, x, w, steps, warmup, stream):
+    """The training pair: mean time of moe_layer_forward keeping its gate and
+    up products (saved_ab), and of moe_layer_backward after it (reading that
+    forward's workspace and products), with the backward's per-kernel
+    durations from the library's events."""
+    import numpy as np
+    import torch
+
+    from fine_grained_mixture_amd import _lib, synth
+    from fine_grained_mixture_amd.layer import (allocate_backward_workspace, allocate_grads,
+                                                allocate_outputs, allocate_workspace)
+
+    dev = x.device
+    dy = torch.from_numpy(synth.make_upstream(wl)).to(dev)
+    out = allocate_outputs(cfg, wl.T, dev, saved_ab=True)
+    ws = allocate_workspace(cfg, wl.T, dev)
+    g = allocate_grads(cfg, wl.T, dev)
+    bws = allocate_backward_workspace(cfg, wl.T, dev)
+
+    def fstep():
+        _lib.moe_layer_forward(cfg, wl.T, x.data_ptr(), w.struct, out.struct, ws.data_ptr(),
+                               ws.numel(), stream)
+
+    for _ in range(warmup):
+        fstep()
+    torch.cuda.synchronize()
+    f0 = torch.cuda.Event(enable_timing=True)
+    f1 = torch.cuda.Event(enable_timing=True)
+    f0.record()
+    for _ in range(steps):
+        fstep()
+    f1.record()
+    torch.cuda.synchronize()
+    fwd_ms = f0.elapsed_time(f1) / steps
+
+    def bstep(events=None):
+        a = (cfg, wl.T, x.data_ptr(), w.struct, out.struct, dy.data_ptr(), 1.0, g.struct,
+             ws.data_ptr(), ws.numel(), bws.data_ptr(), bws.numel(), stream)
+        if events is None:
+            _lib.moe_layer_backward(*a)
+            return 0
+        return _lib.moe_layer_backward_timed(*a, [e.cuda_event for e in events])
+
+    for _ in range(warmup):
+        bstep()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        bstep()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    n_ev = 32
+    sets = []
+    for _ in range(steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+        for e in evs:
+            e.record()
+        sets.append(evs)
+    torch.cuda.synchronize()
+    n_k = 0
+    for evs in sets:
+        n_k = bstep(evs)
+    torch.cuda.synchronize()
+    names = [_lib.moe_stage_name(i) for i in range(n_k)]
+    dur = {n: [] for n in names}
+    for evs in sets:
+        for i, n in enumerate(names):
+            dur[n].append(evs[2 * i].elapsed_time(evs[2 * i + 1]) * 1e3)
+    return fwd_ms, ms, {n: float(np.mean(v)) for n, v in dur.items()}
 
 
 def traffic_from_profile(kernel_src: str):
@@ -284,6 +374,19 @@ def main():
         torch.cuda.synchronize()
         result["bias_update_us"] = e0.elapsed_time(e1) * 1e3 / args.steps
         sb.copy_(saved)
+    if wl.dtype == "bf16" and wl.rank == 0 and wl.n_routed % 8 == 0 and not args.no_backward:
+        fms, bms, bst = time_backward(wl, cfg, x, w, args.steps, args.warmup, stream)
+        bfl = backward_flops(wl, rows)
+        gemm = {n: f for n, f in bfl.items() if n in bst}
+        bwd = {"ms_per_step": bms, "tokens_per_s": wl.T / (bms * 1e-3),
+               "forward_saving_products_ms": fms,
+               "fwd_plus_bwd_tokens_per_s": wl.T / ((bms + fms) * 1e-3),
+               "flops": sum(bfl.values()),
+               "gemm_tflops": sum(gemm.values()) / (sum(bst[n] for n in gemm) * 1e-6) / 1e12,
+               "stage_us_mean": bst}
+        for n, f in gemm.items():
+            bwd[n + "_tflops"] = f / (bst[n] * 1e-6) / 1e12
+        result["backward"] = bwd
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_tokens)
     print(json.dumps(result))

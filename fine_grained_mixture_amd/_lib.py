@@ -36,7 +36,7 @@ WEIGHT_FIELDS = ("w_router", "logit_bias", "select_bias", "w_gate", "w_up", "w_d
                  "u_down", "s_down", "v_down", "sh_gate", "sh_up", "sh_down")
 OUTPUT_FIELDS = ("topk_idx", "topk_gate", "topk_margin", "counts", "kept", "offsets",
                  "sorted_token", "row_of_slot", "dropped", "n_dropped", "aux", "f", "P",
-                 "y", "y_lowp")
+                 "y", "y_lowp", "saved_ab")
 
 
 class MoeWeights(ctypes.Structure):

@@ -93,7 +93,7 @@ Layout make_layout(const moe_config* c, int64_t T) {
     off = align_up(off + bytes);
     return at;
   };
-  L.logits = take(fused_router(c) ? 0 : (size_t)T * E * 4);
+  L.logits = take((size_t)T * E * 4);
   L.blk_counts = take((size_t)L.nblk * E * 4);
   L.blk_base = take((size_t)L.nblk * E * 4);
   L.blk_psum = take((size_t)L.nblk * E * 4);
@@ -204,6 +204,7 @@ void run_route(Runner& R, const moe_config* c, const Layout& L, const void* x,
     r.topk_margin = o->topk_margin;
     r.blk_counts = at<int32_t>(ws, L.blk_counts);
     r.blk_psum = at<float>(ws, L.blk_psum);
+    r.logits = logits;
     r.T = T;
     r.d = c->hidden;
     r.E = E;
@@ -308,7 +309,7 @@ void run_rank(Runner& R, const moe_config* c, const Layout& L, moe_outputs* o, v
 void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool shared,
              const void* a_routed, const int32_t* a_rows, const int32_t* offsets,
              const void* a_shared, const moe_weights* w, float* y_routed, float* y_shared,
-             void* ws) {
+             void* ws, float* saved_ab = nullptr) {
   const int64_t T = L.T, d = c->hidden, F = c->ffn, S = c->n_shared;
   const bool bf = c->dtype == MOE_BF16;
   // tile shapes: bf16 256 x 128 (gate/up: 256 x (64 + 64)); fp32 64 x 64
@@ -373,6 +374,11 @@ void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool 
       p.C = h_sh;
       p.ldc = S * F;
       p.c_group_col = F;
+      if (saved_ab) {
+        p.ab = saved_ab + L.R * 2 * F;
+        p.ab_ld = S * 2 * F;
+        p.ab_group_col = 2 * F;
+      }
       p.M = (int32_t)T;
       p.N = (int32_t)F;
       p.K = (int32_t)d;
@@ -391,6 +397,10 @@ void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool 
       p.ldb = F;
       p.C = h;
       p.ldc = F;
+      if (saved_ab) {
+        p.ab = saved_ab;
+        p.ab_ld = 2 * F;
+      }
       p.row_off = offsets;
       p.plan = plan;
       p.N = (int32_t)F;
@@ -486,7 +496,8 @@ int layer_forward(const moe_config* c, int64_t T, const void* x, const moe_weigh
   float* y_sh = c->n_shared > 0 ? at<float>(ws, L.y_sh) : nullptr;
   run_route(R, c, L, x, w, o, ws, true);
   run_rank(R, c, L, o, ws);
-  run_ffn(R, c, L, true, true, x, o->sorted_token, o->offsets, x, w, y_perm, y_sh, ws);
+  float* saved_ab = c->dtype == MOE_BF16 && c->rank == 0 ? o->saved_ab : nullptr;
+  run_ffn(R, c, L, true, true, x, o->sorted_token, o->offsets, x, w, y_perm, y_sh, ws, saved_ab);
   run_combine(R, c, T, y_perm, y_sh, o);
   st = finish(tl);
   return st ? st : tl.n;
@@ -496,7 +507,7 @@ int layer_forward(const moe_config* c, int64_t T, const void* x, const moe_weigh
 // ---- backward ---------------------------------------------------------------
 // Rows of the split-K chunks of the products summed over all tokens.
 constexpr int kRouterKChunk = 512;
-constexpr int kSharedKChunk = 2048;
+constexpr int kSharedKChunk = 4096;
 
 bool backward_supported(const moe_config* c) {
   return c->dtype == MOE_BF16 && c->rank == 0 && c->n_routed % 8 == 0;
@@ -504,8 +515,8 @@ bool backward_supported(const moe_config* c) {
 
 struct BwdLayout {
   int64_t T = 0, R = 0, nch_r = 1, nch_s = 1;
-  size_t dyr = 0, dysh = 0, dg = 0, logits = 0, dl = 0, dab = 0, dabsh = 0, xperm = 0, dxp = 0,
-         dxsh = 0, plan = 0, part_r = 0, part_g = 0, part_u = 0, part_d = 0, total = 0;
+  size_t dyr = 0, dysh = 0, dg = 0, dl = 0, dab = 0, dabsh = 0, xperm = 0, dxp = 0,
+         dxsh = 0, part_r = 0, part_g = 0, part_u = 0, part_d = 0, total = 0;
 };
 
 BwdLayout make_bwd_layout(const moe_config* c, int64_t T) {
@@ -524,14 +535,12 @@ BwdLayout make_bwd_layout(const moe_config* c, int64_t T) {
   B.dyr = take((size_t)B.R * d * 2);
   B.dysh = take((size_t)T * d * 2 * (S > 0));
   B.dg = take((size_t)T * k * 4);
-  B.logits = take(fused_router(c) ? (size_t)T * E * 4 : 0);
   B.dl = take((size_t)T * E * 2);
   B.dab = take((size_t)B.R * 2 * F * 2);
   B.dabsh = take((size_t)T * S * 2 * F * 2);
   B.xperm = take((size_t)B.R * d * 2);
   B.dxp = take((size_t)B.R * d * 4);
   B.dxsh = take((size_t)T * d * 4 * (S > 0));
-  B.plan = take((size_t)(1 + 2 * (ceil_div(B.R, kSwigluBwdBM) + E)) * 4);
   B.part_r = take(B.nch_r > 1 ? (size_t)B.nch_r * d * E * 4 : 0);
   const size_t shp = (S > 0 && B.nch_s > 1) ? (size_t)S * B.nch_s * d * F * 4 : 0;
   B.part_g = take(shp);
@@ -579,14 +588,13 @@ int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weig
   uint16_t* dyr = at<uint16_t>(bws, B.dyr);
   uint16_t* dysh = S > 0 ? at<uint16_t>(bws, B.dysh) : nullptr;
   float* dg = at<float>(bws, B.dg);
-  float* logits = fused_router(c) ? at<float>(bws, B.logits) : at<float>(fws, L.logits);
+  const float* logits = at<float>(fws, L.logits);   // the forward router's
   uint16_t* dl = at<uint16_t>(bws, B.dl);
   void* dab = at<void>(bws, B.dab);
   void* dabsh = at<void>(bws, B.dabsh);
   void* xperm = at<void>(bws, B.xperm);
   float* dxp = at<float>(bws, B.dxp);
   float* dxsh = S > 0 ? at<float>(bws, B.dxsh) : nullptr;
-  int32_t* plan128 = at<int32_t>(bws, B.plan);
   const float* y_perm = at<float>(fws, L.y_perm);
   const void* h = at<void>(fws, L.h);
   const void* h_sh = at<void>(fws, L.h_sh);
@@ -596,6 +604,8 @@ int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weig
     // upstream rows of the expert products and the gate gradients
     CombineBwdArgs cb{};
     cb.dy = dy;
+    cb.x = static_cast<const uint16_t*>(x);
+    cb.x_perm = static_cast<uint16_t*>(xperm);
     cb.y_routed = y_perm;
     cb.row_of_slot = o->row_of_slot;
     cb.topk_gate = o->topk_gate;
@@ -607,27 +617,6 @@ int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weig
     cb.k = (int32_t)k;
     Rn.run("combine_bwd", [&] { return launch_combine_bwd(cb, Rn.stream); });
 
-    // router logits (the fused forward router keeps none)
-    if (fused_router(c)) {
-      GemmLaunch G{};
-      GemmProblem& p = G.p[0];
-      p.A = x;
-      p.lda = d;
-      p.B0 = w->w_router;
-      p.ldb = E;
-      p.C = logits;
-      p.ldc = E;
-      p.col_bias = w->logit_bias;
-      p.M = (int32_t)T;
-      p.N = (int32_t)E;
-      p.K = (int32_t)d;
-      p.G = 1;
-      p.n_tiles_n = (int32_t)ceil_div(E, 128);
-      p.max_m_tiles = (int32_t)ceil_div(T, kGemmBigBM);
-      G.n_problems = 1;
-      G.tiles0 = p.max_m_tiles * p.n_tiles_n;
-      Rn.run("router_logits", [&] { return launch_gemm_big(G, kEpiStoreF32, Rn.stream); });
-    }
     RouterBwdArgs rb{};
     rb.logits = logits;
     rb.topk_idx = o->topk_idx;
@@ -643,15 +632,58 @@ int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weig
     rb.aux_scale = (float)((double)aux_grad * c->aux_coef * (double)E / (double)T);
     Rn.run("router_bwd", [&] { return launch_router_bwd(rb, Rn.stream); });
 
-    Rn.run("gather", [&] {
-      return launch_gather(x, o->sorted_token, o->offsets, (int32_t)E, R, d * 2, xperm, Rn.stream);
-    });
-    Rn.run("plan", [&] {
-      return launch_plan(o->offsets, (int32_t)E, kSwigluBwdBM, plan128, Rn.stream);
-    });
-
-    // SwiGLU backward (shared experts, then routed)
-    {
+    if (o->saved_ab) {
+      // dh = dy W_down^T with the SwiGLU backward in the epilogue, on the
+      // forward's saved gate and up products (shared experts, then routed)
+      BwdLaunch BL{};
+      int np = 0;
+      if (S > 0) {
+        BwdGemm& p = BL.p[np++] = bwd_problem();
+        p.A = dysh;
+        p.lda = d;
+        p.B0 = w->sh_down;
+        p.ldb = d;
+        p.b_group = F * d;
+        p.C0 = static_cast<float*>(dabsh);   // bf16 output
+        p.ldc = S * 2 * F;
+        p.c_group = 2 * F;
+        p.ab = o->saved_ab + R * 2 * F;
+        p.ab_ld = S * 2 * F;
+        p.ab_group = 2 * F;
+        p.half = (int32_t)F;
+        p.M = (int32_t)T;
+        p.N = (int32_t)F;
+        p.K = (int32_t)d;
+        p.G = (int32_t)S;
+        p.k_chunk = p.K;
+        p.n_tiles_m = (int32_t)ceil_div(T, kGemmBigBM);
+        p.n_tiles_n = (int32_t)ceil_div(F, 128);
+      }
+      {
+        BwdGemm& p = BL.p[np++] = bwd_problem();
+        p.A = dyr;
+        p.lda = d;
+        p.B0 = w->w_down;
+        p.ldb = d;
+        p.b_group = F * d;
+        p.C0 = static_cast<float*>(dab);     // bf16 output
+        p.ldc = 2 * F;
+        p.ab = o->saved_ab;
+        p.ab_ld = 2 * F;
+        p.half = (int32_t)F;
+        p.m_off = o->offsets;
+        p.plan = plan256;
+        p.N = (int32_t)F;
+        p.K = (int32_t)d;
+        p.G = (int32_t)E;
+        p.n_tiles_n = (int32_t)ceil_div(F, 128);
+        p.max_m_tiles = (int32_t)L.max_tiles;
+      }
+      BL.n = np;
+      Rn.run("dh_gemm", [&] { return launch_gemm_bwd(BL, true, true, kBwdSwiGLU, Rn.stream); });
+    } else {
+    // SwiGLU backward with the gate and up products recomputed (shared
+    // experts, then routed)
       SwigluBwdLaunch SL{};
       int np = 0;
       if (S > 0) {
@@ -686,16 +718,16 @@ int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weig
         p.DAB = dab;
         p.ldab = 2 * F;
         p.m_off = o->offsets;
-        p.plan = plan128;
+        p.plan = plan256;
         p.d = (int32_t)d;
         p.F = (int32_t)F;
         p.G = (int32_t)E;
         p.n_tiles_n = (int32_t)(F / 64);
-        p.max_m_tiles = (int32_t)(ceil_div(R, kSwigluBwdBM) + E);
+        p.max_m_tiles = (int32_t)L.max_tiles;
       }
       SL.n = np;
       const SwigluBwdProblem& p0 = SL.p[0];
-      SL.tiles0 = p0.plan ? p0.max_m_tiles * p0.n_tiles_n
+      SL.tiles0 = p0.plan ? 2 * p0.max_m_tiles * p0.n_tiles_n
                           : p0.G * (int32_t)ceil_div(p0.M, kSwigluBwdBM) * p0.n_tiles_n;
       Rn.run("swiglu_bwd", [&] { return launch_swiglu_bwd(SL, Rn.stream); });
     }
@@ -758,7 +790,9 @@ int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weig
         p.max_m_tiles = (int32_t)L.max_tiles;
       }
       BL.n = np;
-      Rn.run("dgrad_gemm", [&] { return launch_gemm_bwd(BL, true, true, Rn.stream); });
+      Rn.run("dgrad_gemm", [&] {
+        return launch_gemm_bwd(BL, true, true, kBwdStoreF32, Rn.stream);
+      });
     }
     DxGatherArgs dx{};
     dx.dx_rows = dxp;
@@ -874,7 +908,9 @@ int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weig
       p.n_tiles_n = (int32_t)ceil_div(E, 128);
     }
     BL.n = np;
-    Rn.run("wgrad_gemm", [&] { return launch_gemm_bwd(BL, false, false, Rn.stream); });
+    Rn.run("wgrad_gemm", [&] {
+      return launch_gemm_bwd(BL, false, false, kBwdStoreF32, Rn.stream);
+    });
     if (B.nch_r > 1) {
       Rn.run("reduce_router", [&] {
         return launch_reduce_chunks(at<float>(bws, B.part_r), g->dw_router, 1, B.nch_r, d * E,

@@ -6,7 +6,8 @@
 //   bf16, the operand of the expert products) and the gate's gradient is the
 //   dot product of dy[t] with that expert's output row. One wave per token,
 //   16-byte pieces of dy per lane, the k dot products reduced across the wave
-//   in a fixed order.
+//   in a fixed order. The token's row is also copied to its slots' rows of
+//   x_perm, the row order of the weight-gradient products.
 // router_bwd_kernel: the gradient of the router logits. The top-k choice and
 //   the slot counts are held fixed; the gates depend on the logits through the
 //   softmax (renormalised over the selected experts or not) or through the
@@ -58,12 +59,20 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(CombineBwdArgs a) {
       part[j] = 0.f;
     }
     const floatx4* dyt = reinterpret_cast<const floatx4*>(a.dy + t * a.d);
+    const u32x2* xt = reinterpret_cast<const u32x2*>(a.x + t * a.d);
     for (int c = lane; c < d4; c += 64) {
       const floatx4 g = dyt[c];
+      u32x2 xv = {0u, 0u};
+      if (a.x_perm) xv = xt[c];
       floatx4 v[KMAX];
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
         if (kept[j]) v[j] = yr[(int64_t)row[j] * d4 + c];
+      if (a.x_perm) {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+          if (kept[j]) reinterpret_cast<u32x2*>(a.x_perm + (int64_t)row[j] * a.d)[c] = xv;
+      }
       if (a.dy_shared)
         reinterpret_cast<u32x2*>(a.dy_shared + t * a.d)[c] = pack_bf16x4(g[0], g[1], g[2], g[3]);
 #pragma unroll

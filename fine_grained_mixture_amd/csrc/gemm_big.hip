@@ -281,6 +281,21 @@ gemm_big_kernel(GemmLaunch L) {
       __builtin_amdgcn_wave_barrier();
     }
   } else {
+    if (P.ab) {
+      // the gate and up sums themselves, for the backward: lane l32 of each
+      // 32 x 32 block holds one column
+      float* abp = P.ab + tile.g * P.ab_group_col + tile.n0 + 32 * wn + l32;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int row = row_base + 32 * i + 8 * (q >> 2) + 4 * lhi + (q & 3);
+          if (row < tile.r_end) {
+            abp[(int64_t)row * P.ab_ld] = acc[i][0][q];
+            abp[(int64_t)row * P.ab_ld + N] = acc[i][1][q];
+          }
+        }
+    }
     bf16_t* C = static_cast<bf16_t*>(P.C);
     bf16_t* st = reinterpret_cast<bf16_t*>(stage);
 #pragma unroll

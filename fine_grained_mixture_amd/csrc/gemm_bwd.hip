@@ -86,7 +86,7 @@ __device__ __forceinline__ bf16x8 frag_ks(const unsigned char* t, int k, int n) 
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <bool A_KC, bool B_KC>
+template <bool A_KC, bool B_KC, int EPI>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_bwd_kernel(BwdLaunch L) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * kStageBytes];
@@ -290,7 +290,7 @@ gemm_bwd_kernel(BwdLaunch L) {
   const int row_base = r0 + 128 * wm;
   const int col = n0 + 64 * wn + 4 * (lane & 15);
   float* cbase = nullptr;
-  if (col < N) {
+  if (EPI == kBwdStoreF32 && col < N) {
     cbase = (col < P.c_split ? P.C0 + col : P.C1 + (col - P.c_split)) + s * P.c_group +
             (int64_t)c * P.c_chunk;
   }
@@ -307,7 +307,30 @@ gemm_bwd_kernel(BwdLaunch L) {
       const int r = 4 * rr + (lane >> 4);
       const int row = row_base + 32 * i + r;
       const floatx4 v = *reinterpret_cast<const floatx4*>(&st[r * 72 + 4 * (lane & 15)]);
-      if (row < r_end && cbase) *reinterpret_cast<floatx4*>(cbase + (int64_t)row * P.ldc) = v;
+      if (EPI == kBwdStoreF32) {
+        if (row < r_end && cbase) *reinterpret_cast<floatx4*>(cbase + (int64_t)row * P.ldc) = v;
+      } else if (row < r_end && col < N) {
+        // v = dh at columns col .. col + 3; a and b from the forward
+        const float* abr = P.ab + s * P.ab_group + (int64_t)row * P.ab_ld + col;
+        const floatx4 av = *reinterpret_cast<const floatx4*>(abr);
+        const floatx4 bv = *reinterpret_cast<const floatx4*>(abr + P.half);
+        float da[4], db[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-av[e]));
+          da[e] = v[e] * bv[e] * (sg * (1.0f + av[e] * (1.0f - sg)));
+          db[e] = v[e] * (av[e] * sg);
+        }
+        bf16_t* o = static_cast<bf16_t*>(static_cast<void*>(P.C0)) + s * P.c_group +
+                    (int64_t)row * P.ldc + col;
+        u32x2 pa, pb;
+        pa[0] = (uint32_t)f32_to_bf16(da[0]) | ((uint32_t)f32_to_bf16(da[1]) << 16);
+        pa[1] = (uint32_t)f32_to_bf16(da[2]) | ((uint32_t)f32_to_bf16(da[3]) << 16);
+        pb[0] = (uint32_t)f32_to_bf16(db[0]) | ((uint32_t)f32_to_bf16(db[1]) << 16);
+        pb[1] = (uint32_t)f32_to_bf16(db[2]) | ((uint32_t)f32_to_bf16(db[3]) << 16);
+        *reinterpret_cast<u32x2*>(o) = pa;
+        *reinterpret_cast<u32x2*>(o + P.half) = pb;
+      }
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -334,10 +357,13 @@ swiglu_bwd_kernel(SwigluBwdLaunch L) {
   const int nt = local % P.n_tiles_n, mt = local / P.n_tiles_n;
   int s, r0, r_end;
   if (P.plan) {
-    if (mt >= P.plan[0]) return;
-    s = P.plan[1 + 2 * mt];
-    r0 = P.plan[2 + 2 * mt];
-    r_end = min(P.m_off[s + 1], r0 + kSB);
+    // the plan's tiles are kGemmBigBM rows: work item mt takes half mt & 1
+    const int pt = mt >> 1;
+    if (pt >= P.plan[0]) return;
+    s = P.plan[1 + 2 * pt];
+    const int p0 = P.plan[2 + 2 * pt];
+    r0 = p0 + kSB * (mt & 1);
+    r_end = min(P.m_off[s + 1], p0 + kGemmBigBM);
   } else {
     const int mtg = (P.M + kSB - 1) / kSB;
     s = mt / mtg;
@@ -468,7 +494,7 @@ int64_t bwd_tiles(const BwdGemm& P) {
   return (int64_t)P.G * P.n_chunks * P.n_tiles_m * P.n_tiles_n;
 }
 
-hipError_t launch_gemm_bwd(BwdLaunch& L, bool a_kc, bool b_kc, hipStream_t s) {
+hipError_t launch_gemm_bwd(BwdLaunch& L, bool a_kc, bool b_kc, int epi, hipStream_t s) {
   if (L.n < 1 || L.n > kBwdMaxProblems) return hipErrorInvalidValue;
   int64_t total = 0;
   for (int i = 0; i < L.n; ++i) {
@@ -488,10 +514,20 @@ hipError_t launch_gemm_bwd(BwdLaunch& L, bool a_kc, bool b_kc, hipStream_t s) {
   if (total == 0) return hipSuccess;
   if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)total), block(kThreads);
-  if (a_kc && b_kc) hipLaunchKernelGGL((gemm_bwd_kernel<true, true>), grid, block, 0, s, L);
-  else if (!a_kc && !b_kc) hipLaunchKernelGGL((gemm_bwd_kernel<false, false>), grid, block, 0, s, L);
-  else if (a_kc) hipLaunchKernelGGL((gemm_bwd_kernel<true, false>), grid, block, 0, s, L);
-  else hipLaunchKernelGGL((gemm_bwd_kernel<false, true>), grid, block, 0, s, L);
+  // the layouts the layer backward uses: dgrad and dh (k-contiguous both),
+  // wgrad (k-strided both)
+  if (epi == kBwdSwiGLU) {
+    if (!a_kc || !b_kc) return hipErrorInvalidValue;
+    for (int i = 0; i < L.n; ++i)
+      if (!L.p[i].ab || L.p[i].N % 4 || L.p[i].half < L.p[i].N) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_bwd_kernel<true, true, kBwdSwiGLU>), grid, block, 0, s, L);
+  } else if (a_kc && b_kc) {
+    hipLaunchKernelGGL((gemm_bwd_kernel<true, true, kBwdStoreF32>), grid, block, 0, s, L);
+  } else if (!a_kc && !b_kc) {
+    hipLaunchKernelGGL((gemm_bwd_kernel<false, false, kBwdStoreF32>), grid, block, 0, s, L);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -501,7 +537,7 @@ hipError_t launch_swiglu_bwd(const SwigluBwdLaunch& L, hipStream_t s) {
   for (int i = 0; i < L.n; ++i) {
     const SwigluBwdProblem& P = L.p[i];
     if (P.d % kBK || P.F % kSN || P.d < kBK) return hipErrorInvalidValue;
-    const int64_t t = P.plan ? (int64_t)P.max_m_tiles * P.n_tiles_n
+    const int64_t t = P.plan ? (int64_t)2 * P.max_m_tiles * P.n_tiles_n
                              : (int64_t)P.G * ((P.M + kSB - 1) / kSB) * P.n_tiles_n;
     if (i == 0 && t != L.tiles0) return hipErrorInvalidValue;
     total += t;

@@ -42,6 +42,10 @@ struct GemmProblem {
   int64_t ldc;
   int64_t c_group_col;
   const float* col_bias;     // [N] or null, added in the fp32 epilogue
+  float* ab;                 // SwiGLU epilogue, or null: the gate and up sums,
+                             // gate at ab[row * ab_ld + g * ab_group_col + n],
+                             // up N columns further
+  int64_t ab_ld, ab_group_col;
   const int32_t* row_off;    // [G+1] device, or null for uniform groups
   const int32_t* plan;       // device tile list for row_off groups: plan[0] = count,
                              // then (group, first row) pairs
@@ -104,6 +108,7 @@ struct RouteSmallArgs {
   float* topk_margin;        // or null
   int32_t* blk_counts;       // [nblk, E]
   float* blk_psum;           // [nblk, E]
+  float* logits;             // [T, E] or null: the logits, logit_bias included
   int64_t T;
   int32_t d, E, k, score, renorm;
 };
@@ -202,6 +207,12 @@ hipError_t launch_lowrank(const LowRankArgs& a, hipStream_t s);
 //   Output: column n < c_split goes to C0, n >= c_split to C1 at n - c_split;
 //     element offset s * c_group + c * c_chunk + row * ldc. An empty k range
 //     writes zeros.
+enum BwdEpilogue : int {
+  kBwdStoreF32 = 0,   // C (float) as above
+  kBwdSwiGLU = 1,     // the product is dh: with a = ab[row, n], b = ab[row, half + n]
+                      // (ab + s * ab_group, leading dimension ab_ld), writes bf16
+                      // C0[row, n] = dh b SiLU'(a) and C0[row, half + n] = dh SiLU(a)
+};
 struct BwdGemm {
   const void* A;
   const int32_t* a_gather;   // k-contiguous A only
@@ -220,6 +231,9 @@ struct BwdGemm {
   int32_t k_chunk, n_chunks;
   int32_t M, N, K, G;
   int32_t n_tiles_m, n_tiles_n, max_m_tiles;
+  const float* ab;           // kBwdSwiGLU only
+  int64_t ab_ld, ab_group;
+  int32_t half;
 };
 constexpr int kBwdMaxProblems = 5;
 // Problems of one launch share the operand layouts; tiles of p[i] are
@@ -231,14 +245,15 @@ struct BwdLaunch {
 };
 // Work items (workgroups) of one problem.
 int64_t bwd_tiles(const BwdGemm& P);
-hipError_t launch_gemm_bwd(BwdLaunch& L, bool a_kcontig, bool b_kcontig, hipStream_t s);
+hipError_t launch_gemm_bwd(BwdLaunch& L, bool a_kcontig, bool b_kcontig, int epilogue,
+                           hipStream_t s);
 
 // SwiGLU backward of one expert group, fused with the recomputation of its
 // gate and up products: for rows r of group s and columns f < F
 //   a = X[xrow(r)] Wg_s[:, f],  b = X[xrow(r)] Wu_s[:, f],  dh = DY[r] Wd_s[f, :]^T
 //   DAB[r, f] = bf16(dh b SiLU'(a)),  DAB[r, F + f] = bf16(dh SiLU(a))
-// (+ s * ab_group). Rows: plan tiles of kSwigluBwdBM rows over m_off, or
-// rows [0, M) of each group s < G.
+// (+ s * ab_group). Rows: the two kSwigluBwdBM-row halves of each tile of a
+// kGemmBigBM-row plan over m_off, or rows [0, M) of each group s < G.
 constexpr int kSwigluBwdBM = 128;
 struct SwigluBwdProblem {
   const void* X;
@@ -265,9 +280,12 @@ hipError_t launch_swiglu_bwd(const SwigluBwdLaunch& L, hipStream_t s);
 // Upstream rows of the expert products and the gate gradients, one token per
 // wave: for kept slots j of token t (row = row_of_slot[t, j])
 //   dy_routed[row] = bf16(gate[t, j] dy[t]),  dgate[t, j] = <dy[t], y_routed[row]>
-// (dgate 0 for dropped slots), and dy_shared[t] = bf16(dy[t]) when non-null.
+// (dgate 0 for dropped slots), dy_shared[t] = bf16(dy[t]) when non-null, and
+// the token rows of the expert products x_perm[row] = x[t] when non-null.
 struct CombineBwdArgs {
   const float* dy;
+  const uint16_t* x;         // [T, d] bf16
+  uint16_t* x_perm;          // [R_max, d] bf16 or null
   const float* y_routed;
   const int32_t* row_of_slot;
   const float* topk_gate;

@@ -176,6 +176,9 @@ __global__ void __launch_bounds__(256) route_small_kernel(RouteSmallArgs a, int 
   int64_t out_t = -1;
   int out_idx = 0;
   float out_gate = 0.f, out_margin = 0.f;
+  float out_lg[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) out_lg[j] = 0.f;
   auto store_out = [&]() {
     if (out_t >= 0) {
       if (l16 < k) {
@@ -183,6 +186,11 @@ __global__ void __launch_bounds__(256) route_small_kernel(RouteSmallArgs a, int 
         a.topk_gate[out_t * k + l16] = out_gate;
       }
       if (a.topk_margin && l16 == 15) a.topk_margin[out_t] = out_margin;
+      if (a.logits) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+          if (eid[j] < E) a.logits[out_t * E + eid[j]] = out_lg[j];
+      }
     }
   };
 
@@ -312,6 +320,8 @@ __global__ void __launch_bounds__(256) route_small_kernel(RouteSmallArgs a, int 
     const float inv = 1.0f / tot;
 
     out_t = tval ? t : -1;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) out_lg[j] = lg[j];
 #pragma unroll
     for (int r = 0; r < KMAX; ++r) {
       if (l16 == r) {

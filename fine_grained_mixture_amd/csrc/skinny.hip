@@ -147,9 +147,13 @@ __global__ void __launch_bounds__(256) skinny_kernel(GemmLaunch L, int nch0, int
         static_cast<float*>(P.C)[(int64_t)row * P.ldc + ccol] = v0;
       } else {
         static_cast<bf16_t*>(P.C)[(int64_t)row * P.ldc + ccol] = f32_to_bf16(silu_f32(v0) * v1);
+        if (P.ab) {
+          float* abp = P.ab + (int64_t)row * P.ab_ld + (int64_t)g * P.ab_group_col + n0 + col;
+          abp[0] = v0;
+          abp[N] = v1;
+        }
       }
     }
-    (void)N;
   }
 }
 

@@ -72,7 +72,9 @@ class Outputs:
 
 
 def allocate_outputs(cfg: MoeConfig, T: int, device="cuda", *, margin=True, dropped=True,
-                     fP=True, y_lowp=False) -> Outputs:
+                     fP=True, y_lowp=False, saved_ab=False) -> Outputs:
+    """Output tensors of one layer call. saved_ab: also keep the forward's gate
+    and up products for the backward (bf16 dense layers)."""
     E, k, d = cfg.n_routed, cfg.top_k, cfg.hidden
     R = _lib.moe_max_rows(cfg, T)
     i32 = dict(dtype=torch.int32, device=device)
@@ -93,6 +95,8 @@ def allocate_outputs(cfg: MoeConfig, T: int, device="cuda", *, margin=True, drop
         "P": torch.empty((E,), **f32) if fP else None,
         "y": torch.empty((T, d), **f32),
         "y_lowp": torch.empty((T, d), dtype=torch_dtype(cfg), device=device) if y_lowp else None,
+        "saved_ab": (torch.empty((R * 2 * cfg.ffn + T * cfg.n_shared * 2 * cfg.ffn,), **f32)
+                     if saved_ab else None),
     }
     return Outputs(t, MoeOutputs(**{n: _ptr(t[n]) for n in _lib.OUTPUT_FIELDS}))
 

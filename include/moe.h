@@ -120,6 +120,14 @@ typedef struct {
   float   *P;             /* [E] optional: mean routing probability per expert    */
   float   *y;             /* [T, d] float32 layer output                          */
   void    *y_lowp;        /* [T, d] optional copy of y in cfg.dtype               */
+  float   *saved_ab;      /* optional, bf16 dense layers (ignored otherwise): the
+                             gate and up products a = x W_gate, b = x W_up that
+                             moe_layer_forward computes, float32, for
+                             moe_layer_backward to read instead of recomputing:
+                             [R_max, 2F] (dispatched row r: a at columns [0, F),
+                             b at [F, 2F)), then [T, S, 2F] (token t, shared
+                             expert s). Rows at and beyond offsets[E] of the
+                             first block are left untouched.                  */
 } moe_outputs;
 
 /* Capacity C = ceil(num * T * k / (den * E)) in exact integer arithmetic, as for

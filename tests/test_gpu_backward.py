@@ -30,9 +30,9 @@ pytestmark = pytest.mark.gpu
 NAMES = ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dsh_gate", "dsh_up", "dsh_down")
 
 
-def _gpu_fwd_bwd(wl, inp, dy, aux_grad):
+def _gpu_fwd_bwd(wl, inp, dy, aux_grad, saved=False):
     cfg, x, w = P.upload(wl, inp)
-    out = L.allocate_outputs(cfg, wl.T, x.device)
+    out = L.allocate_outputs(cfg, wl.T, x.device, saved_ab=saved)
     ws = L.allocate_workspace(cfg, wl.T, x.device)
     L.layer_forward(cfg, x, w, out, ws)
     dyt = torch.from_numpy(dy).to(x.device)
@@ -43,11 +43,11 @@ def _gpu_fwd_bwd(wl, inp, dy, aux_grad):
     return fwd, grads
 
 
-def _check(wl, *, aux_grad=1.0, zero_dy=False):
-    print(f"\n[case] {wl} aux_grad={aux_grad} zero_dy={zero_dy}", flush=True)
+def _check(wl, *, aux_grad=1.0, zero_dy=False, saved=False):
+    print(f"\n[case] {wl} aux_grad={aux_grad} zero_dy={zero_dy} saved={saved}", flush=True)
     inp = synth.make_inputs(wl)
     dy = np.zeros((wl.T, wl.hidden), np.float32) if zero_dy else synth.make_upstream(wl)
-    fwd, g = _gpu_fwd_bwd(wl, inp, dy, aux_grad)
+    fwd, g = _gpu_fwd_bwd(wl, inp, dy, aux_grad, saved)
     P.check_parity(wl, inp, fwd, tokens=[], check_y=False)
     spec = P.spec_of(wl)
     gi = fwd["topk_idx"].astype(np.int64)
@@ -93,6 +93,53 @@ CASES = {
 @pytest.mark.parametrize("name", list(CASES))
 def test_backward_parity(name):
     _check(CASES[name])
+
+
+# the forward keeps its gate and up products; the backward then runs dh alone
+SAVED = ["quartz_small", "moonfrost_small_capacity", "sutra_small_sigmoid", "quartz_no_shared",
+         "one_token", "wide_ffn_k1"]
+
+
+@pytest.mark.parametrize("name", SAVED)
+def test_backward_parity_saved_products(name):
+    _check(CASES[name], saved=True)
+
+
+def test_saving_products_leaves_forward_unchanged():
+    """y and the routing are bitwise the same with saved_ab; the saved gate and
+    up products match the oracle's x W_gate and x W_up on sampled rows."""
+    for wl in (synth.QUARTZ.replace(T=300, hidden=256, ffn=128, seed=12),
+               synth.QUARTZ.replace(T=3, hidden=256, ffn=128, seed=13)):
+        inp = synth.make_inputs(wl)
+        cfg, x, w = P.upload(wl, inp)
+        outs = []
+        for saved in (False, True):
+            out = L.allocate_outputs(cfg, wl.T, x.device, saved_ab=saved)
+            ws = L.allocate_workspace(cfg, wl.T, x.device)
+            L.layer_forward(cfg, x, w, out, ws)
+            torch.cuda.synchronize()
+            outs.append(out)
+        for key in ("y", "topk_idx", "topk_gate", "row_of_slot", "sorted_token"):
+            assert torch.equal(outs[0][key], outs[1][key]), key
+        ab = outs[1]["saved_ab"].cpu().numpy().astype(np.float64)
+        F, S, k = wl.ffn, wl.n_shared, wl.top_k
+        R = wl.T * k
+        rows = outs[1]["row_of_slot"].cpu().numpy()
+        idx = outs[1]["topk_idx"].cpu().numpy()
+        xs = inp["x"].astype(np.float64)
+        for t in sorted({0, wl.T // 2, wl.T - 1}):
+            for j in range(k):
+                e, r = int(idx[t, j]), int(rows[t, j])
+                want = np.concatenate([xs[t] @ inp["w_gate"][e], xs[t] @ inp["w_up"][e]])
+                got = ab[r * 2 * F:(r + 1) * 2 * F]
+                scale = np.abs(xs[t]) @ np.abs(np.concatenate([inp["w_gate"][e], inp["w_up"][e]], 1))
+                assert np.all(np.abs(got - want) <= 1e-5 * scale + 1e-30), (t, j)
+            for s_ in range(S):
+                want = np.concatenate([xs[t] @ inp["sh_gate"][s_], xs[t] @ inp["sh_up"][s_]])
+                o = R * 2 * F + (t * S + s_) * 2 * F
+                got = ab[o:o + 2 * F]
+                scale = np.abs(xs[t]) @ np.abs(np.concatenate([inp["sh_gate"][s_], inp["sh_up"][s_]], 1))
+                assert np.all(np.abs(got - want) <= 1e-5 * scale + 1e-30), (t, s_)
 
 
 def test_backward_aux_only():
