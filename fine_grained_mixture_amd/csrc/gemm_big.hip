@@ -282,19 +282,29 @@ gemm_big_kernel(GemmLaunch L) {
     }
   } else {
     if (P.ab) {
-      // the gate and up sums themselves, for the backward: lane l32 of each
-      // 32 x 32 block holds one column
-      float* abp = P.ab + tile.g * P.ab_group_col + tile.n0 + 32 * wn + l32;
+      // the gate and up sums themselves, for the backward: each of the two is
+      // staged as the wave's 128 rows x 32 columns (row pitch 36 floats), then
+      // written as 16-byte pieces, 8 per row
+      float* sf = reinterpret_cast<float*>(stage);
+      float* abp = P.ab + tile.g * P.ab_group_col + tile.n0 + 32 * wn + 4 * (lane & 7);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int half = 0; half < 2; ++half) {
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int row = row_base + 32 * i + 8 * (q >> 2) + 4 * lhi + (q & 3);
-          if (row < tile.r_end) {
-            abp[(int64_t)row * P.ab_ld] = acc[i][0][q];
-            abp[(int64_t)row * P.ab_ld + N] = acc[i][1][q];
-          }
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 16; ++q)
+            sf[(32 * i + 8 * (q >> 2) + 4 * lhi + (q & 3)) * 36 + l32] = acc[i][half][q];
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+          const int r = 8 * it + (lane >> 3);
+          const int row = row_base + r;
+          const floatx4 v = *reinterpret_cast<const floatx4*>(&sf[r * 36 + 4 * (lane & 7)]);
+          if (row < tile.r_end)
+            *reinterpret_cast<floatx4*>(abp + (int64_t)row * P.ab_ld + half * N) = v;
         }
+        __builtin_amdgcn_wave_barrier();
+      }
     }
     bf16_t* C = static_cast<bf16_t*>(P.C);
     bf16_t* st = reinterpret_cast<bf16_t*>(stage);

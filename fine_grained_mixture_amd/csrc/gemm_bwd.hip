@@ -283,56 +283,94 @@ gemm_bwd_kernel(BwdLaunch L) {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- epilogue through a private 18 KiB LDS slice per wave
+  // ---- epilogue through a private 18 KiB LDS slice per wave: each 32-row
+  // block of the wave's results is staged, then written as 16-byte pieces of
+  // rows (lane -> row 4 rr + L / 16 of the block, columns col .. col + 3)
   __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4));
   __builtin_amdgcn_s_barrier();
   float* st = reinterpret_cast<float*>(smem + wave * (kStages * kStageBytes / 4));
   const int row_base = r0 + 128 * wm;
   const int col = n0 + 64 * wn + 4 * (lane & 15);
-  float* cbase = nullptr;
-  if (EPI == kBwdStoreF32 && col < N) {
-    cbase = (col < P.c_split ? P.C0 + col : P.C1 + (col - P.c_split)) + s * P.c_group +
-            (int64_t)c * P.c_chunk;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  auto stage_block = [&](int i) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q)
         st[(8 * (q >> 2) + 4 * lhi + (q & 3)) * 72 + 32 * j + l32] = acc[i][j][q];
-    __builtin_amdgcn_wave_barrier();
+  };
+  if (EPI == kBwdStoreF32) {
+    float* cbase = nullptr;
+    if (col < N) {
+      cbase = (col < P.c_split ? P.C0 + col : P.C1 + (col - P.c_split)) + s * P.c_group +
+              (int64_t)c * P.c_chunk;
+    }
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      const int r = 4 * rr + (lane >> 4);
-      const int row = row_base + 32 * i + r;
-      const floatx4 v = *reinterpret_cast<const floatx4*>(&st[r * 72 + 4 * (lane & 15)]);
-      if (EPI == kBwdStoreF32) {
+    for (int i = 0; i < 4; ++i) {
+      stage_block(i);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const int r = 4 * rr + (lane >> 4);
+        const int row = row_base + 32 * i + r;
+        const floatx4 v = *reinterpret_cast<const floatx4*>(&st[r * 72 + 4 * (lane & 15)]);
         if (row < r_end && cbase) *reinterpret_cast<floatx4*>(cbase + (int64_t)row * P.ldc) = v;
-      } else if (row < r_end && col < N) {
-        // v = dh at columns col .. col + 3; a and b from the forward
-        const float* abr = P.ab + s * P.ab_group + (int64_t)row * P.ab_ld + col;
-        const floatx4 av = *reinterpret_cast<const floatx4*>(abr);
-        const floatx4 bv = *reinterpret_cast<const floatx4*>(abr + P.half);
-        float da[4], db[4];
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  } else {
+    // dh in acc; a and b of the same elements come from the forward. The
+    // loads of block i + 1 are issued before block i is processed, so their
+    // latency overlaps its arithmetic and stores (addresses are clamped into
+    // the valid rows and columns; out-of-range results are not stored).
+    const float* abase = P.ab + s * P.ab_group + min(col, N - 4);
+    floatx4 ca[8], cb[8], na[8], nb[8];
+    auto load_ab = [&](int i, floatx4* va, floatx4* vb) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-av[e]));
-          da[e] = v[e] * bv[e] * (sg * (1.0f + av[e] * (1.0f - sg)));
-          db[e] = v[e] * (av[e] * sg);
+      for (int rr = 0; rr < 8; ++rr) {
+        const int row = min(row_base + 32 * i + 4 * rr + (lane >> 4), r_end - 1);
+        const float* p = abase + (int64_t)row * P.ab_ld;
+        va[rr] = *reinterpret_cast<const floatx4*>(p);
+        vb[rr] = *reinterpret_cast<const floatx4*>(p + P.half);
+      }
+    };
+    load_ab(0, ca, cb);
+    bf16_t* obase = static_cast<bf16_t*>(static_cast<void*>(P.C0)) + s * P.c_group + col;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      stage_block(i);
+      if (i + 1 < 4) load_ab(i + 1, na, nb);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const int r = 4 * rr + (lane >> 4);
+        const int row = row_base + 32 * i + r;
+        const floatx4 v = *reinterpret_cast<const floatx4*>(&st[r * 72 + 4 * (lane & 15)]);
+        if (row < r_end && col < N) {
+          float da[4], db[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float a = ca[rr][e], b = cb[rr][e];
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+            da[e] = v[e] * b * (sg * (1.0f + a * (1.0f - sg)));
+            db[e] = v[e] * (a * sg);
+          }
+          u32x2 pa, pb;
+          pa[0] = (uint32_t)f32_to_bf16(da[0]) | ((uint32_t)f32_to_bf16(da[1]) << 16);
+          pa[1] = (uint32_t)f32_to_bf16(da[2]) | ((uint32_t)f32_to_bf16(da[3]) << 16);
+          pb[0] = (uint32_t)f32_to_bf16(db[0]) | ((uint32_t)f32_to_bf16(db[1]) << 16);
+          pb[1] = (uint32_t)f32_to_bf16(db[2]) | ((uint32_t)f32_to_bf16(db[3]) << 16);
+          bf16_t* o = obase + (int64_t)row * P.ldc;
+          *reinterpret_cast<u32x2*>(o) = pa;
+          *reinterpret_cast<u32x2*>(o + P.half) = pb;
         }
-        bf16_t* o = static_cast<bf16_t*>(static_cast<void*>(P.C0)) + s * P.c_group +
-                    (int64_t)row * P.ldc + col;
-        u32x2 pa, pb;
-        pa[0] = (uint32_t)f32_to_bf16(da[0]) | ((uint32_t)f32_to_bf16(da[1]) << 16);
-        pa[1] = (uint32_t)f32_to_bf16(da[2]) | ((uint32_t)f32_to_bf16(da[3]) << 16);
-        pb[0] = (uint32_t)f32_to_bf16(db[0]) | ((uint32_t)f32_to_bf16(db[1]) << 16);
-        pb[1] = (uint32_t)f32_to_bf16(db[2]) | ((uint32_t)f32_to_bf16(db[3]) << 16);
-        *reinterpret_cast<u32x2*>(o) = pa;
-        *reinterpret_cast<u32x2*>(o + P.half) = pb;
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        ca[rr] = na[rr];
+        cb[rr] = nb[rr];
       }
     }
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
