@@ -538,3 +538,117 @@ def layer_backward(x, weights: dict, spec: LayerSpec, dy, aux_grad=0.0, fwd=None
         out["M_dw_router"] = (ax[:, :, None] * adl[:, None, :]).max(axis=0)
         out["S_dw_router"] = ax.T @ adl
     return out
+
+
+def _router_dl(l, idx, gates, dg, f, spec: LayerSpec, aux_grad, T):
+    """Gradient of the loss with respect to the logits l [T, E] (unrounded):
+    the gate terms of the selected experts and the aux statistic's term,
+    vectorised over tokens (the same formulas as layer_backward's token loop)."""
+    E, k = spec.n_routed, spec.top_k
+    _, prob, sig = router_scores(l, spec)
+    dl = np.zeros((T, E))
+    ar = np.arange(T)[:, None]
+    c = aux_grad * spec.aux_coef * E / T
+    if spec.score == SOFTMAX and spec.renorm:
+        gd = np.sum(gates * dg, axis=1, keepdims=True)
+        np.add.at(dl, (ar, idx), gates * (dg - gd))
+    elif spec.score == SOFTMAX:
+        psel = np.take_along_axis(prob, idx, 1)
+        dl -= prob * np.sum(psel * dg, axis=1, keepdims=True)
+        np.add.at(dl, (ar, idx), psel * dg)
+    else:
+        st = np.take_along_axis(sig, idx, 1)
+        gd = np.sum(gates * dg, axis=1, keepdims=True)
+        dsig = (dg - gd) / st.sum(axis=1, keepdims=True)
+        np.add.at(dl, (ar, idx), dsig * st * (1.0 - st))
+    if spec.score == SOFTMAX:
+        dl += c * prob * (f[None, :] - (prob @ f)[:, None])
+    else:
+        ssum = sig.sum(axis=1, keepdims=True)
+        dl += c * (f[None, :] - (prob @ f)[:, None]) / ssum * sig * (1.0 - sig)
+    return dl
+
+
+def layer_backward_batched(x, weights: dict, spec: LayerSpec, dy, aux_grad=0.0, fwd=None):
+    """The same gradients as layer_backward (same readings, same rounding
+    points), computed per expert over all of its rows at once with matrix
+    products instead of token by token, for full-size checks.
+
+    Returns the gradients, their S_<name> (sum of the product terms'
+    magnitudes, as in layer_backward) and B_<name>, an upper bound of
+    layer_backward's M_<name>: the product of the largest magnitudes of the two
+    operands over the summed index.
+    """
+    if spec.rank != 0:
+        raise NotImplementedError("backward of low-rank experts")
+    x64 = np.asarray(x, np.float64)
+    T, d = x64.shape
+    E, k, S, F = spec.n_routed, spec.top_k, spec.n_shared, spec.ffn
+    rho = _rho(spec)
+    if fwd is None:
+        fwd = layer_forward(x, weights, spec, tokens=[])
+    dy = np.asarray(dy, np.float64)
+    idx, gates, rows = fwd["idx"], fwd["gates"], fwd["row_of_slot"]
+    out = {"dx": np.zeros((T, d)), "S_dx": np.zeros((T, d)), "B_dx": np.zeros((T, d))}
+    dg = np.zeros((T, k))
+
+    def colmax(m):
+        return np.abs(m).max(axis=0) if m.shape[0] else np.zeros(m.shape[1])
+
+    def expert(tok, g, wg, wu, wd):
+        X = x64[tok]
+        DY = rho(g[:, None] * dy[tok])
+        A = X @ wg
+        Bv = X @ wu
+        Hh = rho(silu(A) * Bv)
+        DH = DY @ wd.T
+        DA = rho(DH * Bv * dsilu(A))
+        DB = rho(DH * silu(A))
+        aX, aDA, aDB, aH, aDY = np.abs(X), np.abs(DA), np.abs(DB), np.abs(Hh), np.abs(DY)
+        res = {
+            "gate": (X.T @ DA, aX.T @ aDA, np.outer(colmax(X), colmax(DA))),
+            "up": (X.T @ DB, aX.T @ aDB, np.outer(colmax(X), colmax(DB))),
+            "down": (Hh.T @ DY, aH.T @ aDY, np.outer(colmax(Hh), colmax(DY))),
+        }
+        DX = DA @ wg.T + DB @ wu.T
+        SDX = aDA @ np.abs(wg).T + aDB @ np.abs(wu).T
+        rmax = np.maximum(aDA.max(axis=1, initial=0.0)[:, None] * np.abs(wg).max(axis=1)[None, :],
+                          aDB.max(axis=1, initial=0.0)[:, None] * np.abs(wu).max(axis=1)[None, :])
+        out["dx"][tok] += DX
+        out["S_dx"][tok] += SDX
+        np.maximum(out["B_dx"][tok], rmax, out=rmax)
+        out["B_dx"][tok] = rmax
+        return Hh @ wd, res
+
+    ex = Experts(weights, spec)
+    for kind, n in (("w", E), ("sh", S)):
+        if n == 0:
+            continue
+        acc = {p: [] for p in ("gate", "up", "down")}
+        for e in range(n):
+            if kind == "w":
+                ts, js = np.nonzero((idx == e) & (rows >= 0))
+                Y, res = expert(ts, gates[ts, js], ex.gate[e], ex.up[e], ex.down[e])
+                dg[ts, js] = np.sum(dy[ts] * Y, axis=1)
+            else:
+                _, res = expert(np.arange(T), np.ones(T), ex.sh[0][e], ex.sh[1][e], ex.sh[2][e])
+            for p in acc:
+                acc[p].append(res[p])
+        pre = "dw_" if kind == "w" else "dsh_"
+        for p, lst in acc.items():
+            out[pre + p] = np.stack([r[0] for r in lst])
+            out["S_" + pre + p] = np.stack([r[1] for r in lst])
+            out["B_" + pre + p] = np.stack([r[2] for r in lst])
+
+    l = router_logits(x, weights["w_router"], weights.get("logit_bias"))
+    dl = rho(_router_dl(l, idx, gates, dg, np.asarray(fwd["f"], np.float64), spec, aux_grad, T))
+    wr = np.asarray(weights["w_router"], np.float64)
+    out["dx"] += dl @ wr.T
+    out["S_dx"] += np.abs(dl) @ np.abs(wr).T
+    out["B_dx"] = np.maximum(out["B_dx"], np.abs(dl).max(axis=1, initial=0.0)[:, None]
+                             * np.abs(wr).max(axis=1)[None, :])
+    out["dw_router"] = x64.T @ dl
+    out["S_dw_router"] = np.abs(x64).T @ np.abs(dl)
+    out["B_dw_router"] = np.outer(colmax(x64), colmax(dl))
+    out["dl"], out["dg"] = dl, dg
+    return out

@@ -580,3 +580,26 @@ def test_backward_error_scales_bound_the_gradients():
     for name in ("dw_gate", "dw_up", "dw_down"):
         np.testing.assert_allclose(g1["M_" + name], np.abs(g1[name]), rtol=1e-12)
         np.testing.assert_allclose(g1["S_" + name], np.abs(g1[name]), rtol=1e-12)
+
+
+@pytest.mark.parametrize("case", BWD_CASES)
+@pytest.mark.parametrize("bf16", [False, True])
+def test_batched_backward_equals_token_loop(case, bf16):
+    """The per-expert batched backward (full-size checks) gives the token
+    loop's gradients and error sums S, and bounds its largest terms M."""
+    T, d, E, k, S, F, score, renorm, cap = case
+    w = _f64(_inputs(T, d, E, k, S, F, seed=60 + T, score=score, logit_std=0.5,
+                     select_std=0.2 if score == "sigmoid" else 0.0))
+    spec = _spec(d, E, k, S, F, score=score, renorm=renorm, capacity=cap, bf16=bf16,
+                 aux_coef=0.05)
+    x = w.pop("x")
+    dy = np.random.default_rng(8).standard_normal((T, d))
+    a = oracle.layer_backward(x, w, spec, dy, aux_grad=1.3, scales=True)
+    b = oracle.layer_backward_batched(x, w, spec, dy, aux_grad=1.3)
+    names = ["dx", "dw_router", "dw_gate", "dw_up", "dw_down"]
+    if S:
+        names += ["dsh_gate", "dsh_up", "dsh_down"]
+    for n in names:
+        assert _rel(b[n], a[n]) < 1e-10, n
+        assert _rel(b["S_" + n], a["S_" + n]) < 1e-10, n
+        assert np.all(b["B_" + n] >= a["M_" + n] * (1 - 1e-12)), n
