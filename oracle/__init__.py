@@ -7,4 +7,5 @@ from .moe_oracle import (LayerSpec, SOFTMAX, SIGMOID, round_bf16, silu, sigmoid,
                          router_logits, router_scores, select_topk, token_gates,
                          dispatch, swiglu, lowrank_apply, lowrank_swiglu, Experts,
                          aux_statistic, bias_update, route, layer_forward, dsilu,
-                         layer_backward, layer_backward_batched)
+                         layer_backward, layer_backward_batched, E4M3_MAX, e4m3_round,
+                         fp8_scale_exp, fp8_quantize, swiglu_fp8)

@@ -66,6 +66,7 @@ class LayerSpec:
     capacity: int = 0    # 0: dropless
     aux_coef: float = 0.01
     bf16: bool = True    # rho rounds to bf16 (bf16 workloads); identity for float32
+    fp8: bool = False    # expert products on fp8 (e4m3) codes: weights per column, rows per row
 
 
 # ---------------------------------------------------------------------------
@@ -92,6 +93,47 @@ def round_bf16(a) -> np.ndarray:
     out[big] = np.copysign(np.inf, a[big])
     out[~fin] = a[~fin]
     return out
+
+
+# ---------------------------------------------------------------------------
+# fp8 (the storage ladder's first rung, dormouse "TSCT low-rank experts" card):
+# OCP E4M3 -- sign, 4 exponent bits (bias 7), 3 mantissa bits; normal values
+# (1 + m/8) 2^(e-7) for e = 1..15 except the all-ones code (NaN), subnormals
+# (m/8) 2^-6; largest finite 448. A vector is stored as codes times one power of
+# two 2^s per row (activations) or per output column (weights), s the smallest
+# integer with amax 2^-s <= 448, so that scaling is exact and the only rounding
+# is round-to-nearest-even of v 2^-s onto the E4M3 grid.
+# ---------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_round(v) -> np.ndarray:
+    """Nearest E4M3 value to v (|v| <= 448), ties to the even mantissa."""
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    frac, ex = np.frexp(np.where(a > 0, a, 1.0))       # a = frac 2^ex, frac in [0.5, 1)
+    e = ex - 1                                          # a = (2 frac) 2^e, 2 frac in [1, 2)
+    normal = a >= 2.0 ** -6
+    qn = np.ldexp(np.rint(np.ldexp(a, 3 - e)), e - 3)   # 3 fraction bits at exponent e
+    qs = np.ldexp(np.rint(np.ldexp(a, 9)), -9)          # subnormal spacing 2^-9
+    q = np.where(normal, qn, qs)
+    return np.copysign(q, v)
+
+
+def fp8_scale_exp(amax) -> np.ndarray:
+    """Smallest integer s with amax 2^-s <= 448 (0 where amax is 0)."""
+    amax = np.asarray(amax, np.float64)
+    frac, ex = np.frexp(np.where(amax > 0, amax, 1.0))  # amax = frac 2^ex
+    s = np.where(frac <= 0.875, ex - 9, ex - 8)          # 448 = 0.875 2^9
+    return np.where(amax > 0, s, 0).astype(np.int64)
+
+
+def fp8_quantize(m, axis):
+    """Quantise m along `axis` (the summed dimension of its product): one
+    scale per slice. Returns (the dequantised values q 2^s, s)."""
+    m = np.asarray(m, np.float64)
+    s = fp8_scale_exp(np.max(np.abs(m), axis=axis, keepdims=True))
+    return np.ldexp(e4m3_round(np.ldexp(m, -s)), s), np.squeeze(s, axis)
 
 
 def _rho(spec: LayerSpec):
@@ -257,12 +299,50 @@ def lowrank_swiglu(xrow, f, rho):
     return lowrank_apply(h, f["u_down"], f["s_down"], f["v_down"], rho)
 
 
+class _Fp8Bank:
+    """float64 values of an expert bank quantised per output column (fp8)."""
+
+    def __init__(self, arr):
+        self.arr = arr
+        self.cache = {}
+
+    def __getitem__(self, e):
+        m = self.cache.get(e)
+        if m is None:
+            m = fp8_quantize(np.asarray(self.arr[e], np.float64), axis=0)[0]
+            self.cache[e] = m
+        return m
+
+
+def swiglu_fp8(xrow, w_gate, w_up, w_down, rho):
+    """SwiGLU with fp8 products: the row entering each product is quantised
+    (x over d, h = rho(SiLU(a) b) over F); the weights come quantised."""
+    xq = fp8_quantize(xrow, axis=0)[0]
+    h = rho(silu(xq @ w_gate) * (xq @ w_up))
+    return fp8_quantize(h, axis=0)[0] @ w_down
+
+
 class Experts:
     """Routed and shared expert weights of one layer in float64."""
 
     def __init__(self, weights: dict, spec: LayerSpec):
         self.spec = spec
         self.rho = _rho(spec)
+        if spec.fp8:
+            if spec.rank != 0 or not spec.bf16:
+                raise ValueError("fp8 experts: dense bf16 layers only")
+            self.gate = _Fp8Bank(weights["w_gate"])
+            self.up = _Fp8Bank(weights["w_up"])
+            self.down = _Fp8Bank(weights["w_down"])
+            self.S = spec.n_shared
+            if self.S > 0:
+                S, F, d = self.S, spec.ffn, spec.hidden
+                # the shared experts' down projections are one product over
+                # their stacked S F rows (summed experts): one scale per column
+                self.sh = [_Fp8Bank(weights["sh_gate"]), _Fp8Bank(weights["sh_up"])]
+                self.sh_down = fp8_quantize(
+                    np.asarray(weights["sh_down"], np.float64).reshape(S * F, d), axis=0)[0]
+            return
         if spec.rank == 0:
             self.gate = _Bank(weights["w_gate"])
             self.up = _Bank(weights["w_up"])
@@ -277,12 +357,20 @@ class Experts:
                        _Bank(weights["sh_down"])]
 
     def routed(self, xrow, e):
+        if self.spec.fp8:
+            return swiglu_fp8(xrow, self.gate[e], self.up[e], self.down[e], self.rho)
         if self.spec.rank == 0:
             return swiglu(xrow, self.gate[e], self.up[e], self.down[e], self.rho)
         f = {n: b[e] for n, b in self.lr.items()}
         return lowrank_swiglu(xrow, f, self.rho)
 
     def shared(self, xrow):
+        if self.spec.fp8:
+            # h of every shared expert, quantised as one row of S F values
+            xq = fp8_quantize(xrow, axis=0)[0]
+            h = np.concatenate([self.rho(silu(xq @ self.sh[0][s]) * (xq @ self.sh[1][s]))
+                                for s in range(self.S)])
+            return fp8_quantize(h, axis=0)[0] @ self.sh_down
         out = np.zeros(self.spec.hidden)
         for s in range(self.S):
             out = out + swiglu(xrow, self.sh[0][s], self.sh[1][s], self.sh[2][s], self.rho)
@@ -448,8 +536,8 @@ def layer_backward(x, weights: dict, spec: LayerSpec, dy, aux_grad=0.0, fwd=None
     formed from rounded operands; the terms of dx are its products' terms
     with the weights).
     """
-    if spec.rank != 0:
-        raise NotImplementedError("backward of low-rank experts")
+    if spec.rank != 0 or spec.fp8:
+        raise NotImplementedError("backward of low-rank or fp8 experts")
     x = np.asarray(x)
     T, d = x.shape
     E, k, S, F = spec.n_routed, spec.top_k, spec.n_shared, spec.ffn
@@ -579,8 +667,8 @@ def layer_backward_batched(x, weights: dict, spec: LayerSpec, dy, aux_grad=0.0, 
     layer_backward's M_<name>: the product of the largest magnitudes of the two
     operands over the summed index.
     """
-    if spec.rank != 0:
-        raise NotImplementedError("backward of low-rank experts")
+    if spec.rank != 0 or spec.fp8:
+        raise NotImplementedError("backward of low-rank or fp8 experts")
     x64 = np.asarray(x, np.float64)
     T, d = x64.shape
     E, k, S, F = spec.n_routed, spec.top_k, spec.n_shared, spec.ffn

@@ -603,3 +603,110 @@ def test_batched_backward_equals_token_loop(case, bf16):
         assert _rel(b[n], a[n]) < 1e-10, n
         assert _rel(b["S_" + n], a["S_" + n]) < 1e-10, n
         assert np.all(b["B_" + n] >= a["M_" + n] * (1 - 1e-12)), n
+
+
+# ---------------------------------------------------------------- fp8 (E4M3)
+def _e4m3_codes():
+    """Every finite E4M3 value from the bit layout, by brute enumeration."""
+    vals = []
+    for c in range(256):
+        sgn, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            continue
+        v = (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+        vals.append((-v if sgn else v, c))
+    return vals
+
+
+def test_e4m3_round_matches_torch_on_every_bf16_value():
+    bits = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+    v = bits[np.isfinite(bits) & (np.abs(bits) <= 448)].astype(np.float64)
+    ours = oracle.e4m3_round(v)
+    ref = torch.tensor(v, dtype=torch.float32).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_e4m3_round_is_nearest_with_ties_to_even():
+    codes = _e4m3_codes()
+    pos = sorted({abs(v) for v, _ in codes})
+    assert len(pos) == 127 and pos[-1] == 448.0 and pos[1] == 2.0 ** -9
+    grid = np.array(pos)
+    rng = np.random.default_rng(0)
+    mids = (grid[:-1] + grid[1:]) / 2
+    v = np.concatenate([mids, -mids, rng.uniform(-448, 448, 5000),
+                        rng.uniform(-1, 1, 5000) * 2.0 ** -5])
+    q = oracle.e4m3_round(v)
+    code_of = {val: c for val, c in codes if val >= 0}
+    for x, y in zip(v, q):
+        d = np.abs(grid - abs(x))
+        best = grid[d == d.min()]
+        if len(best) == 2:   # tie: the even code (even mantissa)
+            best = [b for b in best if code_of[b] % 2 == 0]
+        assert abs(y) == best[0] and (y == 0 or (x > 0) == (y > 0))
+
+
+def test_fp8_scale_rule():
+    s = oracle.fp8_scale_exp
+    assert s(448.0) == 0 and s(448.0 * 2 ** -5) == -5 and s(449.0) == 1 and s(0.0) == 0
+    assert s(1.0) == -8 and s(0.875) == -9 and s(2.0 ** -20) == -28
+    rng = np.random.default_rng(1)
+    amax = np.exp(rng.uniform(-30, 30, 2000))
+    e = s(amax)
+    assert np.all(np.ldexp(amax, -e) <= 448.0)          # fits
+    assert np.all(np.ldexp(amax, -(e - 1)) > 448.0)     # and is the smallest that fits
+
+
+def test_fp8_quantize_error_and_exact_cases():
+    rng = np.random.default_rng(2)
+    m = rng.standard_normal((40, 30)) * np.exp(rng.uniform(-5, 5, (1, 30)))
+    q, s = oracle.fp8_quantize(m, axis=0)
+    assert s.shape == (30,)
+    scale = np.ldexp(1.0, s)[None, :]
+    # relative error <= 2^-4 where normal, absolute <= 2^-10 scale where subnormal
+    err = np.abs(q - m)
+    assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(m), 2.0 ** -10 * scale) * (1 + 1e-12))
+    assert np.all(np.abs(q) <= 448 * scale)
+    # values already on the grid (with a column maximum that keeps the scale) stay
+    grid = np.array(sorted({abs(v) for v, _ in _e4m3_codes()}))
+    g = rng.choice(grid, (20, 6)) * rng.choice([-1, 1], (20, 6))
+    g[0] = 448.0
+    g = np.ldexp(g, np.array([-12, -3, 0, 2, 5, 9])[None, :])
+    np.testing.assert_array_equal(oracle.fp8_quantize(g, axis=0)[0], g)
+
+
+def test_fp8_layer_reduces_to_quantised_h_on_grid_inputs():
+    """With x rows and weight columns already on their E4M3 grids (scales
+    preserved), the fp8 layer is the bf16 layer with h quantised; h's
+    quantisation here goes through torch's float8_e4m3fn."""
+    T, d, E, k, S, F = 6, 32, 4, 2, 1, 16
+    rng = np.random.default_rng(3)
+    grid = np.array(sorted({abs(v) for v, _ in _e4m3_codes()}))
+    def ongrid(shape, sc):
+        a = rng.choice(grid[grid <= 240], shape) * rng.choice([-1, 1], shape)
+        return np.ldexp(a, sc)
+    x = ongrid((T, d), 0)
+    x[:, 0] = 448.0                       # every row's scale is 1
+    w = _inputs(T, d, E, k, S, F, seed=4, bf16=True)
+    for n in ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down"):
+        a = ongrid(w[n].shape, -9)
+        a[..., 0, :] = 448.0 * 2.0 ** -9  # every column's scale is 2^-9
+        w[n] = a
+    w["x"] = x
+    spec8 = _spec(d, E, k, S, F, bf16=True, fp8=True)
+    got = oracle.layer_forward(x, w, spec8)
+    ref = oracle.layer_forward(x, w, _spec(d, E, k, S, F, bf16=True), tokens=[])
+    rho = oracle.round_bf16
+    def q_torch(h):
+        s = oracle.fp8_scale_exp(np.max(np.abs(h)))
+        t = torch.tensor(np.ldexp(h, -s), dtype=torch.float32).to(torch.float8_e4m3fn)
+        return np.ldexp(t.to(torch.float64).numpy(), s)
+    y = np.zeros((T, d))
+    for t in range(T):
+        hs = np.concatenate([rho(oracle.silu(x[t] @ w["sh_gate"][s_]) * (x[t] @ w["sh_up"][s_]))
+                             for s_ in range(S)])
+        y[t] = q_torch(hs) @ w["sh_down"].reshape(S * F, d)
+        for j in range(k):
+            e = int(ref["idx"][t, j])
+            h = rho(oracle.silu(x[t] @ w["w_gate"][e]) * (x[t] @ w["w_up"][e]))
+            y[t] += ref["gates"][t, j] * (q_torch(h) @ w["w_down"][e])
+    np.testing.assert_allclose(got["y"], y, rtol=1e-12, atol=1e-12)
