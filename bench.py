@@ -8,7 +8,8 @@ synthetic inputs already resident in device memory. Prints one JSON line.
 For bf16 dense layers the line also carries the training pair under
 "backward": the forward that keeps its gate and up products, the
 moe_layer_backward call after it, forward + backward tokens/s, and the
-backward products' TFLOP/s.
+backward products' TFLOP/s; and under "fp8" the same layer with fp8 (E4M3)
+expert weights (moe_quantize_fp8), its step time and expert-GEMM rates.
 
 Per-kernel durations come from HIP events that the library records on the
 launch stream between its kernels (moe_layer_forward_timed); the dominant
@@ -30,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 
@@ -41,6 +43,7 @@ def parse():
     ap.add_argument("--workload", default="quartz")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the layer backward")
+    ap.add_argument("--no-fp8", action="store_true", help="skip timing the fp8-expert layer")
     ap.add_argument("--cpu-tokens", type=int, default=1536,
                     help="tokens of the workload the CPU oracle processes")
     ap.add_argument("--tokens", type=int, default=0,
@@ -69,7 +72,7 @@ def copy_calibration(mib: int):
 def algorithmic(wl, rows):
     """Algorithmic FLOPs and bytes of each stage for `rows` dispatched rows."""
     T, d, E, k, S, F, r = wl.T, wl.hidden, wl.n_routed, wl.top_k, wl.n_shared, wl.ffn, wl.rank
-    b = 2 if wl.dtype == "bf16" else 4
+    b = 2 if wl.dtype in ("bf16", "fp8") else 4
     if r == 0:
         gate_up = 4.0 * d * F * rows
         down = 2.0 * d * F * rows
@@ -173,6 +176,61 @@ def time_backward(wl, cfg, x, w, steps, warmup, stream):
     return fwd_ms, ms, {n: float(np.mean(v)) for n, v in dur.items()}
 
 
+def time_fp8(wl, inp, x, steps, warmup, stream):
+    """The same layer with fp8 (E4M3) expert weights: mean step time and the
+    per-kernel durations from the library's events."""
+    import numpy as np
+    import torch
+
+    from fine_grained_mixture_amd import _lib
+    from fine_grained_mixture_amd.layer import (DeviceWeights, allocate_outputs,
+                                                allocate_workspace, config_from_workload)
+
+    wl8 = wl.replace(dtype="fp8")
+    cfg = config_from_workload(wl8)
+    w = DeviceWeights.from_numpy(inp, cfg, x.device)
+    out = allocate_outputs(cfg, wl.T, x.device)
+    ws = allocate_workspace(cfg, wl.T, x.device)
+
+    def step(events=None):
+        if events is None:
+            _lib.moe_layer_forward(cfg, wl.T, x.data_ptr(), w.struct, out.struct, ws.data_ptr(),
+                                   ws.numel(), stream)
+            return 0
+        return _lib.moe_layer_forward_timed(cfg, wl.T, x.data_ptr(), w.struct, out.struct,
+                                            ws.data_ptr(), ws.numel(), stream,
+                                            [e.cuda_event for e in events])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    sets = []
+    for _ in range(steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(32)]
+        for e in evs:
+            e.record()
+        sets.append(evs)
+    torch.cuda.synchronize()
+    n_k = 0
+    for evs in sets:
+        n_k = step(evs)
+    torch.cuda.synchronize()
+    names = [_lib.moe_stage_name(i) for i in range(n_k)]
+    dur = {n: [] for n in names}
+    for evs in sets:
+        for i, n in enumerate(names):
+            dur[n].append(evs[2 * i].elapsed_time(evs[2 * i + 1]) * 1e3)
+    return ms, {n: float(np.mean(v)) for n, v in dur.items()}
+
+
 def traffic_from_profile(kernel_src: str):
     """HBM bytes per launch of the gate/up kernel from the committed counter
     summary, if it was taken from the current kernel source; else None."""
@@ -197,7 +255,8 @@ def cpu_baseline(wl, inp, n_tokens):
     spec = oracle.LayerSpec(hidden=wl.hidden, n_routed=wl.n_routed, top_k=wl.top_k,
                             n_shared=wl.n_shared, ffn=wl.ffn, rank=wl.rank, score=wl.score,
                             renorm=bool(wl.renorm), capacity=sub.capacity,
-                            aux_coef=wl.aux_coef, bf16=wl.dtype == "bf16")
+                            aux_coef=wl.aux_coef, bf16=wl.dtype in ("bf16", "fp8"),
+                            fp8=wl.dtype == "fp8")
     sinp = dict(inp)
     sinp["x"] = np.ascontiguousarray(inp["x"][: sub.T])
     with threadpool_limits(limits=1):
@@ -233,7 +292,7 @@ def main():
     inp = synth.make_inputs(wl)
     cfg = config_from_workload(wl)
     dev = torch.device("cuda:0")
-    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    dt = torch.bfloat16 if wl.dtype in ("bf16", "fp8") else torch.float32
     x = torch.from_numpy(inp["x"]).to(device=dev, dtype=dt)
     w = DeviceWeights.from_numpy(inp, cfg, dev)
     out = allocate_outputs(cfg, wl.T, dev)
@@ -387,6 +446,17 @@ def main():
         for n, f in gemm.items():
             bwd[n + "_tflops"] = f / (bst[n] * 1e-6) / 1e12
         result["backward"] = bwd
+    if wl.dtype == "bf16" and wl.rank == 0 and not args.no_fp8:
+        fms8, st8 = time_fp8(wl, inp, x, args.steps, args.warmup, stream)
+        gu8 = alg["gate_up_flops"] + alg["shared_gate_up_flops"]
+        dn8 = alg["down_flops"] + alg["shared_down_flops"]
+        result["fp8"] = {
+            "ms_per_step": fms8, "tokens_per_s": wl.T / (fms8 * 1e-3), "stage_us_mean": st8,
+            "gate_up_tflops": gu8 / (st8["gate_up_gemm"] * 1e-6) / 1e12,
+            "gate_up_frac_of_fp8_peak": gu8 / (st8["gate_up_gemm"] * 1e-6) / 1e12 / PEAK_FP8_TFLOPS,
+            "expert_gemm_tflops": (gu8 + dn8) / ((st8["gate_up_gemm"] + st8["down_gemm"]) * 1e-6)
+            / 1e12,
+        }
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_tokens)
     print(json.dumps(result))

@@ -14,12 +14,13 @@ from ctypes import POINTER, c_char_p, c_float, c_int, c_int32, c_int64, c_size_t
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_FP8 = 0, 1, 2
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_GROUPS_ROUTED, MOE_GROUPS_SHARED = 1, 2
 
 EXPORTED = ("moe_capacity", "moe_max_rows", "moe_workspace_bytes", "moe_route", "moe_permute",
-            "moe_grouped_ffn", "moe_combine", "moe_bias_update", "moe_layer_forward",
+            "moe_grouped_ffn", "moe_combine", "moe_bias_update", "moe_quantize_fp8",
+            "moe_layer_forward",
             "moe_layer_forward_timed", "moe_backward_workspace_bytes", "moe_layer_backward",
             "moe_layer_backward_timed", "moe_stage_name", "moe_status_str", "moe_last_error")
 
@@ -33,7 +34,9 @@ class MoeConfig(ctypes.Structure):
 
 WEIGHT_FIELDS = ("w_router", "logit_bias", "select_bias", "w_gate", "w_up", "w_down",
                  "u_gate", "s_gate", "v_gate", "u_up", "s_up", "v_up",
-                 "u_down", "s_down", "v_down", "sh_gate", "sh_up", "sh_down")
+                 "u_down", "s_down", "v_down", "sh_gate", "sh_up", "sh_down",
+                 "w_gate_scale", "w_up_scale", "w_down_scale", "sh_gate_scale", "sh_up_scale",
+                 "sh_down_scale")
 OUTPUT_FIELDS = ("topk_idx", "topk_gate", "topk_margin", "counts", "kept", "offsets",
                  "sorted_token", "row_of_slot", "dropped", "n_dropped", "aux", "f", "P",
                  "y", "y_lowp", "saved_ab")
@@ -90,6 +93,7 @@ def load():
                                     c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "moe_combine": (c_int, [cfgp, c_int64, c_void_p, c_void_p, op, c_void_p]),
         "moe_bias_update": (c_int, [cfgp, c_int64, c_void_p, c_void_p, c_float, c_void_p]),
+        "moe_quantize_fp8": (c_int, [cfgp, wp, wp, c_void_p]),
         "moe_layer_forward": (c_int, [cfgp, c_int64, c_void_p, wp, op, c_void_p, c_size_t,
                                       c_void_p]),
         "moe_layer_forward_timed": (c_int, [cfgp, c_int64, c_void_p, wp, op, c_void_p,
@@ -150,6 +154,11 @@ def moe_grouped_ffn(cfg, T, groups, x_perm, offsets, x_shared, w, y_routed, y_sh
 def moe_bias_update(cfg, T, counts, select_bias, gamma, stream) -> None:
     _check(load().moe_bias_update(ctypes.byref(cfg), T, counts, select_bias, gamma, stream),
            "moe_bias_update")
+
+
+def moe_quantize_fp8(cfg, src, dst, stream) -> None:
+    _check(load().moe_quantize_fp8(ctypes.byref(cfg), ctypes.byref(src), ctypes.byref(dst),
+                                   stream), "moe_quantize_fp8")
 
 
 def moe_combine(cfg, T, y_routed, y_shared, o, stream) -> None:

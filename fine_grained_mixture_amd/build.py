@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "gemm.hip", "gemm_big.hip", "skinny.hip", "route.hip", "route_small.hip",
-           "combine.hip", "lowrank.hip", "gemm_bwd.hip", "backward.hip"]
+           "combine.hip", "lowrank.hip", "gemm_bwd.hip", "backward.hip", "fp8.hip"]
 
 # -packed-fp32-ops: no packed fp32 VALU instructions in the device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

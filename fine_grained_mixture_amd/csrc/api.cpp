@@ -40,17 +40,23 @@ bool valid_config(const moe_config* c) {
   if (c->score == MOE_SIGMOID && c->renorm_topk != 1) return false;
   if (c->renorm_topk != 0 && c->renorm_topk != 1) return false;
   if (c->capacity < 0) return false;
-  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return false;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16 && c->dtype != MOE_FP8) return false;
   return true;
 }
 
-// Low-rank experts: rank 64 with bf16 (the fused kernel's shape).
+// Low-rank experts: rank 64 with bf16 (the fused kernel's shape); fp8 experts
+// are dense.
 bool supported_config(const moe_config* c) {
   if (c->rank != 0 && (c->rank != 64 || c->dtype != MOE_BF16)) return false;
+  if (c->dtype == MOE_FP8 && c->rank != 0) return false;
   return true;
 }
 
-size_t elem_size(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
+// x, W_r and the activations are bf16 for MOE_BF16 and MOE_FP8.
+bool act_bf16(const moe_config* c) { return c->dtype != MOE_F32; }
+bool fp8(const moe_config* c) { return c->dtype == MOE_FP8; }
+
+size_t elem_size(const moe_config* c) { return act_bf16(c) ? 2 : 4; }
 
 int plan_bm(const moe_config* c) {
   if (c->dtype == MOE_F32) return kGemmBM_F32;
@@ -59,7 +65,7 @@ int plan_bm(const moe_config* c) {
 
 // bf16 layers with few experts use the fused router (16-token blocks).
 bool fused_router(const moe_config* c) {
-  return c->dtype == MOE_BF16 && c->n_routed <= kRouteSmallMaxE;
+  return act_bf16(c) && c->n_routed <= kRouteSmallMaxE;
 }
 int route_tb(const moe_config* c, int64_t T) {
   return fused_router(c) ? kRouteBlockSmall * route_small_groups(T, c->top_k) : kRouteBlock;
@@ -69,7 +75,10 @@ struct Layout {
   int64_t T = 0, R = 0, nblk = 0, max_tiles = 0;
   int tb = kRouteBlock;
   size_t logits = 0, blk_counts = 0, blk_base = 0, blk_psum = 0, psum_tot = 0, plan = 0;
-  size_t h = 0, h_sh = 0, y_perm = 0, y_sh = 0, total = 0;
+  size_t h = 0, h_sh = 0, y_perm = 0, y_sh = 0;
+  // fp8 experts: quantised rows and their scales
+  size_t xq = 0, xs = 0, xq_sh = 0, xs_sh = 0, hq = 0, hs = 0, hq_sh = 0, hs_sh = 0;
+  size_t total = 0;
 };
 
 int64_t max_rows(const moe_config* c, int64_t T) {
@@ -103,6 +112,17 @@ Layout make_layout(const moe_config* c, int64_t T) {
   L.h_sh = take((size_t)T * S * F * es);
   L.y_perm = take((size_t)L.R * d * 4);
   L.y_sh = take(S > 0 ? (size_t)T * d * 4 : 0);
+  if (c->dtype == MOE_FP8) {
+    const int64_t xr = std::max<int64_t>(L.R, T);   // x rows (layer) or x_perm rows (stage)
+    L.xq = take((size_t)xr * d);
+    L.xs = take((size_t)xr * 4);
+    L.xq_sh = take((size_t)T * d);
+    L.xs_sh = take((size_t)T * 4);
+    L.hq = take((size_t)L.R * F);
+    L.hs = take((size_t)L.R * 4);
+    L.hq_sh = take((size_t)T * S * F);
+    L.hs_sh = take((size_t)T * 4);
+  }
   L.total = off;
   return L;
 }
@@ -174,6 +194,11 @@ bool permute_outputs_ok(const moe_outputs* o, int64_t T) {
 }
 bool expert_weights_ok(const moe_config* c, const moe_weights* w, bool routed, bool shared) {
   if (!w) return false;
+  if (c->dtype == MOE_FP8) {
+    if (routed && (!w->w_gate_scale || !w->w_up_scale || !w->w_down_scale)) return false;
+    if (shared && c->n_shared > 0 && (!w->sh_gate_scale || !w->sh_up_scale || !w->sh_down_scale))
+      return false;
+  }
   if (routed) {
     if (c->rank == 0) {
       if (!w->w_gate || !w->w_up || !w->w_down) return false;
@@ -228,13 +253,13 @@ void run_route(Runner& R, const moe_config* c, const Layout& L, const void* x,
     p.N = E;
     p.K = c->hidden;
     p.G = 1;
-    const int bn = c->dtype == MOE_BF16 ? 128 : 64;
-    const int bm = c->dtype == MOE_BF16 ? kGemmBM : kGemmBM_F32;
+    const int bn = act_bf16(c) ? 128 : 64;
+    const int bm = act_bf16(c) ? kGemmBM : kGemmBM_F32;
     p.n_tiles_n = (int32_t)ceil_div(E, bn);
     p.max_m_tiles = (int32_t)ceil_div(T, bm);
     G.n_problems = 1;
     G.tiles0 = p.max_m_tiles * p.n_tiles_n;
-    if (c->dtype == MOE_BF16 && E % 8 == 0) {
+    if (act_bf16(c) && E % 8 == 0) {
       // many experts: the large-tile kernel (256 x 128 tiles)
       p.n_tiles_n = (int32_t)ceil_div(E, 128);
       p.max_m_tiles = (int32_t)ceil_div(T, kGemmBigBM);
@@ -242,7 +267,7 @@ void run_route(Runner& R, const moe_config* c, const Layout& L, const void* x,
       R.run("router_gemm", [&] { return launch_gemm_big(G, kEpiStoreF32, R.stream); });
     } else {
       R.run("router_gemm", [&] {
-        return c->dtype == MOE_BF16 ? launch_gemm_bf16(G, kEpiStoreF32, R.stream)
+        return act_bf16(c) ? launch_gemm_bf16(G, kEpiStoreF32, R.stream)
                                     : launch_gemm_f32(G, kEpiStoreF32, R.stream);
       });
     }
@@ -304,6 +329,156 @@ void run_rank(Runner& R, const moe_config* c, const Layout& L, moe_outputs* o, v
   R.run("rank", [&] { return launch_rank(r, R.stream); });
 }
 
+
+// fp8 expert FFN: quantise the rows entering the gate/up products, the fp8
+// gate/up GEMM with SwiGLU (h in bf16, as in the bf16 path), quantise h rows,
+// the fp8 down GEMM. Routed rows A = a_routed gathered through a_rows (token
+// rows) or the dispatched rows themselves; shared rows A = a_shared.
+void run_ffn_fp8(Runner& R, const moe_config* c, const Layout& L, bool routed, bool shared,
+                 const void* a_routed, const int32_t* a_rows, const int32_t* offsets,
+                 const void* a_shared, const moe_weights* w, float* y_routed, float* y_shared,
+                 void* ws) {
+  const int64_t T = L.T, d = c->hidden, F = c->ffn, S = c->n_shared, E = c->n_routed;
+  void* h = at<void>(ws, L.h);
+  void* h_sh = at<void>(ws, L.h_sh);
+  const int32_t* plan = at<int32_t>(ws, L.plan);
+  uint8_t* xq = at<uint8_t>(ws, L.xq);
+  float* xs = at<float>(ws, L.xs);
+  uint8_t* xq_sh = at<uint8_t>(ws, L.xq_sh);
+  float* xs_sh = at<float>(ws, L.xs_sh);
+  const uint16_t* src_r = static_cast<const uint16_t*>(a_routed);
+  const uint16_t* src_s = static_cast<const uint16_t*>(a_shared);
+  // token rows gathered by the GEMM (the layer call): one quantisation of x
+  // serves the routed and the shared products
+  const bool same_rows = routed && shared && a_rows && src_r == src_s;
+  if (routed) {
+    R.run("quant_x", [&] {
+      return a_rows ? launch_quant_rows(src_r, d, T, (int32_t)d, nullptr, xq, xs, R.stream)
+                    : launch_quant_rows(src_r, d, L.R, (int32_t)d, offsets + E, xq, xs, R.stream);
+    });
+  }
+  if (shared && !same_rows) {
+    R.run("quant_x_shared", [&] {
+      return launch_quant_rows(src_s, d, T, (int32_t)d, nullptr, xq_sh, xs_sh, R.stream);
+    });
+  }
+  const uint8_t* xq_shared = same_rows ? xq : xq_sh;
+  const float* xs_shared = same_rows ? xs : xs_sh;
+  const bool both = routed && shared;
+  {
+    GemmLaunch G{};
+    int np = 0;
+    if (shared) {
+      GemmProblem& p = G.p[np++];
+      p.A = xq_shared;
+      p.lda = d;
+      p.a_scale = xs_shared;
+      p.B0 = w->sh_gate;
+      p.B1 = w->sh_up;
+      p.b_group_stride = F * d;
+      p.ldb = d;
+      p.b_scale0 = w->sh_gate_scale;
+      p.b_scale1 = w->sh_up_scale;
+      p.b_scale_group = F;
+      p.C = h_sh;
+      p.ldc = S * F;
+      p.c_group_col = F;
+      p.M = (int32_t)T;
+      p.N = (int32_t)F;
+      p.K = (int32_t)d;
+      p.G = (int32_t)S;
+      p.n_tiles_n = (int32_t)(F / 64);
+      p.max_m_tiles = (int32_t)(S * ceil_div(T, kGemmBigBM));
+    }
+    if (routed) {
+      GemmProblem& p = G.p[np++];
+      p.A = xq;
+      p.a_rows = a_rows;
+      p.lda = d;
+      p.a_scale = xs;
+      p.B0 = w->w_gate;
+      p.B1 = w->w_up;
+      p.b_group_stride = F * d;
+      p.ldb = d;
+      p.b_scale0 = w->w_gate_scale;
+      p.b_scale1 = w->w_up_scale;
+      p.b_scale_group = F;
+      p.C = h;
+      p.ldc = F;
+      p.row_off = offsets;
+      p.plan = plan;
+      p.N = (int32_t)F;
+      p.K = (int32_t)d;
+      p.G = (int32_t)E;
+      p.n_tiles_n = (int32_t)(F / 64);
+      p.max_m_tiles = (int32_t)L.max_tiles;
+    }
+    G.n_problems = np;
+    G.tiles0 = G.p[0].max_m_tiles * G.p[0].n_tiles_n;
+    R.run(both || routed ? "gate_up_gemm" : "shared_gate_up_gemm",
+          [&] { return launch_gemm_fp8(G, kEpiSwiGLU, R.stream); });
+  }
+  uint8_t* hq = at<uint8_t>(ws, L.hq);
+  float* hs = at<float>(ws, L.hs);
+  uint8_t* hq_sh = at<uint8_t>(ws, L.hq_sh);
+  float* hs_sh = at<float>(ws, L.hs_sh);
+  R.run("quant_h", [&] {
+    hipError_t e = hipSuccess;
+    if (routed)
+      e = launch_quant_rows(static_cast<const uint16_t*>(h), F, L.R, (int32_t)F, offsets + E, hq,
+                            hs, R.stream);
+    if (e == hipSuccess && shared)
+      e = launch_quant_rows(static_cast<const uint16_t*>(h_sh), S * F, T, (int32_t)(S * F),
+                            nullptr, hq_sh, hs_sh, R.stream);
+    return e;
+  });
+  {
+    GemmLaunch G{};
+    int np = 0;
+    if (shared) {
+      GemmProblem& p = G.p[np++];
+      p.A = hq_sh;
+      p.lda = S * F;
+      p.a_scale = hs_sh;
+      p.B0 = w->sh_down;          // [d, S F]: the S experts' down projections summed
+      p.ldb = S * F;
+      p.b_scale0 = w->sh_down_scale;
+      p.C = y_shared;
+      p.ldc = d;
+      p.M = (int32_t)T;
+      p.N = (int32_t)d;
+      p.K = (int32_t)(S * F);
+      p.G = 1;
+      p.n_tiles_n = (int32_t)ceil_div(d, 128);
+      p.max_m_tiles = (int32_t)ceil_div(T, kGemmBigBM);
+    }
+    if (routed) {
+      GemmProblem& p = G.p[np++];
+      p.A = hq;
+      p.lda = F;
+      p.a_scale = hs;
+      p.B0 = w->w_down;
+      p.b_group_stride = d * F;
+      p.ldb = F;
+      p.b_scale0 = w->w_down_scale;
+      p.b_scale_group = d;
+      p.C = y_routed;
+      p.ldc = d;
+      p.row_off = offsets;
+      p.plan = plan;
+      p.N = (int32_t)d;
+      p.K = (int32_t)F;
+      p.G = (int32_t)E;
+      p.n_tiles_n = (int32_t)ceil_div(d, 128);
+      p.max_m_tiles = (int32_t)L.max_tiles;
+    }
+    G.n_problems = np;
+    G.tiles0 = G.p[0].max_m_tiles * G.p[0].n_tiles_n;
+    R.run(both || routed ? "down_gemm" : "shared_down_gemm",
+          [&] { return launch_gemm_fp8(G, kEpiStoreF32, R.stream); });
+  }
+}
+
 // Expert FFN launches. Routed rows: A = a_routed with optional row gather;
 // shared rows: A = a_shared (T rows).
 void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool shared,
@@ -321,6 +496,11 @@ void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool 
   void* h = at<void>(ws, L.h);
   void* h_sh = at<void>(ws, L.h_sh);
   const int32_t* plan = at<int32_t>(ws, L.plan);
+  if (fp8(c)) {
+    run_ffn_fp8(R, c, L, routed, shared, a_routed, a_rows, offsets, a_shared, w, y_routed,
+                y_shared, ws);
+    return;
+  }
 
   // decode-sized batches: the weight-streaming skinny kernel
   const bool skinny = bf && T <= kSkinnyMaxT;
@@ -468,7 +648,7 @@ void run_combine(Runner& R, const moe_config* c, int64_t T, const float* y_route
   a.T = T;
   a.d = c->hidden;
   a.k = c->top_k;
-  a.dtype = c->dtype;
+  a.dtype = act_bf16(c) ? MOE_BF16 : MOE_F32;
   R.run("combine", [&] { return launch_combine(a, R.stream); });
 }
 
@@ -1031,6 +1211,35 @@ int moe_combine(const moe_config* c, int64_t T, const float* y_routed, const flo
   Runner R{static_cast<hipStream_t>(stream), &tl};
   run_combine(R, c, T, y_routed, c->n_shared > 0 ? y_shared : nullptr, o);
   return finish(tl);
+}
+
+int moe_quantize_fp8(const moe_config* c, const moe_weights* src, moe_weights* dst,
+                     void* stream) {
+  if (!valid_config(c) || c->dtype != MOE_FP8) return MOE_EINVAL;
+  if (c->rank != 0) return MOE_EUNSUPPORTED;
+  if (!src || !dst) return MOE_EINVAL;
+  moe_config bc = *c;
+  bc.dtype = MOE_BF16;
+  if (!expert_weights_ok(&bc, src, true, true) || !expert_weights_ok(c, dst, true, true))
+    return MOE_EINVAL;
+  const int64_t d = c->hidden, F = c->ffn, S = c->n_shared, E = c->n_routed;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto q = [&](const void* w, int64_t G, int64_t K, int64_t N, const void* out,
+               const float* scale) {
+    return launch_quant_cols(static_cast<const uint16_t*>(w), G, (int32_t)K, (int32_t)N,
+                             static_cast<uint8_t*>(const_cast<void*>(out)),
+                             const_cast<float*>(scale), s);
+  };
+  hipError_t e = q(src->w_gate, E, d, F, dst->w_gate, dst->w_gate_scale);
+  if (e == hipSuccess) e = q(src->w_up, E, d, F, dst->w_up, dst->w_up_scale);
+  if (e == hipSuccess) e = q(src->w_down, E, F, d, dst->w_down, dst->w_down_scale);
+  if (S > 0) {
+    if (e == hipSuccess) e = q(src->sh_gate, S, d, F, dst->sh_gate, dst->sh_gate_scale);
+    if (e == hipSuccess) e = q(src->sh_up, S, d, F, dst->sh_up, dst->sh_up_scale);
+    // the S down projections as one [S F, d] matrix
+    if (e == hipSuccess) e = q(src->sh_down, 1, S * F, d, dst->sh_down, dst->sh_down_scale);
+  }
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
 int moe_bias_update(const moe_config* c, int64_t T, const int32_t* counts, float* select_bias,

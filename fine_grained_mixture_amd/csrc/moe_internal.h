@@ -42,6 +42,11 @@ struct GemmProblem {
   int64_t ldc;
   int64_t c_group_col;
   const float* col_bias;     // [N] or null, added in the fp32 epilogue
+  const float* a_scale;      // fp8 products: per A row (indexed like A's rows after
+                             // the a_rows gather), and per B column of group g at
+  const float* b_scale0;     // b_scale + g * b_scale_group (b_scale1: the dual's up)
+  const float* b_scale1;
+  int64_t b_scale_group;
   float* ab;                 // SwiGLU epilogue, or null: the gate and up sums,
                              // gate at ab[row * ab_ld + g * ab_group_col + n],
                              // up N columns further
@@ -74,6 +79,20 @@ hipError_t launch_gemm_bf16(const GemmLaunch& L, int epilogue, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmLaunch& L, int epilogue, hipStream_t s);
 // 256 x 128 tiles (dual: 256 x (64 + 64)); N multiple of 8, K of 32.
 hipError_t launch_gemm_big(const GemmLaunch& L, int epilogue, hipStream_t s);
+// fp8 (E4M3) products: A rows and B = W^T rows both k-contiguous codes
+// (B0/B1 + g * b_group_stride + n * ldb + k), 256 x 128 tiles (dual: 256 x
+// (64 + 64)); the epilogue multiplies by a_scale[row] * b_scale[col]. K
+// multiple of 64.
+hipError_t launch_gemm_fp8(const GemmLaunch& L, int epilogue, hipStream_t s);
+// Quantise rows to E4M3: for row r < min(rows, *n_valid) (n_valid may be
+// null), s = the smallest power of two with amax(row) / s <= 448, codes
+// q[r * K + k] = RNE(src[r * ld + k] / s) and scale[r] = s. K multiple of 8.
+hipError_t launch_quant_rows(const uint16_t* src, int64_t ld, int64_t rows, int32_t K,
+                             const int32_t* n_valid, uint8_t* q, float* scale, hipStream_t s);
+// Quantise the columns of W[g] ([K, N] bf16, g < G) to E4M3 codes stored
+// k-contiguous: q[g][n][k], scale[g][n]. K and N multiples of 8.
+hipError_t launch_quant_cols(const uint16_t* w, int64_t G, int32_t K, int32_t N, uint8_t* q,
+                             float* scale, hipStream_t s);
 // Tile list of a row_off problem from offsets[0..G] (one workgroup).
 // Few rows per group (bf16): one workgroup per (group, 64 columns), weights
 // streamed once per pass of 4 rows; row_off groups or uniform groups of M rows.

@@ -12,7 +12,8 @@ import torch
 from . import _lib
 from ._lib import MoeConfig, MoeOutputs, MoeWeights
 
-_DT = {"bf16": (_lib.MOE_BF16, torch.bfloat16), "f32": (_lib.MOE_F32, torch.float32)}
+_DT = {"bf16": (_lib.MOE_BF16, torch.bfloat16), "f32": (_lib.MOE_F32, torch.float32),
+       "fp8": (_lib.MOE_FP8, torch.bfloat16)}
 
 
 def make_config(hidden, n_routed, top_k, n_shared, ffn, *, rank=0, score="softmax",
@@ -32,7 +33,8 @@ def config_from_workload(wl) -> MoeConfig:
 
 
 def torch_dtype(cfg: MoeConfig):
-    return torch.bfloat16 if cfg.dtype == _lib.MOE_BF16 else torch.float32
+    """Element type of x, W_r and the activations (bf16 also for fp8 experts)."""
+    return torch.float32 if cfg.dtype == _lib.MOE_F32 else torch.bfloat16
 
 
 def _ptr(t) -> int | None:
@@ -48,6 +50,8 @@ class DeviceWeights:
 
     @classmethod
     def from_numpy(cls, inputs: dict, cfg: MoeConfig, device="cuda") -> "DeviceWeights":
+        if cfg.dtype == _lib.MOE_FP8:
+            return cls.quantized_fp8(inputs, cfg, device)
         dt = torch_dtype(cfg)
         t = {}
         for n in _lib.WEIGHT_FIELDS:
@@ -60,6 +64,33 @@ class DeviceWeights:
                 t[n] = torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(device=device,
                                                                                  dtype=dt)
         return cls(t)
+
+
+def quantized_fp8(inputs: dict, cfg: MoeConfig, device="cuda") -> DeviceWeights:
+    """Device weights of an fp8 layer: the bf16 weights are uploaded and their
+    expert matrices quantised on the device by moe_quantize_fp8 (codes stored
+    transposed, one power-of-two scale per output column)."""
+    E, d, F, S = cfg.n_routed, cfg.hidden, cfg.ffn, cfg.n_shared
+    bcfg = MoeConfig.from_buffer_copy(cfg)
+    bcfg.dtype = _lib.MOE_BF16
+    src = DeviceWeights.from_numpy(inputs, bcfg, device)
+    u8 = dict(dtype=torch.uint8, device=device)
+    f32 = dict(dtype=torch.float32, device=device)
+    t = {n: src.t[n] for n in ("w_router", "logit_bias", "select_bias") if n in src.t}
+    t.update(w_gate=torch.empty((E, F, d), **u8), w_up=torch.empty((E, F, d), **u8),
+             w_down=torch.empty((E, d, F), **u8), w_gate_scale=torch.empty((E, F), **f32),
+             w_up_scale=torch.empty((E, F), **f32), w_down_scale=torch.empty((E, d), **f32))
+    if S:
+        t.update(sh_gate=torch.empty((S, F, d), **u8), sh_up=torch.empty((S, F, d), **u8),
+                 sh_down=torch.empty((d, S * F), **u8), sh_gate_scale=torch.empty((S, F), **f32),
+                 sh_up_scale=torch.empty((S, F), **f32), sh_down_scale=torch.empty((d,), **f32))
+    dst = DeviceWeights(t)
+    _lib.moe_quantize_fp8(cfg, src.struct, dst.struct, current_stream())
+    torch.cuda.current_stream().synchronize()   # src is freed on return
+    return dst
+
+
+DeviceWeights.quantized_fp8 = staticmethod(quantized_fp8)
 
 
 @dataclass

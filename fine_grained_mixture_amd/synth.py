@@ -51,7 +51,8 @@ class Workload:
     renorm: int = 1        # softmax: renormalise gates over the top-k
     capacity_factor: str = ""  # "" dropless; else C = ceil(cf*T*k/E), e.g. "5/4"
     aux_coef: float = 0.01
-    dtype: str = "bf16"    # "bf16" | "f32" for x and every weight
+    dtype: str = "bf16"    # "bf16" | "f32" for x and every weight; "fp8": bf16 draws,
+                           # the expert products on fp8 codes of the same weights
     logit_offset_std: float = 0.0   # per-expert N(0, std) added to logits
     select_bias_std: float = 0.0    # per-expert N(0, std) selection-only bias
     zipf_s: float = 0.0             # logit offset -s*ln(i+1) by expert id
@@ -123,7 +124,7 @@ def make_inputs(wl: Workload) -> dict:
     sh_up [S,d,F], sh_down [S,F,d].
     """
     rng = np.random.default_rng(wl.seed)
-    bf = wl.dtype == "bf16"
+    bf = wl.dtype in ("bf16", "fp8")
     T, d, E, S, F, r = wl.T, wl.hidden, wl.n_routed, wl.n_shared, wl.ffn, wl.rank
     out: dict = {}
     out["x"] = _normal(rng, (T, d), wl.x_std, bf)

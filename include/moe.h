@@ -35,8 +35,9 @@
  *   - Calls that share a workspace on different streams race; calls on one
  *     stream are ordered.
  *   - Limits of this build: 1 <= k <= 15, k <= E <= 4096; d and F multiples of
- *     64; T*k < 2^31; rank is 0 or 64 with bf16 (low-rank float32 experts are
- *     MOE_EUNSUPPORTED); sigmoid scoring requires renorm_topk == 1.
+ *     64; T*k < 2^31; rank is 0 or 64 with bf16 (low-rank float32 or fp8
+ *     experts are MOE_EUNSUPPORTED); sigmoid scoring requires renorm_topk == 1;
+ *     MOE_FP8 runs in moe_layer_forward and moe_grouped_ffn.
  */
 #ifndef FGM_MOE_H
 #define FGM_MOE_H
@@ -56,7 +57,9 @@ typedef enum {
   MOE_EHIP = -4           /* a HIP call failed; moe_last_error() holds its text      */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;        /* type of x and weights */
+/* type of x and weights. MOE_FP8: x, W_r, biases and the layer's activations as
+   for MOE_BF16; the dense expert weights are fp8 codes (see moe_weights). */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8 = 2 } moe_dtype;
 typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score;  /* router scoring rule   */
 
 /* moe_grouped_ffn `groups` bits */
@@ -97,6 +100,20 @@ typedef struct {
   const void *sh_gate;       /* [S, d, F] */
   const void *sh_up;         /* [S, d, F] */
   const void *sh_down;       /* [S, F, d] */
+  /* MOE_FP8 (the storage ladder's fp8 rung, dormouse "TSCT low-rank experts"
+     card): every expert matrix W[in, out] is stored as OCP E4M3 codes (one byte)
+     in the transposed order q[out, in], with one float32 power-of-two scale per
+     output column, W[i, o] ~= code(q[o, i]) * scale[o] (moe_quantize_fp8). The
+     pointers above then hold the codes:
+       w_gate, w_up [E, F, d]; w_down [E, d, F]; sh_gate, sh_up [S, F, d];
+       sh_down [d, S*F]: the S shared down projections as one [S*F, d] matrix
+       (they are summed), so one scale per output column over all S*F rows. */
+  const float *w_gate_scale;   /* [E, F] */
+  const float *w_up_scale;     /* [E, F] */
+  const float *w_down_scale;   /* [E, d] */
+  const float *sh_gate_scale;  /* [S, F] */
+  const float *sh_up_scale;    /* [S, F] */
+  const float *sh_down_scale;  /* [d]    */
 } moe_weights;
 
 /* Device output buffers, caller-allocated. R_max = T*k (dropless) or
@@ -176,6 +193,17 @@ int moe_grouped_ffn(const moe_config *cfg, int64_t T, int32_t groups,
    y_shared may be NULL (S == 0). Writes o->y and (o->y_lowp).               */
 int moe_combine(const moe_config *cfg, int64_t T, const float *y_routed,
                 const float *y_shared, moe_outputs *o, void *stream);
+
+/* fp8 expert weights from bf16 ones (cfg->dtype == MOE_FP8; rank 0). For every
+   expert matrix of src (bf16, the MOE_BF16 layouts) writes dst's codes and
+   scales (layouts in moe_weights): per output column o the scale is the smallest
+   power of two s with max_i |W[i, o]| / s <= 448, and each code is W[i, o] / s
+   rounded to the nearest E4M3 value, ties to even. The activations entering each
+   fp8 product (x rows over d, h rows over F -- for the shared experts one row of
+   S*F) are quantised the same way, per row, inside moe_layer_forward. dst's
+   arrays are caller-allocated device memory; src->w_router is not touched.   */
+int moe_quantize_fp8(const moe_config *cfg, const moe_weights *src, moe_weights *dst,
+                     void *stream);
 
 /* Loss-free balancing step (dormouse site, stack list "dropless MoE + LFB":
    balancing by a router bias instead of an auxiliary loss; Sutra-1.3B site,

@@ -314,12 +314,18 @@ class _Fp8Bank:
         return m
 
 
-def swiglu_fp8(xrow, w_gate, w_up, w_down, rho):
+def swiglu_fp8(xrow, w_gate, w_up, w_down, rho, with_max=False):
     """SwiGLU with fp8 products: the row entering each product is quantised
-    (x over d, h = rho(SiLU(a) b) over F); the weights come quantised."""
+    (x over d, h = rho(SiLU(a) b) over F); the weights come quantised. With
+    ``with_max`` also returns, per output column, the largest magnitude of one
+    term of the down product (the error scale of a quantised h entry)."""
     xq = fp8_quantize(xrow, axis=0)[0]
     h = rho(silu(xq @ w_gate) * (xq @ w_up))
-    return fp8_quantize(h, axis=0)[0] @ w_down
+    hq = fp8_quantize(h, axis=0)[0]
+    y = hq @ w_down
+    if not with_max:
+        return y
+    return y, (np.abs(hq)[:, None] * np.abs(w_down)).max(axis=0)
 
 
 class Experts:
@@ -356,21 +362,25 @@ class Experts:
             self.sh = [_Bank(weights["sh_gate"]), _Bank(weights["sh_up"]),
                        _Bank(weights["sh_down"])]
 
-    def routed(self, xrow, e):
+    def routed(self, xrow, e, with_max=False):
         if self.spec.fp8:
-            return swiglu_fp8(xrow, self.gate[e], self.up[e], self.down[e], self.rho)
+            return swiglu_fp8(xrow, self.gate[e], self.up[e], self.down[e], self.rho, with_max)
         if self.spec.rank == 0:
             return swiglu(xrow, self.gate[e], self.up[e], self.down[e], self.rho)
         f = {n: b[e] for n, b in self.lr.items()}
         return lowrank_swiglu(xrow, f, self.rho)
 
-    def shared(self, xrow):
+    def shared(self, xrow, with_max=False):
         if self.spec.fp8:
             # h of every shared expert, quantised as one row of S F values
             xq = fp8_quantize(xrow, axis=0)[0]
             h = np.concatenate([self.rho(silu(xq @ self.sh[0][s]) * (xq @ self.sh[1][s]))
                                 for s in range(self.S)])
-            return fp8_quantize(h, axis=0)[0] @ self.sh_down
+            hq = fp8_quantize(h, axis=0)[0]
+            y = hq @ self.sh_down
+            if not with_max:
+                return y
+            return y, (np.abs(hq)[:, None] * np.abs(self.sh_down)).max(axis=0)
         out = np.zeros(self.spec.hidden)
         for s in range(self.S):
             out = out + swiglu(xrow, self.sh[0][s], self.sh[1][s], self.sh[2][s], self.rho)
@@ -440,12 +450,14 @@ def route(x, w_router, spec: LayerSpec, logit_bias=None, select_bias=None,
 
 
 def layer_forward(x, weights: dict, spec: LayerSpec, tokens=None,
-                  override_idx=None, override_mask=None):
+                  override_idx=None, override_mask=None, scales=False):
     """The whole layer. y is evaluated for ``tokens`` (default: all tokens),
     routing and dispatch for every token (capacity decisions need them all).
 
     Returns a dict with the router outputs, the dispatch tables, the aux
-    statistic and ``y`` [len(tokens), d] in float64.
+    statistic and ``y`` [len(tokens), d] in float64. With ``scales`` (fp8
+    experts), also ``M_y``: per element of y the largest magnitude of one term
+    g h_f W_down[f, c] of its down products.
     """
     x = np.asarray(x)
     T = x.shape[0]
@@ -456,19 +468,36 @@ def layer_forward(x, weights: dict, spec: LayerSpec, tokens=None,
     experts = Experts(weights, spec)
     toks = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
     y = np.zeros((len(toks), spec.hidden))
+    want_max = scales and spec.fp8
+    m_y = np.zeros((len(toks), spec.hidden)) if want_max else None
     for n, t in enumerate(toks):
         xrow = np.asarray(x[t], np.float64)
-        acc = experts.shared(xrow) if spec.n_shared > 0 else np.zeros(spec.hidden)
+        acc = np.zeros(spec.hidden)
+        if spec.n_shared > 0:
+            if want_max:
+                ys, ms = experts.shared(xrow, True)
+                acc = acc + ys
+                m_y[n] = ms
+            else:
+                acc = acc + experts.shared(xrow)
         for j in range(spec.top_k):
             if dsp["row_of_slot"][t, j] < 0:
                 continue                      # dropped slot contributes nothing
-            acc = acc + r["gates"][t, j] * experts.routed(xrow, int(r["idx"][t, j]))
+            g = r["gates"][t, j]
+            if want_max:
+                yr, mr = experts.routed(xrow, int(r["idx"][t, j]), True)
+                acc = acc + g * yr
+                m_y[n] = np.maximum(m_y[n], g * mr)
+            else:
+                acc = acc + g * experts.routed(xrow, int(r["idx"][t, j]))
         y[n] = acc
     out = dict(r)
     out.update(dsp)
     out.update(aux)
     out["tokens"] = toks
     out["y"] = y
+    if want_max:
+        out["M_y"] = m_y
     return out
 
 

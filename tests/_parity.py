@@ -7,7 +7,12 @@ key margin exceeds 1e-4 in the oracle):
     bit-exact, after the oracle is re-run with near-tie tokens forced to the
     GPU's selection (either choice is correct for them);
   * gates within 1e-5 absolute, aux within 1e-4 relative;
-  * max |y_gpu - y_oracle| <= 1e-2 * RMS(y_oracle) over the checked tokens.
+  * max |y_gpu - y_oracle| <= 1e-2 * RMS(y_oracle) over the checked tokens;
+    for fp8 experts per element 1e-2 * RMS(y_oracle) + 2^-2 M_y, M_y the
+    largest single term g h_f W_down[f, c] of that element's down products:
+    both sides quantise h from their own bf16 h, and where those differ by one
+    bf16 ulp the E4M3 code can differ by one step (at most 2^-3 of h), which
+    the bound allows twice at the largest term.
 """
 from __future__ import annotations
 
@@ -23,18 +28,20 @@ NEAR_TIE = 1e-4
 Y_TOL = 1e-2
 GATE_TOL = 1e-5
 AUX_RTOL = 1e-4
+FP8_FLIP_TOKENS = 0.1
 
 
 def spec_of(wl) -> oracle.LayerSpec:
     return oracle.LayerSpec(hidden=wl.hidden, n_routed=wl.n_routed, top_k=wl.top_k,
                             n_shared=wl.n_shared, ffn=wl.ffn, rank=wl.rank, score=wl.score,
                             renorm=bool(wl.renorm), capacity=wl.capacity,
-                            aux_coef=wl.aux_coef, bf16=wl.dtype == "bf16")
+                            aux_coef=wl.aux_coef, bf16=wl.dtype in ("bf16", "fp8"),
+                            fp8=wl.dtype == "fp8")
 
 
 def upload(wl, inp, device="cuda"):
     cfg = config_from_workload(wl)
-    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    dt = torch.bfloat16 if wl.dtype in ("bf16", "fp8") else torch.float32
     x = torch.from_numpy(inp["x"]).to(device=device, dtype=dt)
     w = DeviceWeights.from_numpy(inp, cfg, device)
     return cfg, x, w
@@ -90,7 +97,7 @@ def check_parity(wl, inp, g, tokens=None, *, check_y=True):
     # oracle with the near-tie tokens forced to the GPU's choice
     ov = near & ~same
     ref = oracle.layer_forward(inp["x"], inp, spec, tokens=[] if not check_y else tokens,
-                               override_idx=gi, override_mask=ov)
+                               override_idx=gi, override_mask=ov, scales=spec.fp8)
     for key in ("counts", "kept", "offsets"):
         np.testing.assert_array_equal(g[key], ref[key], err_msg=key)
     assert int(g["n_dropped"][0]) == ref["n_dropped"]
@@ -125,7 +132,18 @@ def check_parity(wl, inp, g, tokens=None, *, check_y=True):
         err = float(np.max(np.abs(yg - yr))) if len(toks) else 0.0
         rep.update(y_err=err, y_rms=rms, y_rel=err / rms if rms else 0.0, checked=len(toks))
         assert np.all(np.isfinite(yg))
-        assert err <= Y_TOL * rms, f"max|dy| {err:.3e} > {Y_TOL} * RMS {rms:.3e}"
+        if spec.fp8:
+            tol = Y_TOL * rms + 2.0 ** -2 * ref["M_y"]
+            ratio = float(np.max(np.abs(yg - yr) / tol)) if len(toks) else 0.0
+            # flips touch only the tokens whose h row had one: the share of
+            # tokens with any element beyond the plain bound stays small
+            beyond = np.any(np.abs(yg - yr) > Y_TOL * rms, axis=1) if len(toks) else np.zeros(0)
+            frac = float(np.mean(beyond)) if len(toks) else 0.0
+            rep.update(y_tol_ratio=ratio, tokens_beyond_rms_bound=frac)
+            assert ratio <= 1.0, f"max |dy| / (1e-2 RMS + 2^-2 M_y) = {ratio:.3f}"
+            assert frac <= FP8_FLIP_TOKENS, f"{frac:.3f} of tokens beyond 1e-2 RMS"
+        else:
+            assert err <= Y_TOL * rms, f"max|dy| {err:.3e} > {Y_TOL} * RMS {rms:.3e}"
     return rep
 
 

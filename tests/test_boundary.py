@@ -20,7 +20,7 @@ HEADER = os.path.join(ROOT, "include", "moe.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -68,7 +68,7 @@ def test_max_rows_and_workspace(lib):
                                                             wl.n_routed * wl.capacity)
         assert r == want
         ws = _lib.moe_workspace_bytes(cfg, wl.T)
-        es = 2 if wl.dtype == "bf16" else 4
+        es = 2 if wl.dtype in ("bf16", "fp8") else 4
         # at least the routed intermediates and the fp32 routed outputs
         assert ws >= r * wl.ffn * es + r * wl.hidden * 4
         assert ws % 256 == 0 or ws > 0

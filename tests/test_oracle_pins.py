@@ -710,3 +710,16 @@ def test_fp8_layer_reduces_to_quantised_h_on_grid_inputs():
             h = rho(oracle.silu(x[t] @ w["w_gate"][e]) * (x[t] @ w["w_up"][e]))
             y[t] += ref["gates"][t, j] * (q_torch(h) @ w["w_down"][e])
     np.testing.assert_allclose(got["y"], y, rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_term_maxima_bound_the_output():
+    """M_y (the largest single down-product term of each output element) is
+    positive and bounds y by the term count: |y| <= (k + S) F M_y."""
+    T, d, E, k, S, F = 7, 32, 4, 2, 2, 16
+    w = _inputs(T, d, E, k, S, F, seed=9, bf16=True)
+    spec = _spec(d, E, k, S, F, bf16=True, fp8=True)
+    f = oracle.layer_forward(w["x"], w, spec, scales=True)
+    assert f["M_y"].shape == f["y"].shape and np.all(f["M_y"] > 0)
+    assert np.all(np.abs(f["y"]) <= (k + S) * F * f["M_y"] * (1 + 1e-12))
+    g = oracle.layer_forward(w["x"], w, spec)
+    np.testing.assert_array_equal(g["y"], f["y"])
