@@ -48,7 +48,11 @@ bool valid_config(const moe_config* c) {
 // are dense.
 bool supported_config(const moe_config* c) {
   if (c->rank != 0 && (c->rank != 64 || c->dtype != MOE_BF16)) return false;
-  if (c->dtype == MOE_FP8 && c->rank != 0) return false;
+  // fp8: dense experts; the rows entering the products (x over d, h over F,
+  // the shared h over S F) are quantised whole in registers, up to 4096 values
+  if (c->dtype == MOE_FP8 && (c->rank != 0 || c->hidden > 4096 ||
+                              (int64_t)c->n_shared * c->ffn > 4096 || c->ffn > 4096))
+    return false;
   return true;
 }
 

@@ -7,8 +7,8 @@
 // Scaling by a power of two is exact, so the only rounding is the hardware's
 // round-to-nearest-even onto the grid (v_cvt_pk_fp8_f32).
 //
-// quant_rows_kernel: one wave per row; the row's maximum magnitude by a wave
-//   reduction, then 8 codes per lane and pass.
+// quant_rows_kernel: one wave per row, the row held in registers; its maximum
+//   magnitude by a wave reduction, then 8 codes per 16-byte piece.
 // quant_cols_kernel: weights [K, N] -> codes [N, K] (k-contiguous, the order
 //   the MFMA operand is read in) and one scale per column.
 // gemm_fp8_kernel: both operands k-contiguous codes. 256 x 128 output tiles
@@ -303,6 +303,9 @@ gemm_fp8_kernel(GemmLaunch L) {
   }
 }
 
+// One row per wave; the row's 16-byte pieces stay in registers (NP per lane)
+// between the maximum and the conversion.
+template <int NP>
 __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* src, int64_t ld,
                                                          int64_t rows, int K,
                                                          const int32_t* n_valid, uint8_t* q,
@@ -314,30 +317,41 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* src, in
   const int np = K / 8;
   for (int64_t r = (int64_t)blockIdx.x * 4 + wave; r < nrows; r += (int64_t)gridDim.x * 4) {
     const u32x4* s4 = reinterpret_cast<const u32x4*>(src + r * ld);
-    float amax = 0.f;
-    for (int p = lane; p < np; p += 64) {
-      const u32x4 v = s4[p];
+    u32x4 v[NP];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        amax = fmaxf(amax, fabsf(__uint_as_float(v[i] << 16)));
-        amax = fmaxf(amax, fabsf(__uint_as_float(v[i] & 0xffff0000u)));
+    for (int i = 0; i < NP; ++i) {
+      const int p = lane + 64 * i;
+      v[i] = s4[min(p, np - 1)];
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      if (lane + 64 * i < np) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          amax = fmaxf(amax, fabsf(__uint_as_float(v[i][e] << 16)));
+          amax = fmaxf(amax, fabsf(__uint_as_float(v[i][e] & 0xffff0000u)));
+        }
       }
     }
     amax = wave_max(amax);
     const int sc = fp8_scale_exp(amax);
     u32x2* out = reinterpret_cast<u32x2*>(q + r * K);
-    for (int p = lane; p < np; p += 64) {
-      const u32x4 v = s4[p];
-      float f[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[2 * i] = ldexpf(__uint_as_float(v[i] << 16), -sc);
-        f[2 * i + 1] = ldexpf(__uint_as_float(v[i] & 0xffff0000u), -sc);
+    for (int i = 0; i < NP; ++i) {
+      const int p = lane + 64 * i;
+      if (p < np) {
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f[2 * e] = ldexpf(__uint_as_float(v[i][e] << 16), -sc);
+          f[2 * e + 1] = ldexpf(__uint_as_float(v[i][e] & 0xffff0000u), -sc);
+        }
+        u32x2 w;
+        w[0] = pack4_fp8(f[0], f[1], f[2], f[3]);
+        w[1] = pack4_fp8(f[4], f[5], f[6], f[7]);
+        out[p] = w;
       }
-      u32x2 w;
-      w[0] = pack4_fp8(f[0], f[1], f[2], f[3]);
-      w[1] = pack4_fp8(f[4], f[5], f[6], f[7]);
-      out[p] = w;
     }
     if (lane == 0) scale[r] = ldexpf(1.0f, sc);
   }
@@ -403,10 +417,19 @@ hipError_t launch_gemm_fp8(const GemmLaunch& L, int epilogue, hipStream_t s) {
 hipError_t launch_quant_rows(const uint16_t* src, int64_t ld, int64_t rows, int32_t K,
                              const int32_t* n_valid, uint8_t* q, float* scale, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  if (K % 8 || ld % 8 || K <= 0) return hipErrorInvalidValue;
-  const int64_t waves = rows < 8192 ? rows : 8192;
-  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, src,
-                     ld, rows, K, n_valid, q, scale);
+  // rows of up to 64 * 8 * 8 = 4096 values, kept in registers
+  if (K % 8 || ld % 8 || K <= 0 || K > 4096) return hipErrorInvalidValue;
+  const int64_t waves = rows < (1 << 20) ? rows : (1 << 20);
+  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  const int np = K / 8;
+  if (np <= 64)
+    hipLaunchKernelGGL((quant_rows_kernel<1>), grid, block, 0, s, src, ld, rows, K, n_valid, q, scale);
+  else if (np <= 128)
+    hipLaunchKernelGGL((quant_rows_kernel<2>), grid, block, 0, s, src, ld, rows, K, n_valid, q, scale);
+  else if (np <= 256)
+    hipLaunchKernelGGL((quant_rows_kernel<4>), grid, block, 0, s, src, ld, rows, K, n_valid, q, scale);
+  else
+    hipLaunchKernelGGL((quant_rows_kernel<8>), grid, block, 0, s, src, ld, rows, K, n_valid, q, scale);
   return hipGetLastError();
 }
 

@@ -86,7 +86,8 @@ hipError_t launch_gemm_big(const GemmLaunch& L, int epilogue, hipStream_t s);
 hipError_t launch_gemm_fp8(const GemmLaunch& L, int epilogue, hipStream_t s);
 // Quantise rows to E4M3: for row r < min(rows, *n_valid) (n_valid may be
 // null), s = the smallest power of two with amax(row) / s <= 448, codes
-// q[r * K + k] = RNE(src[r * ld + k] / s) and scale[r] = s. K multiple of 8.
+// q[r * K + k] = RNE(src[r * ld + k] / s) and scale[r] = s. K multiple of 8,
+// at most 4096.
 hipError_t launch_quant_rows(const uint16_t* src, int64_t ld, int64_t rows, int32_t K,
                              const int32_t* n_valid, uint8_t* q, float* scale, hipStream_t s);
 // Quantise the columns of W[g] ([K, N] bf16, g < G) to E4M3 codes stored
