@@ -27,6 +27,8 @@
 // The epilogue stages each wave's results through a private LDS slice and
 // writes whole 16-byte pieces of rows (fp32 rows, or bf16 h = SiLU(gate) * up).
 
+#include <type_traits>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -192,7 +194,12 @@ gemm_big_kernel(GemmLaunch L) {
   // MFMAs. A load whose issue stalls (the CU's load path is shared by eight
   // waves) then waits behind MFMAs already in flight instead of in front of
   // them.
-  auto step = [&](int st, int kt_next) {
+  // NI: how many of the wave's four 32-row blocks hold rows of the tile (the
+  // last tile of an expert is partial); the others skip their fragment reads
+  // and MFMAs, which frees the SIMD for the co-resident workgroup's wave. The
+  // loads and barriers are the same for every wave.
+  auto step = [&](int st, int kt_next, auto ni) {
+    constexpr int NI = decltype(ni)::value;
     const unsigned char* As = smem + st * kStageBytes;
     const unsigned char* Bs = As + kAStage * 2;
     const uint32_t Asn = smem_base + (kt_next % kStages) * kStageBytes;
@@ -203,27 +210,30 @@ gemm_big_kernel(GemmLaunch L) {
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NI; ++i)
         a[ks][i] = *reinterpret_cast<const bf16x8*>(As + a_off(128 * wm + 32 * i + l32, 2 * ks + lhi));
+      if (NI > 0) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int k = 16 * ks + bk_lane;
-        const int n = bcol[j];
-        const int o0 = b_off(k, n >> 3) + 2 * (n & 7);
-        const int o1 = b_off(k + 4, n >> 3) + 2 * (n & 7);
-        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) shortx4*)(Bs + o0));
-        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) shortx4*)(Bs + o1));
-        const shortx8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        b[ks][j] = __builtin_bit_cast(bf16x8, v);
+        for (int j = 0; j < 2; ++j) {
+          const int k = 16 * ks + bk_lane;
+          const int n = bcol[j];
+          const int o0 = b_off(k, n >> 3) + 2 * (n & 7);
+          const int o1 = b_off(k + 4, n >> 3) + 2 * (n & 7);
+          const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) shortx4*)(Bs + o0));
+          const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) shortx4*)(Bs + o1));
+          const shortx8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          b[ks][j] = __builtin_bit_cast(bf16x8, v);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int ks = q >> 3, i = (q >> 1) & 3, j = q & 1;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0);
+      if (i < NI)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0);
       if (do_issue && q < 6) {
         __builtin_amdgcn_sched_barrier(0);
         if (q < 4) dma16(a_src[q] + k0n, Asn + (4 * wave_u + q) * 1024);
@@ -235,16 +245,29 @@ gemm_big_kernel(GemmLaunch L) {
 
   constexpr int kWaitVm6 = 6 | (7 << 4) | (15 << 8);
   constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
-  issue(0);
-  if (nk > 1) issue(1);
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(kWaitVm6);   // step kt landed
-    else __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();   // stage kt published; stage (kt - 1) % 3 released
-    __builtin_amdgcn_sched_barrier(0);
-    step(kt % kStages, kt + 2);
-    __builtin_amdgcn_sched_barrier(0);
+  auto main_loop = [&](auto ni) {
+    issue(0);
+    if (nk > 1) issue(1);
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(kWaitVm6);   // step kt landed
+      else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();   // stage kt published; stage (kt - 1) % 3 released
+      __builtin_amdgcn_sched_barrier(0);
+      step(kt % kStages, kt + 2, ni);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  {
+    const int rows_here = tile.r_end - tile.r0 - 128 * wm;
+    const int nib = __builtin_amdgcn_readfirstlane(min(4, max(0, (rows_here + 31) / 32)));
+    switch (nib) {
+      case 4: main_loop(std::integral_constant<int, 4>()); break;
+      case 3: main_loop(std::integral_constant<int, 3>()); break;
+      case 2: main_loop(std::integral_constant<int, 2>()); break;
+      case 1: main_loop(std::integral_constant<int, 1>()); break;
+      default: main_loop(std::integral_constant<int, 0>()); break;
+    }
   }
 
   // ---- epilogue through a private 18 KiB LDS slice per wave
