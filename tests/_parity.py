@@ -12,7 +12,8 @@ key margin exceeds 1e-4 in the oracle):
     largest single term g h_f W_down[f, c] of that element's down products:
     both sides quantise h from their own bf16 h, and where those differ by one
     bf16 ulp the E4M3 code can differ by one step (at most 2^-3 of h), which
-    the bound allows twice at the largest term.
+    the bound allows twice at the largest term; and at most max(2, 10%) of the
+    checked tokens may have any element beyond the plain 1e-2 RMS bound.
 """
 from __future__ import annotations
 
@@ -141,7 +142,9 @@ def check_parity(wl, inp, g, tokens=None, *, check_y=True):
             frac = float(np.mean(beyond)) if len(toks) else 0.0
             rep.update(y_tol_ratio=ratio, tokens_beyond_rms_bound=frac)
             assert ratio <= 1.0, f"max |dy| / (1e-2 RMS + 2^-2 M_y) = {ratio:.3f}"
-            assert frac <= FP8_FLIP_TOKENS, f"{frac:.3f} of tokens beyond 1e-2 RMS"
+            # (at least two tokens allowed, so that tiny batches are not judged by share)
+            allowed = max(2, int(FP8_FLIP_TOKENS * len(toks)))
+            assert int(beyond.sum()) <= allowed, f"{frac:.3f} of tokens beyond 1e-2 RMS"
         else:
             assert err <= Y_TOL * rms, f"max|dy| {err:.3e} > {Y_TOL} * RMS {rms:.3e}"
     return rep

@@ -87,6 +87,17 @@ CASES = {
     "one_token": synth.QUARTZ.replace(T=1, hidden=128, ffn=64),
     "wide_ffn_k1": synth.Workload("wk", T=260, hidden=192, n_routed=8, top_k=1, n_shared=3,
                                   ffn=320, seed=6),
+    # edge cases: nearly every slot dropped; every expert selected with raw
+    # softmax gates; sigmoid without shared experts; widths that leave partial
+    # column tiles in every product; a handful of tokens
+    "capacity_one": synth.QUARTZ.replace(T=200, hidden=128, ffn=64,
+                                         capacity_factor="1/200"),
+    "all_experts_raw_softmax": synth.Workload("ak", T=150, hidden=128, n_routed=8, top_k=8,
+                                              n_shared=1, ffn=64, renorm=0, seed=7),
+    "sigmoid_no_shared": synth.SUTRA.replace(T=333, hidden=128, ffn=64, n_shared=0),
+    "odd_widths": synth.Workload("ow", T=257, hidden=192, n_routed=16, top_k=3, n_shared=3,
+                                 ffn=192, logit_offset_std=0.3, seed=11),
+    "three_tokens": synth.QUARTZ.replace(T=3, hidden=256, ffn=128, seed=12),
 }
 
 

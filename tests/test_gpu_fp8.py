@@ -55,6 +55,10 @@ SMALL = {
     "one_token": synth.QUARTZ.replace(T=1, hidden=128, ffn=64, dtype="fp8"),
     "three_shared": synth.Workload("s3", T=260, hidden=192, n_routed=16, top_k=3, n_shared=3,
                                    ffn=192, dtype="fp8", seed=6),
+    "capacity_one": synth.QUARTZ.replace(T=200, hidden=128, ffn=64, capacity_factor="1/200",
+                                         dtype="fp8"),
+    "decode_t2": synth.QUARTZ.replace(T=2, dtype="fp8", seed=5),
+    "decode_t4": synth.SUTRA.replace(T=4, dtype="fp8", seed=8),
 }
 
 
