@@ -54,12 +54,17 @@ __device__ __forceinline__ floatx4 mfma(const bf16x8& a, const bf16x8& b, const 
 }
 
 __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[kBM * kLd];        // A k-chunk
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2 * kR * kLd];     // U_gate|U_up chunk, [n][k]
-  __shared__ __attribute__((aligned(16))) bf16_t Zs[kBM * kLdZ];       // zg | zu
-  __shared__ __attribute__((aligned(16))) bf16_t Hs[kBM * kLd];        // 64-column chunk of h
-  __shared__ __attribute__((aligned(16))) bf16_t Bd[kR * kLd];         // U_down chunk, [n][k]
-  __shared__ __attribute__((aligned(16))) bf16_t Zd[kBM * kLd];        // zd
+  // zg | zu lives through stages 1-3; the other tiles share one region, as
+  // no two of the groups are live together: stage 1 (A chunk, U_gate|U_up
+  // chunk), stages 2-3 (h chunk, U_down chunk), stage 4 (zd). 44 KiB in all,
+  // so three workgroups fit on a CU.
+  __shared__ __attribute__((aligned(16))) bf16_t Zs[kBM * kLdZ];                 // zg | zu
+  __shared__ __attribute__((aligned(16))) bf16_t Sh[kBM * kLd + 2 * kR * kLd];   // shared region
+  bf16_t* const As = Sh;                 // [kBM][kLd]    stage 1
+  bf16_t* const Bs = Sh + kBM * kLd;     // [2 kR][kLd]   stage 1, [n][k]
+  bf16_t* const Hs = Sh;                 // [kBM][kLd]    stages 2-3
+  bf16_t* const Bd = Sh + kBM * kLd;     // [kR][kLd]     stages 2-3, [n][k]
+  bf16_t* const Zd = Sh;                 // [kBM][kLd]    stage 4
 
   const int tile = blockIdx.x;
   if (tile >= a.plan[0]) return;
@@ -100,20 +105,26 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc1[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < d; k0 += 64) {
-    u32x4 ar[2];
-    uint32_t br[2][8];
+  // the next K-step's A rows and U columns are requested before this step's
+  // MFMAs, so their latency overlaps the arithmetic
+  u32x4 ar[2];
+  uint32_t br[2][8];
+  auto load1 = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) ar[i] = *reinterpret_cast<const u32x4*>(a_src[i] + k0);
     load_b_pair(Ug + (int64_t)(k0 + 8 * bq) * kR + 2 * bp, kR, br[0]);
     load_b_pair(Uu + (int64_t)(k0 + 8 * bq) * kR + 2 * bp, kR, br[1]);
-    __syncthreads();
+  };
+  load1(0);
+  for (int k0 = 0; k0 < d; k0 += 64) {
+    __syncthreads();   // the previous step's tiles are consumed
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       *reinterpret_cast<u32x4*>(&As[(a_rb + 32 * i) * kLd + 8 * a_c]) = ar[i];
     store_b_pair(Bs, 2 * bp, bq, br[0]);
     store_b_pair(Bs, kR + 2 * bp, bq, br[1]);
     __syncthreads();
+    if (k0 + 64 < d) load1(k0 + 64);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       bf16x8 av[4], bv[2];
@@ -146,24 +157,32 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
   floatx4 accd[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) accd[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-  for (int f0 = 0; f0 < F; f0 += 64) {
-    // U_down rows f0..f0+63 (transposing load into registers early)
-    uint32_t bd[8];
+  // per 64 columns of F: U_down rows (transposing load) and the V_gate / V_up
+  // fragments, requested one chunk ahead
+  uint32_t bd[8];
+  bf16x8 bgv[2], buv[2];
+  auto load2 = [&](int f0) {
     load_b_pair(Ud + (int64_t)(f0 + 8 * bq) * kR + 2 * bp, kR, bd);
-    floatx4 accg[4], accu[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) accg[i] = accu[i] = floatx4{0.f, 0.f, 0.f, 0.f};
     const int n = f0 + 16 * wave + lr;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8 bg = *reinterpret_cast<const bf16x8*>(Vg + (int64_t)n * kR + 32 * kk + lk);
-      const bf16x8 bu = *reinterpret_cast<const bf16x8*>(Vu + (int64_t)n * kR + 32 * kk + lk);
+      bgv[kk] = *reinterpret_cast<const bf16x8*>(Vg + (int64_t)n * kR + 32 * kk + lk);
+      buv[kk] = *reinterpret_cast<const bf16x8*>(Vu + (int64_t)n * kR + 32 * kk + lk);
+    }
+  };
+  load2(0);
+  for (int f0 = 0; f0 < F; f0 += 64) {
+    floatx4 accg[4], accu[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) accg[i] = accu[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bf16x8 ag = *reinterpret_cast<const bf16x8*>(&Zs[(16 * i + lr) * kLdZ + 32 * kk + lk]);
         const bf16x8 au = *reinterpret_cast<const bf16x8*>(&Zs[(16 * i + lr) * kLdZ + kR + 32 * kk + lk]);
-        accg[i] = mfma(ag, bg, accg[i]);
-        accu[i] = mfma(au, bu, accu[i]);
+        accg[i] = mfma(ag, bgv[kk], accg[i]);
+        accu[i] = mfma(au, buv[kk], accu[i]);
       }
     }
 #pragma unroll
@@ -174,6 +193,7 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
             f32_to_bf16(silu_f32(accg[i][q]) * accu[i][q]);
     store_b_pair(Bd, 2 * bp, bq, bd);
     __syncthreads();
+    if (f0 + 64 < F) load2(f0 + 64);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&Bd[(16 * wave + lr) * kLd + 32 * kk + lk]);
@@ -198,20 +218,31 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
 
   // ---- stage 4: y = zd V_down^T, 64 output columns per pass
   float* Y = a.y;
+  // V_down fragments requested one 64-column pass ahead
+  bf16x8 bvd[2];
+  auto load4 = [&](int n0) {
+    const int n = n0 + 16 * wave + lr;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      bvd[kk] = *reinterpret_cast<const bf16x8*>(Vd + (int64_t)n * kR + 32 * kk + lk);
+  };
+  load4(0);
   for (int n0 = 0; n0 < d; n0 += 64) {
     floatx4 acc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const int n = n0 + 16 * wave + lr;
+    const bf16x8 b0 = bvd[0], b1 = bvd[1];
+    if (n0 + 64 < d) load4(n0 + 64);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(Vd + (int64_t)n * kR + 32 * kk + lk);
+      const bf16x8 bv = kk ? b1 : b0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Zd[(16 * i + lr) * kLd + 32 * kk + lk]);
         acc[i] = mfma(av, bv, acc[i]);
       }
     }
+    const int n = n0 + 16 * wave + lr;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
