@@ -300,16 +300,19 @@ def lowrank_swiglu(xrow, f, rho):
 
 
 class _Fp8Bank:
-    """float64 values of an expert bank quantised per output column (fp8)."""
+    """float64 values of an expert bank quantised to fp8, one scale per output
+    column of the product the matrix enters: reduced over `axis` (0 for
+    W[in, out], 1 for a factor V[out, r] entering z V^T)."""
 
-    def __init__(self, arr):
+    def __init__(self, arr, axis=0):
         self.arr = arr
+        self.axis = axis
         self.cache = {}
 
     def __getitem__(self, e):
         m = self.cache.get(e)
         if m is None:
-            m = fp8_quantize(np.asarray(self.arr[e], np.float64), axis=0)[0]
+            m = fp8_quantize(np.asarray(self.arr[e], np.float64), axis=self.axis)[0]
             self.cache[e] = m
         return m
 
@@ -335,11 +338,21 @@ class Experts:
         self.spec = spec
         self.rho = _rho(spec)
         if spec.fp8:
-            if spec.rank != 0 or not spec.bf16:
-                raise ValueError("fp8 experts: dense bf16 layers only")
-            self.gate = _Fp8Bank(weights["w_gate"])
-            self.up = _Fp8Bank(weights["w_up"])
-            self.down = _Fp8Bank(weights["w_down"])
+            if not spec.bf16:
+                raise ValueError("fp8 experts: bf16 layers only")
+            if spec.rank == 0:
+                self.gate = _Fp8Bank(weights["w_gate"])
+                self.up = _Fp8Bank(weights["w_up"])
+                self.down = _Fp8Bank(weights["w_down"])
+            else:
+                # low-rank factors stored in fp8: U[in, r] per column r, V[out, r]
+                # per row (its product z V^T sums over r); s stays bf16; the
+                # products and their rounding points are the bf16 ones
+                self.lr = {n: _Fp8Bank(weights[n], axis=0)
+                           for n in ("u_gate", "u_up", "u_down")}
+                self.lr.update({n: _Fp8Bank(weights[n], axis=1)
+                                for n in ("v_gate", "v_up", "v_down")})
+                self.lr.update({n: _Bank(weights[n]) for n in ("s_gate", "s_up", "s_down")})
             self.S = spec.n_shared
             if self.S > 0:
                 S, F, d = self.S, spec.ffn, spec.hidden
@@ -363,8 +376,12 @@ class Experts:
                        _Bank(weights["sh_down"])]
 
     def routed(self, xrow, e, with_max=False):
-        if self.spec.fp8:
+        if self.spec.fp8 and self.spec.rank == 0:
             return swiglu_fp8(xrow, self.gate[e], self.up[e], self.down[e], self.rho, with_max)
+        if self.spec.fp8:
+            f = {n: b[e] for n, b in self.lr.items()}
+            y = lowrank_swiglu(xrow, f, self.rho)
+            return (y, np.zeros_like(y)) if with_max else y
         if self.spec.rank == 0:
             return swiglu(xrow, self.gate[e], self.up[e], self.down[e], self.rho)
         f = {n: b[e] for n, b in self.lr.items()}

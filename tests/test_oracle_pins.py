@@ -723,3 +723,32 @@ def test_fp8_term_maxima_bound_the_output():
     assert np.all(np.abs(f["y"]) <= (k + S) * F * f["M_y"] * (1 + 1e-12))
     g = oracle.layer_forward(w["x"], w, spec)
     np.testing.assert_array_equal(g["y"], f["y"])
+
+
+def test_fp8_lowrank_factors_are_the_bf16_layer_on_quantised_factors():
+    """fp8 low-rank experts: the bf16 low-rank layer evaluated on factors
+    quantised by the stated rule (U per column, V per row), which equals the
+    scales folded where the kernel applies them: U's into s, V's onto the
+    product's output columns."""
+    T, d, E, k, S, F, r = 5, 64, 4, 2, 0, 64, 64
+    w = _inputs(T, d, E, k, S, F, seed=31, rank=r, bf16=True)
+    spec8 = _spec(d, E, k, S, F, rank=r, bf16=True, fp8=True)
+    got = oracle.layer_forward(w["x"], w, spec8)
+    wq = dict(w)
+    for n in ("u_gate", "u_up", "u_down"):
+        wq[n] = np.stack([oracle.fp8_quantize(np.asarray(w[n][e], np.float64), 0)[0]
+                          for e in range(E)])
+    for n in ("v_gate", "v_up", "v_down"):
+        wq[n] = np.stack([oracle.fp8_quantize(np.asarray(w[n][e], np.float64), 1)[0]
+                          for e in range(E)])
+    ref = oracle.layer_forward(w["x"], wq, _spec(d, E, k, S, F, rank=r, bf16=True))
+    np.testing.assert_array_equal(got["y"], ref["y"])
+    # folding: (x U_q 2^su) * s = (x U_q) * (s 2^su) exactly; V's scale per output
+    e = 1
+    u, su = oracle.fp8_quantize(np.asarray(w["u_gate"][e], np.float64), 0)
+    v, sv = oracle.fp8_quantize(np.asarray(w["v_gate"][e], np.float64), 1)
+    uq, vq = np.ldexp(u, -su[None, :]), np.ldexp(v, -sv[:, None])
+    assert np.all(np.abs(uq) <= 448) and np.all(np.abs(vq) <= 448)
+    xr = np.asarray(w["x"][0], np.float64)
+    np.testing.assert_array_equal((xr @ u) * w["s_gate"][e],
+                                  (xr @ uq) * (np.asarray(w["s_gate"][e], np.float64) * np.ldexp(1.0, su)))
