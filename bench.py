@@ -176,6 +176,17 @@ def time_backward(wl, cfg, x, w, steps, warmup, stream):
     return fwd_ms, ms, {n: float(np.mean(v)) for n, v in dur.items()}
 
 
+def lowrank_expert_bytes(wl, fp8):
+    """Bytes of one low-rank expert's parameters: six factors of (d + F) r
+    values in total ((2d + F) r for U, (2F + d) r for V), 3r bf16 s values and,
+    with fp8 factors, one fp32 scale per column of U and per row of V."""
+    d, F, r = wl.hidden, wl.ffn, wl.rank
+    n = 3 * (d + F) * r
+    if not fp8:
+        return 2 * (n + 3 * r)
+    return n + 2 * 3 * r + 4 * (3 * r + 2 * F + d)
+
+
 def time_fp8(wl, inp, x, steps, warmup, stream):
     """The same layer with fp8 (E4M3) expert weights: mean step time and the
     per-kernel durations from the library's events."""
@@ -378,8 +389,7 @@ def main():
         us = stage_us[dom]
         kept = out["kept"].cpu().numpy()
         used = int((kept > 0).sum())
-        wbytes = used * (2 * (wl.hidden * wl.rank + wl.ffn * wl.rank) +
-                         (wl.ffn * wl.rank + wl.rank * wl.hidden) + 3 * wl.rank) * 2
+        wbytes = used * lowrank_expert_bytes(wl, fp8=False)
         io = rows * wl.hidden * 2 + rows * wl.hidden * 4
         achieved = (wbytes + io) / (us * 1e-6) / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS,
@@ -446,6 +456,18 @@ def main():
         for n, f in gemm.items():
             bwd[n + "_tflops"] = f / (bst[n] * 1e-6) / 1e12
         result["backward"] = bwd
+    if wl.dtype == "bf16" and wl.rank > 0 and not args.no_fp8:
+        # low-rank experts with fp8 factors: the same HBM-bound kernel streams
+        # half the weight bytes
+        fms8, st8 = time_fp8(wl, inp, x, args.steps, args.warmup, stream)
+        us8 = st8["lowrank_experts"]
+        b8 = used * lowrank_expert_bytes(wl, fp8=True) + io
+        result["fp8"] = {
+            "ms_per_step": fms8, "tokens_per_s": wl.T / (fms8 * 1e-3), "stage_us_mean": st8,
+            "lowrank_experts_algorithmic_bytes": b8,
+            "lowrank_experts_gbs": b8 / (us8 * 1e-6) / 1e9,
+            "lowrank_experts_frac_of_hbm_peak": b8 / (us8 * 1e-6) / 1e9 / PEAK_HBM_GBS,
+        }
     if wl.dtype == "bf16" and wl.rank == 0 and not args.no_fp8:
         fms8, st8 = time_fp8(wl, inp, x, args.steps, args.warmup, stream)
         gu8 = alg["gate_up_flops"] + alg["shared_gate_up_flops"]

@@ -36,7 +36,8 @@ WEIGHT_FIELDS = ("w_router", "logit_bias", "select_bias", "w_gate", "w_up", "w_d
                  "u_gate", "s_gate", "v_gate", "u_up", "s_up", "v_up",
                  "u_down", "s_down", "v_down", "sh_gate", "sh_up", "sh_down",
                  "w_gate_scale", "w_up_scale", "w_down_scale", "sh_gate_scale", "sh_up_scale",
-                 "sh_down_scale")
+                 "sh_down_scale", "u_gate_scale", "u_up_scale", "u_down_scale", "v_gate_scale",
+                 "v_up_scale", "v_down_scale")
 OUTPUT_FIELDS = ("topk_idx", "topk_gate", "topk_margin", "counts", "kept", "offsets",
                  "sorted_token", "row_of_slot", "dropped", "n_dropped", "aux", "f", "P",
                  "y", "y_lowp", "saved_ab")

@@ -47,11 +47,11 @@ bool valid_config(const moe_config* c) {
 // Low-rank experts: rank 64 with bf16 (the fused kernel's shape); fp8 experts
 // are dense.
 bool supported_config(const moe_config* c) {
-  if (c->rank != 0 && (c->rank != 64 || c->dtype != MOE_BF16)) return false;
+  if (c->rank != 0 && (c->rank != 64 || c->dtype == MOE_F32)) return false;
   // fp8: dense experts; the rows entering the products (x over d, h over F,
   // the shared h over S F) are quantised whole in registers, up to 4096 values
-  if (c->dtype == MOE_FP8 && (c->rank != 0 || c->hidden > 4096 ||
-                              (int64_t)c->n_shared * c->ffn > 4096 || c->ffn > 4096))
+  if (c->dtype == MOE_FP8 && (c->hidden > 4096 || (int64_t)c->n_shared * c->ffn > 4096 ||
+                              c->ffn > 4096))
     return false;
   return true;
 }
@@ -117,13 +117,16 @@ Layout make_layout(const moe_config* c, int64_t T) {
   L.y_perm = take((size_t)L.R * d * 4);
   L.y_sh = take(S > 0 ? (size_t)T * d * 4 : 0);
   if (c->dtype == MOE_FP8) {
-    const int64_t xr = std::max<int64_t>(L.R, T);   // x rows (layer) or x_perm rows (stage)
+    // x rows (layer) or x_perm rows (stage); low-rank experts quantise no
+    // routed activations (only their factors are fp8)
+    const int64_t xr = c->rank > 0 ? 0 : std::max<int64_t>(L.R, T);
+    const int64_t hr = c->rank > 0 ? 0 : L.R;
     L.xq = take((size_t)xr * d);
     L.xs = take((size_t)xr * 4);
     L.xq_sh = take((size_t)T * d);
     L.xs_sh = take((size_t)T * 4);
-    L.hq = take((size_t)L.R * F);
-    L.hs = take((size_t)L.R * 4);
+    L.hq = take((size_t)hr * F);
+    L.hs = take((size_t)hr * 4);
     L.hq_sh = take((size_t)T * S * F);
     L.hs_sh = take((size_t)T * 4);
   }
@@ -199,7 +202,12 @@ bool permute_outputs_ok(const moe_outputs* o, int64_t T) {
 bool expert_weights_ok(const moe_config* c, const moe_weights* w, bool routed, bool shared) {
   if (!w) return false;
   if (c->dtype == MOE_FP8) {
-    if (routed && (!w->w_gate_scale || !w->w_up_scale || !w->w_down_scale)) return false;
+    if (routed && c->rank == 0 && (!w->w_gate_scale || !w->w_up_scale || !w->w_down_scale))
+      return false;
+    if (routed && c->rank > 0 &&
+        (!w->u_gate_scale || !w->u_up_scale || !w->u_down_scale || !w->v_gate_scale ||
+         !w->v_up_scale || !w->v_down_scale))
+      return false;
     if (shared && c->n_shared > 0 && (!w->sh_gate_scale || !w->sh_up_scale || !w->sh_down_scale))
       return false;
   }
@@ -500,11 +508,6 @@ void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool 
   void* h = at<void>(ws, L.h);
   void* h_sh = at<void>(ws, L.h_sh);
   const int32_t* plan = at<int32_t>(ws, L.plan);
-  if (fp8(c)) {
-    run_ffn_fp8(R, c, L, routed, shared, a_routed, a_rows, offsets, a_shared, w, y_routed,
-                y_shared, ws);
-    return;
-  }
 
   // decode-sized batches: the weight-streaming skinny kernel
   const bool skinny = bf && T <= kSkinnyMaxT;
@@ -536,10 +539,24 @@ void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool 
     lr.F = (int32_t)F;
     lr.E = c->n_routed;
     lr.max_tiles = (int32_t)L.max_tiles;
+    if (fp8(c)) {
+      lr.fp8 = 1;
+      lr.u_gate_scale = w->u_gate_scale;
+      lr.u_up_scale = w->u_up_scale;
+      lr.u_down_scale = w->u_down_scale;
+      lr.v_gate_scale = w->v_gate_scale;
+      lr.v_up_scale = w->v_up_scale;
+      lr.v_down_scale = w->v_down_scale;
+    }
     R.run("lowrank_experts", [&] { return launch_lowrank(lr, R.stream); });
   }
   if (c->rank > 0) routed = false;   // the dense launches below serve the shared experts
   if (!routed && !shared) return;
+  if (fp8(c)) {
+    run_ffn_fp8(R, c, L, routed, shared, a_routed, a_rows, offsets, a_shared, w, y_routed,
+                y_shared, ws);
+    return;
+  }
   // stage names: routed and shared launches are told apart when only one
   // group is present
   const bool both = routed && shared;
@@ -1220,7 +1237,7 @@ int moe_combine(const moe_config* c, int64_t T, const float* y_routed, const flo
 int moe_quantize_fp8(const moe_config* c, const moe_weights* src, moe_weights* dst,
                      void* stream) {
   if (!valid_config(c) || c->dtype != MOE_FP8) return MOE_EINVAL;
-  if (c->rank != 0) return MOE_EUNSUPPORTED;
+  if (!supported_config(c)) return MOE_EUNSUPPORTED;
   if (!src || !dst) return MOE_EINVAL;
   moe_config bc = *c;
   bc.dtype = MOE_BF16;
@@ -1234,9 +1251,27 @@ int moe_quantize_fp8(const moe_config* c, const moe_weights* src, moe_weights* d
                              static_cast<uint8_t*>(const_cast<void*>(out)),
                              const_cast<float*>(scale), s);
   };
-  hipError_t e = q(src->w_gate, E, d, F, dst->w_gate, dst->w_gate_scale);
-  if (e == hipSuccess) e = q(src->w_up, E, d, F, dst->w_up, dst->w_up_scale);
-  if (e == hipSuccess) e = q(src->w_down, E, F, d, dst->w_down, dst->w_down_scale);
+  hipError_t e = hipSuccess;
+  if (c->rank == 0) {
+    e = q(src->w_gate, E, d, F, dst->w_gate, dst->w_gate_scale);
+    if (e == hipSuccess) e = q(src->w_up, E, d, F, dst->w_up, dst->w_up_scale);
+    if (e == hipSuccess) e = q(src->w_down, E, F, d, dst->w_down, dst->w_down_scale);
+  } else {
+    const int64_t r = c->rank;
+    // U [in, r] per column r, written transposed [r, in]
+    e = q(src->u_gate, E, d, r, dst->u_gate, dst->u_gate_scale);
+    if (e == hipSuccess) e = q(src->u_up, E, d, r, dst->u_up, dst->u_up_scale);
+    if (e == hipSuccess) e = q(src->u_down, E, F, r, dst->u_down, dst->u_down_scale);
+    // V [out, r] per row: rows of r values
+    auto qr = [&](const void* v, int64_t rows, const void* out, const float* scale) {
+      return launch_quant_rows(static_cast<const uint16_t*>(v), r, rows, (int32_t)r, nullptr,
+                               static_cast<uint8_t*>(const_cast<void*>(out)),
+                               const_cast<float*>(scale), s);
+    };
+    if (e == hipSuccess) e = qr(src->v_gate, E * F, dst->v_gate, dst->v_gate_scale);
+    if (e == hipSuccess) e = qr(src->v_up, E * F, dst->v_up, dst->v_up_scale);
+    if (e == hipSuccess) e = qr(src->v_down, E * d, dst->v_down, dst->v_down_scale);
+  }
   if (S > 0) {
     if (e == hipSuccess) e = q(src->sh_gate, S, d, F, dst->sh_gate, dst->sh_gate_scale);
     if (e == hipSuccess) e = q(src->sh_up, S, d, F, dst->sh_up, dst->sh_up_scale);

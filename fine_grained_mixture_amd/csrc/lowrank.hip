@@ -10,6 +10,12 @@
 // with rho = round to bf16 and every product accumulated in fp32 by
 // v_mfma_f32_16x16x32_bf16.
 //
+// fp8 factors (the storage ladder's fp8 rung): the codes are widened to bf16
+// exactly on their way to the MFMA, U's power-of-two column scales are folded
+// into s and V's are applied to the product's output columns, so the products
+// and rounding points are the bf16 ones; U codes arrive transposed ([r, in],
+// k-contiguous), which needs no transposing loader.
+//
 // One workgroup per (expert, chunk of up to 64 rows), from the device tile
 // list. The rank-r intermediates and h never leave the CU: zg|zu and zd live in
 // LDS, and h is produced 64 columns at a time and immediately folded into the
@@ -49,10 +55,35 @@ __device__ __forceinline__ void store_b_pair(bf16_t* lds, int row, int kq, const
   *reinterpret_cast<u32x4*>(&lds[(row + 1) * kLd + 8 * kq]) = hi;
 }
 
+// Four E4M3 codes (byte i = value i) to four bf16 values, exactly: an E4M3
+// value has at most four significant bits.
+__device__ __forceinline__ u32x2 cvt4_fp8_bf16(uint32_t w) {
+  typedef float floatx2 __attribute__((ext_vector_type(2)));
+  const floatx2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const floatx2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  u32x2 r;
+  r[0] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xffff0000u);
+  r[1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xffff0000u);
+  return r;
+}
+__device__ __forceinline__ bf16x8 cvt8_fp8_bf16(u32x2 w) {
+  const u32x2 a = cvt4_fp8_bf16(w[0]), b = cvt4_fp8_bf16(w[1]);
+  const u32x4 v = {a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+// 16 codes to 16 bf16 values written as two 16-byte pieces.
+__device__ __forceinline__ void store16_fp8_bf16(bf16_t* dst, u32x4 w) {
+  const u32x2 a = cvt4_fp8_bf16(w[0]), b = cvt4_fp8_bf16(w[1]);
+  const u32x2 c = cvt4_fp8_bf16(w[2]), d = cvt4_fp8_bf16(w[3]);
+  *reinterpret_cast<u32x4*>(dst) = u32x4{a[0], a[1], b[0], b[1]};
+  *reinterpret_cast<u32x4*>(dst + 8) = u32x4{c[0], c[1], d[0], d[1]};
+}
+
 __device__ __forceinline__ floatx4 mfma(const bf16x8& a, const bf16x8& b, const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+template <bool Q8>
 __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
   // zg | zu lives through stages 1-3; the other tiles share one region, as
   // no two of the groups are live together: stage 1 (A chunk, U_gate|U_up
@@ -83,6 +114,13 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
   const bf16_t* Vu = static_cast<const bf16_t*>(a.v_up) + (int64_t)e * F * kR;
   const bf16_t* Ud = static_cast<const bf16_t*>(a.u_down) + (int64_t)e * F * kR;
   const bf16_t* Vd = static_cast<const bf16_t*>(a.v_down) + (int64_t)e * d * kR;
+  // fp8 factors: U codes [r][in] (k-contiguous rows), V codes [out][r]
+  const uint8_t* Ug8 = static_cast<const uint8_t*>(a.u_gate) + (int64_t)e * kR * d;
+  const uint8_t* Uu8 = static_cast<const uint8_t*>(a.u_up) + (int64_t)e * kR * d;
+  const uint8_t* Ud8 = static_cast<const uint8_t*>(a.u_down) + (int64_t)e * kR * F;
+  const uint8_t* Vg8 = static_cast<const uint8_t*>(a.v_gate) + (int64_t)e * F * kR;
+  const uint8_t* Vu8 = static_cast<const uint8_t*>(a.v_up) + (int64_t)e * F * kR;
+  const uint8_t* Vd8 = static_cast<const uint8_t*>(a.v_down) + (int64_t)e * d * kR;
   const bf16_t* sg = static_cast<const bf16_t*>(a.s_gate) + (int64_t)e * kR;
   const bf16_t* su = static_cast<const bf16_t*>(a.s_up) + (int64_t)e * kR;
   const bf16_t* sd = static_cast<const bf16_t*>(a.s_down) + (int64_t)e * kR;
@@ -109,11 +147,22 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
   // MFMAs, so their latency overlaps the arithmetic
   u32x4 ar[2];
   uint32_t br[2][8];
+  // fp8: B-tile row n = t / 2 (gate rows 0..63, up 64..127), 32 codes at
+  // k0 + 32 (t % 2)
+  u32x4 bq8[2];
+  const uint8_t* u8_src = ((tid >> 1) < kR ? Ug8 + (int64_t)(tid >> 1) * d
+                                           : Uu8 + (int64_t)((tid >> 1) - kR) * d) +
+                          32 * (tid & 1);
   auto load1 = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) ar[i] = *reinterpret_cast<const u32x4*>(a_src[i] + k0);
-    load_b_pair(Ug + (int64_t)(k0 + 8 * bq) * kR + 2 * bp, kR, br[0]);
-    load_b_pair(Uu + (int64_t)(k0 + 8 * bq) * kR + 2 * bp, kR, br[1]);
+    if (Q8) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) bq8[i] = *reinterpret_cast<const u32x4*>(u8_src + k0 + 16 * i);
+    } else {
+      load_b_pair(Ug + (int64_t)(k0 + 8 * bq) * kR + 2 * bp, kR, br[0]);
+      load_b_pair(Uu + (int64_t)(k0 + 8 * bq) * kR + 2 * bp, kR, br[1]);
+    }
   };
   load1(0);
   for (int k0 = 0; k0 < d; k0 += 64) {
@@ -121,8 +170,14 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       *reinterpret_cast<u32x4*>(&As[(a_rb + 32 * i) * kLd + 8 * a_c]) = ar[i];
-    store_b_pair(Bs, 2 * bp, bq, br[0]);
-    store_b_pair(Bs, kR + 2 * bp, bq, br[1]);
+    if (Q8) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        store16_fp8_bf16(&Bs[(tid >> 1) * kLd + 32 * (tid & 1) + 16 * i], bq8[i]);
+    } else {
+      store_b_pair(Bs, 2 * bp, bq, br[0]);
+      store_b_pair(Bs, kR + 2 * bp, bq, br[1]);
+    }
     __syncthreads();
     if (k0 + 64 < d) load1(k0 + 64);
 #pragma unroll
@@ -144,7 +199,10 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int col = 32 * wave + 16 * j + lr;
-    const float sc = col < kR ? bf16_to_f32(sg[col]) : bf16_to_f32(su[col - kR]);
+    float sc = col < kR ? bf16_to_f32(sg[col]) : bf16_to_f32(su[col - kR]);
+    if (Q8)   // U's column scale folded into s (a power of two: exact)
+      sc *= col < kR ? a.u_gate_scale[(int64_t)e * kR + col]
+                     : a.u_up_scale[(int64_t)e * kR + col - kR];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -160,14 +218,27 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
   // per 64 columns of F: U_down rows (transposing load) and the V_gate / V_up
   // fragments, requested one chunk ahead
   uint32_t bd[8];
+  u32x4 bd8;              // fp8: U_down codes, row t / 4, 16 codes at f0 + 16 (t % 4)
   bf16x8 bgv[2], buv[2];
+  float vgs = 1.f, vus = 1.f;   // fp8: V rows' scales of this lane's column
   auto load2 = [&](int f0) {
-    load_b_pair(Ud + (int64_t)(f0 + 8 * bq) * kR + 2 * bp, kR, bd);
     const int n = f0 + 16 * wave + lr;
+    if (Q8) {
+      bd8 = *reinterpret_cast<const u32x4*>(Ud8 + (int64_t)(tid >> 2) * F + f0 + 16 * (tid & 3));
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bgv[kk] = *reinterpret_cast<const bf16x8*>(Vg + (int64_t)n * kR + 32 * kk + lk);
-      buv[kk] = *reinterpret_cast<const bf16x8*>(Vu + (int64_t)n * kR + 32 * kk + lk);
+      for (int kk = 0; kk < 2; ++kk) {
+        bgv[kk] = cvt8_fp8_bf16(*reinterpret_cast<const u32x2*>(Vg8 + (int64_t)n * kR + 32 * kk + lk));
+        buv[kk] = cvt8_fp8_bf16(*reinterpret_cast<const u32x2*>(Vu8 + (int64_t)n * kR + 32 * kk + lk));
+      }
+      vgs = a.v_gate_scale[(int64_t)e * F + n];
+      vus = a.v_up_scale[(int64_t)e * F + n];
+    } else {
+      load_b_pair(Ud + (int64_t)(f0 + 8 * bq) * kR + 2 * bp, kR, bd);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bgv[kk] = *reinterpret_cast<const bf16x8*>(Vg + (int64_t)n * kR + 32 * kk + lk);
+        buv[kk] = *reinterpret_cast<const bf16x8*>(Vu + (int64_t)n * kR + 32 * kk + lk);
+      }
     }
   };
   load2(0);
@@ -190,8 +261,9 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         Hs[(16 * i + 4 * (lane >> 4) + q) * kLd + 16 * wave + lr] =
-            f32_to_bf16(silu_f32(accg[i][q]) * accu[i][q]);
-    store_b_pair(Bd, 2 * bp, bq, bd);
+            f32_to_bf16(silu_f32(accg[i][q] * vgs) * (accu[i][q] * vus));
+    if (Q8) store16_fp8_bf16(&Bd[(tid >> 2) * kLd + 16 * (tid & 3)], bd8);
+    else store_b_pair(Bd, 2 * bp, bq, bd);
     __syncthreads();
     if (f0 + 64 < F) load2(f0 + 64);
 #pragma unroll
@@ -207,7 +279,8 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
   }
   {
     const int col = 16 * wave + lr;
-    const float sc = bf16_to_f32(sd[col]);
+    float sc = bf16_to_f32(sd[col]);
+    if (Q8) sc *= a.u_down_scale[(int64_t)e * kR + col];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -220,11 +293,17 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
   float* Y = a.y;
   // V_down fragments requested one 64-column pass ahead
   bf16x8 bvd[2];
+  float vds = 1.f;
   auto load4 = [&](int n0) {
     const int n = n0 + 16 * wave + lr;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-      bvd[kk] = *reinterpret_cast<const bf16x8*>(Vd + (int64_t)n * kR + 32 * kk + lk);
+    for (int kk = 0; kk < 2; ++kk) {
+      if (Q8)
+        bvd[kk] = cvt8_fp8_bf16(*reinterpret_cast<const u32x2*>(Vd8 + (int64_t)n * kR + 32 * kk + lk));
+      else
+        bvd[kk] = *reinterpret_cast<const bf16x8*>(Vd + (int64_t)n * kR + 32 * kk + lk);
+    }
+    if (Q8) vds = a.v_down_scale[(int64_t)e * d + n];
   };
   load4(0);
   for (int n0 = 0; n0 < d; n0 += 64) {
@@ -232,6 +311,7 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
     const bf16x8 b0 = bvd[0], b1 = bvd[1];
+    const float ys = vds;
     if (n0 + 64 < d) load4(n0 + 64);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -248,7 +328,7 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int row = r0 + 16 * i + 4 * (lane >> 4) + q;
-        if (row < r_end) Y[(int64_t)row * d + n] = acc[i][q];
+        if (row < r_end) Y[(int64_t)row * d + n] = Q8 ? acc[i][q] * ys : acc[i][q];
       }
   }
 }
@@ -257,7 +337,10 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
 
 hipError_t launch_lowrank(const LowRankArgs& a, hipStream_t s) {
   if (a.max_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(lowrank_kernel, dim3((unsigned)a.max_tiles), dim3(256), 0, s, a);
+  if (a.fp8)
+    hipLaunchKernelGGL((lowrank_kernel<true>), dim3((unsigned)a.max_tiles), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((lowrank_kernel<false>), dim3((unsigned)a.max_tiles), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -194,11 +194,17 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
 // Fused low-rank (rank 64) SwiGLU experts, bf16. Rows of expert e are
 // [offsets[e], offsets[e+1]); A row of dispatched row r is a_rows[r] (or r).
+// fp8 factors (fp8 != 0): U codes stored transposed [E, r, in], V codes
+// [E, out, r] as in bf16, each with power-of-two scales: u_*_scale [E, r],
+// v_gate/up_scale [E, F], v_down_scale [E, d]; s stays bf16.
 struct LowRankArgs {
   const void* A;             // [*, d] bf16 token rows
   const int32_t* a_rows;     // [R_max] or null
   int64_t lda;
   const void *u_gate, *s_gate, *v_gate, *u_up, *s_up, *v_up, *u_down, *s_down, *v_down;
+  const float *u_gate_scale, *u_up_scale, *u_down_scale;
+  const float *v_gate_scale, *v_up_scale, *v_down_scale;
+  int32_t fp8;
   const int32_t* offsets;    // [E+1]
   const int32_t* plan;       // tile list with kLowRankBM rows per tile
   float* y;                  // [R_max, d]

@@ -77,9 +77,19 @@ def quantized_fp8(inputs: dict, cfg: MoeConfig, device="cuda") -> DeviceWeights:
     u8 = dict(dtype=torch.uint8, device=device)
     f32 = dict(dtype=torch.float32, device=device)
     t = {n: src.t[n] for n in ("w_router", "logit_bias", "select_bias") if n in src.t}
-    t.update(w_gate=torch.empty((E, F, d), **u8), w_up=torch.empty((E, F, d), **u8),
-             w_down=torch.empty((E, d, F), **u8), w_gate_scale=torch.empty((E, F), **f32),
-             w_up_scale=torch.empty((E, F), **f32), w_down_scale=torch.empty((E, d), **f32))
+    r = cfg.rank
+    if r == 0:
+        t.update(w_gate=torch.empty((E, F, d), **u8), w_up=torch.empty((E, F, d), **u8),
+                 w_down=torch.empty((E, d, F), **u8), w_gate_scale=torch.empty((E, F), **f32),
+                 w_up_scale=torch.empty((E, F), **f32), w_down_scale=torch.empty((E, d), **f32))
+    else:
+        t.update(u_gate=torch.empty((E, r, d), **u8), u_up=torch.empty((E, r, d), **u8),
+                 u_down=torch.empty((E, r, F), **u8), v_gate=torch.empty((E, F, r), **u8),
+                 v_up=torch.empty((E, F, r), **u8), v_down=torch.empty((E, d, r), **u8),
+                 u_gate_scale=torch.empty((E, r), **f32), u_up_scale=torch.empty((E, r), **f32),
+                 u_down_scale=torch.empty((E, r), **f32), v_gate_scale=torch.empty((E, F), **f32),
+                 v_up_scale=torch.empty((E, F), **f32), v_down_scale=torch.empty((E, d), **f32),
+                 s_gate=src.t["s_gate"], s_up=src.t["s_up"], s_down=src.t["s_down"])
     if S:
         t.update(sh_gate=torch.empty((S, F, d), **u8), sh_up=torch.empty((S, F, d), **u8),
                  sh_down=torch.empty((d, S * F), **u8), sh_gate_scale=torch.empty((S, F), **f32),

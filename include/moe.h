@@ -35,7 +35,7 @@
  *   - Calls that share a workspace on different streams race; calls on one
  *     stream are ordered.
  *   - Limits of this build: 1 <= k <= 15, k <= E <= 4096; d and F multiples of
- *     64; T*k < 2^31; rank is 0 or 64 with bf16 (low-rank float32 or fp8
+ *     64; T*k < 2^31; rank is 0 or 64 with bf16 or fp8 (low-rank float32
  *     experts are MOE_EUNSUPPORTED); sigmoid scoring requires renorm_topk == 1;
  *     MOE_FP8 runs in moe_layer_forward and moe_grouped_ffn, with d, F and
  *     S*F at most 4096.
@@ -115,6 +115,16 @@ typedef struct {
   const float *sh_gate_scale;  /* [S, F] */
   const float *sh_up_scale;    /* [S, F] */
   const float *sh_down_scale;  /* [d]    */
+  /* MOE_FP8 with rank r: the factor pointers above hold E4M3 codes, U stored
+     transposed (u_gate, u_up [E, r, d]; u_down [E, r, F]) and V as in bf16
+     (v_gate, v_up [E, F, r]; v_down [E, d, r]), with power-of-two scales per
+     column of U and per row of V; s_gate, s_up, s_down stay bf16. */
+  const float *u_gate_scale;   /* [E, r] */
+  const float *u_up_scale;     /* [E, r] */
+  const float *u_down_scale;   /* [E, r] */
+  const float *v_gate_scale;   /* [E, F] */
+  const float *v_up_scale;     /* [E, F] */
+  const float *v_down_scale;   /* [E, d] */
 } moe_weights;
 
 /* Device output buffers, caller-allocated. R_max = T*k (dropless) or
@@ -195,14 +205,18 @@ int moe_grouped_ffn(const moe_config *cfg, int64_t T, int32_t groups,
 int moe_combine(const moe_config *cfg, int64_t T, const float *y_routed,
                 const float *y_shared, moe_outputs *o, void *stream);
 
-/* fp8 expert weights from bf16 ones (cfg->dtype == MOE_FP8; rank 0). For every
-   expert matrix of src (bf16, the MOE_BF16 layouts) writes dst's codes and
-   scales (layouts in moe_weights): per output column o the scale is the smallest
-   power of two s with max_i |W[i, o]| / s <= 448, and each code is W[i, o] / s
-   rounded to the nearest E4M3 value, ties to even. The activations entering each
-   fp8 product (x rows over d, h rows over F -- for the shared experts one row of
-   S*F) are quantised the same way, per row, inside moe_layer_forward. dst's
-   arrays are caller-allocated device memory; src->w_router is not touched.   */
+/* fp8 expert weights from bf16 ones (cfg->dtype == MOE_FP8). For every expert
+   matrix of src (bf16, the MOE_BF16 layouts) writes dst's codes and scales
+   (layouts in moe_weights): per output column o of the product the matrix
+   enters, the scale is the smallest power of two s with max |W[., o]| / s <= 448,
+   and each code is W / s rounded to the nearest E4M3 value, ties to even.
+   Dense experts (rank 0) then run on the fp8 MFMA: the activations entering
+   each product (x rows over d, h rows over F -- for the shared experts one row
+   of S*F) are quantised the same way, per row, inside moe_layer_forward.
+   Low-rank experts (rank 64) store only their factors in fp8: U per column,
+   V per row (its product z V^T sums over r); the products stay bf16 and
+   dst->s_gate, s_up, s_down must point to the bf16 s vectors. dst's arrays
+   are caller-allocated device memory; src->w_router is not touched.          */
 int moe_quantize_fp8(const moe_config *cfg, const moe_weights *src, moe_weights *dst,
                      void *stream);
 

@@ -6,7 +6,8 @@ to even). The layer then meets the forward's acceptance: routing bit-exact
 after the near-tie override, gates and aux as for bf16, and
 max |y - y_oracle| <= 1e-2 RMS(y_oracle), the oracle quantising the same rows
 (x over d, h over F; the shared experts' h as one row of S F) with the same
-rule.
+rule. Low-rank experts keep only their factors in fp8 (products bf16), so
+the bound there is the bf16 one.
 """
 import numpy as np
 import pytest
@@ -45,6 +46,36 @@ def test_weight_quantization_matches_oracle():
             np.testing.assert_array_equal(got[g], ref.T, err_msg=name)
 
 
+def test_factor_quantization_matches_oracle():
+    """Low-rank experts: U codes (written transposed, [E, r, in]) with one scale
+    per column r, V codes [E, out, r] with one scale per row; s is left bf16."""
+    wl = synth.DORMOUSE.replace(T=8, hidden=256, ffn=192, n_routed=12, dtype="fp8", seed=23)
+    inp = synth.make_inputs(wl)
+    cfg = L.config_from_workload(wl)
+    w = L.DeviceWeights.from_numpy(inp, cfg)
+    torch.cuda.synchronize()
+    E, d, F, r = wl.n_routed, wl.hidden, wl.ffn, wl.rank
+    for name, n_in in (("u_gate", d), ("u_up", d), ("u_down", F)):
+        codes = w.t[name].reshape(E, r, n_in)
+        scale = w.t[name + "_scale"].reshape(E, r).cpu().numpy().astype(np.float64)
+        got = _decode(codes) * scale[:, :, None]            # [E, r, in]
+        for e in range(E):
+            ref, s = oracle.fp8_quantize(np.asarray(inp[name][e], np.float64), axis=0)
+            np.testing.assert_array_equal(scale[e], np.ldexp(1.0, s), err_msg=name)
+            np.testing.assert_array_equal(got[e], ref.T, err_msg=name)
+    for name, n_out in (("v_gate", F), ("v_up", F), ("v_down", d)):
+        codes = w.t[name].reshape(E, n_out, r)
+        scale = w.t[name + "_scale"].reshape(E, n_out).cpu().numpy().astype(np.float64)
+        got = _decode(codes) * scale[:, :, None]
+        for e in range(E):
+            ref, s = oracle.fp8_quantize(np.asarray(inp[name][e], np.float64), axis=1)
+            np.testing.assert_array_equal(scale[e], np.ldexp(1.0, s), err_msg=name)
+            np.testing.assert_array_equal(got[e], ref, err_msg=name)
+    for name in ("s_gate", "s_up", "s_down"):
+        np.testing.assert_array_equal(w.t[name].float().cpu().numpy(),
+                                      np.asarray(inp[name], np.float32), err_msg=name)
+
+
 SMALL = {
     "quartz_small": synth.QUARTZ.replace(T=517, hidden=256, ffn=128, dtype="fp8"),
     "moonfrost_small_capacity": synth.MOONFROST.replace(T=1000, hidden=256, ffn=128,
@@ -59,6 +90,10 @@ SMALL = {
                                          dtype="fp8"),
     "decode_t2": synth.QUARTZ.replace(T=2, dtype="fp8", seed=5),
     "decode_t4": synth.SUTRA.replace(T=4, dtype="fp8", seed=8),
+    "dormouse_small": synth.DORMOUSE.replace(T=600, hidden=256, ffn=128, dtype="fp8"),
+    "dormouse_small_shared": synth.DORMOUSE.replace(T=333, hidden=256, ffn=192, n_shared=2,
+                                                    renorm=1, dtype="fp8", seed=4),
+    "dormouse_decode": synth.DORMOUSE.replace(T=3, dtype="fp8", seed=9),
 }
 
 
@@ -79,6 +114,7 @@ def test_fp8_small_parity(name):
 FULL = {
     "quartz": synth.QUARTZ.replace(dtype="fp8"),
     "moonfrost": synth.MOONFROST.replace(dtype="fp8"),
+    "dormouse": synth.DORMOUSE.replace(dtype="fp8"),
 }
 
 
