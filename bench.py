@@ -176,6 +176,73 @@ def time_backward(wl, cfg, x, w, steps, warmup, stream):
     return fwd_ms, ms, {n: float(np.mean(v)) for n, v in dur.items()}
 
 
+def per_call_ms(step, n, flush=None):
+    """Each call timed alone between two events on the launch stream, after
+    `flush` when given: (p10, median, p90) in ms and, for timed steps, the
+    per-stage medians in us."""
+    import numpy as np
+    import torch
+
+    calls = []
+    for _ in range(n):
+        if flush is not None:
+            flush()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        calls.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in calls])
+    return [float(np.percentile(ms, q)) for q in (10, 50, 90)]
+
+
+def clock_and_power(step):
+    """Shader clock and socket power read by rocm-smi (a child process) while
+    the layer runs back to back; None where the tool is missing or says
+    nothing."""
+    import subprocess
+    import threading
+
+    import torch
+
+    got = {}
+
+    def sample():
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"],
+                               capture_output=True, text=True, timeout=20)
+            got["text"] = r.stdout
+        except Exception as ex:      # no tool, no permission, time-out
+            got["error"] = type(ex).__name__
+
+    th = threading.Thread(target=sample)
+    t0 = time.perf_counter()
+    th.start()
+    while th.is_alive() and time.perf_counter() - t0 < 25:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+    th.join()
+    res = {"sclk_mhz": None, "power_w": None, "source": "rocm-smi during back-to-back calls"}
+    try:
+        data = json.loads(got.get("text", ""))
+        card = next(iter(data.values()))
+        for key, val in card.items():
+            m = re.search(r"([0-9]+(?:\.[0-9]+)?)", str(val))
+            if not m:
+                continue
+            if ("sclk" in key.lower() and "level" not in key.lower()
+                    and res["sclk_mhz"] is None):
+                res["sclk_mhz"] = float(m.group(1))
+            elif "power" in key.lower() and res["power_w"] is None:
+                res["power_w"] = float(m.group(1))
+    except (ValueError, StopIteration, AttributeError):
+        res["error"] = got.get("error", "unparsed output")
+    return res
+
+
 def lowrank_expert_bytes(wl, fp8):
     """Bytes of one low-rank expert's parameters: six factors of (d + F) r
     values in total ((2d + F) r for U, (2F + d) r for V), 3r bf16 s values and,
@@ -359,6 +426,20 @@ def main():
     stage_us = {n: float(np.mean(v)) for n, v in dur.items()}
     stage_us_med = {n: float(np.median(v)) for n, v in dur.items()}
 
+    # distribution of single calls, warm and after evicting the caches (a
+    # 512 MiB write, twice the 256 MiB Infinity Cache, before each call)
+    warm_p = per_call_ms(step, args.steps)
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    fill = [0]
+
+    def flush():
+        fill[0] ^= 1
+        flush_buf.fill_(fill[0])
+
+    cold_p = per_call_ms(step, args.steps, flush)
+    del flush_buf
+    clk = clock_and_power(step)
+
     rows = int(out["offsets"][-1].item())
     alg = algorithmic(wl, rows)
     kernel_src = os.path.join(ROOT, "fine_grained_mixture_amd", "csrc", "gemm_big.hip")
@@ -425,6 +506,9 @@ def main():
         "expert_gemm_frac_of_peak": expert_tflops / PEAK_BF16_TFLOPS,
         "stage_us_mean": stage_us,
         "stage_us_median": stage_us_med,
+        "call_ms_p10_p50_p90": warm_p,
+        "cold_call_ms_p10_p50_p90": cold_p,
+        "clock": clk,
         "combine_gbs": alg["combine_bytes"] / (stage_us["combine"] * 1e-6) / 1e9,
         "layer_flops": alg["router_flops"] + alg["gate_up_flops"] + alg["down_flops"]
         + alg["shared_gate_up_flops"] + alg["shared_down_flops"],
