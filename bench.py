@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the layer backward")
     ap.add_argument("--no-fp8", action="store_true", help="skip timing the fp8-expert layer")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="do not sample the shader clock with rocm-smi (use under a profiler)")
     ap.add_argument("--cpu-tokens", type=int, default=1536,
                     help="tokens of the workload the CPU oracle processes")
     ap.add_argument("--tokens", type=int, default=0,
@@ -198,48 +200,75 @@ def per_call_ms(step, n, flush=None):
     return [float(np.percentile(ms, q)) for q in (10, 50, 90)]
 
 
-def clock_and_power(step):
-    """Shader clock and socket power read by rocm-smi (a child process) while
-    the layer runs back to back; None where the tool is missing or says
-    nothing."""
+def clock_sampler(path, seconds):
+    """Child process: append one `rocm-smi --showclocks --json` reading per
+    line (with its time) to `path` until `seconds` pass or the parent exits.
+    It is started before the parent touches the GPU and never uses it."""
     import subprocess
-    import threading
 
+    parent = os.getppid()
+    end = time.time() + seconds
+    with open(path, "w") as f:
+        while time.time() < end and os.getppid() == parent:
+            try:
+                r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                                   text=True, timeout=20)
+                f.write(json.dumps({"t": time.time(), "out": r.stdout}) + "\n")
+                f.flush()
+            except Exception:      # no tool or a time-out: nothing to record
+                return
+            time.sleep(0.1)
+
+
+def start_clock_sampler():
+    import subprocess
+    import tempfile
+
+    fd, path = tempfile.mkstemp(prefix="moe_clock_", suffix=".jsonl")
+    os.close(fd)
+    proc = subprocess.Popen([sys.executable, os.path.abspath(__file__), "--clock-sampler", path],
+                            stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+    return proc, path
+
+
+def clock_during(step, sampler, seconds=3.0):
+    """Median shader clock of the sampler's readings taken while the layer
+    runs back to back for `seconds`; None where there are none."""
+    import numpy as np
     import torch
 
-    got = {}
-
-    def sample():
-        try:
-            r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"],
-                               capture_output=True, text=True, timeout=20)
-            got["text"] = r.stdout
-        except Exception as ex:      # no tool, no permission, time-out
-            got["error"] = type(ex).__name__
-
-    th = threading.Thread(target=sample)
-    t0 = time.perf_counter()
-    th.start()
-    while th.is_alive() and time.perf_counter() - t0 < 25:
+    res = {"sclk_mhz": None, "samples": 0,
+           "source": "rocm-smi (a process started before the GPU was used) during back-to-back calls"}
+    if sampler is None:
+        return res
+    proc, path = sampler
+    t0 = time.time()
+    while time.time() - t0 < seconds:
         for _ in range(20):
             step()
         torch.cuda.synchronize()
-    th.join()
-    res = {"sclk_mhz": None, "power_w": None, "source": "rocm-smi during back-to-back calls"}
-    try:
-        data = json.loads(got.get("text", ""))
-        card = next(iter(data.values()))
-        for key, val in card.items():
-            m = re.search(r"([0-9]+(?:\.[0-9]+)?)", str(val))
-            if not m:
+    t1 = time.time()
+    proc.terminate()
+    proc.wait(timeout=30)
+    vals = []
+    with open(path) as f:
+        for line in f:
+            try:
+                rec = json.loads(line)
+                if not (t0 <= rec["t"] <= t1):
+                    continue
+                card = next(iter(json.loads(rec["out"]).values()))
+                for key, val in card.items():
+                    m = re.search(r"([0-9]+(?:\.[0-9]+)?)", str(val))
+                    if m and "sclk" in key.lower() and "level" not in key.lower():
+                        vals.append(float(m.group(1)))
+                        break
+            except (ValueError, KeyError, StopIteration, AttributeError):
                 continue
-            if ("sclk" in key.lower() and "level" not in key.lower()
-                    and res["sclk_mhz"] is None):
-                res["sclk_mhz"] = float(m.group(1))
-            elif "power" in key.lower() and res["power_w"] is None:
-                res["power_w"] = float(m.group(1))
-    except (ValueError, StopIteration, AttributeError):
-        res["error"] = got.get("error", "unparsed output")
+    os.unlink(path)
+    if vals:
+        res["sclk_mhz"] = float(np.median(vals))
+        res["samples"] = len(vals)
     return res
 
 
@@ -348,6 +377,9 @@ def cpu_baseline(wl, inp, n_tokens):
 
 
 def main():
+    if len(sys.argv) == 3 and sys.argv[1] == "--clock-sampler":
+        clock_sampler(sys.argv[2], 300)
+        return
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this MoE layer build has no multi-GPU path "
@@ -356,6 +388,8 @@ def main():
     if args.copy_mib > 0:
         copy_calibration(args.copy_mib)
         return
+    # started before anything here uses the GPU
+    sampler = None if args.no_clock else start_clock_sampler()
     import numpy as np
     import torch
 
@@ -438,7 +472,7 @@ def main():
 
     cold_p = per_call_ms(step, args.steps, flush)
     del flush_buf
-    clk = clock_and_power(step)
+    clk = clock_during(step, sampler)
 
     rows = int(out["offsets"][-1].item())
     alg = algorithmic(wl, rows)

@@ -26,20 +26,50 @@ namespace {
 // ---------------------------------------------------------------------------
 // top-k (many experts): one wave per token, the waves of a workgroup sharing
 // one tb-token block, tb / nwaves consecutive tokens per wave. Lane l owns
-// experts l, l + 64, ...; each lane keeps its best R (key, id) pairs packed so
-// that a larger integer is a larger key or, for equal keys, the lower id;
-// then R rounds of a wave-wide maximum pick the winners in descending key
-// order, the winning lane advancing its list. Everything per token is
-// branch-free apart from wave-uniform control flow: experts past E carry key
-// -inf. The next token's logit row is loaded while the current one is
-// reduced, and a token's outputs are stored after that load is issued
+// experts l, l + 64, ... and caches its best two (key, expert) pairs, in the
+// selection order (larger key first, then the lower expert). Each of the
+// k + 1 rounds takes the wave-wide maximum key; a single lane holding it wins
+// (found with a ballot), several lanes holding it (equal keys) fall back to
+// the lowest expert id among them. The winner moves its second pair up. A
+// lane that wins twice has no cached pair left: before the next round it
+// re-scans its experts ranked after the last one it gave away. Everything
+// per token is branch-free apart from wave-uniform control flow: experts past
+// E carry key -inf. The next token's logit row is loaded while the current
+// one is reduced, and a token's outputs are stored after that load is issued
 // (stores count in vmcnt, so earlier stores would hold up the wait for it).
 // ---------------------------------------------------------------------------
 // Threads per workgroup: as many waves as the per-lane registers allow
-// (EPL logits, scores and sums plus the R-entry candidate list).
+// (EPL logits, keys, scores and sums).
 template <int EPL, int R>
 constexpr int topk_threads() {
-  return (EPL <= 4 && R <= 8) ? 1024 : (EPL <= 16 ? 512 : 256);
+  return EPL <= 4 ? 1024 : (EPL <= 16 ? 512 : 256);
+}
+
+__device__ __forceinline__ int wave_min_i32(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// Best two of the lane's experts ranked after (lk, lm) in the selection
+// order: key < lk, or key == lk with a larger index m (a larger expert id).
+template <int EPL>
+__device__ __forceinline__ void lane_top2(const float (&key)[EPL], float lk, int lm, float& k1,
+                                          int& m1, float& k2, int& m2) {
+  k1 = -INFINITY;
+  k2 = -INFINITY;
+  m1 = 0;
+  m2 = 0;
+#pragma unroll
+  for (int m = 0; m < EPL; ++m) {
+    const bool elig = key[m] < lk || (key[m] == lk && m > lm);
+    const float v = elig ? key[m] : -INFINITY;
+    const bool c1 = v > k1, c2 = v > k2;
+    k2 = c1 ? k1 : (c2 ? v : k2);
+    m2 = c1 ? m1 : (c2 ? m : m2);
+    k1 = c1 ? v : k1;
+    m1 = c1 ? m : m1;
+  }
 }
 
 template <int EPL, int R, bool SIG>
@@ -49,7 +79,9 @@ __global__ void __launch_bounds__((topk_threads<EPL, R>())) topk_kernel(TopkArgs
   float* s_ps = reinterpret_cast<float*>(smem_raw) + a.E;        // [E]
 
   const int E = a.E, k = a.k;
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  // wave-uniform, so token indices and row descriptors live in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int blk = blockIdx.x;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     s_cnt[e] = 0;
@@ -71,11 +103,26 @@ __global__ void __launch_bounds__((topk_threads<EPL, R>())) topk_kernel(TopkArgs
   const int64_t t_begin = (int64_t)blk * a.tb + wave * per_wave;
   const int64_t t_end = min(a.T, t_begin + per_wave);
 
+  // a token's logit row through a buffer descriptor of exactly E floats:
+  // lanes past E read 0 from the hardware's range check, with one address
+  // register and immediate offsets for the whole row
   float nxt[EPL];
   auto load_row = [&](int64_t t) {
-    const float* row = a.logits + t * E;
+    // t is the same in every lane: say so, so that the descriptor is built
+    // in scalar registers (a per-lane one would need a waterfall loop)
+    // (readfirstlane returns a signed int: both halves go through uint32_t,
+    // so that the low word is never sign-extended into the high one)
+    const uint64_t base = reinterpret_cast<uint64_t>(a.logits + t * E);
+    const uint32_t hi = static_cast<uint32_t>(
+        __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(base >> 32))));
+    const uint32_t lo = static_cast<uint32_t>(
+        __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(base))));
+    const uint64_t ubase = (static_cast<uint64_t>(hi) << 32) | lo;
+    const __amdgpu_buffer_rsrc_t row = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(ubase), (short)0, E * 4, 0x00020000);
 #pragma unroll
-    for (int m = 0; m < EPL; ++m) nxt[m] = row[min(lane + 64 * m, E - 1)];
+    for (int m = 0; m < EPL; ++m)
+      nxt[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(row, (lane + 64 * m) * 4, 0, 0));
   };
   if (t_begin < t_end) load_row(t_begin);
   int64_t out_t = -1;
@@ -92,31 +139,27 @@ __global__ void __launch_bounds__((topk_threads<EPL, R>())) topk_kernel(TopkArgs
   };
 
   for (int64_t t = t_begin; t < t_end; ++t) {
-    // scores of this lane's experts (SIG: sigmoid(l), else the logit)
-    float sc[EPL];
-    uint64_t cand[R];
-#pragma unroll
-    for (int i = 0; i < R; ++i) cand[i] = 0;
+    // scores of this lane's experts (SIG: sigmoid(l), else the logit) and
+    // their selection keys
+    float sc[EPL], key[EPL];
 #pragma unroll
     for (int m = 0; m < EPL; ++m) {
       const bool ok = lane + 64 * m < E;
       const float l = nxt[m];
-      sc[m] = SIG ? 1.0f / (1.0f + __expf(-l)) : l;
-      const float key = ok ? (SIG ? sc[m] + sbias[m] : l) : -INFINITY;
-      // insert into the descending list
-      uint64_t c = pack_key_id(key, lane + 64 * m);
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const bool gt = c > cand[i];
-        const uint64_t hi = gt ? c : cand[i];
-        c = gt ? cand[i] : c;
-        cand[i] = hi;
-      }
+      if (SIG) sc[m] = 1.0f / (1.0f + __expf(-l));
+      key[m] = ok ? (SIG ? sc[m] + sbias[m] : l) : -INFINITY;
     }
     store_out();
     load_row(min(t + 1, t_end - 1));
 
-    // R rounds of the wave-wide maximum
+    float k1, k2;
+    int m1, m2;
+    lane_top2<EPL>(key, INFINITY, -1, k1, m1, k2, m2);
+    int cached = 2;          // pairs of the lane still exact
+    float lk = INFINITY;     // the lane's last pair given away
+    int lm = -1;
+
+    // k + 1 rounds of the wave-wide maximum
     int sel_id[R];
     float sel_key[R];
 #pragma unroll
@@ -124,32 +167,56 @@ __global__ void __launch_bounds__((topk_threads<EPL, R>())) topk_kernel(TopkArgs
       sel_id[r] = 0;
       sel_key[r] = 0.f;
       if (r < rounds) {
-        const uint64_t mx = wave_max_u64(cand[0]);
-        if (cand[0] == mx) {
-#pragma unroll
-          for (int i = 0; i < R - 1; ++i) cand[i] = cand[i + 1];
-          cand[R - 1] = 0;
+        const float mx = wave_max(k1);
+        const uint64_t tied = __ballot(k1 == mx);
+        int wl;
+        if (__popcll(tied) == 1) {
+          wl = __ffsll((unsigned long long)tied) - 1;
+        } else {   // equal keys in several lanes: the lowest expert id
+          const int cand = k1 == mx ? lane + 64 * m1 : INT_MAX;
+          wl = __builtin_amdgcn_readfirstlane(wave_min_i32(cand)) & 63;
         }
-        sel_id[r] = packed_id(mx);
-        sel_key[r] = packed_key(mx);
+        const int wm = __builtin_amdgcn_readlane(m1, wl);
+        sel_id[r] = wl + 64 * wm;
+        sel_key[r] = mx;
+        if (lane == wl) {
+          lk = k1;
+          lm = m1;
+          k1 = k2;
+          m1 = m2;
+          k2 = -INFINITY;
+          --cached;
+        }
+        if (r + 1 < rounds && __ballot(cached == 0) != 0) {
+          float n1, n2;
+          int j1, j2;
+          lane_top2<EPL>(key, lk, lm, n1, j1, n2, j2);
+          if (cached == 0) {
+            k1 = n1;
+            m1 = j1;
+            k2 = n2;
+            m2 = j2;
+            cached = 2;
+          }
+        }
       }
     }
 
-    // gates and routing probabilities
+  // gates and routing probabilities
     float my_gate = 0.f;
     int my_id = 0;
     if (!SIG) {
       const float mxl = sel_key[0];
       float se = 0.f;
 #pragma unroll
-      for (int m = 0; m < EPL; ++m) {
-        sc[m] = lane + 64 * m < E ? __expf(sc[m] - mxl) : 0.f;
-        se += sc[m];
+      for (int m = 0; m < EPL; ++m) {   // the key is the logit, -inf past E
+        key[m] = __expf(key[m] - mxl);
+        se += key[m];
       }
       se = wave_sum(se);
       const float inv = 1.0f / se;
 #pragma unroll
-      for (int m = 0; m < EPL; ++m) psum[m] += sc[m] * inv;
+      for (int m = 0; m < EPL; ++m) psum[m] += key[m] * inv;
       float ssel = 0.f;
 #pragma unroll
       for (int r = 0; r < R; ++r) {

@@ -9,6 +9,8 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
+
 from fine_grained_mixture_amd import layer as L
 from fine_grained_mixture_amd import synth
 from fine_grained_mixture_amd._lib import MOE_GROUPS_ROUTED, MOE_GROUPS_SHARED
@@ -58,6 +60,43 @@ EDGE = {
                                       n_shared=1, ffn=64, renorm=0),
     "tiny_f32_capacity": synth.TINY.replace(T=200, capacity_factor="1/2", seed=3),
 }
+
+
+# exact ties: a zero router leaves the logits equal to an integer-valued bias
+# (few distinct values, so most experts tie with others); the selection is
+# then the k largest biases with lower expert ids first among equals, in that
+# order, the same for every token. The many-expert cases take the top-k
+# kernel's tie path in every round.
+TIES = {
+    "many_softmax": synth.Workload("tie_m", T=150, hidden=128, n_routed=300, top_k=5,
+                                   n_shared=0, ffn=64, renorm=1),
+    "many_softmax_k15": synth.Workload("tie_k", T=70, hidden=128, n_routed=100, top_k=15,
+                                       n_shared=0, ffn=64, renorm=0),
+    "many_sigmoid": synth.Workload("tie_s", T=150, hidden=128, n_routed=200, top_k=6,
+                                   n_shared=0, ffn=64, score="sigmoid", renorm=1),
+    "few_softmax": synth.Workload("tie_f", T=150, hidden=128, n_routed=24, top_k=6,
+                                  n_shared=0, ffn=64, renorm=1),
+}
+
+
+@pytest.mark.parametrize("name", list(TIES))
+def test_exact_ties_take_lower_ids(name):
+    wl = TIES[name]
+    print(f"\n[case] ties {wl}", flush=True)
+    inp = synth.make_inputs(wl)
+    inp["w_router"] = np.zeros_like(inp["w_router"])
+    bias = np.random.default_rng(17).integers(-2, 3, size=wl.n_routed).astype(np.float32)
+    if wl.score == "sigmoid":
+        inp["select_bias"] = bias
+    else:
+        inp["logit_bias"] = bias
+    g = P.run_gpu(wl, inp)
+    order = np.argsort(-bias, kind="stable")[:wl.top_k]
+    np.testing.assert_array_equal(g["topk_idx"], np.broadcast_to(order, (wl.T, wl.top_k)))
+    r0 = oracle.route(inp["x"], inp["w_router"], P.spec_of(wl), inp.get("logit_bias"),
+                      inp.get("select_bias"))
+    np.testing.assert_array_equal(g["topk_idx"], r0["idx"])
+    np.testing.assert_allclose(g["topk_gate"], r0["gates"], rtol=0, atol=1e-6)
 
 
 # decode-sized batches (T <= 4 take the weight-streaming skinny expert kernel;
