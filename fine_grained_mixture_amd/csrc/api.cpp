@@ -225,8 +225,57 @@ bool expert_weights_ok(const moe_config* c, const moe_weights* w, bool routed, b
 }
 
 // ---- stage bodies (no validation) ------------------------------------------
+ScanArgs scan_args(const moe_config* c, const Layout& L, moe_outputs* o, void* ws,
+                   bool with_plan) {
+  ScanArgs s{};
+  s.blk_counts = at<int32_t>(ws, L.blk_counts);
+  s.blk_psum = at<float>(ws, L.blk_psum);
+  s.blk_base = at<int32_t>(ws, L.blk_base);
+  s.counts = o->counts;
+  s.kept = o->kept;
+  s.offsets = o->offsets;
+  s.n_dropped = o->n_dropped;
+  s.aux = o->aux;
+  s.f = o->f;
+  s.P = o->P;
+  s.psum_tot = at<float>(ws, L.psum_tot);
+  s.plan = with_plan ? at<int32_t>(ws, L.plan) : nullptr;
+  s.plan_bm = plan_bm(c);
+  s.nblk = (int32_t)L.nblk;
+  s.E = c->n_routed;
+  s.k = c->top_k;
+  s.capacity = c->capacity;
+  s.T = L.T;
+  s.aux_coef = c->aux_coef;
+  return s;
+}
+
+RankArgs rank_args(const moe_config* c, const Layout& L, moe_outputs* o, void* ws) {
+  RankArgs r{};
+  r.topk_idx = o->topk_idx;
+  r.blk_base = at<int32_t>(ws, L.blk_base);
+  r.offsets = o->offsets;
+  r.row_of_slot = o->row_of_slot;
+  r.sorted_token = o->sorted_token;
+  r.dropped = o->dropped;
+  r.T = L.T;
+  r.E = c->n_routed;
+  r.k = c->top_k;
+  r.capacity = c->capacity;
+  r.nblk = (int32_t)L.nblk;
+  r.tb = L.tb;
+  return r;
+}
+
+// The layer call ranks in the scan's launch when the fused router made few
+// blocks of few experts.
+bool scan_rank_fused(const moe_config* c, const Layout& L) {
+  return fused_router(c) && L.T > 0 && L.nblk <= 256;
+}
+
 void run_route(Runner& R, const moe_config* c, const Layout& L, const void* x,
-               const moe_weights* w, moe_outputs* o, void* ws, bool with_plan) {
+               const moe_weights* w, moe_outputs* o, void* ws, bool with_plan,
+               bool scan = true) {
   const int64_t T = L.T;
   const int E = c->n_routed;
   float* logits = at<float>(ws, L.logits);
@@ -300,45 +349,21 @@ void run_route(Runner& R, const moe_config* c, const Layout& L, const void* x,
     t.tb = L.tb;
     R.run("topk", [&] { return launch_topk(t, R.stream); });
   }
-  ScanArgs s{};
-  s.blk_counts = at<int32_t>(ws, L.blk_counts);
-  s.blk_psum = at<float>(ws, L.blk_psum);
-  s.blk_base = at<int32_t>(ws, L.blk_base);
-  s.counts = o->counts;
-  s.kept = o->kept;
-  s.offsets = o->offsets;
-  s.n_dropped = o->n_dropped;
-  s.aux = o->aux;
-  s.f = o->f;
-  s.P = o->P;
-  s.psum_tot = at<float>(ws, L.psum_tot);
-  s.plan = with_plan ? at<int32_t>(ws, L.plan) : nullptr;
-  s.plan_bm = plan_bm(c);
-  s.nblk = (int32_t)L.nblk;
-  s.E = E;
-  s.k = c->top_k;
-  s.capacity = c->capacity;
-  s.T = T;
-  s.aux_coef = c->aux_coef;
+  if (!scan) return;
+  const ScanArgs s = scan_args(c, L, o, ws, with_plan);
   R.run("scan", [&] { return launch_scan(s, R.stream); });
 }
 
 void run_rank(Runner& R, const moe_config* c, const Layout& L, moe_outputs* o, void* ws) {
   if (L.T == 0) return;
-  RankArgs r{};
-  r.topk_idx = o->topk_idx;
-  r.blk_base = at<int32_t>(ws, L.blk_base);
-  r.offsets = o->offsets;
-  r.row_of_slot = o->row_of_slot;
-  r.sorted_token = o->sorted_token;
-  r.dropped = o->dropped;
-  r.T = L.T;
-  r.E = c->n_routed;
-  r.k = c->top_k;
-  r.capacity = c->capacity;
-  r.nblk = (int32_t)L.nblk;
-  r.tb = L.tb;
+  const RankArgs r = rank_args(c, L, o, ws);
   R.run("rank", [&] { return launch_rank(r, R.stream); });
+}
+
+void run_scan_rank(Runner& R, const moe_config* c, const Layout& L, moe_outputs* o, void* ws) {
+  const ScanArgs s = scan_args(c, L, o, ws, true);
+  const RankArgs r = rank_args(c, L, o, ws);
+  R.run("scan_rank", [&] { return launch_scan_rank(s, r, R.stream); });
 }
 
 
@@ -695,8 +720,13 @@ int layer_forward(const moe_config* c, int64_t T, const void* x, const moe_weigh
   Runner R{static_cast<hipStream_t>(stream), &tl};
   float* y_perm = at<float>(ws, L.y_perm);
   float* y_sh = c->n_shared > 0 ? at<float>(ws, L.y_sh) : nullptr;
-  run_route(R, c, L, x, w, o, ws, true);
-  run_rank(R, c, L, o, ws);
+  if (scan_rank_fused(c, L)) {
+    run_route(R, c, L, x, w, o, ws, true, false);
+    run_scan_rank(R, c, L, o, ws);
+  } else {
+    run_route(R, c, L, x, w, o, ws, true);
+    run_rank(R, c, L, o, ws);
+  }
   float* saved_ab = c->dtype == MOE_BF16 && c->rank == 0 ? o->saved_ab : nullptr;
   run_ffn(R, c, L, true, true, x, o->sorted_token, o->offsets, x, w, y_perm, y_sh, ws, saved_ab);
   run_combine(R, c, T, y_perm, y_sh, o);

@@ -174,6 +174,8 @@ struct RankArgs {
   int32_t tb;                // tokens per block, as for the top-k tables
 };
 hipError_t launch_rank(const RankArgs& a, hipStream_t s);
+// scan and rank in one launch: E <= 64, nblk <= 256, the same blocks for both.
+hipError_t launch_scan_rank(const ScanArgs& a, const RankArgs& r, hipStream_t s);
 
 // x_perm[r] = x[sorted_token[r]] for r < offsets[E]; row_bytes multiple of 16.
 hipError_t launch_gather(const void* x, const int32_t* sorted_token, const int32_t* offsets,

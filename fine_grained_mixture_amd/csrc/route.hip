@@ -486,6 +486,70 @@ __global__ void __launch_bounds__(1024) scan_kernel(ScanArgs a) {
   }
 }
 
+// One wave, lane e = expert e (E <= 64), given expert e's pre-drop slot count
+// c and probability sum P: capacity, counts, kept, offsets, drops, the aux
+// statistic and the tile list of the routed grouped GEMM. Returns expert e's
+// first row.
+__device__ int scan_outputs(const ScanArgs& a, int c, float P) {
+  const int E = a.E;
+  const int e = lane_id();
+  const bool ve = e < E;
+  const int kp = ve ? (a.capacity > 0 ? min(c, a.capacity) : c) : 0;
+  int incl = kp;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(incl, o, 64);
+    if (e >= o) incl += n;
+  }
+  const int excl = incl - kp;
+  const int total_kept = __shfl(incl, 63, 64);
+  int drop = ve ? c - kp : 0;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) drop += __shfl_xor(drop, m, 64);
+  if (ve) {
+    a.counts[e] = c;
+    a.kept[e] = kp;
+    a.offsets[e] = excl;
+  }
+  if (e == 0) {
+    a.offsets[E] = total_kept;
+    a.n_dropped[0] = drop;
+  }
+
+  // aux statistic: f_e = counts_e / (T k), P_e = psum_e / T
+  const double fe = ve && a.T > 0 ? (double)c / ((double)a.T * a.k) : 0.0;
+  const double Pe = ve && a.T > 0 ? (double)P / (double)a.T : 0.0;
+  if (ve && a.f) a.f[e] = (float)fe;
+  if (ve && a.P) a.P[e] = (float)Pe;
+  double prod = fe * Pe;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) prod += __shfl_xor(prod, m, 64);
+  if (e == 0) {
+    const double raw = (double)E * prod;
+    a.aux[0] = (float)raw;
+    a.aux[1] = (float)(a.aux_coef * raw);
+  }
+
+  // tile list of the routed grouped GEMM, (expert, first row) in expert order
+  if (a.plan) {
+    const int nt = (kp + a.plan_bm - 1) / a.plan_bm;
+    int ti = nt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int n = __shfl_up(ti, o, 64);
+      if (e >= o) ti += n;
+    }
+    const int total = __shfl(ti, 63, 64);
+    int tp = ti - nt;
+    for (int r = 0; r < kp; r += a.plan_bm, ++tp) {
+      a.plan[1 + 2 * tp] = e;
+      a.plan[2 + 2 * tp] = excl + r;
+    }
+    if (e == 0) a.plan[0] = total;
+  }
+  return excl;
+}
+
 // Few experts (E <= 64): the blocks are split into 16 contiguous parts, one
 // wave each, lane e summing expert e over its part; after one workgroup
 // barrier every wave writes the block prefix of its part and wave 0 alone
@@ -551,7 +615,7 @@ __global__ void __launch_bounds__(1024) scan_small_kernel(ScanArgs a) {
   }
   if (part != 0) return;
 
-  // 3) wave 0: totals, capacity, offsets, drops
+  // 3) wave 0: totals and probability sums, then the per-expert outputs
   int c = 0;
   float P = 0.f;
   if (ve) {
@@ -560,100 +624,51 @@ __global__ void __launch_bounds__(1024) scan_small_kernel(ScanArgs a) {
       P += s_p[q][e];
     }
   }
-  const int kp = ve ? (a.capacity > 0 ? min(c, a.capacity) : c) : 0;
-  int incl = kp;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(incl, o, 64);
-    if (e >= o) incl += n;
-  }
-  const int excl = incl - kp;
-  const int total_kept = __shfl(incl, 63, 64);
-  int drop = c - kp;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) drop += __shfl_xor(drop, m, 64);
-  if (ve) {
-    a.counts[e] = c;
-    a.kept[e] = kp;
-    a.offsets[e] = excl;
-  }
-  if (e == 0) {
-    a.offsets[E] = total_kept;
-    a.n_dropped[0] = drop;
-  }
-
-  // 4) aux statistic: f_e = counts_e / (T k), P_e = psum_e / T
-  const double fe = ve && a.T > 0 ? (double)c / ((double)a.T * a.k) : 0.0;
-  const double Pe = ve && a.T > 0 ? (double)P / (double)a.T : 0.0;
-  if (ve && a.f) a.f[e] = (float)fe;
-  if (ve && a.P) a.P[e] = (float)Pe;
-  double prod = fe * Pe;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) prod += __shfl_xor(prod, m, 64);
-  if (e == 0) {
-    const double raw = (double)E * prod;
-    a.aux[0] = (float)raw;
-    a.aux[1] = (float)(a.aux_coef * raw);
-  }
-
-  // 5) tile list of the routed grouped GEMM, (expert, first row) in expert order
-  if (a.plan) {
-    const int nt = (kp + a.plan_bm - 1) / a.plan_bm;
-    int ti = nt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int n = __shfl_up(ti, o, 64);
-      if (e >= o) ti += n;
-    }
-    const int total = __shfl(ti, 63, 64);
-    int tp = ti - nt;
-    for (int r = 0; r < kp; r += a.plan_bm, ++tp) {
-      a.plan[1 + 2 * tp] = e;
-      a.plan[2 + 2 * tp] = excl + r;
-    }
-    if (e == 0) a.plan[0] = total;
-  }
+  scan_outputs(a, c, P);
 }
 
 // ---------------------------------------------------------------------------
-// rank: one wave per 64-token block, 4 blocks per workgroup. Slots are visited
-// in token order (t, then j) 64 at a time; lanes holding the same expert are
-// found with ballots over the id bits, and each lane's position is the
-// expert's running count plus the number of lower lanes with that expert.
+// rank: one wave per block of tb tokens. Slots are visited in token order (t,
+// then j) 64 at a time; lanes holding the same expert are found with ballots
+// over the id bits, and each lane's position is the expert's running count
+// plus the number of lower lanes with that expert.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) rank_kernel(RankArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  constexpr int kMaxChunks = 15;   // tb * k / 64 with tb = 64, k <= 15
-  const int E = a.E, k = a.k;
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  int* cnt = reinterpret_cast<int*>(smem_raw) + wave * 2 * E;
-  int* offs = cnt + E;
-  const int b = blockIdx.x * 4 + wave;
-  if (b >= a.nblk) return;
-  int nbits = 0;
-  while ((1 << nbits) < E) ++nbits;
+constexpr int kMaxChunks = 15;   // tb * k / 64 slots of a block, tb * k <= 960
 
-  const int64_t s_begin = (int64_t)b * a.tb * k;
-  const int64_t s_end = min(a.T, (int64_t)(b + 1) * a.tb) * k;
-  // every expert id of the block and its base counts, requested at once
+struct BlockIds {
   int ids[kMaxChunks];
+};
+
+// Every expert id of block b, requested at once.
+__device__ __forceinline__ void load_block_ids(const RankArgs& a, int b, BlockIds& B) {
+  const int lane = lane_id();
+  const int64_t s_begin = (int64_t)b * a.tb * a.k;
+  const int64_t s_end = min(a.T, (int64_t)(b + 1) * a.tb) * a.k;
 #pragma unroll
   for (int c = 0; c < kMaxChunks; ++c) {
     const int64_t s = s_begin + 64 * c + lane;
-    ids[c] = s < s_end ? a.topk_idx[s] : -1;
+    B.ids[c] = s < s_end ? a.topk_idx[s] : -1;
   }
-  for (int e = lane; e < E; e += 64) {
-    cnt[e] = a.blk_base[(int64_t)b * E + e];
-    offs[e] = a.offsets[e];
-  }
-  __builtin_amdgcn_wave_barrier();
+}
+
+// Ranks block b. cnt[e] (this wave's own LDS row) starts as the slots of
+// expert e in earlier blocks and is advanced; offs[e] is the expert's first
+// row.
+__device__ __forceinline__ void rank_block(const RankArgs& a, int b, const BlockIds& B, int* cnt,
+                                           const int* offs) {
+  const int E = a.E, k = a.k;
+  const int lane = lane_id();
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const int64_t s_begin = (int64_t)b * a.tb * k;
+  const int64_t s_end = min(a.T, (int64_t)(b + 1) * a.tb) * k;
   const uint64_t lt = lanemask_lt();
 #pragma unroll
   for (int c = 0; c < kMaxChunks; ++c) {
     const int64_t s = s_begin + 64 * c + lane;
     if (s_begin + 64 * c >= s_end) break;
     const bool valid = s < s_end;
-    const int e = valid ? ids[c] : 0;
+    const int e = valid ? B.ids[c] : 0;
     uint64_t match = __ballot(valid);
     for (int bit = 0; bit < nbits; ++bit) {
       const bool on = (e >> bit) & 1;
@@ -675,6 +690,115 @@ __global__ void __launch_bounds__(256) rank_kernel(RankArgs a) {
       if (a.dropped) a.dropped[s] = keep ? 0 : 1;
     }
   }
+}
+
+// Four blocks per workgroup; each wave copies its block's base counts and the
+// expert offsets into its own LDS rows.
+__global__ void __launch_bounds__(256) rank_kernel(RankArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  const int E = a.E;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  int* cnt = reinterpret_cast<int*>(smem_raw) + wave * 2 * E;
+  int* offs = cnt + E;
+  const int b = blockIdx.x * 4 + wave;
+  if (b >= a.nblk) return;
+  BlockIds B;
+  load_block_ids(a, b, B);
+  for (int e = lane; e < E; e += 64) {
+    cnt[e] = a.blk_base[(int64_t)b * E + e];
+    offs[e] = a.offsets[e];
+  }
+  __builtin_amdgcn_wave_barrier();
+  rank_block(a, b, B, cnt, offs);
+}
+
+// ---------------------------------------------------------------------------
+// scan and rank in one launch, for the layer call with few experts (E <= 64)
+// and few blocks (nblk <= kScanParts * kScanReg): every workgroup derives the
+// per-expert totals and its blocks' prefixes from the block tables itself,
+// 16 waves summing one part of the blocks each as scan_small_kernel does
+// (nblk * E * 4 bytes read from L2 per workgroup, less than the cost of a
+// second launch and its wait); workgroup 0 also writes the per-expert
+// outputs, the aux statistic and the tile list; then wave w of workgroup g
+// ranks block 16 g + w from the bases and offsets kept in LDS.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(1024) scan_rank_small_kernel(ScanArgs a, RankArgs r) {
+  __shared__ int s_c[kScanParts][64];
+  __shared__ float s_p[kScanParts][64];
+  __shared__ int s_base[kScanParts][64];   // the bases of blocks g0 .. g0 + 15
+  __shared__ int s_off[64];
+  const int E = a.E, nblk = a.nblk;
+  const int e = lane_id(), part = threadIdx.x >> 6;
+  const bool ve = e < E;
+  const bool lead = blockIdx.x == 0;
+  const int g0 = kScanParts * blockIdx.x;
+  const int rb = g0 + part;   // the block this wave ranks
+  BlockIds B;
+  if (rb < nblk) load_block_ids(r, rb, B);
+
+  // 1) this part's totals, blocks in order (at most kScanReg of them)
+  const int b0 = (int)((int64_t)part * nblk / kScanParts);
+  const int b1 = (int)((int64_t)(part + 1) * nblk / kScanParts);
+  int creg[kScanReg];
+#pragma unroll
+  for (int i = 0; i < kScanReg; ++i)
+    creg[i] = ve && b0 + i < b1 ? a.blk_counts[(int64_t)(b0 + i) * E + e] : 0;
+  float ps = 0.f;
+  if (lead) {
+    float preg[kScanReg];
+#pragma unroll
+    for (int i = 0; i < kScanReg; ++i)
+      preg[i] = ve && b0 + i < b1 ? a.blk_psum[(int64_t)(b0 + i) * E + e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kScanReg; ++i) ps += preg[i];
+  }
+  int cs = 0;
+#pragma unroll
+  for (int i = 0; i < kScanReg; ++i) cs += creg[i];
+  s_c[part][e] = cs;
+  s_p[part][e] = ps;
+  __syncthreads();
+
+  // 2) the bases of this workgroup's blocks, written by the wave holding each
+  //    block's part, and the experts' first rows
+  int base = 0;
+  for (int q = 0; q < part; ++q) base += s_c[q][e];
+#pragma unroll
+  for (int i = 0; i < kScanReg; ++i) {
+    const int b = b0 + i;
+    if (b < b1 && b >= g0 && b < g0 + kScanParts) s_base[b - g0][e] = base;
+    base += creg[i];
+  }
+  if (part == 0) {
+    int c = 0;
+    float P = 0.f;
+    if (ve) {
+      for (int q = 0; q < kScanParts; ++q) {
+        c += s_c[q][e];
+        P += s_p[q][e];
+      }
+    }
+    // 3) workgroup 0 writes the per-expert outputs; every workgroup keeps
+    //    the first rows
+    int excl;
+    if (lead) {
+      excl = scan_outputs(a, c, P);
+    } else {
+      const int kp = ve ? (a.capacity > 0 ? min(c, a.capacity) : c) : 0;
+      int incl = kp;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int n = __shfl_up(incl, o, 64);
+        if (e >= o) incl += n;
+      }
+      excl = incl - kp;
+    }
+    s_off[e] = excl;
+  }
+  __syncthreads();
+
+  // 4) rank this wave's block
+  if (rb < nblk) rank_block(r, rb, B, s_base[part], s_off);
 }
 
 // ---------------------------------------------------------------------------
@@ -754,6 +878,16 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(scan_cols_kernel, dim3((a.E + 63) / 64), dim3(1024), 0, s, a);
     hipLaunchKernelGGL(scan_kernel<false>, dim3(1), dim3(1024), (size_t)a.E * 8, s, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_rank(const ScanArgs& a, const RankArgs& r, hipStream_t s) {
+  if (a.nblk == 0) return hipSuccess;
+  if (a.E > 64 || a.nblk > kScanParts * kScanReg || (int64_t)r.tb * r.k > 64 * kMaxChunks ||
+      r.nblk != a.nblk)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(scan_rank_small_kernel, dim3((a.nblk + kScanParts - 1) / kScanParts),
+                     dim3(1024), 0, s, a, r);
   return hipGetLastError();
 }
 
