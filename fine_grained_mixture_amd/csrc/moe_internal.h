@@ -11,9 +11,9 @@ namespace moe {
 
 // Tokens per routing block: the top-k kernels histogram, and the rank kernel
 // ranks, blocks of this many consecutive tokens (one workgroup / one wave
-// each). The fused small-E router uses 16-token blocks, the generic one 64.
+// each). The fused small-E router uses 16-token blocks, the generic one 32.
 constexpr int kRouteBlockSmall = 16;
-constexpr int kRouteBlock = 64;
+constexpr int kRouteBlock = 32;
 // Largest expert count the fused small-E router handles.
 constexpr int kRouteSmallMaxE = 64;
 // Rows per M-tile of the grouped GEMMs.

@@ -335,6 +335,7 @@ __device__ double block_sum_fixed(double v, double* smem) {
 // block tables and each block's exclusive prefix (slots of the expert in
 // earlier blocks, i.e. earlier tokens). 1024 threads: the blocks are split
 // over 1024 / CW row groups, each summing its consecutive blocks.
+template <int kColReg>
 __device__ void scan_columns(const ScanArgs& a, int c0, int CW, int* s_part, float* s_fpart,
                              int* cnt_out, float* psum_out) {
   const int E = a.E, nblk = a.nblk;
@@ -344,9 +345,22 @@ __device__ void scan_columns(const ScanArgs& a, int c0, int CW, int* s_part, flo
   const int per = (nblk + RG - 1) / RG;
   const int b0 = min(nblk, rg * per), b1 = min(nblk, b0 + per);
   const int e = c0 + cl;
+  // a range of up to kColReg blocks is read once, all loads in flight, and
+  // kept in registers for the prefix pass below
+  const bool in_reg = b1 - b0 <= kColReg;
+  int creg[kColReg];
   int cs = 0;
   float ps = 0.f;
-  if (e < E) {
+  if (e < E && in_reg) {
+#pragma unroll
+    for (int i = 0; i < kColReg; ++i)
+      creg[i] = b0 + i < b1 ? a.blk_counts[(int64_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+    for (int i = 0; i < kColReg; ++i) {
+      cs += creg[i];
+      if (b0 + i < b1) ps += a.blk_psum[(int64_t)(b0 + i) * E + e];
+    }
+  } else if (e < E) {
 #pragma unroll 8
     for (int b = b0; b < b1; ++b) {
       cs += a.blk_counts[(int64_t)b * E + e];
@@ -371,10 +385,18 @@ __device__ void scan_columns(const ScanArgs& a, int c0, int CW, int* s_part, flo
   __syncthreads();
   if (e < E) {
     int run = s_part[tid];
+    if (in_reg) {
+#pragma unroll
+      for (int i = 0; i < kColReg; ++i) {
+        if (b0 + i < b1) a.blk_base[(int64_t)(b0 + i) * E + e] = run;
+        run += creg[i];
+      }
+    } else {
 #pragma unroll 8
-    for (int b = b0; b < b1; ++b) {
-      a.blk_base[(int64_t)b * E + e] = run;
-      run += a.blk_counts[(int64_t)b * E + e];
+      for (int b = b0; b < b1; ++b) {
+        a.blk_base[(int64_t)b * E + e] = run;
+        run += a.blk_counts[(int64_t)b * E + e];
+      }
     }
   }
   __syncthreads();
@@ -382,11 +404,14 @@ __device__ void scan_columns(const ScanArgs& a, int c0, int CW, int* s_part, flo
 
 __device__ __forceinline__ int scan_cw(int E) { return E <= 16 ? 16 : (E <= 32 ? 32 : 64); }
 
-// Many experts: one workgroup per 64-expert column, totals to global memory.
+// Many experts: one workgroup per 16 experts (64 row groups of the blocks, so
+// that many CUs share the latency-bound reads), totals to global memory.
+constexpr int kScanColsW = 16;
 __global__ void __launch_bounds__(1024) scan_cols_kernel(ScanArgs a) {
   __shared__ int s_part[1024];
   __shared__ float s_fpart[1024];
-  scan_columns(a, blockIdx.x * 64, 64, s_part, s_fpart, a.counts, a.psum_tot);
+  scan_columns<16>(a, blockIdx.x * kScanColsW, kScanColsW, s_part, s_fpart, a.counts,
+                   a.psum_tot);
 }
 
 // FUSED: the column pass runs here (few experts); otherwise the totals come
@@ -406,7 +431,7 @@ __global__ void __launch_bounds__(1024) scan_kernel(ScanArgs a) {
   // 1) per-expert totals and the block prefix
   if (FUSED) {
     const int CW = scan_cw(E);
-    for (int c0 = 0; c0 < E; c0 += CW) scan_columns(a, c0, CW, s_part, s_fpart, s_cnt, s_P);
+    for (int c0 = 0; c0 < E; c0 += CW) scan_columns<8>(a, c0, CW, s_part, s_fpart, s_cnt, s_P);
   } else {
     for (int e = tid; e < E; e += blockDim.x) {
       s_cnt[e] = a.counts[e];
@@ -712,6 +737,39 @@ __global__ void __launch_bounds__(256) rank_kernel(RankArgs a) {
   rank_block(a, b, B, cnt, offs);
 }
 
+// Blocks of at most 64 slots (one chunk) and many experts: no running count
+// crosses chunks, so each lane reads just its own expert's base and first row
+// instead of the wave copying both tables of E entries.
+__global__ void __launch_bounds__(256) rank_one_chunk_kernel(RankArgs a) {
+  const int E = a.E, k = a.k;
+  const int lane = lane_id();
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (b >= a.nblk) return;
+  const int64_t s_begin = (int64_t)b * a.tb * k;
+  const int64_t s_end = min(a.T, (int64_t)(b + 1) * a.tb) * k;
+  const int64_t s = s_begin + lane;
+  const bool valid = s < s_end;
+  const int e = valid ? a.topk_idx[s] : 0;
+  const int base = valid ? a.blk_base[(int64_t)b * E + e] : 0;
+  const int off = valid ? a.offsets[e] : 0;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  uint64_t match = __ballot(valid);
+  for (int bit = 0; bit < nbits; ++bit) {
+    const bool on = (e >> bit) & 1;
+    const uint64_t bb = __ballot(valid && on);
+    match &= on ? bb : ~bb;
+  }
+  if (valid) {
+    const int pos = base + __popcll(match & lanemask_lt());
+    const bool keep = a.capacity == 0 || pos < a.capacity;
+    const int row = keep ? off + pos : -1;
+    a.row_of_slot[s] = row;
+    if (keep) a.sorted_token[row] = (int32_t)(s / k);
+    if (a.dropped) a.dropped[s] = keep ? 0 : 1;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // scan and rank in one launch, for the layer call with few experts (E <= 64)
 // and few blocks (nblk <= kScanParts * kScanReg): every workgroup derives the
@@ -875,7 +933,8 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
   } else if (!a.psum_tot) {
     hipLaunchKernelGGL(scan_kernel<true>, dim3(1), dim3(1024), (size_t)a.E * 8, s, a);
   } else {
-    hipLaunchKernelGGL(scan_cols_kernel, dim3((a.E + 63) / 64), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(scan_cols_kernel, dim3((a.E + kScanColsW - 1) / kScanColsW), dim3(1024),
+                       0, s, a);
     hipLaunchKernelGGL(scan_kernel<false>, dim3(1), dim3(1024), (size_t)a.E * 8, s, a);
   }
   return hipGetLastError();
@@ -893,8 +952,11 @@ hipError_t launch_scan_rank(const ScanArgs& a, const RankArgs& r, hipStream_t s)
 
 hipError_t launch_rank(const RankArgs& a, hipStream_t s) {
   if (a.nblk == 0) return hipSuccess;
-  if ((int64_t)a.tb * a.k > 64 * 15) return hipErrorInvalidValue;   // ids held in registers
-  hipLaunchKernelGGL(rank_kernel, dim3((a.nblk + 3) / 4), dim3(256), (size_t)a.E * 32, s, a);
+  if ((int64_t)a.tb * a.k > 64 * kMaxChunks) return hipErrorInvalidValue;   // ids in registers
+  if ((int64_t)a.tb * a.k <= 64 && a.E > 64)
+    hipLaunchKernelGGL(rank_one_chunk_kernel, dim3((a.nblk + 3) / 4), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(rank_kernel, dim3((a.nblk + 3) / 4), dim3(256), (size_t)a.E * 32, s, a);
   return hipGetLastError();
 }
 

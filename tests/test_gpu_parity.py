@@ -59,6 +59,10 @@ EDGE = {
     "many_experts_k8": synth.Workload("k8", T=190, hidden=128, n_routed=300, top_k=8,
                                       n_shared=1, ffn=64, renorm=0),
     "tiny_f32_capacity": synth.TINY.replace(T=200, capacity_factor="1/2", seed=3),
+    # many experts, two active: routing blocks of one 64-slot chunk, with drops
+    "many_experts_k2_capacity": synth.Workload("mc", T=333, hidden=128, n_routed=128, top_k=2,
+                                               n_shared=0, ffn=64, capacity_factor="3/2",
+                                               logit_offset_std=0.5),
 }
 
 
