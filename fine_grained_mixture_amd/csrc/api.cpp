@@ -47,7 +47,10 @@ bool valid_config(const moe_config* c) {
 // Low-rank experts: rank 64 with bf16 (the fused kernel's shape); fp8 experts
 // are dense.
 bool supported_config(const moe_config* c) {
-  if (c->rank != 0 && (c->rank != 64 || c->dtype == MOE_F32)) return false;
+  // low-rank experts: bf16 with rank 16, 32, 48 or 64; fp8 factors with rank 64
+  if (c->rank != 0 && (c->rank > 64 || c->rank % 16 || c->dtype == MOE_F32 ||
+                       (c->dtype == MOE_FP8 && c->rank != 64)))
+    return false;
   // fp8: dense experts; the rows entering the products (x over d, h over F,
   // the shared h over S F) are quantised whole in registers, up to 4096 values
   if (c->dtype == MOE_FP8 && (c->hidden > 4096 || (int64_t)c->n_shared * c->ffn > 4096 ||
@@ -564,6 +567,7 @@ void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool 
     lr.F = (int32_t)F;
     lr.E = c->n_routed;
     lr.max_tiles = (int32_t)L.max_tiles;
+    lr.rank = c->rank;
     if (fp8(c)) {
       lr.fp8 = 1;
       lr.u_gate_scale = w->u_gate_scale;

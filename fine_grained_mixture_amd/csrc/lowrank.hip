@@ -31,7 +31,8 @@
 namespace moe {
 namespace {
 
-constexpr int kR = 64;          // rank
+constexpr int kR = 64;          // rank of the tiles; a smaller rank (16, 32, 48) runs
+                                // with the factor entries past it read as zero
 constexpr int kBM = kLowRankBM; // 64 rows per workgroup
 constexpr int kLd = 72;         // padded LDS row for 64-wide k tiles
 constexpr int kLdZ = 136;       // padded LDS row for the [rows, 2r] zg|zu tile
@@ -83,7 +84,7 @@ __device__ __forceinline__ floatx4 mfma(const bf16x8& a, const bf16x8& b, const 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <bool Q8>
+template <bool Q8, bool FULL>
 __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
   // zg | zu lives through stages 1-3; the other tiles share one region, as
   // no two of the groups are live together: stage 1 (A chunk, U_gate|U_up
@@ -106,24 +107,27 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lk = 8 * (lane >> 4);
   const int d = a.d, F = a.F;
+  // factor row length; columns rk .. kR - 1 of every tile are zero (FULL: the
+  // rank is kR and every mask folds away)
+  const int rk = FULL ? kR : a.rank;
 
   const bf16_t* A = static_cast<const bf16_t*>(a.A);
-  const bf16_t* Ug = static_cast<const bf16_t*>(a.u_gate) + (int64_t)e * d * kR;
-  const bf16_t* Uu = static_cast<const bf16_t*>(a.u_up) + (int64_t)e * d * kR;
-  const bf16_t* Vg = static_cast<const bf16_t*>(a.v_gate) + (int64_t)e * F * kR;
-  const bf16_t* Vu = static_cast<const bf16_t*>(a.v_up) + (int64_t)e * F * kR;
-  const bf16_t* Ud = static_cast<const bf16_t*>(a.u_down) + (int64_t)e * F * kR;
-  const bf16_t* Vd = static_cast<const bf16_t*>(a.v_down) + (int64_t)e * d * kR;
+  const bf16_t* Ug = static_cast<const bf16_t*>(a.u_gate) + (int64_t)e * d * rk;
+  const bf16_t* Uu = static_cast<const bf16_t*>(a.u_up) + (int64_t)e * d * rk;
+  const bf16_t* Vg = static_cast<const bf16_t*>(a.v_gate) + (int64_t)e * F * rk;
+  const bf16_t* Vu = static_cast<const bf16_t*>(a.v_up) + (int64_t)e * F * rk;
+  const bf16_t* Ud = static_cast<const bf16_t*>(a.u_down) + (int64_t)e * F * rk;
+  const bf16_t* Vd = static_cast<const bf16_t*>(a.v_down) + (int64_t)e * d * rk;
   // fp8 factors: U codes [r][in] (k-contiguous rows), V codes [out][r]
-  const uint8_t* Ug8 = static_cast<const uint8_t*>(a.u_gate) + (int64_t)e * kR * d;
-  const uint8_t* Uu8 = static_cast<const uint8_t*>(a.u_up) + (int64_t)e * kR * d;
-  const uint8_t* Ud8 = static_cast<const uint8_t*>(a.u_down) + (int64_t)e * kR * F;
-  const uint8_t* Vg8 = static_cast<const uint8_t*>(a.v_gate) + (int64_t)e * F * kR;
-  const uint8_t* Vu8 = static_cast<const uint8_t*>(a.v_up) + (int64_t)e * F * kR;
-  const uint8_t* Vd8 = static_cast<const uint8_t*>(a.v_down) + (int64_t)e * d * kR;
-  const bf16_t* sg = static_cast<const bf16_t*>(a.s_gate) + (int64_t)e * kR;
-  const bf16_t* su = static_cast<const bf16_t*>(a.s_up) + (int64_t)e * kR;
-  const bf16_t* sd = static_cast<const bf16_t*>(a.s_down) + (int64_t)e * kR;
+  const uint8_t* Ug8 = static_cast<const uint8_t*>(a.u_gate) + (int64_t)e * rk * d;
+  const uint8_t* Uu8 = static_cast<const uint8_t*>(a.u_up) + (int64_t)e * rk * d;
+  const uint8_t* Ud8 = static_cast<const uint8_t*>(a.u_down) + (int64_t)e * rk * F;
+  const uint8_t* Vg8 = static_cast<const uint8_t*>(a.v_gate) + (int64_t)e * F * rk;
+  const uint8_t* Vu8 = static_cast<const uint8_t*>(a.v_up) + (int64_t)e * F * rk;
+  const uint8_t* Vd8 = static_cast<const uint8_t*>(a.v_down) + (int64_t)e * d * rk;
+  const bf16_t* sg = static_cast<const bf16_t*>(a.s_gate) + (int64_t)e * rk;
+  const bf16_t* su = static_cast<const bf16_t*>(a.s_up) + (int64_t)e * rk;
+  const bf16_t* sd = static_cast<const bf16_t*>(a.s_down) + (int64_t)e * rk;
 
   // A rows of this chunk (clamped: rows past r_end are computed, never stored)
   const int a_c = tid & 7, a_rb = tid >> 3;
@@ -150,18 +154,24 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
   // fp8: B-tile row n = t / 2 (gate rows 0..63, up 64..127), 32 codes at
   // k0 + 32 (t % 2)
   u32x4 bq8[2];
-  const uint8_t* u8_src = ((tid >> 1) < kR ? Ug8 + (int64_t)(tid >> 1) * d
-                                           : Uu8 + (int64_t)((tid >> 1) - kR) * d) +
+  const int u8_row = (tid >> 1) & (kR - 1);   // U row (rank index) of this thread
+  const bool u8_ok = u8_row < rk;
+  const uint8_t* u8_src = ((tid >> 1) < kR ? Ug8 : Uu8) + (int64_t)(u8_ok ? u8_row : 0) * d +
                           32 * (tid & 1);
+  const bool b_ok = 2 * bp < rk;   // this thread's column pair of U is within the rank
   auto load1 = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) ar[i] = *reinterpret_cast<const u32x4*>(a_src[i] + k0);
     if (Q8) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) bq8[i] = *reinterpret_cast<const u32x4*>(u8_src + k0 + 16 * i);
+      for (int i = 0; i < 2; ++i)
+        bq8[i] = u8_ok ? *reinterpret_cast<const u32x4*>(u8_src + k0 + 16 * i) : u32x4{0, 0, 0, 0};
+    } else if (b_ok) {
+      load_b_pair(Ug + (int64_t)(k0 + 8 * bq) * rk + 2 * bp, rk, br[0]);
+      load_b_pair(Uu + (int64_t)(k0 + 8 * bq) * rk + 2 * bp, rk, br[1]);
     } else {
-      load_b_pair(Ug + (int64_t)(k0 + 8 * bq) * kR + 2 * bp, kR, br[0]);
-      load_b_pair(Uu + (int64_t)(k0 + 8 * bq) * kR + 2 * bp, kR, br[1]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) br[0][i] = br[1][i] = 0u;
     }
   };
   load1(0);
@@ -199,10 +209,10 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int col = 32 * wave + 16 * j + lr;
-    float sc = col < kR ? bf16_to_f32(sg[col]) : bf16_to_f32(su[col - kR]);
-    if (Q8)   // U's column scale folded into s (a power of two: exact)
-      sc *= col < kR ? a.u_gate_scale[(int64_t)e * kR + col]
-                     : a.u_up_scale[(int64_t)e * kR + col - kR];
+    const int rc = col & (kR - 1);   // rank index of this column
+    float sc = rc >= rk ? 0.f : (col < kR ? bf16_to_f32(sg[rc]) : bf16_to_f32(su[rc]));
+    if (Q8 && rc < rk)   // U's column scale folded into s (a power of two: exact)
+      sc *= col < kR ? a.u_gate_scale[(int64_t)e * rk + rc] : a.u_up_scale[(int64_t)e * rk + rc];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -224,20 +234,31 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
   auto load2 = [&](int f0) {
     const int n = f0 + 16 * wave + lr;
     if (Q8) {
-      bd8 = *reinterpret_cast<const u32x4*>(Ud8 + (int64_t)(tid >> 2) * F + f0 + 16 * (tid & 3));
+      bd8 = (tid >> 2) < rk
+                ? *reinterpret_cast<const u32x4*>(Ud8 + (int64_t)(tid >> 2) * F + f0 + 16 * (tid & 3))
+                : u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        bgv[kk] = cvt8_fp8_bf16(*reinterpret_cast<const u32x2*>(Vg8 + (int64_t)n * kR + 32 * kk + lk));
-        buv[kk] = cvt8_fp8_bf16(*reinterpret_cast<const u32x2*>(Vu8 + (int64_t)n * kR + 32 * kk + lk));
+        const bool ok = 32 * kk + lk < rk;
+        bgv[kk] = ok ? cvt8_fp8_bf16(*reinterpret_cast<const u32x2*>(Vg8 + (int64_t)n * rk + 32 * kk + lk))
+                     : bf16x8{};
+        buv[kk] = ok ? cvt8_fp8_bf16(*reinterpret_cast<const u32x2*>(Vu8 + (int64_t)n * rk + 32 * kk + lk))
+                     : bf16x8{};
       }
       vgs = a.v_gate_scale[(int64_t)e * F + n];
       vus = a.v_up_scale[(int64_t)e * F + n];
     } else {
-      load_b_pair(Ud + (int64_t)(f0 + 8 * bq) * kR + 2 * bp, kR, bd);
+      if (b_ok) {
+        load_b_pair(Ud + (int64_t)(f0 + 8 * bq) * rk + 2 * bp, rk, bd);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bd[i] = 0u;
+      }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        bgv[kk] = *reinterpret_cast<const bf16x8*>(Vg + (int64_t)n * kR + 32 * kk + lk);
-        buv[kk] = *reinterpret_cast<const bf16x8*>(Vu + (int64_t)n * kR + 32 * kk + lk);
+        const bool ok = 32 * kk + lk < rk;
+        bgv[kk] = ok ? *reinterpret_cast<const bf16x8*>(Vg + (int64_t)n * rk + 32 * kk + lk) : bf16x8{};
+        buv[kk] = ok ? *reinterpret_cast<const bf16x8*>(Vu + (int64_t)n * rk + 32 * kk + lk) : bf16x8{};
       }
     }
   };
@@ -279,8 +300,8 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
   }
   {
     const int col = 16 * wave + lr;
-    float sc = bf16_to_f32(sd[col]);
-    if (Q8) sc *= a.u_down_scale[(int64_t)e * kR + col];
+    float sc = col < rk ? bf16_to_f32(sd[col]) : 0.f;
+    if (Q8 && col < rk) sc *= a.u_down_scale[(int64_t)e * rk + col];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -298,10 +319,13 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
     const int n = n0 + 16 * wave + lr;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      if (Q8)
-        bvd[kk] = cvt8_fp8_bf16(*reinterpret_cast<const u32x2*>(Vd8 + (int64_t)n * kR + 32 * kk + lk));
+      const bool ok = 32 * kk + lk < rk;
+      if (!ok)
+        bvd[kk] = bf16x8{};
+      else if (Q8)
+        bvd[kk] = cvt8_fp8_bf16(*reinterpret_cast<const u32x2*>(Vd8 + (int64_t)n * rk + 32 * kk + lk));
       else
-        bvd[kk] = *reinterpret_cast<const bf16x8*>(Vd + (int64_t)n * kR + 32 * kk + lk);
+        bvd[kk] = *reinterpret_cast<const bf16x8*>(Vd + (int64_t)n * rk + 32 * kk + lk);
     }
     if (Q8) vds = a.v_down_scale[(int64_t)e * d + n];
   };
@@ -337,10 +361,16 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowRankArgs a) {
 
 hipError_t launch_lowrank(const LowRankArgs& a, hipStream_t s) {
   if (a.max_tiles <= 0) return hipSuccess;
-  if (a.fp8)
-    hipLaunchKernelGGL((lowrank_kernel<true>), dim3((unsigned)a.max_tiles), dim3(256), 0, s, a);
+  if (a.rank < 16 || a.rank > kR || a.rank % 16) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)a.max_tiles), block(256);
+  if (a.fp8 && a.rank == kR)
+    hipLaunchKernelGGL((lowrank_kernel<true, true>), grid, block, 0, s, a);
+  else if (a.fp8)
+    hipLaunchKernelGGL((lowrank_kernel<true, false>), grid, block, 0, s, a);
+  else if (a.rank == kR)
+    hipLaunchKernelGGL((lowrank_kernel<false, true>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((lowrank_kernel<false>), dim3((unsigned)a.max_tiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((lowrank_kernel<false, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

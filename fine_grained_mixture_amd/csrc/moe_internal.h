@@ -211,6 +211,7 @@ struct LowRankArgs {
   const int32_t* plan;       // tile list with kLowRankBM rows per tile
   float* y;                  // [R_max, d]
   int32_t d, F, E, max_tiles;
+  int32_t rank;              // 16, 32, 48 or 64
 };
 hipError_t launch_lowrank(const LowRankArgs& a, hipStream_t s);
 

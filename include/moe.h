@@ -35,8 +35,9 @@
  *   - Calls that share a workspace on different streams race; calls on one
  *     stream are ordered.
  *   - Limits of this build: 1 <= k <= 15, k <= E <= 4096; d and F multiples of
- *     64; T*k < 2^31; rank is 0 or 64 with bf16 or fp8 (low-rank float32
- *     experts are MOE_EUNSUPPORTED); sigmoid scoring requires renorm_topk == 1;
+ *     64; T*k < 2^31; rank is 0, or 16, 32, 48 or 64 with bf16, or 64 with
+ *     fp8 (low-rank float32 experts are MOE_EUNSUPPORTED); sigmoid scoring
+ *     requires renorm_topk == 1;
  *     MOE_FP8 runs in moe_layer_forward and moe_grouped_ffn, with d, F and
  *     S*F at most 4096.
  */

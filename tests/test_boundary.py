@@ -96,6 +96,22 @@ def test_invalid_config_rejected(lib, bad):
     assert st == _lib.MOE_EINVAL
 
 
+@pytest.mark.parametrize("rank,dtype", [(8, "bf16"), (40, "bf16"), (80, "bf16"), (128, "bf16"),
+                                        (32, "fp8"), (64, "f32")])
+def test_unsupported_rank_rejected_before_any_launch(lib, rank, dtype):
+    cfg = _cfg(rank=rank, dtype=dtype)
+    w = _lib.MoeWeights(**{n: 0x1000 for n in _lib.WEIGHT_FIELDS})
+    o = _lib.MoeOutputs(**{n: 0x1000 for n in _lib.OUTPUT_FIELDS})
+    st = lib.moe_layer_forward(ctypes.byref(cfg), 64, 0x1000, ctypes.byref(w), ctypes.byref(o),
+                               0x1000, 1 << 30, None)
+    assert st == _lib.MOE_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("rank", [16, 32, 48, 64])
+def test_low_ranks_accepted(lib, rank):
+    assert _lib.moe_workspace_bytes(_cfg(rank=rank), 64) > 0
+
+
 def test_null_pointers_and_workspace_rejected(lib):
     cfg = _cfg()
     full_w = _lib.MoeWeights(**{n: 0x1000 for n in ("w_router", "w_gate", "w_up", "w_down",

@@ -37,6 +37,11 @@ SMALL = {
     "sutra_small": synth.SUTRA.replace(T=700, hidden=384, ffn=192),
     "dormouse_small": synth.DORMOUSE.replace(T=600, hidden=256, ffn=128),
     "dormouse_small_renorm": synth.DORMOUSE.replace(T=600, hidden=256, ffn=128, renorm=1),
+    # ranks below 64: the kernel's rank-64 tiles with the factor entries past r read as zero
+    "dormouse_small_rank16": synth.DORMOUSE.replace(T=300, hidden=192, ffn=320, rank=16, seed=3),
+    "dormouse_small_rank32": synth.DORMOUSE.replace(T=420, hidden=256, ffn=128, rank=32,
+                                                    n_shared=1, seed=4),
+    "dormouse_small_rank48": synth.DORMOUSE.replace(T=500, hidden=128, ffn=192, rank=48, seed=5),
 }
 
 
