@@ -338,10 +338,10 @@ def time_fp8(wl, inp, x, steps, warmup, stream):
     return ms, {n: float(np.mean(v)) for n, v in dur.items()}
 
 
-def traffic_from_profile(kernel_src: str):
-    """HBM bytes per launch of the gate/up kernel from the committed counter
+def traffic_from_profile(kernel_src: str, summary: str = "gate_up_gemm_quartz_counters.md"):
+    """HBM bytes per launch of a dominant kernel from its committed counter
     summary, if it was taken from the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "gate_up_gemm_quartz_counters.md")
+    path = os.path.join(ROOT, "profiles", summary)
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -476,6 +476,9 @@ def main():
 
     rows = int(out["offsets"][-1].item())
     alg = algorithmic(wl, rows)
+
+    def full_shape(name):
+        return wl.name == name and wl.T == synth.WORKLOADS[name].T
     kernel_src = os.path.join(ROOT, "fine_grained_mixture_amd", "csrc", "gemm_big.hip")
     # every expert GEMM stage present and its algorithmic FLOPs
     gemm_stages = {"gate_up_gemm": alg["gate_up_flops"], "down_gemm": alg["down_flops"],
@@ -496,7 +499,8 @@ def main():
         achieved = gemm_stages["gate_up_gemm"] / (gu_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": traffic_from_profile(kernel_src)}
+                # the counters were taken at the Quartz shape
+                "traffic": traffic_from_profile(kernel_src) if full_shape("quartz") else None}
     elif wl.rank > 0:
         # dominant kernel: the fused low-rank experts, bound by streaming the
         # factor weights of every expert that received rows
@@ -508,7 +512,10 @@ def main():
         io = rows * wl.hidden * 2 + rows * wl.hidden * 4
         achieved = (wbytes + io) / (us * 1e-6) / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                "traffic": traffic_from_profile(
+                    os.path.join(ROOT, "fine_grained_mixture_amd", "csrc", "lowrank.hip"),
+                    "lowrank_experts_dormouse_counters.md") if full_shape("dormouse") else None,
                 "algorithmic_bytes": wbytes + io}
     else:
         dom = "gate_up_gemm"
