@@ -205,3 +205,11 @@ def test_backward_validation(lib):
         nb = _lib.moe_backward_workspace_bytes(bad, T)
         st = call(c=bad, nbytes=_lib.moe_workspace_bytes(bad, T), bbytes=nb)
         assert st == _lib.MOE_EUNSUPPORTED
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library the binding raises; there is no fallback path."""
+    monkeypatch.setattr(_lib, "_LIB", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libmoe.so"))
+    with pytest.raises(RuntimeError, match="is missing"):
+        _lib.load()
