@@ -35,9 +35,11 @@ __device__ __forceinline__ float silu_f32(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
-// Monotone map of a float onto uint32 (larger float -> larger integer).
+// Monotone map of a float onto uint32 (larger float -> larger integer); -0
+// maps as +0, so that the two zeros compare equal, as floats do.
 __device__ __forceinline__ uint32_t float_orderable(float f) {
   uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 __device__ __forceinline__ float orderable_float(uint32_t o) {
@@ -56,13 +58,6 @@ __device__ __forceinline__ int packed_id(uint64_t p) {
 }
 __device__ __forceinline__ float packed_key(uint64_t p) {
   return orderable_float(static_cast<uint32_t>(p >> 32));
-}
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
-  uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
-  lo = __shfl_xor(lo, mask, kWave);
-  hi = __shfl_xor(hi, mask, kWave);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 // Intra-row (16-lane) exchanges on the DPP path: after the quad_perm steps a
@@ -90,16 +85,6 @@ __device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
 }
 
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = max_u64(v, dpp_u64<kDppQuadXor1>(v));
-  v = max_u64(v, dpp_u64<kDppQuadXor2>(v));
-  v = max_u64(v, dpp_u64<kDppRowHalfMirror>(v));
-  v = max_u64(v, dpp_u64<kDppRowMirror>(v));
-  v = max_u64(v, shfl_xor_u64(v, 16));
-  v = max_u64(v, shfl_xor_u64(v, 32));
-  return v;
-}
 
 // Sums and maxima: every lane ends with the same value, combined in a fixed
 // order, so the result does not depend on scheduling.
