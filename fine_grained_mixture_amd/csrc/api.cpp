@@ -276,9 +276,15 @@ bool scan_rank_fused(const moe_config* c, const Layout& L) {
   return fused_router(c) && L.T > 0 && L.nblk <= 256;
 }
 
+// One routing block for the whole batch in the layer call: the fused router
+// also scans and ranks it.
+bool route_tail_fused(const moe_config* c, const Layout& L) {
+  return fused_router(c) && L.T > 0 && L.nblk == 1;
+}
+
 void run_route(Runner& R, const moe_config* c, const Layout& L, const void* x,
                const moe_weights* w, moe_outputs* o, void* ws, bool with_plan,
-               bool scan = true) {
+               bool scan = true, bool tail = false) {
   const int64_t T = L.T;
   const int E = c->n_routed;
   float* logits = at<float>(ws, L.logits);
@@ -300,6 +306,14 @@ void run_route(Runner& R, const moe_config* c, const Layout& L, const void* x,
     r.k = c->top_k;
     r.score = c->score;
     r.renorm = c->renorm_topk;
+    if (tail) {
+      const ScanArgs sa = scan_args(c, L, o, ws, with_plan);
+      const RankArgs ra = rank_args(c, L, o, ws);
+      R.run("route_scan_rank", [&] {
+        return launch_route_small(r, L.tb / kRouteBlockSmall, R.stream, &sa, &ra);
+      });
+      return;
+    }
     R.run("route", [&] {
       return launch_route_small(r, L.tb / kRouteBlockSmall, R.stream);
     });
@@ -724,7 +738,9 @@ int layer_forward(const moe_config* c, int64_t T, const void* x, const moe_weigh
   Runner R{static_cast<hipStream_t>(stream), &tl};
   float* y_perm = at<float>(ws, L.y_perm);
   float* y_sh = c->n_shared > 0 ? at<float>(ws, L.y_sh) : nullptr;
-  if (scan_rank_fused(c, L)) {
+  if (route_tail_fused(c, L)) {
+    run_route(R, c, L, x, w, o, ws, true, false, true);
+  } else if (scan_rank_fused(c, L)) {
     run_route(R, c, L, x, w, o, ws, true, false);
     run_scan_rank(R, c, L, o, ws);
   } else {

@@ -136,7 +136,13 @@ struct RouteSmallArgs {
 // handles for T tokens; its routing blocks are kRouteBlockSmall * groups
 // tokens long.
 int route_small_groups(int64_t T, int k);
-hipError_t launch_route_small(const RouteSmallArgs& a, int groups, hipStream_t s);
+struct ScanArgs;
+struct RankArgs;
+// With tail_scan and tail_rank (the launch makes a single routing block), the
+// launch also writes the scan's outputs and ranks the block.
+hipError_t launch_route_small(const RouteSmallArgs& a, int groups, hipStream_t s,
+                              const ScanArgs* tail_scan = nullptr,
+                              const RankArgs* tail_rank = nullptr);
 
 struct ScanArgs {
   const int32_t* blk_counts;  // [nblk, E]

@@ -27,6 +27,7 @@
 
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "route_tail.h"
 
 #include <algorithm>
 
@@ -79,7 +80,8 @@ constexpr int slice_bytes() {
 // RES: every wave's K range fits its LDS slice and the fragment registers, so
 // W_r is staged once and each group only loads token rows.
 template <int NS, int KMAX, bool DMA, bool RES>
-__global__ void __launch_bounds__(256) route_small_kernel(RouteSmallArgs a, int groups) {
+__global__ void __launch_bounds__(256) route_small_kernel(RouteSmallArgs a, int groups,
+                                                          ScanArgs sa, RankArgs ra) {
   constexpr int EP = 16 * NS;
   constexpr int ws_slice = slice_bytes<NS>();
   __shared__ __attribute__((aligned(16))) unsigned char s_w[kWaves][ws_slice + kWsPad];
@@ -362,16 +364,32 @@ __global__ void __launch_bounds__(256) route_small_kernel(RouteSmallArgs a, int 
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 256) {
-    int c = 0;
-    float p = 0.f;
+  // E <= 64: thread e (a lane of wave 0) holds expert e's totals
+  int c = 0;
+  float p = 0.f;
+  if (tid < E) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      c += s_ct[w][e];
-      p += s_ps[w][e];
+      c += s_ct[w][tid];
+      p += s_ps[w][tid];
     }
-    a.blk_counts[(int64_t)blockIdx.x * E + e] = c;
-    a.blk_psum[(int64_t)blockIdx.x * E + e] = p;
+    a.blk_counts[(int64_t)blockIdx.x * E + tid] = c;
+    a.blk_psum[(int64_t)blockIdx.x * E + tid] = p;
+  }
+
+  // One routing block for the whole batch (the layer call, T <= 16 G): this
+  // workgroup holds everything the scan and the rank need, so wave 0 writes
+  // the per-expert outputs and ranks the block here instead of in a second
+  // launch. The block's expert ids were stored before the barrier above.
+  if (sa.E > 0 && wave == 0) {
+    __shared__ int s_cnt0[64], s_off0[64];
+    const int excl = scan_outputs(sa, c, p);
+    s_cnt0[lane] = 0;   // no earlier blocks
+    s_off0[lane] = excl;
+    __builtin_amdgcn_wave_barrier();
+    BlockIds B;
+    load_block_ids(ra, 0, B);
+    rank_block(ra, 0, B, s_cnt0, s_off0);
   }
 }
 
@@ -395,9 +413,21 @@ int route_small_groups(int64_t T, int k) {
   return (int)std::max<int64_t>(G, 1);
 }
 
-hipError_t launch_route_small(const RouteSmallArgs& a, int groups, hipStream_t s) {
+hipError_t launch_route_small(const RouteSmallArgs& a, int groups, hipStream_t s,
+                              const ScanArgs* tail_scan, const RankArgs* tail_rank) {
   const int64_t nblk = (a.T + (int64_t)kTB * groups - 1) / ((int64_t)kTB * groups);
   if (nblk == 0) return hipSuccess;
+  // scan and rank in this launch: one block of the same tokens, slot ids in
+  // the rank's registers
+  ScanArgs sa{};
+  RankArgs ra{};
+  if (tail_scan && tail_rank) {
+    if (nblk != 1 || tail_scan->nblk != 1 || tail_rank->nblk != 1 ||
+        (int64_t)tail_rank->tb * tail_rank->k > 64 * kMaxChunks || tail_rank->T != a.T)
+      return hipErrorInvalidValue;
+    sa = *tail_scan;
+    ra = *tail_rank;
+  }
   if (a.E > kRouteSmallMaxE || a.k + 1 > 16 || a.d % 32 || groups < 1) return hipErrorInvalidValue;
   const int ns = (a.E + 15) / 16;
   const int k1 = a.k + 1;
@@ -417,10 +447,10 @@ hipError_t launch_route_small(const RouteSmallArgs& a, int groups, hipStream_t s
   do {                                                                                    \
     if (res)                                                                              \
       hipLaunchKernelGGL((route_small_kernel<NSV, KM, DM, true>), dim3((unsigned)nblk),   \
-                         dim3(256), 0, s, a, groups);                                     \
+                         dim3(256), 0, s, a, groups, sa, ra);                                     \
     else                                                                                  \
       hipLaunchKernelGGL((route_small_kernel<NSV, KM, DM, false>), dim3((unsigned)nblk),  \
-                         dim3(256), 0, s, a, groups);                                     \
+                         dim3(256), 0, s, a, groups, sa, ra);                                     \
   } while (0)
 #define MOE_RS(NSV, KM)                   \
   do {                                    \
