@@ -175,10 +175,21 @@ def test_determinism_bitwise():
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
 
 
-@pytest.mark.parametrize("base", ["quartz", "tiny"])
+STAGED = {
+    "quartz": synth.QUARTZ.replace(T=700, hidden=256, ffn=128),
+    "tiny": synth.TINY.replace(T=150),
+    # many experts and low-rank experts: top-k kernel, column scan, one-chunk rank
+    "dormouse": synth.DORMOUSE.replace(T=500, hidden=256, ffn=128),
+    "dormouse_rank32_shared": synth.DORMOUSE.replace(T=300, hidden=128, ffn=192, rank=32,
+                                                     n_shared=1, seed=7),
+    # one routing block: the layer call scans and ranks inside the router's launch
+    "quartz_decode": synth.QUARTZ.replace(T=4, seed=12),
+}
+
+
+@pytest.mark.parametrize("base", list(STAGED))
 def test_stage_entry_points_match_layer(base):
-    wl = (synth.QUARTZ.replace(T=700, hidden=256, ffn=128) if base == "quartz"
-          else synth.TINY.replace(T=150))
+    wl = STAGED[base]
     inp = synth.make_inputs(wl)
     whole = P.run_gpu(wl, inp, y_lowp=True)
     cfg, x, w = P.upload(wl, inp)
