@@ -51,6 +51,10 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 // Source of the lanes whose k lies outside the work item's range.
 __device__ __attribute__((aligned(16))) uint32_t g_zero16[4];
 
+// Direct-to-LDS 16-byte load (lane L writes LDS base + 16 L). Written as asm
+// so that the compiler inserts no waits for it: the ring's vmcnt waits are
+// explicit. m0 is a reserved register, so its clobber is not honoured; the
+// compiler uses m0 nowhere else in these kernels, which a CPU test checks.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
