@@ -44,6 +44,9 @@ constexpr int XB = 16;                    // k steps of token-row fragments in f
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef short shortx8 __attribute__((ext_vector_type(8)));
 
+// Direct-to-LDS 16-byte load (lane L writes LDS base + 16 L), as asm so that
+// the compiler adds no waits for it. m0 is a reserved register, so its clobber
+// is not honoured; the compiler uses m0 nowhere else here (a CPU test checks).
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :

@@ -1,6 +1,6 @@
 """Properties of the generated gfx950 code that the kernels rely on.
 
-The grouped GEMMs issue their direct-to-LDS loads from inline asm
+The grouped GEMMs and the fused router issue their direct-to-LDS loads from inline asm
 (`s_mov_b32 m0, base` then `global_load_lds_dwordx4`), so that the compiler
 adds no waits of its own for them. m0 is a reserved register: the compiler
 ignores the asm's clobber of it. That is only safe while the compiler itself
@@ -19,7 +19,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "fine_grained_mixture_amd", "csrc")
 
 
-@pytest.mark.parametrize("src", ["gemm_big.hip", "fp8.hip", "gemm_bwd.hip"])
+@pytest.mark.parametrize("src", ["gemm_big.hip", "fp8.hip", "gemm_bwd.hip", "route_small.hip"])
 def test_m0_only_written_by_the_lds_dma_asm(src, tmp_path):
     try:
         hipcc = build.hipcc()
