@@ -64,6 +64,11 @@ EDGE = {
     "many_experts_k8": synth.Workload("k8", T=190, hidden=128, n_routed=300, top_k=8,
                                       n_shared=1, ffn=64, renorm=0),
     "tiny_f32_capacity": synth.TINY.replace(T=200, capacity_factor="1/2", seed=3),
+    # rank-64 experts under extreme skew (one expert takes almost every token,
+    # 24 row chunks) and under capacity drops
+    "lowrank_zipf_skew": synth.DORMOUSE.replace(T=1500, hidden=256, ffn=128, zipf_s=1.1, seed=11),
+    "lowrank_capacity": synth.DORMOUSE.replace(T=900, hidden=128, ffn=128, capacity_factor="3/2",
+                                               logit_offset_std=0.5, seed=13),
     # many experts, two active: routing blocks of one 64-slot chunk, with drops
     "many_experts_k2_capacity": synth.Workload("mc", T=333, hidden=128, n_routed=128, top_k=2,
                                                n_shared=0, ffn=64, capacity_factor="3/2",
