@@ -44,15 +44,15 @@ bool valid_config(const moe_config* c) {
   return true;
 }
 
-// Low-rank experts: rank 64 with bf16 (the fused kernel's shape); fp8 experts
-// are dense.
+// What this build's kernels cover beyond valid_config: low-rank experts up to
+// the fused kernel's rank-64 tiles, fp8 rows that fit the quantiser's registers.
 bool supported_config(const moe_config* c) {
   // low-rank experts: bf16 with rank 16, 32, 48 or 64; fp8 factors with rank 64
   if (c->rank != 0 && (c->rank > 64 || c->rank % 16 || c->dtype == MOE_F32 ||
                        (c->dtype == MOE_FP8 && c->rank != 64)))
     return false;
-  // fp8: dense experts; the rows entering the products (x over d, h over F,
-  // the shared h over S F) are quantised whole in registers, up to 4096 values
+  // fp8: the rows entering the dense products (x over d, h over F, the shared
+  // h over S F) are quantised whole in registers, up to 4096 values
   if (c->dtype == MOE_FP8 && (c->hidden > 4096 || (int64_t)c->n_shared * c->ffn > 4096 ||
                               c->ffn > 4096))
     return false;

@@ -200,7 +200,8 @@ struct CombineArgs {
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
-// Fused low-rank (rank 64) SwiGLU experts, bf16. Rows of expert e are
+// Fused low-rank SwiGLU experts (rank 16, 32, 48 or 64 in rank-64 tiles), bf16
+// products. Rows of expert e are
 // [offsets[e], offsets[e+1]); A row of dispatched row r is a_rows[r] (or r).
 // fp8 factors (fp8 != 0): U codes stored transposed [E, r, in], V codes
 // [E, out, r] as in bf16, each with power-of-two scales: u_*_scale [E, r],
