@@ -201,13 +201,20 @@ def per_call_ms(step, n, flush=None):
 
 
 def clock_sampler(path, seconds):
-    """Child process: append one `rocm-smi --showclocks --json` reading per
-    line (with its time) to `path` until `seconds` pass or the parent exits.
-    It is started before the parent touches the GPU and never uses it."""
+    """Child process: once `path`.go exists, append one `rocm-smi
+    --showclocks --json` reading per line (with its time) to `path` until
+    `seconds` pass or the parent exits. It is started before the parent
+    touches the GPU and never uses it."""
     import subprocess
 
     parent = os.getppid()
     end = time.time() + seconds
+    # idle until the parent's clock window opens, so the timed steps run
+    # without the tool beside them
+    while not os.path.exists(path + ".go"):
+        if time.time() >= end or os.getppid() != parent:
+            return
+        time.sleep(0.05)
     with open(path, "w") as f:
         while time.time() < end and os.getppid() == parent:
             try:
@@ -242,6 +249,7 @@ def clock_during(step, sampler, seconds=3.0):
     if sampler is None:
         return res
     proc, path = sampler
+    open(path + ".go", "w").close()
     t0 = time.time()
     while time.time() - t0 < seconds:
         for _ in range(20):
@@ -265,7 +273,9 @@ def clock_during(step, sampler, seconds=3.0):
                         break
             except (ValueError, KeyError, StopIteration, AttributeError):
                 continue
-    os.unlink(path)
+    for f in (path, path + ".go"):
+        if os.path.exists(f):
+            os.unlink(f)
     if vals:
         res["sclk_mhz"] = float(np.median(vals))
         res["samples"] = len(vals)
