@@ -533,6 +533,31 @@ def main():
         achieved = gemm_stages["gate_up_gemm"] / (gu_us * 1e-6) / 1e12
         roof = {"bound": "alu", "kernel": dom, "achieved": achieved, "peak": 157.3,
                 "unit": "TFLOP/s", "frac": achieved / 157.3, "traffic": None}
+    # every stage against its own bound: MFMA for the products, HBM for the
+    # streaming stages (algorithmic FLOPs or bytes over the event-timed mean);
+    # scan and rank are latency-bound and carry no roofline
+    peak_mm = PEAK_BF16_TFLOPS if wl.dtype != "f32" else 157.3
+    stage_work = {"router_gemm": ("mfma", alg["router_flops"]),
+                  "route": ("hbm", alg["route_bytes"] + 8 * wl.T * wl.top_k),
+                  "route_scan_rank": ("hbm", alg["route_bytes"] + 8 * wl.T * wl.top_k),
+                  "topk": ("hbm", alg["topk_bytes"]),
+                  "combine": ("hbm", alg["combine_bytes"])}
+    stage_work.update({n: ("mfma", f) for n, f in gemm_stages.items() if n != "lowrank_experts"})
+    if wl.rank > 0:
+        stage_work["lowrank_experts"] = ("hbm", roof["algorithmic_bytes"])
+    stage_roof = {}
+    for n, (bound, work) in stage_work.items():
+        if n not in stage_us or stage_us[n] <= 0:
+            continue
+        if bound == "mfma":
+            ach = work / (stage_us[n] * 1e-6) / 1e12
+            stage_roof[n] = {"bound": "mfma" if wl.dtype != "f32" else "alu", "achieved": ach,
+                             "unit": "TFLOP/s", "frac": ach / peak_mm}
+        else:
+            ach = work / (stage_us[n] * 1e-6) / 1e9
+            stage_roof[n] = {"bound": "hbm", "achieved": ach, "unit": "GB/s",
+                             "frac": ach / PEAK_HBM_GBS}
+
     result = {
         "metric": "MoE layer fwd tokens/s + expert-GEMM TFLOP/s (% MFMA peak), Quartz shape",
         "value": wl.T / (ms_per_step * 1e-3),
@@ -560,6 +585,7 @@ def main():
         "call_ms_p10_p50_p90": warm_p,
         "cold_call_ms_p10_p50_p90": cold_p,
         "clock": clk,
+        "stage_roofline": stage_roof,
         "combine_gbs": alg["combine_bytes"] / (stage_us["combine"] * 1e-6) / 1e9,
         "layer_flops": alg["router_flops"] + alg["gate_up_flops"] + alg["down_flops"]
         + alg["shared_gate_up_flops"] + alg["shared_down_flops"],
