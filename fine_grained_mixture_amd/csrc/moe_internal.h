@@ -113,6 +113,8 @@ struct TopkArgs {
   int64_t T;
   int32_t E, k, score, renorm;
   int32_t tb;                // tokens per block (multiple of 4)
+  int32_t wave_rows;         // set by launch_topk: waves keep their probability
+                             // sums in LDS rows (0: they add them in turn)
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 

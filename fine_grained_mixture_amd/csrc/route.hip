@@ -77,7 +77,7 @@ template <int EPL, int R, bool SIG>
 __global__ void __launch_bounds__((topk_threads<EPL, R>())) topk_kernel(TopkArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   int* s_cnt = reinterpret_cast<int*>(smem_raw);                 // [E]
-  float* s_ps = reinterpret_cast<float*>(smem_raw) + a.E;        // [E]
+  float* s_ps = reinterpret_cast<float*>(smem_raw) + a.E;        // [E] or [waves][E]
 
   const int E = a.E, k = a.k;
   const int lane = lane_id();
@@ -272,7 +272,25 @@ __global__ void __launch_bounds__((topk_threads<EPL, R>())) topk_kernel(TopkArgs
   }
   store_out();
 
-  // per-block probability sums: waves add into LDS one after another
+  // per-block probability sums, the waves' partials added in wave order: each
+  // wave's partials in an LDS row of its own, then each thread sums its
+  // experts' rows (one barrier); without room for the rows, the waves add
+  // into one row in turn (a barrier each). Both give the same sums.
+  if (a.wave_rows) {
+#pragma unroll
+    for (int m = 0; m < EPL; ++m) {
+      const int e = lane + 64 * m;
+      if (e < E) s_ps[wave * E + e] = psum[m];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      float p = 0.f;
+      for (int w = 0; w < nwaves; ++w) p += s_ps[w * E + e];
+      a.blk_counts[(int64_t)blk * E + e] = s_cnt[e];
+      a.blk_psum[(int64_t)blk * E + e] = p;
+    }
+    return;
+  }
   for (int w = 0; w < nwaves; ++w) {
     if (wave == w) {
 #pragma unroll
@@ -775,17 +793,28 @@ __global__ void __launch_bounds__(256) gather_kernel(const unsigned char* x,
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   const int nblk = (int)((a.T + a.tb - 1) / a.tb);
   if (nblk == 0) return hipSuccess;
-  const size_t shm = (size_t)a.E * 8;
   const int epl = (a.E + 63) / 64;
   const int k1 = a.k + 1;
+  // LDS: counts [E] and the waves' probability-sum rows [waves][E] when they
+  // fit in 48 KiB, else one shared row
+  auto args = [&](int threads, size_t& shm) {
+    TopkArgs b = a;
+    const int nw = threads / 64;
+    const size_t rows = (size_t)a.E * 4 * (1 + nw);
+    b.wave_rows = rows <= 48 * 1024 ? nw : 0;
+    shm = b.wave_rows ? rows : (size_t)a.E * 8;
+    return b;
+  };
 #define MOE_TOPK(EPLV, KM)                                                                   \
   do {                                                                                       \
+    size_t shm = 0;                                                                          \
+    const TopkArgs b = args(topk_threads<EPLV, KM>(), shm);                                  \
     if (a.score == MOE_SIGMOID)                                                              \
       hipLaunchKernelGGL((topk_kernel<EPLV, KM, true>), dim3(nblk),                          \
-                         dim3(topk_threads<EPLV, KM>()), shm, s, a);                         \
+                         dim3(topk_threads<EPLV, KM>()), shm, s, b);                         \
     else                                                                                     \
       hipLaunchKernelGGL((topk_kernel<EPLV, KM, false>), dim3(nblk),                         \
-                         dim3(topk_threads<EPLV, KM>()), shm, s, a);                         \
+                         dim3(topk_threads<EPLV, KM>()), shm, s, b);                         \
   } while (0)
 #define MOE_TOPK_K(EPLV)                \
   do {                                  \

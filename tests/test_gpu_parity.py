@@ -69,6 +69,9 @@ EDGE = {
     "lowrank_zipf_skew": synth.DORMOUSE.replace(T=1500, hidden=256, ffn=128, zipf_s=1.1, seed=11),
     "lowrank_capacity": synth.DORMOUSE.replace(T=900, hidden=128, ffn=128, capacity_factor="3/2",
                                                logit_offset_std=0.5, seed=13),
+    # 3000 experts: the top-k workgroup's probability sums take the one-row LDS path
+    "experts_3000": synth.Workload("e3000", T=100, hidden=128, n_routed=3000, top_k=4,
+                                   n_shared=0, ffn=64, seed=14),
     # many experts, two active: routing blocks of one 64-slot chunk, with drops
     "many_experts_k2_capacity": synth.Workload("mc", T=333, hidden=128, n_routed=128, top_k=2,
                                                n_shared=0, ffn=64, capacity_factor="3/2",
