@@ -108,8 +108,10 @@ gemm_big_kernel(GemmLaunch L) {
     // M-tile share its A rows, and the M-tiles of an expert, about four at
     // the Quartz shape, share its weights in that XCD's L2), with the runs
     // themselves dealt round-robin so that long tiles (the shared experts'
-    // down projection has twice the K) spread over all XCDs. Runs of two
-    // M-tiles measured 1-2% slower, runs of eight slower still.
+    // down projection has twice the K) spread over several XCDs (four at the
+    // Quartz shape: 128 such tiles make four runs). Runs of two M-tiles
+    // measured 1-2% slower, runs of eight slower still, and one contiguous
+    // range per XCD cut at equal K-weighted work no faster.
     const int C = L.p[0].n_tiles_n * 4;
     const int full = nwg / (8 * C) * (8 * C);
     if (bid < full) {
