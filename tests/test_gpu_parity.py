@@ -116,9 +116,11 @@ def test_exact_ties_take_lower_ids(name):
     np.testing.assert_allclose(g["topk_gate"], r0["gates"], rtol=0, atol=1e-6)
 
 
-# decode-sized batches (T <= 4 take the weight-streaming skinny expert kernel;
-# the larger ones check the tile kernel at few rows per expert)
+# decode-sized batches (T <= 4 take the weight-streaming skinny expert kernel,
+# T = 1 with only k + S experts busy; the larger ones check the tile kernel at
+# few rows per expert)
 DECODE = {
+    "quartz_t1": synth.QUARTZ.replace(T=1, seed=4),
     "quartz_t2": synth.QUARTZ.replace(T=2, seed=5),
     "quartz_t4": synth.QUARTZ.replace(T=4, seed=10),
     "quartz_t17": synth.QUARTZ.replace(T=17, seed=6),
