@@ -44,7 +44,7 @@ bool valid_config(const moe_config* c) {
   return true;
 }
 
-// What this build's kernels cover beyond valid_config: low-rank experts up to
+// What the library's kernels cover beyond valid_config: low-rank experts up to
 // the fused kernel's rank-64 tiles, fp8 rows that fit the quantiser's registers.
 bool supported_config(const moe_config* c) {
   // low-rank experts: bf16 with rank 16, 32, 48 or 64; fp8 factors with rank 64
@@ -1385,7 +1385,7 @@ const char* moe_status_str(int status) {
   switch (status) {
     case MOE_OK: return "ok";
     case MOE_EINVAL: return "invalid argument";
-    case MOE_EUNSUPPORTED: return "configuration not supported by this build";
+    case MOE_EUNSUPPORTED: return "configuration not supported by this library";
     case MOE_EWORKSPACE: return "workspace missing, misaligned or too small";
     case MOE_EHIP: return "HIP error";
     default: return "unknown status";

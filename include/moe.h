@@ -34,7 +34,7 @@
  *     (except MOE_EHIP, reported when a launch itself fails).
  *   - Calls that share a workspace on different streams race; calls on one
  *     stream are ordered.
- *   - Limits of this build: 1 <= k <= 15, k <= E <= 4096; d and F multiples of
+ *   - Limits of this library: 1 <= k <= 15, k <= E <= 4096; d and F multiples of
  *     64; T*k < 2^31; rank is 0, or 16, 32, 48 or 64 with bf16, or 64 with
  *     fp8 (low-rank float32 experts are MOE_EUNSUPPORTED); sigmoid scoring
  *     requires renorm_topk == 1;
@@ -54,7 +54,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_EINVAL = -1,        /* NULL required pointer or a size/setting out of range   */
-  MOE_EUNSUPPORTED = -2,  /* legal layer this build does not implement (see limits) */
+  MOE_EUNSUPPORTED = -2,  /* legal layer this library does not implement (see limits) */
   MOE_EWORKSPACE = -3,    /* ws is NULL/misaligned or ws_bytes < moe_workspace_bytes */
   MOE_EHIP = -4           /* a HIP call failed; moe_last_error() holds its text      */
 } moe_status;
@@ -283,7 +283,7 @@ size_t moe_backward_workspace_bytes(const moe_config *cfg, int64_t T);
    here and not modified (h, the shared h and the expert output rows of the
    forward live in ws). dy [T, d] float32 device: the loss gradient of o->y;
    aux_grad: the loss gradient of aux (o->aux[1]), finite. bwd_ws: device,
-   256-byte aligned, at least moe_backward_workspace_bytes. This build: bf16
+   256-byte aligned, at least moe_backward_workspace_bytes. This library: bf16
    dense experts with n_routed a multiple of 8, otherwise MOE_EUNSUPPORTED.
    The result does not depend on scheduling (fixed summation orders, no
    atomics).                                                                 */

@@ -200,7 +200,7 @@ def test_backward_validation(lib):
     assert call(bws=0) == _lib.MOE_EWORKSPACE
     assert call(bws=0x1001) == _lib.MOE_EWORKSPACE
     assert call(T=-1) == _lib.MOE_EINVAL
-    # this build's backward: bf16 dense experts, expert count a multiple of 8
+    # the library's backward: bf16 dense experts, expert count a multiple of 8
     for bad in (_cfg(dtype="f32"), _cfg(n_routed=12), _cfg(rank=64)):
         nb = _lib.moe_backward_workspace_bytes(bad, T)
         st = call(c=bad, nbytes=_lib.moe_workspace_bytes(bad, T), bbytes=nb)
