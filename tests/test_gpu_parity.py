@@ -123,6 +123,9 @@ DECODE = {
     "quartz_t1": synth.QUARTZ.replace(T=1, seed=4),
     "quartz_t2": synth.QUARTZ.replace(T=2, seed=5),
     "quartz_t4": synth.QUARTZ.replace(T=4, seed=10),
+    # the first batch past the skinny kernel, and the first with two routing blocks
+    "quartz_t5": synth.QUARTZ.replace(T=5, seed=13),
+    "quartz_t33": synth.QUARTZ.replace(T=33, seed=14),
     "quartz_t17": synth.QUARTZ.replace(T=17, seed=6),
     "quartz_t64": synth.QUARTZ.replace(T=64, seed=7),
     "sutra_t3": synth.SUTRA.replace(T=3, seed=8),
