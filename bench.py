@@ -14,8 +14,9 @@ expert weights (moe_quantize_fp8), its step time and expert-GEMM rates.
 Per-kernel durations come from HIP events that the library records on the
 launch stream between its kernels (moe_layer_forward_timed); the dominant
 kernel's roofline is its algorithmic FLOPs per launch over its mean duration.
-The CPU baseline is the float64 oracle timed on a bounded sample of the same
-workload on the host cores.
+The CPU baseline is the float64 oracle timed over the workload's tokens on
+the host cores (worker processes, before the GPU is used). The streaming
+stages are also timed alone from a cold cache through the stage entry points.
 """
 from __future__ import annotations
 
@@ -46,8 +47,8 @@ def parse():
     ap.add_argument("--no-fp8", action="store_true", help="skip timing the fp8-expert layer")
     ap.add_argument("--no-clock", action="store_true",
                     help="do not sample the shader clock with rocm-smi (use under a profiler)")
-    ap.add_argument("--cpu-tokens", type=int, default=1536,
-                    help="tokens of the workload the CPU oracle processes")
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens of the workload the CPU oracle processes (0: all of them)")
     ap.add_argument("--tokens", type=int, default=0,
                     help="override the workload's token count T (e.g. decode-sized batches)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -363,27 +364,152 @@ def traffic_from_profile(kernel_src: str, summary: str = "gate_up_gemm_quartz_co
     return float(t.group(1)) if m.group(1) == cur else None
 
 
-def cpu_baseline(wl, inp, n_tokens):
-    import numpy as np
+# the CPU baseline's worker processes share these (inherited by fork)
+_CPU_JOB = {}
+# worker processes at most: the host share that goes with one GPU
+MAX_CPU_WORKERS = 16
+
+
+def _oracle_shard(tokens):
+    """One worker: the oracle's layer forward for its share of the tokens
+    (routing and dispatch over the whole batch, as capacity needs), one BLAS
+    thread; returns its own wall time."""
     from threadpoolctl import threadpool_limits
 
     import oracle
-    sub = wl.replace(T=min(n_tokens, wl.T))
-    spec = oracle.LayerSpec(hidden=wl.hidden, n_routed=wl.n_routed, top_k=wl.top_k,
-                            n_shared=wl.n_shared, ffn=wl.ffn, rank=wl.rank, score=wl.score,
-                            renorm=bool(wl.renorm), capacity=sub.capacity,
-                            aux_coef=wl.aux_coef, bf16=wl.dtype in ("bf16", "fp8"),
-                            fp8=wl.dtype == "fp8")
-    sinp = dict(inp)
-    sinp["x"] = np.ascontiguousarray(inp["x"][: sub.T])
+    job = _CPU_JOB
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        oracle.layer_forward(sinp["x"], sinp, spec)
+        oracle.layer_forward(job["inp"]["x"], job["inp"], job["spec"], tokens=tokens)
+        return time.perf_counter() - t0
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, inp, n_tokens):
+    """The float64 oracle (the token loop as it stands) over the workload's
+    tokens, split evenly over worker processes, one per usable host core (at
+    most MAX_CPU_WORKERS), each with one BLAS thread. Runs before this process
+    touches the GPU; the workers are forked and never use it."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    import oracle
+    n = wl.T if n_tokens <= 0 else min(n_tokens, wl.T)
+    spec = oracle.LayerSpec(hidden=wl.hidden, n_routed=wl.n_routed, top_k=wl.top_k,
+                            n_shared=wl.n_shared, ffn=wl.ffn, rank=wl.rank, score=wl.score,
+                            renorm=bool(wl.renorm), capacity=wl.capacity,
+                            aux_coef=wl.aux_coef, bf16=wl.dtype in ("bf16", "fp8"),
+                            fp8=wl.dtype == "fp8")
+    _CPU_JOB.update(inp=inp, spec=spec)
+    workers = max(1, min(len(os.sched_getaffinity(0)), MAX_CPU_WORKERS))
+    shards = [a for a in np.array_split(np.arange(n), workers) if len(a)]
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ.setdefault(var, "1")
+    with mp.get_context("fork").Pool(len(shards)) as pool:
+        pool.map(int, range(len(shards)))             # workers up before the clock starts
+        t0 = time.perf_counter()
+        per = pool.map(_oracle_shard, shards)
         dt = time.perf_counter() - t0
-    return {"value": sub.T / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"the first {sub.T} of the {wl.T} tokens as one batch (full layer: routing, "
-                      f"dispatch, every expert output), float64 NumPy, 1 BLAS thread, "
-                      f"{dt:.1f} s wall"}
+    _CPU_JOB.clear()
+    return {"value": n / dt, "unit": "tokens/s", "cores": len(shards), "kind": "oracle",
+            "cpu_model": cpu_model(), "wall_s": dt,
+            "sample": f"{n} of the {wl.T} tokens of the same inputs, split over "
+                      f"{len(shards)} worker processes (one BLAS thread each; routing and "
+                      f"dispatch over all tokens in every worker, y for its share); "
+                      f"float64 NumPy token loop; slowest worker {max(per):.1f} s"}
+
+
+def run_metadata(wl):
+    """What identifies the run: the sources' hash, the git commit when the
+    tree has one, the seeds of the synthetic inputs."""
+    import subprocess
+    h = hashlib.sha256()
+    src_dirs = [os.path.join(ROOT, "fine_grained_mixture_amd", "csrc"), os.path.join(ROOT, "include")]
+    for dname in src_dirs:
+        for name in sorted(os.listdir(dname)):
+            if name.endswith((".hip", ".cpp", ".h")):
+                h.update(name.encode())
+                h.update(open(os.path.join(dname, name), "rb").read())
+    h.update(open(os.path.abspath(__file__), "rb").read())
+    try:
+        sha = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                             text=True, timeout=10).stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        sha = None
+    return {"source_sha256": h.hexdigest(), "git_sha": sha,
+            "input_seed": wl.seed, "upstream_seed": wl.seed + 1000,
+            "date_utc": time.strftime("%Y-%m-%dT%H:%M:%SZ", time.gmtime())}
+
+
+def cold_stages(wl, cfg, x, w, steps, stream):
+    """The streaming stages alone, each call after a 512 MiB write (twice the
+    Infinity Cache) so that their operands come from HBM, through the stage
+    entry points: moe_permute gathering x_perm, and moe_combine. The gather's
+    time is the median of moe_permute with x_perm less the median without it
+    (the rank alone), both cold. Returns medians and HBM rates."""
+    import numpy as np
+    import torch
+
+    from fine_grained_mixture_amd import _lib
+    from fine_grained_mixture_amd.layer import allocate_outputs, allocate_workspace
+
+    T, d, k = wl.T, wl.hidden, wl.top_k
+    dev = x.device
+    out = allocate_outputs(cfg, T, dev)
+    ws = allocate_workspace(cfg, T, dev)
+    _lib.moe_layer_forward(cfg, T, x.data_ptr(), w.struct, out.struct, ws.data_ptr(), ws.numel(),
+                           stream)
+    R = _lib.moe_max_rows(cfg, T)
+    x_perm = torch.empty((max(R, 1), d), dtype=x.dtype, device=dev)
+    torch.cuda.synchronize()
+    rows = int(out["offsets"][-1].item())
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    fill = [0]
+
+    def flush():
+        fill[0] ^= 1
+        flush_buf.fill_(fill[0])
+
+    def permute(xp):
+        return lambda: _lib.moe_permute(cfg, T, x.data_ptr(), out.struct, xp, ws.data_ptr(),
+                                        ws.numel(), stream)
+
+    yr_off, _ = _lib.moe_workspace_region(cfg, T, _lib.MOE_WS_Y_ROUTED)
+    ys_off, ys_n = _lib.moe_workspace_region(cfg, T, _lib.MOE_WS_Y_SHARED)
+    base = ws.data_ptr()
+
+    def combine():
+        _lib.moe_combine(cfg, T, base + yr_off, base + ys_off if ys_n else None, out.struct,
+                         stream)
+
+    b = x.element_size()
+    rank_ms = per_call_ms(permute(None), steps, flush)[1]
+    perm_ms = per_call_ms(permute(x_perm.data_ptr()), steps, flush)[1]
+    comb_ms = per_call_ms(combine, steps, flush)[1]
+    del flush_buf
+    gather_bytes = T * d * b + rows * d * b + 4 * rows
+    combine_bytes = rows * d * 4 + (T * d * 4 if wl.n_shared else 0) + T * d * 4 + 8 * T * k
+    gather_us = max(perm_ms - rank_ms, 1e-6) * 1e3
+    res = {"protocol": "each call after a 512 MiB device write; medians of the calls",
+           "permute_rank_only_us": rank_ms * 1e3, "permute_with_gather_us": perm_ms * 1e3,
+           "gather_us": gather_us, "gather_bytes": gather_bytes,
+           "gather_gbs": gather_bytes / (gather_us * 1e-6) / 1e9,
+           "combine_us": comb_ms * 1e3, "combine_bytes": combine_bytes,
+           "combine_gbs": combine_bytes / (comb_ms * 1e-6) / 1e9}
+    res["gather_frac_of_hbm_peak"] = res["gather_gbs"] / PEAK_HBM_GBS
+    res["combine_frac_of_hbm_peak"] = res["combine_gbs"] / PEAK_HBM_GBS
+    return res
 
 
 def main():
@@ -398,20 +524,24 @@ def main():
     if args.copy_mib > 0:
         copy_calibration(args.copy_mib)
         return
-    # started before anything here uses the GPU
-    sampler = None if args.no_clock else start_clock_sampler()
-    import numpy as np
-    import torch
-
-    from fine_grained_mixture_amd import _lib, synth
-    from fine_grained_mixture_amd.layer import (DeviceWeights, allocate_outputs,
-                                                allocate_workspace, config_from_workload,
-                                                current_stream)
+    from fine_grained_mixture_amd import synth
 
     wl = synth.WORKLOADS[args.workload]
     if args.tokens > 0:
         wl = wl.replace(T=args.tokens)
     inp = synth.make_inputs(wl)
+    # the CPU baseline's forked workers and the clock sampler start before
+    # anything here uses the GPU
+    cpu = None if args.no_cpu else cpu_baseline(wl, inp, args.cpu_tokens)
+    sampler = None if args.no_clock else start_clock_sampler()
+    import numpy as np
+    import torch
+
+    from fine_grained_mixture_amd import _lib
+    from fine_grained_mixture_amd.layer import (DeviceWeights, allocate_outputs,
+                                                allocate_workspace, config_from_workload,
+                                                current_stream)
+
     cfg = config_from_workload(wl)
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if wl.dtype in ("bf16", "fp8") else torch.float32
@@ -483,6 +613,7 @@ def main():
     cold_p = per_call_ms(step, args.steps, flush)
     del flush_buf
     clk = clock_during(step, sampler)
+    cold = cold_stages(wl, cfg, x, w, args.steps, stream)
 
     rows = int(out["offsets"][-1].item())
     alg = algorithmic(wl, rows)
@@ -584,12 +715,14 @@ def main():
         "stage_us_median": stage_us_med,
         "call_ms_p10_p50_p90": warm_p,
         "cold_call_ms_p10_p50_p90": cold_p,
+        "cold_stages": cold,
         "clock": clk,
         "stage_roofline": stage_roof,
         "combine_gbs": alg["combine_bytes"] / (stage_us["combine"] * 1e-6) / 1e9,
         "layer_flops": alg["router_flops"] + alg["gate_up_flops"] + alg["down_flops"]
         + alg["shared_gate_up_flops"] + alg["shared_down_flops"],
         "wall_s_timed_region": wall,
+        "run": run_metadata(wl),
     }
     if wl.score == "sigmoid":
         # loss-free balancing step on this call's counts (the bias is restored)
@@ -640,8 +773,8 @@ def main():
             "expert_gemm_tflops": (gu8 + dn8) / ((st8["gate_up_gemm"] + st8["down_gemm"]) * 1e-6)
             / 1e12,
         }
-    if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_tokens)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result))
 
 

@@ -18,7 +18,11 @@ MOE_F32, MOE_BF16, MOE_FP8 = 0, 1, 2
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_GROUPS_ROUTED, MOE_GROUPS_SHARED = 1, 2
 
-EXPORTED = ("moe_capacity", "moe_max_rows", "moe_workspace_bytes", "moe_route", "moe_permute",
+MOE_WS_H, MOE_WS_H_SHARED, MOE_WS_Y_ROUTED, MOE_WS_Y_SHARED = 0, 1, 2, 3
+MOE_WS_HQ, MOE_WS_HQ_SCALE, MOE_WS_HQ_SHARED, MOE_WS_HQ_SHARED_SCALE = 4, 5, 6, 7
+
+EXPORTED = ("moe_capacity", "moe_max_rows", "moe_workspace_bytes", "moe_workspace_region",
+            "moe_route", "moe_permute",
             "moe_grouped_ffn", "moe_combine", "moe_bias_update", "moe_quantize_fp8",
             "moe_layer_forward",
             "moe_layer_forward_timed", "moe_backward_workspace_bytes", "moe_layer_backward",
@@ -87,6 +91,8 @@ def load():
         "moe_capacity": (c_int32, [c_int64, c_int64, c_int64, c_int32, c_int32]),
         "moe_max_rows": (c_int64, [cfgp, c_int64]),
         "moe_workspace_bytes": (c_size_t, [cfgp, c_int64]),
+        "moe_workspace_region": (c_int, [cfgp, c_int64, c_int32, POINTER(c_size_t),
+                                         POINTER(c_size_t)]),
         "moe_route": (c_int, [cfgp, c_int64, c_void_p, wp, op, c_void_p, c_size_t, c_void_p]),
         "moe_permute": (c_int, [cfgp, c_int64, c_void_p, op, c_void_p, c_void_p, c_size_t,
                                 c_void_p]),
@@ -133,6 +139,14 @@ def moe_max_rows(cfg: MoeConfig, T: int) -> int:
 
 def moe_workspace_bytes(cfg: MoeConfig, T: int) -> int:
     return load().moe_workspace_bytes(ctypes.byref(cfg), T)
+
+
+def moe_workspace_region(cfg: MoeConfig, T: int, which: int) -> tuple[int, int]:
+    """(byte offset into the workspace, bytes) of an intermediate region."""
+    off, n = c_size_t(0), c_size_t(0)
+    _check(load().moe_workspace_region(ctypes.byref(cfg), T, which, ctypes.byref(off),
+                                       ctypes.byref(n)), "moe_workspace_region")
+    return off.value, n.value
 
 
 def moe_route(cfg, T, x, w, o, ws, ws_bytes, stream) -> None:

@@ -28,11 +28,13 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// A legal layer: d and F multiples of 8, 1 <= k <= E <= 4096. Layers that are
+// legal but outside what the kernels cover are told apart by supported_config.
 bool valid_config(const moe_config* c) {
   if (!c) return false;
-  if (c->hidden <= 0 || c->hidden % 64) return false;
-  if (c->ffn <= 0 || c->ffn % 64) return false;
-  if (c->top_k < 1 || c->top_k > 15) return false;
+  if (c->hidden <= 0 || c->hidden % 8) return false;
+  if (c->ffn <= 0 || c->ffn % 8) return false;
+  if (c->top_k < 1) return false;
   if (c->n_routed < c->top_k || c->n_routed > 4096) return false;
   if (c->n_shared < 0 || c->n_shared > 64) return false;
   if (c->rank < 0) return false;
@@ -47,6 +49,9 @@ bool valid_config(const moe_config* c) {
 // What the library's kernels cover beyond valid_config: low-rank experts up to
 // the fused kernel's rank-64 tiles, fp8 rows that fit the quantiser's registers.
 bool supported_config(const moe_config* c) {
+  // the products' tiles: d and F whole 64-column chunks; the top-k keeps at
+  // most 15 selections per token in registers
+  if (c->hidden % 64 || c->ffn % 64 || c->top_k > 15) return false;
   // low-rank experts: bf16 with rank 16, 32, 48 or 64; fp8 factors with rank 64
   if (c->rank != 0 && (c->rank > 64 || c->rank % 16 || c->dtype == MOE_F32 ||
                        (c->dtype == MOE_FP8 && c->rank != 64)))
@@ -1329,6 +1334,30 @@ int moe_quantize_fp8(const moe_config* c, const moe_weights* src, moe_weights* d
     if (e == hipSuccess) e = q(src->sh_down, 1, S * F, d, dst->sh_down, dst->sh_down_scale);
   }
   return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int moe_workspace_region(const moe_config* c, int64_t T, int32_t which, size_t* offset,
+                         size_t* bytes) {
+  if (!valid_config(c) || T < 0 || !offset || !bytes) return MOE_EINVAL;
+  const Layout L = make_layout(c, T);
+  const int64_t d = c->hidden, F = c->ffn, S = c->n_shared;
+  const size_t es = elem_size(c);
+  const bool q = fp8(c) && c->rank == 0;
+  size_t at = 0, n = 0;
+  switch (which) {
+    case MOE_WS_H: at = L.h; n = (size_t)L.R * F * es; break;
+    case MOE_WS_H_SHARED: at = L.h_sh; n = (size_t)T * S * F * es; break;
+    case MOE_WS_Y_ROUTED: at = L.y_perm; n = (size_t)L.R * d * 4; break;
+    case MOE_WS_Y_SHARED: at = L.y_sh; n = S > 0 ? (size_t)T * d * 4 : 0; break;
+    case MOE_WS_HQ: at = L.hq; n = q ? (size_t)L.R * F : 0; break;
+    case MOE_WS_HQ_SCALE: at = L.hs; n = q ? (size_t)L.R * 4 : 0; break;
+    case MOE_WS_HQ_SHARED: at = L.hq_sh; n = fp8(c) ? (size_t)T * S * F : 0; break;
+    case MOE_WS_HQ_SHARED_SCALE: at = L.hs_sh; n = fp8(c) && S > 0 ? (size_t)T * 4 : 0; break;
+    default: return MOE_EINVAL;
+  }
+  *offset = n ? at : 0;
+  *bytes = n;
+  return MOE_OK;
 }
 
 int moe_bias_update(const moe_config* c, int64_t T, const int32_t* counts, float* select_bias,

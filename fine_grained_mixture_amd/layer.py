@@ -41,12 +41,85 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+def expected_weight_shapes(cfg: MoeConfig) -> dict:
+    """name -> (shape, torch dtype) of every weight tensor the layer reads for
+    cfg (the layouts of moe_weights); optional ones (biases) included."""
+    E, d, F, S, r = cfg.n_routed, cfg.hidden, cfg.ffn, cfg.n_shared, cfg.rank
+    act = torch_dtype(cfg)
+    f32, u8 = torch.float32, torch.uint8
+    out = {"w_router": ((d, E), act), "logit_bias": ((E,), f32), "select_bias": ((E,), f32)}
+    fp8 = cfg.dtype == _lib.MOE_FP8
+    if r == 0 and not fp8:
+        out.update(w_gate=((E, d, F), act), w_up=((E, d, F), act), w_down=((E, F, d), act))
+    elif r == 0:
+        out.update(w_gate=((E, F, d), u8), w_up=((E, F, d), u8), w_down=((E, d, F), u8),
+                   w_gate_scale=((E, F), f32), w_up_scale=((E, F), f32),
+                   w_down_scale=((E, d), f32))
+    elif not fp8:
+        out.update(u_gate=((E, d, r), act), s_gate=((E, r), act), v_gate=((E, F, r), act),
+                   u_up=((E, d, r), act), s_up=((E, r), act), v_up=((E, F, r), act),
+                   u_down=((E, F, r), act), s_down=((E, r), act), v_down=((E, d, r), act))
+    else:
+        out.update(u_gate=((E, r, d), u8), u_up=((E, r, d), u8), u_down=((E, r, F), u8),
+                   v_gate=((E, F, r), u8), v_up=((E, F, r), u8), v_down=((E, d, r), u8),
+                   s_gate=((E, r), act), s_up=((E, r), act), s_down=((E, r), act),
+                   u_gate_scale=((E, r), f32), u_up_scale=((E, r), f32),
+                   u_down_scale=((E, r), f32), v_gate_scale=((E, F), f32),
+                   v_up_scale=((E, F), f32), v_down_scale=((E, d), f32))
+    if S and not fp8:
+        out.update(sh_gate=((S, d, F), act), sh_up=((S, d, F), act), sh_down=((S, F, d), act))
+    elif S:
+        out.update(sh_gate=((S, F, d), u8), sh_up=((S, F, d), u8), sh_down=((d, S * F), u8),
+                   sh_gate_scale=((S, F), f32), sh_up_scale=((S, F), f32),
+                   sh_down_scale=((d,), f32))
+    return out
+
+
+def check_device_tensor(t, shape, dtype, name: str) -> None:
+    """Raise unless t is a contiguous CUDA tensor of this shape and dtype."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on a GPU, not {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, not {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _cfg_key(cfg: MoeConfig) -> tuple:
+    return tuple(getattr(cfg, f) for f, _ in MoeConfig._fields_)
+
+
 class DeviceWeights:
     """Weights of one layer in device memory (names as in moe_weights)."""
 
     def __init__(self, tensors: dict):
         self.t = tensors
         self.struct = MoeWeights(**{n: _ptr(tensors.get(n)) for n in _lib.WEIGHT_FIELDS})
+        self._checked = None
+
+    def check(self, cfg: MoeConfig) -> None:
+        """Raise unless every tensor the layer reads for cfg is present with its
+        shape, dtype and layout (once per configuration)."""
+        key = _cfg_key(cfg)
+        if self._checked == key:
+            return
+        want = expected_weight_shapes(cfg)
+        for n, t in self.t.items():
+            if t is None:
+                continue
+            if n not in want:
+                raise ValueError(f"weight {n} is not read by this configuration")
+            check_device_tensor(t, *want[n], name=n)
+        for n in want:
+            if n not in ("logit_bias", "select_bias") and self.t.get(n) is None:
+                raise ValueError(f"weight {n} is missing")
+        if cfg.score == _lib.MOE_SOFTMAX and self.t.get("select_bias") is not None:
+            raise ValueError("select_bias only applies to the sigmoid rule")
+        self._checked = key
 
     @classmethod
     def from_numpy(cls, inputs: dict, cfg: MoeConfig, device="cuda") -> "DeviceWeights":
@@ -153,35 +226,85 @@ def current_stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+def check_x(cfg: MoeConfig, x: torch.Tensor) -> int:
+    """Raise unless x is a contiguous [T, d] CUDA tensor of the layer's
+    activation type; returns T."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-d [T, d] tensor")
+    check_device_tensor(x, (x.shape[0], cfg.hidden), torch_dtype(cfg), "x")
+    return x.shape[0]
+
+
+def check_workspace(cfg: MoeConfig, T: int, ws: torch.Tensor) -> None:
+    need = _lib.moe_workspace_bytes(cfg, T)
+    check_device_tensor(ws, (ws.numel(),), torch.uint8, "ws")
+    if ws.numel() < need:
+        raise ValueError(f"ws holds {ws.numel()} bytes, the layer needs {need}")
+
+
 def layer_forward(cfg: MoeConfig, x: torch.Tensor, w: DeviceWeights, out: Outputs | None = None,
                   ws: torch.Tensor | None = None) -> Outputs:
-    T = x.shape[0]
+    T = check_x(cfg, x)
+    w.check(cfg)
     out = out or allocate_outputs(cfg, T, x.device)
     ws = ws if ws is not None else allocate_workspace(cfg, T, x.device)
+    check_workspace(cfg, T, ws)
     _lib.moe_layer_forward(cfg, T, x.data_ptr(), w.struct, out.struct, ws.data_ptr(),
                            ws.numel(), current_stream())
     return out
 
 
 def route(cfg, x, w, out, ws):
-    _lib.moe_route(cfg, x.shape[0], x.data_ptr(), w.struct, out.struct, ws.data_ptr(),
+    T = check_x(cfg, x)
+    w.check(cfg)
+    check_workspace(cfg, T, ws)
+    _lib.moe_route(cfg, T, x.data_ptr(), w.struct, out.struct, ws.data_ptr(),
                    ws.numel(), current_stream())
 
 
 def permute(cfg, x, out, ws, x_perm=None):
-    _lib.moe_permute(cfg, x.shape[0], x.data_ptr(), out.struct,
+    T = check_x(cfg, x)
+    check_workspace(cfg, T, ws)
+    if x_perm is not None:
+        _check_rows(cfg, T, x_perm, torch_dtype(cfg), "x_perm")
+    _lib.moe_permute(cfg, T, x.data_ptr(), out.struct,
                      None if x_perm is None else x_perm.data_ptr(), ws.data_ptr(), ws.numel(),
                      current_stream())
 
 
+def _check_rows(cfg, T, t, dtype, name):
+    """A [>= R_max, d] row buffer (routed rows)."""
+    R = _lib.moe_max_rows(cfg, T)
+    if not isinstance(t, torch.Tensor) or t.dim() != 2 or t.shape[0] < R:
+        raise ValueError(f"{name} must be a [R_max = {R}, d] tensor")
+    check_device_tensor(t, (t.shape[0], cfg.hidden), dtype, name)
+
+
 def grouped_ffn(cfg, T, groups, w, ws, *, x_perm=None, offsets=None, x_shared=None,
                 y_routed=None, y_shared=None):
+    w.check(cfg)
+    check_workspace(cfg, T, ws)
+    act = torch_dtype(cfg)
+    if x_perm is not None:
+        _check_rows(cfg, T, x_perm, act, "x_perm")
+    if y_routed is not None:
+        _check_rows(cfg, T, y_routed, torch.float32, "y_routed")
+    if offsets is not None:
+        check_device_tensor(offsets, (cfg.n_routed + 1,), torch.int32, "offsets")
+    if x_shared is not None:
+        check_device_tensor(x_shared, (T, cfg.hidden), act, "x_shared")
+    if y_shared is not None:
+        check_device_tensor(y_shared, (T, cfg.hidden), torch.float32, "y_shared")
     _lib.moe_grouped_ffn(cfg, T, groups, _ptr(x_perm), _ptr(offsets), _ptr(x_shared),
                          w.struct, _ptr(y_routed), _ptr(y_shared), ws.data_ptr(), ws.numel(),
                          current_stream())
 
 
 def combine(cfg, T, y_routed, y_shared, out):
+    if y_routed is not None:
+        _check_rows(cfg, T, y_routed, torch.float32, "y_routed")
+    if y_shared is not None:
+        check_device_tensor(y_shared, (T, cfg.hidden), torch.float32, "y_shared")
     _lib.moe_combine(cfg, T, _ptr(y_routed), _ptr(y_shared), out.struct, current_stream())
 
 
@@ -226,7 +349,8 @@ def layer_backward(cfg: MoeConfig, x: torch.Tensor, w: DeviceWeights, out: Outpu
                    ws: torch.Tensor, dy: torch.Tensor, aux_grad: float = 0.0,
                    grads: Grads | None = None, bws: torch.Tensor | None = None) -> Grads:
     """Gradients of sum(dy * y) + aux_grad * aux after layer_forward(cfg, x, w, out, ws)."""
-    T = x.shape[0]
+    T = check_x(cfg, x)
+    w.check(cfg)
     if dy.dtype != torch.float32 or tuple(dy.shape) != (T, cfg.hidden) or not dy.is_contiguous():
         raise TypeError("dy must be a contiguous float32 [T, d] tensor")
     grads = grads or allocate_grads(cfg, T, x.device)

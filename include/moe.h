@@ -34,12 +34,14 @@
  *     (except MOE_EHIP, reported when a launch itself fails).
  *   - Calls that share a workspace on different streams race; calls on one
  *     stream are ordered.
- *   - Limits of this library: 1 <= k <= 15, k <= E <= 4096; d and F multiples of
- *     64; T*k < 2^31; rank is 0, or 16, 32, 48 or 64 with bf16, or 64 with
- *     fp8 (low-rank float32 experts are MOE_EUNSUPPORTED); sigmoid scoring
- *     requires renorm_topk == 1;
- *     MOE_FP8 runs in moe_layer_forward and moe_grouped_ffn, with d, F and
- *     S*F at most 4096.
+ *   - A legal layer (else MOE_EINVAL): 1 <= k <= E <= 4096; d and F positive
+ *     multiples of 8; 0 <= S <= 64; T*k < 2^31; sigmoid scoring requires
+ *     renorm_topk == 1.
+ *   - Legal layers outside this library's kernels return MOE_EUNSUPPORTED:
+ *     k > 15; d or F not a multiple of 64; rank other than 0, 16, 32, 48 or 64
+ *     with bf16, or 64 with fp8 (low-rank float32 experts are unsupported);
+ *     MOE_FP8 with d, F or S*F above 4096. MOE_FP8 runs in moe_layer_forward
+ *     and moe_grouped_ffn.
  */
 #ifndef FGM_MOE_H
 #define FGM_MOE_H
@@ -68,11 +70,11 @@ typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score;  /* router scoring 
 enum { MOE_GROUPS_ROUTED = 1, MOE_GROUPS_SHARED = 2 };
 
 typedef struct {
-  int32_t hidden;       /* d, multiple of 64                                       */
+  int32_t hidden;       /* d, multiple of 8 (this library: of 64)                  */
   int32_t n_routed;     /* E, routed experts                                       */
   int32_t top_k;        /* k, active routed experts per token                      */
   int32_t n_shared;     /* S, always-on ungated shared experts (0 allowed)         */
-  int32_t ffn;          /* F, width of every expert, multiple of 64                */
+  int32_t ffn;          /* F, width of every expert, multiple of 8 (library: 64)   */
   int32_t rank;         /* 0: dense experts; r > 0: U diag(s) V^T factors of rank r */
   int32_t score;        /* moe_score                                               */
   int32_t renorm_topk;  /* softmax: 1 = gates divided by their top-k sum, 0 = raw
@@ -171,8 +173,36 @@ int64_t moe_max_rows(const moe_config *cfg, int64_t T);
    workspace serves all of them). 0 if cfg is invalid. */
 size_t moe_workspace_bytes(const moe_config *cfg, int64_t T);
 
+/* Intermediates of the expert FFN that moe_layer_forward and moe_grouped_ffn
+   leave in ws, for inspection after the call (parity checks, debugging); valid
+   until the next call on the same ws. moe_workspace_region gives the byte
+   offset into ws and the size of region `which` for this config and T; a size
+   of 0 means the config has no such region. Returns MOE_EINVAL for an invalid
+   config, T < 0, NULL outputs or an unknown region.
+     MOE_WS_H                h [R_max, F] in cfg.dtype's activation type
+                             (bf16 for MOE_FP8): SiLU(a) * b of each dispatched
+                             row, rounded, before the down projection
+     MOE_WS_H_SHARED         [T, S*F]: the same for the shared experts
+     MOE_WS_Y_ROUTED         [R_max, d] float32: each dispatched row's expert output
+     MOE_WS_Y_SHARED         [T, d] float32: the shared experts' summed output
+     MOE_WS_HQ, _HQ_SCALE    MOE_FP8 dense experts: E4M3 codes of h [R_max, F] and
+                             each row's float32 power-of-two scale [R_max]
+     MOE_WS_HQ_SHARED, _HQ_SHARED_SCALE   MOE_FP8: codes [T, S*F], scales [T]
+   Rows at and beyond offsets[E] of the routed regions hold no data.          */
+enum {
+  MOE_WS_H = 0, MOE_WS_H_SHARED = 1, MOE_WS_Y_ROUTED = 2, MOE_WS_Y_SHARED = 3,
+  MOE_WS_HQ = 4, MOE_WS_HQ_SCALE = 5, MOE_WS_HQ_SHARED = 6, MOE_WS_HQ_SHARED_SCALE = 7
+};
+int moe_workspace_region(const moe_config *cfg, int64_t T, int32_t which, size_t *offset,
+                         size_t *bytes);
+
 /* Router projection, scores, top-k, gates, per-expert histogram, capacity,
-   prefix sum and aux statistic.
+   prefix sum and aux statistic (steps: a learned router picks the top k of E
+   routed experts per token -- Vertex AGI research page "Architecture", Quartz
+   model card "Architecture" table, Moonfrost MoE card; sigmoid scores with a
+   selection-only balancing bias -- Sutra-1.3B "48 + 1 experts" card; the
+   0.01-weighted load-balancing statistic -- research page "Architecture";
+   capacity, 0 = dropless -- Moonfrost stacking card, dormouse terminal block).
    In:  x [T,d] device; w->w_router, w->logit_bias, w->select_bias.
    Out: o->topk_idx, topk_gate, (topk_margin), counts, kept, offsets, n_dropped,
         aux, (f), (P); per-block tables kept in ws for moe_permute.           */
@@ -180,14 +210,20 @@ int moe_route(const moe_config *cfg, int64_t T, const void *x, const moe_weights
               moe_outputs *o, void *ws, size_t ws_bytes, void *stream);
 
 /* Token permutation: each kept slot's row in token order per expert, drops,
-   and optionally the gathered rows x_perm[row] = x[sorted_token[row]].
+   and optionally the gathered rows x_perm[row] = x[sorted_token[row]]
+   (grouping the tokens by expert so that each expert runs once over its rows:
+   Moonfrost stacking card, stacked (E, hidden, ffn) expert tensors with
+   capacity-based routing; capacity queues in token order).
    Must follow moe_route with the same cfg, T, outputs and ws on the same stream.
    In:  x [T,d] device (read only if x_perm != NULL).
    Out: o->row_of_slot, sorted_token, (dropped); x_perm [R_max, d] cfg.dtype or NULL. */
 int moe_permute(const moe_config *cfg, int64_t T, const void *x, moe_outputs *o,
                 void *x_perm, void *ws, size_t ws_bytes, void *stream);
 
-/* Grouped SwiGLU expert FFN.
+/* Grouped SwiGLU expert FFN (the experts' gated feed-forward blocks over the
+   stacked expert tensors -- Moonfrost stacking card; two always-on shared
+   experts -- research page "Architecture"; rank-64 U diag(s) V^T experts --
+   dormouse "TSCT low-rank experts" card).
    groups & MOE_GROUPS_ROUTED: for every routed expert e, the rows
      x_perm[offsets[e] : offsets[e+1]] of x_or_xperm ([R_max, d]) go through
      expert e; result rows written to y_routed [R_max, d] float32 (rows at and
@@ -200,7 +236,10 @@ int moe_grouped_ffn(const moe_config *cfg, int64_t T, int32_t groups,
                     const moe_weights *w, float *y_routed, float *y_shared,
                     void *ws, size_t ws_bytes, void *stream);
 
-/* Gate-weighted combine: y[t] = y_shared[t] + sum_{j kept, ascending j}
+/* Gate-weighted combine (each token's output is its shared experts' sum plus
+   its routed experts' outputs weighted by their gates -- research page
+   "Architecture", Moonfrost MoE card; dropped slots add nothing -- Moonfrost
+   stacking card): y[t] = y_shared[t] + sum_{j kept, ascending j}
    topk_gate[t,j] * y_routed[row_of_slot[t,j]], in float32 in that order.
    y_shared may be NULL (S == 0). Writes o->y and (o->y_lowp).               */
 int moe_combine(const moe_config *cfg, int64_t T, const float *y_routed,
@@ -236,7 +275,13 @@ int moe_bias_update(const moe_config *cfg, int64_t T, const int32_t *counts,
                     float *select_bias, float gamma, void *stream);
 
 /* The whole layer forward (route, permute, grouped FFN for routed and shared
-   experts, combine). Intermediates live in ws; fills every output of o.     */
+   experts, combine), as defined at the top of this file from the research
+   page "Architecture" section, the Quartz model card "Architecture" table,
+   the Moonfrost MoE and stacking cards, the Sutra-1.3B "48 + 1 experts" card
+   and the dormouse "dropless MoE" and "TSCT low-rank experts" cards.
+   In: x [T, d] device (cfg.dtype; bf16 for MOE_FP8); w as above. Out: every
+   output of o (optional ones when non-NULL). Intermediates live in ws
+   (moe_workspace_bytes, 256-byte aligned); errors as for every entry point. */
 int moe_layer_forward(const moe_config *cfg, int64_t T, const void *x,
                       const moe_weights *w, moe_outputs *o, void *ws, size_t ws_bytes,
                       void *stream);

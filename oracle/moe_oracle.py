@@ -321,10 +321,12 @@ def swiglu_fp8(xrow, w_gate, w_up, w_down, rho, with_max=False):
     """SwiGLU with fp8 products: the row entering each product is quantised
     (x over d, h = rho(SiLU(a) b) over F); the weights come quantised. With
     ``with_max`` also returns, per output column, the largest magnitude of one
-    term of the down product (the error scale of a quantised h entry)."""
-    xq = fp8_quantize(xrow, axis=0)[0]
+    term of the down product (the error scale of a quantised h entry).
+    ``xrow`` may also be a matrix of rows (each quantised on its own; not with
+    ``with_max``)."""
+    xq = fp8_quantize(xrow, axis=-1)[0]
     h = rho(silu(xq @ w_gate) * (xq @ w_up))
-    hq = fp8_quantize(h, axis=0)[0]
+    hq = fp8_quantize(h, axis=-1)[0]
     y = hq @ w_down
     if not with_max:
         return y
@@ -388,17 +390,19 @@ class Experts:
         return lowrank_swiglu(xrow, f, self.rho)
 
     def shared(self, xrow, with_max=False):
+        """Sum of the shared experts on one token row (or on a matrix of rows,
+        without ``with_max``)."""
         if self.spec.fp8:
             # h of every shared expert, quantised as one row of S F values
-            xq = fp8_quantize(xrow, axis=0)[0]
+            xq = fp8_quantize(xrow, axis=-1)[0]
             h = np.concatenate([self.rho(silu(xq @ self.sh[0][s]) * (xq @ self.sh[1][s]))
-                                for s in range(self.S)])
-            hq = fp8_quantize(h, axis=0)[0]
+                                for s in range(self.S)], axis=-1)
+            hq = fp8_quantize(h, axis=-1)[0]
             y = hq @ self.sh_down
             if not with_max:
                 return y
             return y, (np.abs(hq)[:, None] * np.abs(self.sh_down)).max(axis=0)
-        out = np.zeros(self.spec.hidden)
+        out = np.zeros(np.shape(xrow)[:-1] + (self.spec.hidden,))
         for s in range(self.S):
             out = out + swiglu(xrow, self.sh[0][s], self.sh[1][s], self.sh[2][s], self.rho)
         return out
@@ -515,6 +519,39 @@ def layer_forward(x, weights: dict, spec: LayerSpec, tokens=None,
     out["y"] = y
     if want_max:
         out["M_y"] = m_y
+    return out
+
+
+def layer_forward_batched(x, weights: dict, spec: LayerSpec, override_idx=None,
+                          override_mask=None):
+    """The same layer as layer_forward (same readings, same rounding points,
+    the same order of the per-token sum: shared experts in ascending order,
+    then the kept slots in list order), with every expert evaluated once over
+    all of its rows with matrix products instead of token by token. For
+    full-size checks; routing, dispatch and the aux statistic are
+    layer_forward's own. y [T, d] covers every token."""
+    x = np.asarray(x)
+    T = x.shape[0]
+    out = layer_forward(x, weights, spec, tokens=[], override_idx=override_idx,
+                        override_mask=override_mask)
+    x64 = np.asarray(x, np.float64)
+    ex = Experts(weights, spec)
+    k, d = spec.top_k, spec.hidden
+    idx, gates, rows = out["idx"], out["gates"], out["row_of_slot"]
+    y = np.zeros((T, d))
+    if spec.n_shared > 0 and T > 0:
+        y = y + ex.shared(x64)
+    # one output row per kept (token, slot), every expert over its own rows
+    o = np.zeros((T, k, d))
+    for e in range(spec.n_routed):
+        ts, js = np.nonzero((idx == e) & (rows >= 0))
+        if len(ts):
+            o[ts, js] = ex.routed(x64[ts], e)
+    for j in range(k):
+        kept = rows[:, j] >= 0
+        y[kept] = y[kept] + gates[kept, j, None] * o[kept, j]
+    out["tokens"] = np.arange(T)
+    out["y"] = y
     return out
 
 

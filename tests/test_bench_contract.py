@@ -50,3 +50,17 @@ def test_multi_gpu_run_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_run_metadata_and_cpu_baseline_protocol():
+    """The record names its sources and seeds; the CPU baseline states its
+    workers, CPU model and the tokens it covered (a tiny workload here)."""
+    from fine_grained_mixture_amd import synth
+    wl = synth.TINY
+    meta = bench.run_metadata(wl)
+    assert len(meta["source_sha256"]) == 64 and meta["input_seed"] == wl.seed
+    inp = synth.make_inputs(wl)
+    r = bench.cpu_baseline(wl, inp, 0)
+    assert r["kind"] == "oracle" and r["unit"] == "tokens/s" and r["value"] > 0
+    assert 1 <= r["cores"] <= min(len(os.sched_getaffinity(0)), bench.MAX_CPU_WORKERS)
+    assert r["cpu_model"] and f"{wl.T} of the {wl.T} tokens" in r["sample"]

@@ -82,7 +82,7 @@ def _cfg(**kw):
 
 
 @pytest.mark.parametrize("bad", [
-    dict(hidden=100), dict(ffn=48), dict(top_k=0), dict(top_k=9), dict(top_k=16, n_routed=32),
+    dict(hidden=100), dict(ffn=44), dict(top_k=0), dict(top_k=9), dict(top_k=33, n_routed=32),
     dict(n_routed=5000), dict(score="sigmoid", renorm=False), dict(capacity=-1),
     dict(n_shared=-1),
 ])
@@ -94,6 +94,56 @@ def test_invalid_config_rejected(lib, bad):
     st = lib.moe_layer_forward(ctypes.byref(cfg), 64, 0x1000, ctypes.byref(w), ctypes.byref(o),
                                0x1000, 1 << 30, None)
     assert st == _lib.MOE_EINVAL
+
+
+@pytest.mark.parametrize("legal", [
+    dict(hidden=104), dict(ffn=48), dict(hidden=136, ffn=200), dict(top_k=16, n_routed=32),
+    dict(top_k=32, n_routed=32),
+])
+def test_legal_but_unimplemented_layer_is_unsupported(lib, legal):
+    """Layers the layer's definition allows (d, F multiples of 8; k <= E) but
+    the kernels do not cover: MOE_EUNSUPPORTED, before any launch; their
+    sizes are still reported."""
+    cfg = _cfg(**legal)
+    assert _lib.moe_workspace_bytes(cfg, 64) > 0
+    assert _lib.moe_max_rows(cfg, 64) == 64 * cfg.top_k
+    w = _lib.MoeWeights(**{n: 0x1000 for n in _lib.WEIGHT_FIELDS if n != "select_bias"})
+    o = _lib.MoeOutputs(**{n: 0x1000 for n in _lib.OUTPUT_FIELDS})
+    st = lib.moe_layer_forward(ctypes.byref(cfg), 64, 0x1000, ctypes.byref(w), ctypes.byref(o),
+                               0x1000, 1 << 30, None)
+    assert st == _lib.MOE_EUNSUPPORTED
+    st = lib.moe_route(ctypes.byref(cfg), 64, 0x1000, ctypes.byref(w), ctypes.byref(o), 0x1000,
+                       1 << 30, None)
+    assert st == _lib.MOE_EUNSUPPORTED
+
+
+def test_workspace_regions(lib):
+    """Intermediate regions lie inside the workspace, do not overlap, and have
+    the documented sizes; fp8-only regions are empty otherwise."""
+    from fine_grained_mixture_amd.layer import config_from_workload
+    for wl in list(WORKLOADS.values()) + [WORKLOADS["quartz"].replace(dtype="fp8")]:
+        cfg = config_from_workload(wl)
+        T, R = wl.T, _lib.moe_max_rows(cfg, wl.T)
+        total = _lib.moe_workspace_bytes(cfg, T)
+        es = 2 if wl.dtype in ("bf16", "fp8") else 4
+        S, F, d = wl.n_shared, wl.ffn, wl.hidden
+        q = wl.dtype == "fp8" and wl.rank == 0
+        want = {_lib.MOE_WS_H: R * F * es, _lib.MOE_WS_H_SHARED: T * S * F * es,
+                _lib.MOE_WS_Y_ROUTED: R * d * 4, _lib.MOE_WS_Y_SHARED: T * d * 4 * (S > 0),
+                _lib.MOE_WS_HQ: R * F * q, _lib.MOE_WS_HQ_SCALE: R * 4 * q,
+                _lib.MOE_WS_HQ_SHARED: T * S * F * (wl.dtype == "fp8"),
+                _lib.MOE_WS_HQ_SHARED_SCALE: T * 4 * (wl.dtype == "fp8" and S > 0)}
+        spans = []
+        for which, n in want.items():
+            off, got = _lib.moe_workspace_region(cfg, T, which)
+            assert got == n, (wl.name, which)
+            assert off % 256 == 0 and off + got <= total
+            if got:
+                spans.append((off, off + got))
+        spans.sort()
+        assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+    with pytest.raises(_lib.MoeError):
+        _lib.moe_workspace_region(_cfg(), 64, 99)
 
 
 @pytest.mark.parametrize("rank,dtype", [(8, "bf16"), (40, "bf16"), (80, "bf16"), (128, "bf16"),
@@ -213,3 +263,33 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libmoe.so"))
     with pytest.raises(RuntimeError, match="is missing"):
         _lib.load()
+
+
+def test_binding_rejects_wrong_tensors():
+    """The Python binding checks dtype, shape, device and layout of x and the
+    weights before passing their addresses on (no GPU: CPU tensors are
+    rejected as such, CUDA-less shape and dtype checks run first)."""
+    import torch
+    from fine_grained_mixture_amd import layer as L
+    cfg = _cfg()
+    x = torch.zeros((4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        L.check_x(cfg, x)
+    with pytest.raises(ValueError, match="2-d"):
+        L.check_x(cfg, torch.zeros(128, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        L.check_device_tensor(torch.zeros((4, 64)), (4, 128), torch.float32, "x")
+    want = L.expected_weight_shapes(cfg)
+    assert want["w_gate"] == ((8, 128, 64), torch.bfloat16)
+    assert want["sh_down"] == ((1, 64, 128), torch.bfloat16)
+    w8 = L.expected_weight_shapes(L.make_config(128, 8, 2, 2, 64, dtype="fp8"))
+    assert w8["w_gate"] == ((8, 64, 128), torch.uint8) and w8["sh_down"] == ((128, 128), torch.uint8)
+    lr = L.expected_weight_shapes(L.make_config(128, 8, 2, 0, 64, rank=16))
+    assert lr["u_down"] == ((8, 64, 16), torch.bfloat16) and "w_gate" not in lr
+    # a weight set missing a matrix, or holding one the config does not read
+    w = L.DeviceWeights({})
+    with pytest.raises(ValueError, match="missing"):
+        w.check(cfg)
+    w = L.DeviceWeights({"u_gate": torch.zeros(1)})
+    with pytest.raises(ValueError, match="not read"):
+        w.check(cfg)

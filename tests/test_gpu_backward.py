@@ -48,7 +48,7 @@ def _check(wl, *, aux_grad=1.0, zero_dy=False, saved=False):
     inp = synth.make_inputs(wl)
     dy = np.zeros((wl.T, wl.hidden), np.float32) if zero_dy else synth.make_upstream(wl)
     fwd, g = _gpu_fwd_bwd(wl, inp, dy, aux_grad, saved)
-    P.check_parity(wl, inp, fwd, tokens=[], check_y=False)
+    P.check_parity(wl, inp, fwd, check_y=False)
     spec = P.spec_of(wl)
     gi = fwd["topk_idx"].astype(np.int64)
     ref_f = oracle.layer_forward(inp["x"], inp, spec, tokens=[], override_idx=gi,
@@ -208,7 +208,7 @@ def test_full_size_backward(name):
     inp = synth.make_inputs(wl)
     dy = synth.make_upstream(wl)
     fwd, g = _gpu_fwd_bwd(wl, inp, dy, 1.0, saved)
-    P.check_parity(wl, inp, fwd, tokens=[], check_y=False)
+    P.check_parity(wl, inp, fwd, check_y=False)
     spec = P.spec_of(wl)
     gi = fwd["topk_idx"].astype(np.int64)
     ref_f = oracle.layer_forward(inp["x"], inp, spec, tokens=[], override_idx=gi,

@@ -121,6 +121,59 @@ def test_oracle_equals_bruteforce(case, bf16):
         assert abs(out["margin"][t] - (srt[k - 1] - srt[k])) < 1e-15
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_batched_forward_equals_bruteforce(case, bf16):
+    """The per-expert batched forward (the full-size checks' oracle) against
+    the brute-force evaluation of every expert on every token."""
+    T, d, E, k, S, F, kw = CASES[case]
+    rank = kw.get("rank", 0)
+    w = _inputs(T, d, E, k, S, F, seed=10 + case, rank=rank, score=kw["score"],
+                bf16=bf16, logit_std=0.7, select_std=0.2 if kw["score"] == "sigmoid" else 0)
+    spec = _spec(d, E, k, S, F, bf16=bf16, **kw)
+    out = oracle.layer_forward_batched(w["x"], w, spec)
+    bf = _brute.layer_bruteforce(w["x"], w, E=E, k=k, S=S, F=F, d=d, bf16=bf16,
+                                 score=kw["score"], renorm=kw["renorm"],
+                                 capacity=kw.get("capacity", 0), rank=rank)
+    assert out["y"].shape == (T, d)
+    assert _rel(out["y"], bf["y"]) < 1e-12
+
+
+BATCHED_CASES = [
+    # T, d, E, k, S, F, workload extras
+    (40, 24, 8, 3, 2, 16, dict(logit_std=0.5)),
+    (33, 16, 6, 2, 0, 8, dict(score="sigmoid", select_std=0.2)),
+    (50, 16, 5, 2, 1, 8, dict(logit_std=1.0, capacity=7)),
+    (30, 32, 6, 2, 1, 32, dict(rank=16)),
+    (24, 32, 4, 2, 2, 16, dict(fp8=True)),
+    (20, 64, 4, 2, 1, 64, dict(fp8=True, rank=64)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BATCHED_CASES)))
+def test_batched_forward_equals_token_loop(case):
+    """The batched forward gives the token loop's y on every token (bf16
+    rounding points, capacity drops, low-rank and fp8 experts), with a forced
+    selection too."""
+    T, d, E, k, S, F, kw = BATCHED_CASES[case]
+    kw = dict(kw)
+    score, cap = kw.pop("score", "softmax"), kw.pop("capacity", 0)
+    fp8, rank = kw.pop("fp8", False), kw.pop("rank", 0)
+    w = _inputs(T, d, E, k, S, F, seed=70 + case, rank=rank, score=score, bf16=True, **kw)
+    spec = _spec(d, E, k, S, F, score=score, capacity=cap, rank=rank, bf16=True, fp8=fp8)
+    a = oracle.layer_forward(w["x"], w, spec)
+    b = oracle.layer_forward_batched(w["x"], w, spec)
+    assert _rel(b["y"], a["y"]) < 1e-12
+    for n in ("idx", "gates", "row_of_slot", "counts", "offsets", "sorted_token"):
+        np.testing.assert_array_equal(b[n], a[n], err_msg=n)
+    # forced selection of a third of the tokens
+    mask = np.arange(T) % 3 == 0
+    forced = np.tile(np.arange(E - k, E)[::-1], (T, 1))
+    a = oracle.layer_forward(w["x"], w, spec, override_idx=forced, override_mask=mask)
+    b = oracle.layer_forward_batched(w["x"], w, spec, override_idx=forced, override_mask=mask)
+    assert _rel(b["y"], a["y"]) < 1e-12
+
+
 # ---------------------------------------------------------------- closed forms
 @pytest.mark.parametrize("score,renorm", [("softmax", True), ("softmax", False),
                                           ("sigmoid", True)])
@@ -674,11 +727,18 @@ def test_fp8_quantize_error_and_exact_cases():
     np.testing.assert_array_equal(oracle.fp8_quantize(g, axis=0)[0], g)
 
 
-def test_fp8_layer_reduces_to_quantised_h_on_grid_inputs():
+@pytest.mark.parametrize("S", [1, 2])
+def test_fp8_layer_reduces_to_quantised_h_on_grid_inputs(S):
     """With x rows and weight columns already on their E4M3 grids (scales
     preserved), the fp8 layer is the bf16 layer with h quantised; h's
-    quantisation here goes through torch's float8_e4m3fn."""
-    T, d, E, k, S, F = 6, 32, 4, 2, 1, 16
+    quantisation here goes through torch's float8_e4m3fn. With two shared
+    experts the second one's h is made about 2^16 times larger than the
+    first's, so under the shared h row's one joint scale (the S experts form
+    one product over their stacked S F rows) the first expert's h falls into
+    E4M3's subnormal range, far coarser than under a scale of its own: the
+    check tells the two readings apart (E4M3 is a floating-point grid, so a
+    smaller ratio would leave the first expert's codes unchanged)."""
+    T, d, E, k, F = 6, 32, 4, 2, 16
     rng = np.random.default_rng(3)
     grid = np.array(sorted({abs(v) for v, _ in _e4m3_codes()}))
     def ongrid(shape, sc):
@@ -691,6 +751,11 @@ def test_fp8_layer_reduces_to_quantised_h_on_grid_inputs():
         a = ongrid(w[n].shape, -9)
         a[..., 0, :] = 448.0 * 2.0 ** -9  # every column's scale is 2^-9
         w[n] = a
+    if S == 2:
+        # the second shared expert's gate and up columns 2^8 larger (scale
+        # 2^-1, still on their grids): its h is ~2^16 times the first's
+        w["sh_gate"][1] *= 256.0
+        w["sh_up"][1] *= 256.0
     w["x"] = x
     spec8 = _spec(d, E, k, S, F, bf16=True, fp8=True)
     got = oracle.layer_forward(x, w, spec8)
@@ -701,15 +766,24 @@ def test_fp8_layer_reduces_to_quantised_h_on_grid_inputs():
         t = torch.tensor(np.ldexp(h, -s), dtype=torch.float32).to(torch.float8_e4m3fn)
         return np.ldexp(t.to(torch.float64).numpy(), s)
     y = np.zeros((T, d))
+    y_apart = np.zeros((T, d))         # the other reading: one scale per shared expert
     for t in range(T):
-        hs = np.concatenate([rho(oracle.silu(x[t] @ w["sh_gate"][s_]) * (x[t] @ w["sh_up"][s_]))
-                             for s_ in range(S)])
-        y[t] = q_torch(hs) @ w["sh_down"].reshape(S * F, d)
+        hs = [rho(oracle.silu(x[t] @ w["sh_gate"][s_]) * (x[t] @ w["sh_up"][s_]))
+              for s_ in range(S)]
+        y[t] = q_torch(np.concatenate(hs)) @ w["sh_down"].reshape(S * F, d)
+        y_apart[t] = np.concatenate([q_torch(h) for h in hs]) @ w["sh_down"].reshape(S * F, d)
         for j in range(k):
             e = int(ref["idx"][t, j])
             h = rho(oracle.silu(x[t] @ w["w_gate"][e]) * (x[t] @ w["w_up"][e]))
-            y[t] += ref["gates"][t, j] * (q_torch(h) @ w["w_down"][e])
+            yr = ref["gates"][t, j] * (q_torch(h) @ w["w_down"][e])
+            y[t] += yr
+            y_apart[t] += yr
     np.testing.assert_allclose(got["y"], y, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(oracle.layer_forward_batched(x, w, spec8)["y"], y,
+                               rtol=1e-12, atol=1e-12)
+    if S == 2:
+        # the readings differ by far more than the tolerance of the check above
+        assert np.max(np.abs(y_apart - y)) > 1e6 * 1e-12 * np.max(np.abs(y))
 
 
 def test_fp8_term_maxima_bound_the_output():

@@ -1,0 +1,83 @@
+"""The fp8 parity chain of tests/_parity.py on the CPU: fed the oracle's own
+intermediates it passes, and each kind of planted mistake (a code that is not
+the quantised h, an h entry outside its window, a y element off the codes'
+product) makes it fail. The mistakes are planted in copies of the oracle's
+values; nothing here runs on a GPU.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from fine_grained_mixture_amd import synth
+from tests import _parity as P
+
+
+def _oracle_as_gpu(wl):
+    """Outputs shaped like run_gpu's, with the workspace intermediates the
+    oracle itself forms (h, its codes and row scales)."""
+    inp = synth.make_inputs(wl)
+    spec = P.spec_of(wl)
+    ref = oracle.layer_forward_batched(inp["x"], inp, spec)
+    x = np.asarray(inp["x"], np.float64)
+    ex = oracle.Experts(inp, spec)
+    rho = oracle.round_bf16
+    xq = oracle.fp8_quantize(x, axis=-1)[0]
+
+    def h_of(X, wg, wu):
+        return rho(oracle.silu(X @ wg) * (X @ wu))
+
+    def codes(h):
+        q, s = oracle.fp8_quantize(h, axis=-1)
+        return np.ldexp(q, -s[:, None]), np.ldexp(1.0, s)
+
+    T, R, F, S = wl.T, int(ref["offsets"][-1]), wl.ffn, wl.n_shared
+    h = np.zeros((R, F))
+    for e in range(wl.n_routed):
+        a, b = int(ref["offsets"][e]), int(ref["offsets"][e + 1])
+        if a < b:
+            h[a:b] = h_of(xq[ref["sorted_token"][a:b]], ex.gate[e], ex.up[e])
+    ws = dict(h=h)
+    ws["hq"], ws["hs"] = codes(h)
+    if S:
+        ws["h_sh"] = np.concatenate([h_of(xq, ex.sh[0][s], ex.sh[1][s]) for s in range(S)], axis=-1)
+        ws["hq_sh"], ws["hs_sh"] = codes(ws["h_sh"])
+    g = dict(sorted_token=ref["sorted_token"], ws=ws)
+    return inp, spec, ref, g
+
+
+@pytest.mark.parametrize("S", [0, 1, 2])
+def test_fp8_chain_accepts_the_oracle_and_rejects_planted_mistakes(S):
+    wl = synth.QUARTZ.replace(T=40, hidden=128, ffn=64, n_shared=S, dtype="fp8", seed=S)
+    inp, spec, ref, g = _oracle_as_gpu(wl)
+    y = ref["y"]
+    rms = float(np.sqrt(np.mean(y ** 2)))
+    rep = P.fp8_chain(inp, spec, ref, g, y, rms)
+    assert rep["y_rel_to_gpu_codes"] < 1e-12 and rep["codes_moved"] == 0
+    assert rep["h_window_ratio"] == 0.0
+
+    def fails(mutate):
+        g2 = dict(g, ws={k: v.copy() for k, v in g["ws"].items()})
+        y2 = y.copy()
+        mutate(g2["ws"], y2)
+        with pytest.raises(AssertionError):
+            P.fp8_chain(inp, spec, ref, g2, y2, rms)
+
+    def bump_code(ws, y2):            # a code one E4M3 step off its h
+        r = 3
+        f = int(np.argmax(np.abs(ws["hq"][r])))
+        ws["hq"][r, f] = oracle.e4m3_round(ws["hq"][r, f] * (1 - 2.0 ** -3))
+
+    def move_h(ws, y2):               # h and its codes 20% off the oracle's
+        ws["h"][5] = oracle.round_bf16(ws["h"][5] * 1.2)
+        q, s = oracle.fp8_quantize(ws["h"][5:6], axis=-1)
+        ws["hq"][5], ws["hs"][5] = np.ldexp(q, -s[:, None])[0], np.ldexp(1.0, s)[0]
+
+    def bump_y(ws, y2):               # one output element 2e-2 RMS off
+        y2[7, 11] += 2e-2 * rms
+
+    for m in (bump_code, move_h, bump_y):
+        fails(m)
+    if S:
+        def bump_shared_scale(ws, y2):   # the shared row's scale doubled
+            ws["hs_sh"][2] *= 2.0
+        fails(bump_shared_scale)
