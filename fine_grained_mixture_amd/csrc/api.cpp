@@ -120,7 +120,8 @@ Layout make_layout(const moe_config* c, int64_t T) {
   L.blk_psum = take((size_t)L.nblk * E * 4);
   L.psum_tot = take((size_t)E * 4);
   L.plan = take((size_t)(1 + 2 * L.max_tiles) * 4);
-  L.h = take((size_t)L.R * F * es);
+  // low-rank experts keep their h on chip: no routed h rows
+  L.h = take(c->rank > 0 ? 0 : (size_t)L.R * F * es);
   L.h_sh = take((size_t)T * S * F * es);
   L.y_perm = take((size_t)L.R * d * 4);
   L.y_sh = take(S > 0 ? (size_t)T * d * 4 : 0);
@@ -1191,6 +1192,7 @@ int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weig
   return st ? st : tl.n;
 }
 }  // namespace
+
 }  // namespace moe
 
 using namespace moe;
@@ -1345,7 +1347,7 @@ int moe_workspace_region(const moe_config* c, int64_t T, int32_t which, size_t* 
   const bool q = fp8(c) && c->rank == 0;
   size_t at = 0, n = 0;
   switch (which) {
-    case MOE_WS_H: at = L.h; n = (size_t)L.R * F * es; break;
+    case MOE_WS_H: at = L.h; n = c->rank > 0 ? 0 : (size_t)L.R * F * es; break;
     case MOE_WS_H_SHARED: at = L.h_sh; n = (size_t)T * S * F * es; break;
     case MOE_WS_Y_ROUTED: at = L.y_perm; n = (size_t)L.R * d * 4; break;
     case MOE_WS_Y_SHARED: at = L.y_sh; n = S > 0 ? (size_t)T * d * 4 : 0; break;

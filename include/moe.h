@@ -181,7 +181,8 @@ size_t moe_workspace_bytes(const moe_config *cfg, int64_t T);
    config, T < 0, NULL outputs or an unknown region.
      MOE_WS_H                h [R_max, F] in cfg.dtype's activation type
                              (bf16 for MOE_FP8): SiLU(a) * b of each dispatched
-                             row, rounded, before the down projection
+                             row, rounded, before the down projection (dense
+                             experts; low-rank experts keep h on chip)
      MOE_WS_H_SHARED         [T, S*F]: the same for the shared experts
      MOE_WS_Y_ROUTED         [R_max, d] float32: each dispatched row's expert output
      MOE_WS_Y_SHARED         [T, d] float32: the shared experts' summed output

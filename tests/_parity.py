@@ -95,7 +95,7 @@ def run_gpu(wl, inp, *, y_lowp=False):
     L.layer_forward(cfg, x, w, out, ws)
     torch.cuda.synchronize()
     res = to_numpy(out)
-    if wl.dtype == "fp8" and wl.rank == 0 and wl.T > 0:
+    if wl.dtype == "fp8" and (wl.rank == 0 or wl.n_shared > 0) and wl.T > 0:
         res["ws"] = workspace_intermediates(cfg, wl.T, ws)
     return res
 
@@ -175,7 +175,7 @@ def check_parity(wl, inp, g, *, check_y=True, no_rho=True):
     diff = np.abs(yg - yr)
     err = float(diff.max()) if T else 0.0
     rep.update(y_err=err, y_rms=rms, y_rel=err / rms if rms else 0.0, checked=T)
-    if spec.fp8 and spec.rank == 0 and T:
+    if spec.fp8 and (spec.rank == 0 or spec.n_shared > 0) and T:
         rep.update(fp8_chain(inp, spec, ref, g, yg, rms))
     else:
         assert err <= Y_TOL * rms, f"max|dy| {err:.3e} > {Y_TOL} * RMS {rms:.3e}"
@@ -190,8 +190,9 @@ def check_parity(wl, inp, g, *, check_y=True, no_rho=True):
 
 
 def fp8_chain(inp, spec, ref, g, yg, rms):
-    """fp8 dense experts, checked link by link on every element, from the
-    GPU's own intermediates (read from the workspace):
+    """fp8 dense experts (routed, or the shared experts beside low-rank routed
+    ones), checked link by link on every element, from the GPU's own
+    intermediates (read from the workspace):
 
       1. its E4M3 codes and row scales are the oracle's quantisation of its
          own bf16 h, exactly (routed rows and the shared experts' S F rows);
@@ -265,6 +266,11 @@ def fp8_chain(inp, spec, ref, g, yg, rms):
         if a == b:
             continue
         toks = st[a:b]
+        if spec.rank > 0:
+            # low-rank experts: fp8 factors, bf16 products, no quantised
+            # activation; their rows are the oracle's own
+            yr[a:b] = ex.routed(x[toks], e)
+            continue
         H_or, tol = h_window(xq[toks], axq[toks], ex.gate[e], ex.up[e])
         c = check_rows(w["h"][a:b], w["hq"][a:b], w["hs"][a:b], H_or, tol, f"expert {e}")
         yr[a:b] = c @ ex.down[e]

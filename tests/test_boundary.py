@@ -121,14 +121,15 @@ def test_workspace_regions(lib):
     """Intermediate regions lie inside the workspace, do not overlap, and have
     the documented sizes; fp8-only regions are empty otherwise."""
     from fine_grained_mixture_amd.layer import config_from_workload
-    for wl in list(WORKLOADS.values()) + [WORKLOADS["quartz"].replace(dtype="fp8")]:
+    for wl in list(WORKLOADS.values()) + [WORKLOADS["quartz"].replace(dtype="fp8"),
+                                          WORKLOADS["dormouse"].replace(dtype="fp8", n_shared=2)]:
         cfg = config_from_workload(wl)
         T, R = wl.T, _lib.moe_max_rows(cfg, wl.T)
         total = _lib.moe_workspace_bytes(cfg, T)
         es = 2 if wl.dtype in ("bf16", "fp8") else 4
         S, F, d = wl.n_shared, wl.ffn, wl.hidden
         q = wl.dtype == "fp8" and wl.rank == 0
-        want = {_lib.MOE_WS_H: R * F * es, _lib.MOE_WS_H_SHARED: T * S * F * es,
+        want = {_lib.MOE_WS_H: R * F * es * (wl.rank == 0), _lib.MOE_WS_H_SHARED: T * S * F * es,
                 _lib.MOE_WS_Y_ROUTED: R * d * 4, _lib.MOE_WS_Y_SHARED: T * d * 4 * (S > 0),
                 _lib.MOE_WS_HQ: R * F * q, _lib.MOE_WS_HQ_SCALE: R * 4 * q,
                 _lib.MOE_WS_HQ_SHARED: T * S * F * (wl.dtype == "fp8"),

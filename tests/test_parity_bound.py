@@ -31,13 +31,15 @@ def _oracle_as_gpu(wl):
         return np.ldexp(q, -s[:, None]), np.ldexp(1.0, s)
 
     T, R, F, S = wl.T, int(ref["offsets"][-1]), wl.ffn, wl.n_shared
-    h = np.zeros((R, F))
-    for e in range(wl.n_routed):
-        a, b = int(ref["offsets"][e]), int(ref["offsets"][e + 1])
-        if a < b:
-            h[a:b] = h_of(xq[ref["sorted_token"][a:b]], ex.gate[e], ex.up[e])
-    ws = dict(h=h)
-    ws["hq"], ws["hs"] = codes(h)
+    ws = {}
+    if wl.rank == 0:
+        h = np.zeros((R, F))
+        for e in range(wl.n_routed):
+            a, b = int(ref["offsets"][e]), int(ref["offsets"][e + 1])
+            if a < b:
+                h[a:b] = h_of(xq[ref["sorted_token"][a:b]], ex.gate[e], ex.up[e])
+        ws["h"] = h
+        ws["hq"], ws["hs"] = codes(h)
     if S:
         ws["h_sh"] = np.concatenate([h_of(xq, ex.sh[0][s], ex.sh[1][s]) for s in range(S)], axis=-1)
         ws["hq_sh"], ws["hs_sh"] = codes(ws["h_sh"])
@@ -45,9 +47,10 @@ def _oracle_as_gpu(wl):
     return inp, spec, ref, g
 
 
-@pytest.mark.parametrize("S", [0, 1, 2])
-def test_fp8_chain_accepts_the_oracle_and_rejects_planted_mistakes(S):
-    wl = synth.QUARTZ.replace(T=40, hidden=128, ffn=64, n_shared=S, dtype="fp8", seed=S)
+@pytest.mark.parametrize("S,rank", [(0, 0), (1, 0), (2, 0), (2, 64)])
+def test_fp8_chain_accepts_the_oracle_and_rejects_planted_mistakes(S, rank):
+    wl = synth.QUARTZ.replace(T=40, hidden=128, ffn=64, n_shared=S, dtype="fp8", seed=S,
+                              rank=rank)
     inp, spec, ref, g = _oracle_as_gpu(wl)
     y = ref["y"]
     rms = float(np.sqrt(np.mean(y ** 2)))
@@ -62,22 +65,24 @@ def test_fp8_chain_accepts_the_oracle_and_rejects_planted_mistakes(S):
         with pytest.raises(AssertionError):
             P.fp8_chain(inp, spec, ref, g2, y2, rms)
 
+    hk, qk, sk = ("h", "hq", "hs") if rank == 0 else ("h_sh", "hq_sh", "hs_sh")
+
     def bump_code(ws, y2):            # a code one E4M3 step off its h
         r = 3
-        f = int(np.argmax(np.abs(ws["hq"][r])))
-        ws["hq"][r, f] = oracle.e4m3_round(ws["hq"][r, f] * (1 - 2.0 ** -3))
+        f = int(np.argmax(np.abs(ws[qk][r])))
+        ws[qk][r, f] = oracle.e4m3_round(ws[qk][r, f] * (1 - 2.0 ** -3))
 
     def move_h(ws, y2):               # h and its codes 20% off the oracle's
-        ws["h"][5] = oracle.round_bf16(ws["h"][5] * 1.2)
-        q, s = oracle.fp8_quantize(ws["h"][5:6], axis=-1)
-        ws["hq"][5], ws["hs"][5] = np.ldexp(q, -s[:, None])[0], np.ldexp(1.0, s)[0]
+        ws[hk][5] = oracle.round_bf16(ws[hk][5] * 1.2)
+        q, s = oracle.fp8_quantize(ws[hk][5:6], axis=-1)
+        ws[qk][5], ws[sk][5] = np.ldexp(q, -s[:, None])[0], np.ldexp(1.0, s)[0]
 
     def bump_y(ws, y2):               # one output element 2e-2 RMS off
         y2[7, 11] += 2e-2 * rms
 
     for m in (bump_code, move_h, bump_y):
         fails(m)
-    if S:
+    if S and rank == 0:
         def bump_shared_scale(ws, y2):   # the shared row's scale doubled
             ws["hs_sh"][2] *= 2.0
         fails(bump_shared_scale)
