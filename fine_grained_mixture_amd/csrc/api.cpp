@@ -75,6 +75,29 @@ int plan_bm(const moe_config* c) {
   return c->rank > 0 ? kLowRankBM : kGemmBigBM;
 }
 
+}  // namespace
+
+// Token groups of 16 per workgroup of the fused router: about one workgroup
+// per CU, and a block of 16 G tokens keeps its k-slot ids within the rank
+// kernel's registers (16 G k <= 64 * 15).
+int route_small_groups(int64_t T, int k) {
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      n_cu = n;
+    else
+      n_cu = 256;
+  }
+  const int64_t n16 = (T + kRouteBlockSmall - 1) / kRouteBlockSmall;
+  int64_t G = (n16 + n_cu - 1) / n_cu;
+  G = std::min<int64_t>(G, 60 / k);
+  return (int)std::max<int64_t>(G, 1);
+}
+
+namespace {
+
 // bf16 layers with few experts use the fused router (16-token blocks).
 bool fused_router(const moe_config* c) {
   return act_bf16(c) && c->n_routed <= kRouteSmallMaxE;

@@ -398,24 +398,6 @@ __global__ void __launch_bounds__(256) route_small_kernel(RouteSmallArgs a, int 
 
 }  // namespace
 
-int route_small_groups(int64_t T, int k) {
-  static int n_cu = 0;
-  if (n_cu == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      n_cu = n;
-    else
-      n_cu = 256;
-  }
-  // about one workgroup per CU; a block of 16 G tokens keeps its k-slot ids
-  // within the rank kernel's registers (16 G k <= 64 * 15)
-  const int64_t n16 = (T + kTB - 1) / kTB;
-  int64_t G = (n16 + n_cu - 1) / n_cu;
-  G = std::min<int64_t>(G, 60 / k);
-  return (int)std::max<int64_t>(G, 1);
-}
-
 hipError_t launch_route_small(const RouteSmallArgs& a, int groups, hipStream_t s,
                               const ScanArgs* tail_scan, const RankArgs* tail_rank) {
   const int64_t nblk = (a.T + (int64_t)kTB * groups - 1) / ((int64_t)kTB * groups);

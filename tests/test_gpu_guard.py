@@ -1,0 +1,119 @@
+"""Guard bands around every output buffer and the workspaces (GPU).
+
+Each buffer the library writes is placed between two 4 KiB bands of a known
+byte pattern, and the parts the header says stay untouched (sorted_token
+rows at and past offsets[E], the saved products of rows past it) are filled
+with the same pattern; after the call every band and every such part must
+still hold it. Exactly-sized workspaces (moe_workspace_bytes) are used, so a
+write past their end lands in a band.
+"""
+import numpy as np
+import pytest
+import torch
+
+from fine_grained_mixture_amd import _lib, synth
+from fine_grained_mixture_amd import layer as L
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 4096
+PATTERN = 0xA5
+
+
+class Guarded:
+    """Device buffers carved out of guard-banded byte arrays."""
+
+    def __init__(self, dev):
+        self.dev = dev
+        self.bufs = []
+
+    def alloc(self, shape, dtype):
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        raw = torch.full((n + 2 * GUARD,), PATTERN, dtype=torch.uint8, device=self.dev)
+        self.bufs.append((raw, n))
+        return raw[GUARD:GUARD + n].view(dtype).view(shape)
+
+    def check(self):
+        torch.cuda.synchronize()
+        for raw, n in self.bufs:
+            head = raw[:GUARD]
+            tail = raw[GUARD + n:]
+            assert bool((head == PATTERN).all()) and bool((tail == PATTERN).all()), \
+                f"guard band written (buffer of {n} bytes)"
+
+
+def _outputs(g, cfg, T, saved_ab=False):
+    E, k, d, F, S = cfg.n_routed, cfg.top_k, cfg.hidden, cfg.ffn, cfg.n_shared
+    R = _lib.moe_max_rows(cfg, T)
+    i32, f32 = torch.int32, torch.float32
+    t = {"topk_idx": g.alloc((T, k), i32), "topk_gate": g.alloc((T, k), f32),
+         "topk_margin": g.alloc((T,), f32), "counts": g.alloc((E,), i32),
+         "kept": g.alloc((E,), i32), "offsets": g.alloc((E + 1,), i32),
+         "sorted_token": g.alloc((R,), i32), "row_of_slot": g.alloc((T, k), i32),
+         "dropped": g.alloc((T, k), torch.uint8), "n_dropped": g.alloc((1,), i32),
+         "aux": g.alloc((2,), f32), "f": g.alloc((E,), f32), "P": g.alloc((E,), f32),
+         "y": g.alloc((T, d), f32), "y_lowp": g.alloc((T, d), L.torch_dtype(cfg)),
+         "saved_ab": g.alloc((R * 2 * F + T * S * 2 * F,), f32) if saved_ab else None}
+    return L.Outputs(t, _lib.MoeOutputs(**{n: L._ptr(t[n]) for n in _lib.OUTPUT_FIELDS}))
+
+
+CASES = {
+    "quartz_ragged": synth.QUARTZ.replace(T=517, hidden=256, ffn=128),
+    "moonfrost_capacity": synth.MOONFROST.replace(T=1000, hidden=256, ffn=128),
+    "dormouse_lowrank": synth.DORMOUSE.replace(T=300, hidden=256, ffn=128),
+    "quartz_fp8": synth.QUARTZ.replace(T=333, hidden=256, ffn=128, dtype="fp8"),
+    "quartz_decode": synth.QUARTZ.replace(T=3),
+    "tiny_f32": synth.TINY.replace(T=77),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_forward_writes_stay_inside_their_buffers(name):
+    wl = CASES[name]
+    print(f"\n[case] guard {name}", flush=True)
+    inp = synth.make_inputs(wl)
+    cfg, x, w = P.upload(wl, inp)
+    g = Guarded(x.device)
+    saved = wl.dtype == "bf16" and wl.rank == 0
+    out = _outputs(g, cfg, wl.T, saved_ab=saved)
+    ws = g.alloc((_lib.moe_workspace_bytes(cfg, wl.T),), torch.uint8)
+    _lib.moe_layer_forward(cfg, wl.T, x.data_ptr(), w.struct, out.struct, ws.data_ptr(),
+                           ws.numel(), L.current_stream())
+    g.check()
+    R = int(out["offsets"][-1].item())
+    st = out["sorted_token"][R:].view(torch.uint8)
+    assert bool((st == PATTERN).all()), "sorted_token written past offsets[E]"
+    if saved:
+        rows = out["saved_ab"][:_lib.moe_max_rows(cfg, wl.T) * 2 * wl.ffn].view(-1, 2 * wl.ffn)
+        assert bool((rows[R:].view(torch.uint8) == PATTERN).all()), "saved_ab past offsets[E]"
+    # the call itself is right (the same buffers, checked against the oracle,
+    # whose check expects the unused rows filled with -1)
+    out["sorted_token"][R:] = -1
+    P.check_parity(wl, inp, P.to_numpy(out), no_rho=False)
+
+
+def test_backward_writes_stay_inside_their_buffers():
+    wl = synth.QUARTZ.replace(T=300, hidden=256, ffn=128)
+    print("\n[case] guard backward", flush=True)
+    inp = synth.make_inputs(wl)
+    cfg, x, w = P.upload(wl, inp)
+    out = L.allocate_outputs(cfg, wl.T, x.device, saved_ab=True)
+    ws = L.allocate_workspace(cfg, wl.T, x.device)
+    L.layer_forward(cfg, x, w, out, ws)
+    g = Guarded(x.device)
+    E, d, F, S = cfg.n_routed, cfg.hidden, cfg.ffn, cfg.n_shared
+    f32 = torch.float32
+    t = {"dx": g.alloc((wl.T, d), f32), "dw_router": g.alloc((d, E), f32),
+         "dw_gate": g.alloc((E, d, F), f32), "dw_up": g.alloc((E, d, F), f32),
+         "dw_down": g.alloc((E, F, d), f32), "dsh_gate": g.alloc((S, d, F), f32),
+         "dsh_up": g.alloc((S, d, F), f32), "dsh_down": g.alloc((S, F, d), f32)}
+    grads = L.Grads(t, _lib.MoeGrads(**{n: L._ptr(t[n]) for n in _lib.GRAD_FIELDS}))
+    bws = g.alloc((_lib.moe_backward_workspace_bytes(cfg, wl.T),), torch.uint8)
+    dy = torch.from_numpy(synth.make_upstream(wl)).to(x.device)
+    _lib.moe_layer_backward(cfg, wl.T, x.data_ptr(), w.struct, out.struct, dy.data_ptr(), 1.0,
+                            grads.struct, ws.data_ptr(), ws.numel(), bws.data_ptr(), bws.numel(),
+                            L.current_stream())
+    g.check()
+    for n, v in t.items():
+        assert bool(torch.isfinite(v).all()), n

@@ -86,3 +86,53 @@ def test_fp8_chain_accepts_the_oracle_and_rejects_planted_mistakes(S, rank):
         def bump_shared_scale(ws, y2):   # the shared row's scale doubled
             ws["hs_sh"][2] *= 2.0
         fails(bump_shared_scale)
+
+
+def _float32_lowrank_y(inp, spec, ref):
+    """The low-rank layer evaluated in float32 (NumPy's float32 products: fp32
+    sums in an order of their own), rounded to bf16 at the layer's points."""
+    ex = oracle.Experts(inp, spec)
+    x = np.asarray(inp["x"], np.float32)
+
+    def r32(v):
+        return oracle.round_bf16(v.astype(np.float64)).astype(np.float32)
+
+    def apply(v, u, s, vmat):
+        return r32((v @ u) * s) @ vmat.T
+
+    y = np.zeros(x.shape)
+    idx, gates, rows = ref["idx"], ref["gates"], ref["row_of_slot"]
+    for e in range(spec.n_routed):
+        ts, js = np.nonzero((idx == e) & (rows >= 0))
+        if not len(ts):
+            continue
+        f = {n: np.asarray(b[e], np.float32) for n, b in ex.lr.items()}
+        a = apply(x[ts], f["u_gate"], f["s_gate"], f["v_gate"])
+        b = apply(x[ts], f["u_up"], f["s_up"], f["v_up"])
+        h = r32(a / (1 + np.exp(-a)) * b)
+        np.add.at(y, ts, gates[ts, js][:, None] * apply(h, f["u_down"], f["s_down"], f["v_down"]))
+    return y
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_lowrank_allowance_covers_a_float32_chain_and_catches_a_slip(dtype):
+    """A float32 evaluation of the low-rank chain (another summation order,
+    tipping rounding decisions all along the chain) meets the low-rank
+    acceptance against the oracle; the same evaluation with s_down off by
+    2^-6 (a systematic slip) fails it."""
+    wl = synth.DORMOUSE.replace(T=1500, dtype=dtype, seed=5)
+    inp = synth.make_inputs(wl)
+    spec = P.spec_of(wl)
+    ref = oracle.layer_forward_batched(inp["x"], inp, spec)
+    y = ref["y"]
+    rms = np.sqrt(np.mean(y ** 2))
+    r_y = P.lowrank_zd_allowance(inp, spec, ref)
+    y32 = _float32_lowrank_y(inp, spec, ref)
+    dev = np.abs(y32 - y)
+    assert np.count_nonzero(dev) > 0.1 * dev.size          # the orders differ
+    assert np.max(dev / (P.Y_TOL * rms + r_y)) <= 0.5
+    assert np.sqrt(np.mean(dev ** 2)) / rms <= 0.5 * P.LOWRANK_ERR_RMS
+    bad = dict(inp)
+    bad["s_down"] = (np.asarray(inp["s_down"], np.float64) * (1 + 2.0 ** -6)).astype(np.float32)
+    dev = np.abs(_float32_lowrank_y(bad, spec, ref) - y)
+    assert np.sqrt(np.mean(dev ** 2)) / rms > P.LOWRANK_ERR_RMS
