@@ -186,15 +186,14 @@ def check_parity(wl, inp, g, *, check_y=True, no_rho=True):
     rep.update(y_err=err, y_rms=rms, y_rel=err / rms if rms else 0.0, checked=T)
     # low-rank experts: bf16 rounding points z_g, z_u, h, z_d in a chain
     r_y = lowrank_zd_allowance(inp, spec, ref) if spec.rank > 0 and spec.bf16 and T else None
-    if r_y is not None:
+    if spec.fp8 and (spec.rank == 0 or spec.n_shared > 0) and T:
+        rep.update(fp8_chain(inp, spec, ref, g, yg, rms, r_y))
+    elif r_y is not None:
         # the error's RMS over all elements stays at accumulation-order level
         err_rms = float(np.sqrt(np.mean(diff ** 2))) / rms if rms else 0.0
         rep.update(y_err_rms_rel=err_rms,
                    elements_beyond_rms_bound=int(np.count_nonzero(diff > Y_TOL * rms)))
         assert err_rms <= LOWRANK_ERR_RMS, f"error RMS {err_rms:.2e} of RMS(y)"
-    if spec.fp8 and (spec.rank == 0 or spec.n_shared > 0) and T:
-        rep.update(fp8_chain(inp, spec, ref, g, yg, rms, r_y))
-    elif r_y is not None:
         ratio = float(np.max(diff / (Y_TOL * rms + r_y)))
         rep.update(y_tol_ratio=ratio)
         assert ratio <= 1.0, (f"max |dy| / (1e-2 RMS + z_d ulps) = {ratio:.3f} at "
@@ -347,6 +346,11 @@ def fp8_chain(inp, spec, ref, g, yg, rms, r_lowrank=None):
     rep.update(h_window_ratio=worst_h, h_entries_moved=h_moved, h_entries=h_n,
                codes_moved=code_moved, y_rel_to_gpu_codes=rel_c)
     assert rel_c <= Y_TOL, f"y against the GPU's own codes: {rel_c:.3e} RMS"
+    if r_lowrank is not None:
+        # low-rank routed rows: the error's RMS at accumulation-order level
+        err_rms = float(np.sqrt(np.mean(diff_c ** 2))) / rms if rms else 0.0
+        rep.update(y_err_rms_rel_to_gpu_codes=err_rms)
+        assert err_rms <= LOWRANK_ERR_RMS, f"error RMS {err_rms:.2e} of RMS(y)"
     # end to end against the oracle's own y: a moved code changes one term by
     # at most one E4M3 step (2^-3 of it); two such at the largest term allowed
     diff = np.abs(yg - ref["y"])
