@@ -90,7 +90,7 @@ def test_forward_writes_stay_inside_their_buffers(name):
     # the call itself is right (the same buffers, checked against the oracle,
     # whose check expects the unused rows filled with -1)
     out["sorted_token"][R:] = -1
-    P.check_parity(wl, inp, P.to_numpy(out), no_rho=False)
+    P.check_parity(wl, inp, P.with_intermediates(wl, cfg, P.to_numpy(out), ws), no_rho=False)
 
 
 def test_backward_writes_stay_inside_their_buffers():

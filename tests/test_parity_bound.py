@@ -1,8 +1,10 @@
-"""The fp8 parity chain of tests/_parity.py on the CPU: fed the oracle's own
-intermediates it passes, and each kind of planted mistake (a code that is not
-the quantised h, an h entry outside its window, a y element off the codes'
-product) makes it fail. The mistakes are planted in copies of the oracle's
-values; nothing here runs on a GPU.
+"""The parity checks of tests/_parity.py on the CPU: the dense experts' chain
+(dense_chain), fed the oracle's own intermediates, passes, and each kind of
+planted mistake (a code that is not the quantised h, an h entry outside its
+window, a y element off the product of the GPU's h) makes it fail; the
+low-rank allowance covers a float32 evaluation of the chain and catches a
+systematic slip. The mistakes are planted in copies of the oracle's values;
+nothing here runs on a GPU.
 """
 import numpy as np
 import pytest
@@ -21,12 +23,14 @@ def _oracle_as_gpu(wl):
     x = np.asarray(inp["x"], np.float64)
     ex = oracle.Experts(inp, spec)
     rho = oracle.round_bf16
-    xq = oracle.fp8_quantize(x, axis=-1)[0]
+    xq = oracle.fp8_quantize(x, axis=-1)[0] if spec.fp8 else x
 
     def h_of(X, wg, wu):
         return rho(oracle.silu(X @ wg) * (X @ wu))
 
     def codes(h):
+        if not spec.fp8:
+            return None, None
         q, s = oracle.fp8_quantize(h, axis=-1)
         return np.ldexp(q, -s[:, None]), np.ldexp(1.0, s)
 
@@ -47,23 +51,26 @@ def _oracle_as_gpu(wl):
     return inp, spec, ref, g
 
 
-@pytest.mark.parametrize("S,rank", [(0, 0), (1, 0), (2, 0), (2, 64)])
-def test_fp8_chain_accepts_the_oracle_and_rejects_planted_mistakes(S, rank):
-    wl = synth.QUARTZ.replace(T=40, hidden=128, ffn=64, n_shared=S, dtype="fp8", seed=S,
+@pytest.mark.parametrize("S,rank,dtype", [(0, 0, "fp8"), (1, 0, "fp8"), (2, 0, "fp8"),
+                                          (2, 64, "fp8"), (0, 0, "bf16"), (2, 0, "bf16"),
+                                          (1, 64, "bf16")])
+def test_chain_accepts_the_oracle_and_rejects_planted_mistakes(S, rank, dtype):
+    wl = synth.QUARTZ.replace(T=40, hidden=128, ffn=64, n_shared=S, dtype=dtype, seed=S,
                               rank=rank)
     inp, spec, ref, g = _oracle_as_gpu(wl)
     y = ref["y"]
     rms = float(np.sqrt(np.mean(y ** 2)))
-    rep = P.fp8_chain(inp, spec, ref, g, y, rms)
-    assert rep["y_rel_to_gpu_codes"] < 1e-12 and rep["codes_moved"] == 0
+    r_lr = P.lowrank_zd_allowance(inp, spec, ref) if rank else None
+    rep = P.dense_chain(inp, spec, ref, g, y, rms, r_lr)
+    assert rep["y_rel_to_gpu_h"] < 1e-12 and rep.get("codes_moved", 0) == 0
     assert rep["h_window_ratio"] == 0.0
 
     def fails(mutate):
-        g2 = dict(g, ws={k: v.copy() for k, v in g["ws"].items()})
+        g2 = dict(g, ws={k: None if v is None else v.copy() for k, v in g["ws"].items()})
         y2 = y.copy()
         mutate(g2["ws"], y2)
         with pytest.raises(AssertionError):
-            P.fp8_chain(inp, spec, ref, g2, y2, rms)
+            P.dense_chain(inp, spec, ref, g2, y2, rms, r_lr)
 
     hk, qk, sk = ("h", "hq", "hs") if rank == 0 else ("h_sh", "hq_sh", "hs_sh")
 
@@ -72,17 +79,18 @@ def test_fp8_chain_accepts_the_oracle_and_rejects_planted_mistakes(S, rank):
         f = int(np.argmax(np.abs(ws[qk][r])))
         ws[qk][r, f] = oracle.e4m3_round(ws[qk][r, f] * (1 - 2.0 ** -3))
 
-    def move_h(ws, y2):               # h and its codes 20% off the oracle's
+    def move_h(ws, y2):               # h (and its codes) 20% off the oracle's
         ws[hk][5] = oracle.round_bf16(ws[hk][5] * 1.2)
-        q, s = oracle.fp8_quantize(ws[hk][5:6], axis=-1)
-        ws[qk][5], ws[sk][5] = np.ldexp(q, -s[:, None])[0], np.ldexp(1.0, s)[0]
+        if spec.fp8:
+            q, s = oracle.fp8_quantize(ws[hk][5:6], axis=-1)
+            ws[qk][5], ws[sk][5] = np.ldexp(q, -s[:, None])[0], np.ldexp(1.0, s)[0]
 
     def bump_y(ws, y2):               # one output element 2e-2 RMS off
         y2[7, 11] += 2e-2 * rms
 
-    for m in (bump_code, move_h, bump_y):
+    for m in ((bump_code, move_h, bump_y) if spec.fp8 else (move_h, bump_y)):
         fails(m)
-    if S and rank == 0:
+    if S and rank == 0 and spec.fp8:
         def bump_shared_scale(ws, y2):   # the shared row's scale doubled
             ws["hs_sh"][2] *= 2.0
         fails(bump_shared_scale)
