@@ -81,9 +81,10 @@ def to_numpy(out) -> dict:
     return res
 
 
-def workspace_intermediates(cfg, T, ws) -> dict:
-    """The fp8 layer's h, its E4M3 codes and row scales, read from the
-    workspace after a call (regions from moe_workspace_region), as numpy."""
+def workspace_intermediates(cfg, T, ws, rows) -> dict:
+    """The layer's h (and for fp8 its E4M3 codes and row scales), read from
+    the workspace after a call (regions from moe_workspace_region), as numpy;
+    routed regions up to the `rows` dispatched rows."""
     R, F, S = _lib.moe_max_rows(cfg, T), cfg.ffn, cfg.n_shared
 
     def region(which, dtype, shape):
@@ -91,6 +92,8 @@ def workspace_intermediates(cfg, T, ws) -> dict:
         if n == 0:
             return None
         t = ws[off:off + n].view(dtype).reshape(shape)
+        if shape[0] == R:
+            t = t[:rows]
         if dtype == torch.bfloat16:
             t = t.float()
         if dtype == torch.uint8:
@@ -105,21 +108,21 @@ def workspace_intermediates(cfg, T, ws) -> dict:
                 hs_sh=region(_lib.MOE_WS_HQ_SHARED_SCALE, torch.float32, (T,)))
 
 
-def run_gpu(wl, inp, *, y_lowp=False):
+def run_gpu(wl, inp, *, y_lowp=False, intermediates=True):
     cfg, x, w = upload(wl, inp)
     out = allocate_outputs(cfg, wl.T, x.device, y_lowp=y_lowp)
     ws = allocate_workspace(cfg, wl.T, x.device)
     L.layer_forward(cfg, x, w, out, ws)
     torch.cuda.synchronize()
     res = to_numpy(out)
-    return with_intermediates(wl, cfg, res, ws)
+    return with_intermediates(wl, cfg, res, ws) if intermediates else res
 
 
 def with_intermediates(wl, cfg, res: dict, ws) -> dict:
     """Adds the workspace intermediates that check_parity's chain check reads
     (bf16 or fp8 layers with dense experts, routed or shared)."""
     if wl.dtype in ("bf16", "fp8") and (wl.rank == 0 or wl.n_shared > 0) and wl.T > 0:
-        res["ws"] = workspace_intermediates(cfg, wl.T, ws)
+        res["ws"] = workspace_intermediates(cfg, wl.T, ws, int(res["offsets"][-1]))
     return res
 
 
