@@ -501,12 +501,13 @@ def cold_stages(wl, cfg, x, w, steps, stream):
     gather_bytes = T * d * b + rows * d * b + 4 * rows
     combine_bytes = rows * d * 4 + (T * d * 4 if wl.n_shared else 0) + T * d * 4 + 8 * T * k
     gather_us = max(perm_ms - rank_ms, 1e-6) * 1e3
+    comb_us = comb_ms * 1e3
     res = {"protocol": "each call after a 512 MiB device write; medians of the calls",
            "permute_rank_only_us": rank_ms * 1e3, "permute_with_gather_us": perm_ms * 1e3,
            "gather_us": gather_us, "gather_bytes": gather_bytes,
            "gather_gbs": gather_bytes / (gather_us * 1e-6) / 1e9,
-           "combine_us": comb_ms * 1e3, "combine_bytes": combine_bytes,
-           "combine_gbs": combine_bytes / (comb_ms * 1e-6) / 1e9}
+           "combine_us": comb_us, "combine_bytes": combine_bytes,
+           "combine_gbs": combine_bytes / (comb_us * 1e-6) / 1e9}
     res["gather_frac_of_hbm_peak"] = res["gather_gbs"] / PEAK_HBM_GBS
     res["combine_frac_of_hbm_peak"] = res["combine_gbs"] / PEAK_HBM_GBS
     return res
