@@ -24,7 +24,7 @@ MOE_WS_HQ, MOE_WS_HQ_SCALE, MOE_WS_HQ_SHARED, MOE_WS_HQ_SHARED_SCALE = 4, 5, 6, 
 EXPORTED = ("moe_capacity", "moe_max_rows", "moe_workspace_bytes", "moe_workspace_region",
             "moe_route", "moe_permute",
             "moe_grouped_ffn", "moe_combine", "moe_bias_update", "moe_quantize_fp8",
-            "moe_layer_forward",
+            "moe_layer_forward", "moe_layer_forward_noalloc",
             "moe_layer_forward_timed", "moe_backward_workspace_bytes", "moe_layer_backward",
             "moe_layer_backward_timed", "moe_stage_name", "moe_status_str", "moe_last_error")
 
@@ -103,6 +103,7 @@ def load():
         "moe_quantize_fp8": (c_int, [cfgp, wp, wp, c_void_p]),
         "moe_layer_forward": (c_int, [cfgp, c_int64, c_void_p, wp, op, c_void_p, c_size_t,
                                       c_void_p]),
+        "moe_layer_forward_noalloc": (c_int, [cfgp, c_int64, c_void_p, wp, op, c_void_p]),
         "moe_layer_forward_timed": (c_int, [cfgp, c_int64, c_void_p, wp, op, c_void_p,
                                             c_size_t, c_void_p, POINTER(c_void_p), c_int]),
         "moe_backward_workspace_bytes": (c_size_t, [cfgp, c_int64]),
@@ -184,6 +185,14 @@ def moe_combine(cfg, T, y_routed, y_shared, o, stream) -> None:
 def moe_layer_forward(cfg, T, x, w, o, ws, ws_bytes, stream) -> None:
     _check(load().moe_layer_forward(ctypes.byref(cfg), T, x, ctypes.byref(w), ctypes.byref(o),
                                     ws, ws_bytes, stream), "moe_layer_forward")
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_layer_forward_noalloc(cfg, T, x, w, o, stream) -> None:
+    _check(load().moe_layer_forward_noalloc(ctypes.byref(cfg), T, x, ctypes.byref(w),
+                                            ctypes.byref(o), stream), "moe_layer_forward_noalloc")
 
 
 def moe_layer_forward_timed(cfg, T, x, w, o, ws, ws_bytes, stream, events) -> int:

@@ -1216,6 +1216,32 @@ int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weig
 }
 }  // namespace
 
+int report_hip_error(hipError_t e) { return hip_fail(e); }
+
+// The layer forward for callers that bring their own workspace pointer from
+// elsewhere (the allocation-free entry point's device scratch array).
+int layer_forward_on(const moe_config* c, int64_t T, const void* x, const moe_weights* w,
+                     moe_outputs* o, void* ws, size_t ws_bytes, void* stream) {
+  const int r = layer_forward(c, T, x, w, o, ws, ws_bytes, stream, nullptr, 0);
+  return r < 0 ? r : MOE_OK;
+}
+
+// Validation of a forward call that does not touch the device: MOE_OK, or the
+// status the call would return before launching anything. ws_bytes_out gets
+// the workspace the call needs.
+int layer_forward_check(const moe_config* c, int64_t T, const void* x, const moe_weights* w,
+                        const moe_outputs* o, size_t* ws_bytes_out) {
+  int st = check_common(c, T);
+  if (st) return st;
+  if (!x && T > 0) return MOE_EINVAL;
+  if (!w || !w->w_router || !expert_weights_ok(c, w, true, true)) return MOE_EINVAL;
+  if (c->score == MOE_SOFTMAX && w->select_bias) return MOE_EINVAL;
+  if (!route_outputs_ok(o, T) || !permute_outputs_ok(o, T) || (T > 0 && !o->y))
+    return MOE_EINVAL;
+  *ws_bytes_out = make_layout(c, T).total;
+  return MOE_OK;
+}
+
 }  // namespace moe
 
 using namespace moe;

@@ -366,4 +366,13 @@ hipError_t launch_dx_gather(const DxGatherArgs& a, hipStream_t s);
 hipError_t launch_reduce_chunks(const float* part, float* out, int64_t groups, int64_t chunks,
                                 int64_t n, hipStream_t s);
 
+// Records a failed HIP call's text for moe_last_error(); returns MOE_EHIP.
+int report_hip_error(hipError_t e);
+// The whole layer forward on a given workspace (api.cpp), and its argument
+// validation alone, which touches no device.
+int layer_forward_on(const moe_config* c, int64_t T, const void* x, const moe_weights* w,
+                     moe_outputs* o, void* ws, size_t ws_bytes, void* stream);
+int layer_forward_check(const moe_config* c, int64_t T, const void* x, const moe_weights* w,
+                        const moe_outputs* o, size_t* ws_bytes_out);
+
 }  // namespace moe

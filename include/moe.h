@@ -287,6 +287,23 @@ int moe_layer_forward(const moe_config *cfg, int64_t T, const void *x,
                       const moe_weights *w, moe_outputs *o, void *ws, size_t ws_bytes,
                       void *stream);
 
+/* For callers that cannot allocate device memory or pass a workspace (code
+   under HIP graph capture, tight serving loops, harnesses that forbid
+   allocation): moe_layer_forward with its workspace in a device array of
+   MOE_NOALLOC_SCRATCH_BYTES that the library itself holds, one copy per GPU,
+   kept until the process ends. The caller still passes x, w and o. A call
+   whose moe_workspace_bytes(cfg, T) exceeds the array returns
+   MOE_EWORKSPACE before anything is launched (the Quartz-shaped layer fits
+   up to 1,719 tokens, the Sutra-shaped one 1,737). Nothing in the array has to start at zero:
+   every call writes what it reads there. Every call on one GPU shares that
+   GPU's array, so calls that may overlap on one GPU (different streams, or
+   different host threads) race; calls on one stream are ordered. The
+   device address of each GPU's array is looked up on the first call with
+   that GPU current (hipGetSymbolAddress); no call allocates or frees.     */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_layer_forward_noalloc(const moe_config *cfg, int64_t T, const void *x,
+                              const moe_weights *w, moe_outputs *o, void *stream);
+
 /* Same as moe_layer_forward, and records events[2i] and events[2i+1]
    (hipEvent_t, caller-created) immediately before and after the launch of
    kernel i, on the stream that kernel runs on, for 2i+1 < n_events; returns

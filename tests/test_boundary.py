@@ -294,3 +294,21 @@ def test_binding_rejects_wrong_tensors():
     w = L.DeviceWeights({"u_gate": torch.zeros(1)})
     with pytest.raises(ValueError, match="not read"):
         w.check(cfg)
+
+
+def test_noalloc_entry_point_refuses_before_touching_a_device(lib):
+    """The allocation-free forward validates its arguments and the size of its
+    device array before it looks anything up on a device (no GPU here)."""
+    from fine_grained_mixture_amd.layer import config_from_workload
+    cfg = config_from_workload(WORKLOADS["quartz"])
+    w = _lib.MoeWeights(**{n: 0x1000 for n in ("w_router", "w_gate", "w_up", "w_down",
+                                                 "sh_gate", "sh_up", "sh_down")})
+    o = _lib.MoeOutputs(**{n: 0x1000 for n in _lib.OUTPUT_FIELDS})
+    assert _lib.moe_workspace_bytes(cfg, 4096) > _lib.MOE_NOALLOC_SCRATCH_BYTES
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(cfg), 4096, 0x1000, ctypes.byref(w),
+                                         ctypes.byref(o), None) == _lib.MOE_EWORKSPACE
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(cfg), 64, None, ctypes.byref(w),
+                                         ctypes.byref(o), None) == _lib.MOE_EINVAL
+    bad = _cfg(top_k=0)
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(bad), 64, 0x1000, ctypes.byref(w),
+                                         ctypes.byref(o), None) == _lib.MOE_EINVAL
