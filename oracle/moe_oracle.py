@@ -598,6 +598,52 @@ def _expert_backward(xrow, wg, wu, wd, dyrow, rho, grads, key, scales=None):
     return dx, np.maximum(tg.max(axis=1), tu.max(axis=1)), tg.sum(axis=1) + tu.sum(axis=1)
 
 
+LOWRANK_GRADS = ("du_gate", "ds_gate", "dv_gate", "du_up", "ds_up", "dv_up",
+                 "du_down", "ds_down", "dv_down")
+
+
+def _lowrank_expert_backward(xrow, f, dyrow, rho, grads, key):
+    """One rank-r SwiGLU expert (each matrix W[in, out] = U[in, r] diag(s) V[out, r]^T,
+    dormouse "TSCT low-rank experts" card) on one token row, with the
+    upstream gradient dyrow of its output (already rounded where the layer
+    rounds it). The forward is re-evaluated with its rounding points:
+    z_g = rho((x U_g) s_g), a = z_g V_g^T, the same for up, h = rho(SiLU(a) b),
+    z_d = rho((h U_d) s_d), o = z_d V_d^T; rho is straight-through. The
+    gradients entering the backward's products are rounded with rho where
+    those products take bf16 operands: da and db (as for dense experts) and,
+    in the factor chains, dz_d s_d, dz_g s_g and dz_u s_u. Adds to
+    grads[key][name] for the nine factor gradients and returns dx."""
+    ug = xrow @ f["u_gate"]
+    zg = rho(ug * f["s_gate"])
+    a = zg @ f["v_gate"].T
+    uu = xrow @ f["u_up"]
+    zu = rho(uu * f["s_up"])
+    b = zu @ f["v_up"].T
+    h = rho(silu(a) * b)
+    ud = h @ f["u_down"]
+    zd = rho(ud * f["s_down"])
+    G = grads[key]
+    dzd = f["v_down"].T @ dyrow            # sum over the output columns c of dy_c V_d[c, i]
+    G["dv_down"] += np.outer(dyrow, zd)
+    G["ds_down"] += dzd * ud
+    dud = rho(dzd * f["s_down"])
+    G["du_down"] += np.outer(h, dud)
+    dh = f["u_down"] @ dud
+    da = rho(dh * b * dsilu(a))
+    db = rho(dh * silu(a))
+    dzg = f["v_gate"].T @ da
+    dzu = f["v_up"].T @ db
+    G["dv_gate"] += np.outer(da, zg)
+    G["dv_up"] += np.outer(db, zu)
+    G["ds_gate"] += dzg * ug
+    G["ds_up"] += dzu * uu
+    dug = rho(dzg * f["s_gate"])
+    duu = rho(dzu * f["s_up"])
+    G["du_gate"] += np.outer(xrow, dug)
+    G["du_up"] += np.outer(xrow, duu)
+    return f["u_gate"] @ dug + f["u_up"] @ duu
+
+
 def layer_backward(x, weights: dict, spec: LayerSpec, dy, aux_grad=0.0, fwd=None,
                    scales=False):
     """Gradients of L = sum(dy * y) + aux_grad * aux with respect to x, the
@@ -612,6 +658,10 @@ def layer_backward(x, weights: dict, spec: LayerSpec, dy, aux_grad=0.0, fwd=None
     upstream rows rho(g * dy), the shared upstream rows rho(dy), da and db, and
     the router-logit gradient rho(dl). Everything else is float64.
 
+    Rank-r experts: their factor gradients du_gate, ds_gate, dv_gate, ... (the
+    factors' own shapes) in place of dw_gate/up/down, with the rounding points
+    of _lowrank_expert_backward.
+
     Returns dict dx [T, d], dw_router [d, E], dw_gate/up/down [E, ...] and
     dsh_gate/up/down [S, ...]. With ``scales``, also M_<name> and S_<name> for
     each of them: per element, the largest magnitude of a single product term
@@ -619,8 +669,8 @@ def layer_backward(x, weights: dict, spec: LayerSpec, dy, aux_grad=0.0, fwd=None
     formed from rounded operands; the terms of dx are its products' terms
     with the weights).
     """
-    if spec.rank != 0 or spec.fp8:
-        raise NotImplementedError("backward of low-rank or fp8 experts")
+    if spec.fp8 or (spec.rank != 0 and scales):
+        raise NotImplementedError("backward of fp8 experts; scales of low-rank experts")
     x = np.asarray(x)
     T, d = x.shape
     E, k, S, F = spec.n_routed, spec.top_k, spec.n_shared, spec.ffn
@@ -629,7 +679,13 @@ def layer_backward(x, weights: dict, spec: LayerSpec, dy, aux_grad=0.0, fwd=None
         fwd = layer_forward(x, weights, spec)
     dy = np.asarray(dy, np.float64)
     ex = Experts(weights, spec)
-    grads = {("r", e): [np.zeros((d, F)), np.zeros((d, F)), np.zeros((F, d))] for e in range(E)}
+    if spec.rank == 0:
+        grads = {("r", e): [np.zeros((d, F)), np.zeros((d, F)), np.zeros((F, d))]
+                 for e in range(E)}
+    else:
+        grads = {}
+        lr_grads = {e: {n: np.zeros(np.shape(ex.lr[n[1:]][e])) for n in LOWRANK_GRADS}
+                    for e in range(E)}
     for s in range(S):
         grads[("s", s)] = [np.zeros((d, F)), np.zeros((d, F)), np.zeros((F, d))]
     dx = np.zeros((T, d))
@@ -659,8 +715,13 @@ def layer_backward(x, weights: dict, spec: LayerSpec, dy, aux_grad=0.0, fwd=None
                 continue                      # dropped slot: no gradient
             e = int(idx[t, j])
             dg[t, j] = float(dy[t] @ ex.routed(xrow, e))
-            run_expert(t, xrow, (ex.gate[e], ex.up[e], ex.down[e]), rho(gates[t, j] * dy[t]),
-                       ("r", e))
+            if spec.rank == 0:
+                run_expert(t, xrow, (ex.gate[e], ex.up[e], ex.down[e]),
+                           rho(gates[t, j] * dy[t]), ("r", e))
+            else:
+                f = {n: b[e] for n, b in ex.lr.items()}
+                dx[t] += _lowrank_expert_backward(xrow, f, rho(gates[t, j] * dy[t]), rho,
+                                                  lr_grads, e)
 
     # router: gates -> logits, plus the aux statistic's dependence on the
     # routing distribution (f held fixed)
@@ -693,7 +754,12 @@ def layer_backward(x, weights: dict, spec: LayerSpec, dy, aux_grad=0.0, fwd=None
     dl = rho(dl)            # the operand of the two router products
     dx += dl @ wr.T
     out = dict(dx=dx, dw_router=np.asarray(x, np.float64).T @ dl, dl=dl, dg=dg)
-    names = [("dw_gate", "r", E, 0), ("dw_up", "r", E, 1), ("dw_down", "r", E, 2)]
+    if spec.rank == 0:
+        names = [("dw_gate", "r", E, 0), ("dw_up", "r", E, 1), ("dw_down", "r", E, 2)]
+    else:
+        names = []
+        for n in LOWRANK_GRADS:
+            out[n] = np.stack([lr_grads[e][n] for e in range(E)])
     if S > 0:
         names += [("dsh_gate", "s", S, 0), ("dsh_up", "s", S, 1), ("dsh_down", "s", S, 2)]
     for name, kind, n, i in names:
@@ -742,16 +808,17 @@ def _router_dl(l, idx, gates, dg, f, spec: LayerSpec, aux_grad, T):
 
 def layer_backward_batched(x, weights: dict, spec: LayerSpec, dy, aux_grad=0.0, fwd=None):
     """The same gradients as layer_backward (same readings, same rounding
-    points), computed per expert over all of its rows at once with matrix
-    products instead of token by token, for full-size checks.
+    points; dense or rank-r experts), computed per expert over all of its rows
+    at once with matrix products instead of token by token, for full-size
+    checks.
 
     Returns the gradients, their S_<name> (sum of the product terms'
     magnitudes, as in layer_backward) and B_<name>, an upper bound of
     layer_backward's M_<name>: the product of the largest magnitudes of the two
     operands over the summed index.
     """
-    if spec.rank != 0 or spec.fp8:
-        raise NotImplementedError("backward of low-rank or fp8 experts")
+    if spec.fp8:
+        raise NotImplementedError("backward of fp8 experts")
     x64 = np.asarray(x, np.float64)
     T, d = x64.shape
     E, k, S, F = spec.n_routed, spec.top_k, spec.n_shared, spec.ffn
@@ -792,7 +859,70 @@ def layer_backward_batched(x, weights: dict, spec: LayerSpec, dy, aux_grad=0.0, 
         return Hh @ wd, res
 
     ex = Experts(weights, spec)
-    for kind, n in (("w", E), ("sh", S)):
+
+    def put(name, val, sabs, bmax):
+        out[name], out["S_" + name], out["B_" + name] = val, sabs, bmax
+
+    def lowrank_expert(tok, g, f):
+        """The rank-r expert backward of _lowrank_expert_backward over the
+        expert's rows at once; returns its output rows and the gradients with
+        their scales."""
+        X = x64[tok]
+        DY = rho(g[:, None] * dy[tok])
+        UG = X @ f["u_gate"]
+        ZG = rho(UG * f["s_gate"])
+        A = ZG @ f["v_gate"].T
+        UU = X @ f["u_up"]
+        ZU = rho(UU * f["s_up"])
+        Bv = ZU @ f["v_up"].T
+        Hh = rho(silu(A) * Bv)
+        UD = Hh @ f["u_down"]
+        ZD = rho(UD * f["s_down"])
+        DZD = DY @ f["v_down"]
+        DUD = rho(DZD * f["s_down"])
+        DH = DUD @ f["u_down"].T
+        DA = rho(DH * Bv * dsilu(A))
+        DB = rho(DH * silu(A))
+        DZG = DA @ f["v_gate"]
+        DZU = DB @ f["v_up"]
+        DUG = rho(DZG * f["s_gate"])
+        DUU = rho(DZU * f["s_up"])
+
+        def outer_sum(P, Q):       # P^T Q with its scales
+            aP, aQ = np.abs(P), np.abs(Q)
+            return P.T @ Q, aP.T @ aQ, np.outer(colmax(P), colmax(Q))
+
+        def col_sum(P, Q):         # sum over rows of P * Q, per column
+            t = P * Q
+            return t.sum(axis=0), np.abs(t).sum(axis=0), (np.abs(t).max(axis=0) if len(t)
+                                                          else np.zeros(t.shape[1]))
+        res = {"dv_down": outer_sum(DY, ZD), "ds_down": col_sum(DZD, UD),
+               "du_down": outer_sum(Hh, DUD), "dv_gate": outer_sum(DA, ZG),
+               "dv_up": outer_sum(DB, ZU), "ds_gate": col_sum(DZG, UG),
+               "ds_up": col_sum(DZU, UU), "du_gate": outer_sum(X, DUG),
+               "du_up": outer_sum(X, DUU)}
+        DX = DUG @ f["u_gate"].T + DUU @ f["u_up"].T
+        SDX = np.abs(DUG) @ np.abs(f["u_gate"]).T + np.abs(DUU) @ np.abs(f["u_up"]).T
+        rmax = np.maximum(
+            np.abs(DUG).max(axis=1, initial=0.0)[:, None] * np.abs(f["u_gate"]).max(axis=1)[None, :],
+            np.abs(DUU).max(axis=1, initial=0.0)[:, None] * np.abs(f["u_up"]).max(axis=1)[None, :])
+        out["dx"][tok] += DX
+        out["S_dx"][tok] += SDX
+        out["B_dx"][tok] = np.maximum(out["B_dx"][tok], rmax)
+        return ZD @ f["v_down"].T, res
+
+    if spec.rank > 0:
+        acc = {n: [] for n in LOWRANK_GRADS}
+        for e in range(E):
+            ts, js = np.nonzero((idx == e) & (rows >= 0))
+            f = {n: b[e] for n, b in ex.lr.items()}
+            Y, res = lowrank_expert(ts, gates[ts, js], f)
+            dg[ts, js] = np.sum(dy[ts] * Y, axis=1)
+            for n in LOWRANK_GRADS:
+                acc[n].append(res[n])
+        for n in LOWRANK_GRADS:
+            put(n, *(np.stack([r[i] for r in acc[n]]) for i in range(3)))
+    for kind, n in (("w", E if spec.rank == 0 else 0), ("sh", S)):
         if n == 0:
             continue
         acc = {p: [] for p in ("gate", "up", "down")}

@@ -555,6 +555,105 @@ def test_backward_matches_finite_differences(case):
             assert _rel(g[name], _fd_grad(fn, w[key])) < 1e-7, name
 
 
+LR_BWD_CASES = [
+    # T, d, E, k, S, F, r, score, renorm, capacity
+    (5, 6, 4, 2, 0, 5, 3, "softmax", False, 0),
+    (6, 5, 3, 2, 1, 4, 2, "softmax", True, 0),
+    (5, 4, 5, 2, 0, 3, 2, "sigmoid", True, 0),
+    (8, 4, 3, 2, 0, 3, 2, "softmax", True, 3),     # capacity drops some slots
+]
+
+
+@pytest.mark.parametrize("case", LR_BWD_CASES)
+def test_lowrank_backward_matches_finite_differences(case):
+    """Rank-r experts: every factor gradient (U, s, V of gate, up and down),
+    dx and dW_r against central differences of the forward oracle, selection
+    held fixed, in float64 (rho = identity)."""
+    T, d, E, k, S, F, r, score, renorm, cap = case
+    w = _f64(_inputs(T, d, E, k, S, F, seed=80 + T, rank=r, score=score, logit_std=0.5,
+                     select_std=0.2 if score == "sigmoid" else 0.0))
+    spec = _spec(d, E, k, S, F, rank=r, score=score, renorm=renorm, capacity=cap, bf16=False,
+                 aux_coef=0.05)
+    x = w.pop("x")
+    dy = np.random.default_rng(9).standard_normal((T, d))
+    base = oracle.layer_forward(x, w, spec)
+    if cap:
+        assert base["n_dropped"] > 0
+    g = oracle.layer_backward(x, w, spec, dy, aux_grad=1.3)
+    fn = lambda: _loss(x, w, spec, dy, 1.3, base["idx"])
+    assert _rel(g["dx"], _fd_grad(fn, x)) < 1e-7
+    assert _rel(g["dw_router"], _fd_grad(fn, w["w_router"])) < 1e-7
+    for name in oracle.LOWRANK_GRADS:
+        assert _rel(g[name], _fd_grad(fn, w[name[1:]])) < 1e-7, name
+    if S:
+        for name, key in (("dsh_gate", "sh_gate"), ("dsh_up", "sh_up"), ("dsh_down", "sh_down")):
+            assert _rel(g[name], _fd_grad(fn, w[key])) < 1e-7, name
+
+
+def test_lowrank_backward_equals_the_dense_backward_of_the_product():
+    """With rho = identity a rank-r expert is the dense expert W = U diag(s) V^T,
+    so its factor gradients follow from the dense backward's dW:
+    dU = dW V diag(s), ds = diag(U^T dW V), dV = dW^T U diag(s); dx and dW_r
+    are the dense ones."""
+    T, d, E, k, S, F, r = 12, 10, 5, 2, 1, 7, 4
+    w = _f64(_inputs(T, d, E, k, S, F, seed=5, rank=r, logit_std=0.4))
+    x = w.pop("x")
+    spec = _spec(d, E, k, S, F, rank=r, bf16=False)
+    dense = {n: v for n, v in w.items() if not n[:2] in ("u_", "s_", "v_")}
+    for m, (din, dout) in (("gate", (d, F)), ("up", (d, F)), ("down", (F, d))):
+        dense["w_" + m] = np.stack([w["u_" + m][e] @ np.diag(w["s_" + m][e]) @ w["v_" + m][e].T
+                                    for e in range(E)])
+    dy = np.random.default_rng(2).standard_normal((T, d))
+    g = oracle.layer_backward(x, w, spec, dy, aux_grad=0.9)
+    h = oracle.layer_backward(x, dense, _spec(d, E, k, S, F, bf16=False), dy, aux_grad=0.9)
+    assert _rel(g["dx"], h["dx"]) < 1e-12 and _rel(g["dw_router"], h["dw_router"]) < 1e-12
+    for m in ("gate", "up", "down"):
+        U, s_, V, dW = w["u_" + m], w["s_" + m], w["v_" + m], h["dw_" + m]
+        du = np.stack([dW[e] @ V[e] * s_[e][None, :] for e in range(E)])
+        ds = np.stack([np.einsum("ci,cf,fi->i", U[e], dW[e], V[e]) for e in range(E)])
+        dv = np.stack([dW[e].T @ U[e] * s_[e][None, :] for e in range(E)])
+        assert _rel(g["du_" + m], du) < 1e-12, m
+        assert _rel(g["ds_" + m], ds) < 1e-12, m
+        assert _rel(g["dv_" + m], dv) < 1e-12, m
+
+
+@pytest.mark.parametrize("case", LR_BWD_CASES)
+@pytest.mark.parametrize("bf16", [False, True])
+def test_lowrank_batched_backward_equals_token_loop(case, bf16):
+    """The per-expert batched low-rank backward (full-size checks) gives the
+    token loop's gradients, with the same bf16 rounding points."""
+    T, d, E, k, S, F, r, score, renorm, cap = case
+    w = _f64(_inputs(T + 20, d + 4, E, k, S, F + 8, seed=90 + T, rank=r, score=score,
+                     logit_std=0.5, select_std=0.2 if score == "sigmoid" else 0.0))
+    spec = _spec(d + 4, E, k, S, F + 8, rank=r, score=score, renorm=renorm, capacity=cap,
+                 bf16=bf16, aux_coef=0.05)
+    x = w.pop("x")
+    dy = np.random.default_rng(3).standard_normal((T + 20, d + 4))
+    a = oracle.layer_backward(x, w, spec, dy, aux_grad=1.1)
+    b = oracle.layer_backward_batched(x, w, spec, dy, aux_grad=1.1)
+    names = ["dx", "dw_router", *oracle.LOWRANK_GRADS]
+    if S:
+        names += ["dsh_gate", "dsh_up", "dsh_down"]
+    for n in names:
+        assert _rel(b[n], a[n]) < 1e-10, n
+        assert np.all(b["S_" + n] >= np.abs(b[n]) * (1 - 1e-12)), n
+        assert np.all(b["B_" + n] >= 0), n
+
+
+def test_lowrank_backward_bf16_rounding_points_are_small_perturbations():
+    """The bf16 rounding points move the low-rank gradients by rounding-level
+    amounts only (against the same layer with rho = identity)."""
+    T, d, E, k, S, F, r = 30, 64, 6, 2, 0, 48, 16
+    w = _inputs(T, d, E, k, S, F, seed=12, rank=r, bf16=True, logit_std=0.3)
+    x = w.pop("x")
+    dy = np.random.default_rng(4).standard_normal((T, d))
+    g1 = oracle.layer_backward_batched(x, w, _spec(d, E, k, S, F, rank=r, bf16=True), dy)
+    g0 = oracle.layer_backward_batched(x, w, _spec(d, E, k, S, F, rank=r, bf16=False), dy)
+    for n in ["dx", *oracle.LOWRANK_GRADS]:
+        rel = _rel(g1[n], g0[n])
+        assert 0 < rel < 5e-2, (n, rel)
+
+
 def test_backward_aux_term_alone():
     """With dy = 0 only the aux statistic carries gradient: the expert weights
     get none, and the router gradient matches differences of aux alone."""
