@@ -20,12 +20,17 @@ MOE_GROUPS_ROUTED, MOE_GROUPS_SHARED = 1, 2
 
 MOE_WS_H, MOE_WS_H_SHARED, MOE_WS_Y_ROUTED, MOE_WS_Y_SHARED = 0, 1, 2, 3
 MOE_WS_HQ, MOE_WS_HQ_SCALE, MOE_WS_HQ_SHARED, MOE_WS_HQ_SHARED_SCALE = 4, 5, 6, 7
+MOE_BWS_DY_ROUTED, MOE_BWS_X_PERM, MOE_BWS_DAB, MOE_BWS_DL = 0, 1, 2, 3
+(MOE_BWS_LR_UG, MOE_BWS_LR_UU, MOE_BWS_LR_Z_GU, MOE_BWS_LR_AB, MOE_BWS_LR_H, MOE_BWS_LR_UD,
+ MOE_BWS_LR_ZD, MOE_BWS_LR_DZD, MOE_BWS_LR_DUD, MOE_BWS_LR_DZG, MOE_BWS_LR_DZU,
+ MOE_BWS_LR_DU_GU) = range(4, 16)
 
 EXPORTED = ("moe_capacity", "moe_max_rows", "moe_workspace_bytes", "moe_workspace_region",
             "moe_route", "moe_permute",
             "moe_grouped_ffn", "moe_combine", "moe_bias_update", "moe_quantize_fp8",
             "moe_layer_forward", "moe_layer_forward_noalloc",
-            "moe_layer_forward_timed", "moe_backward_workspace_bytes", "moe_layer_backward",
+            "moe_layer_forward_timed", "moe_backward_workspace_bytes",
+            "moe_backward_workspace_region", "moe_layer_backward",
             "moe_layer_backward_timed", "moe_stage_name", "moe_status_str", "moe_last_error")
 
 
@@ -56,7 +61,8 @@ class MoeOutputs(ctypes.Structure):
 
 
 GRAD_FIELDS = ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dsh_gate", "dsh_up",
-               "dsh_down")
+               "dsh_down", "du_gate", "ds_gate", "dv_gate", "du_up", "ds_up", "dv_up",
+               "du_down", "ds_down", "dv_down")
 
 
 class MoeGrads(ctypes.Structure):
@@ -93,6 +99,8 @@ def load():
         "moe_workspace_bytes": (c_size_t, [cfgp, c_int64]),
         "moe_workspace_region": (c_int, [cfgp, c_int64, c_int32, POINTER(c_size_t),
                                          POINTER(c_size_t)]),
+        "moe_backward_workspace_region": (c_int, [cfgp, c_int64, c_int32, POINTER(c_size_t),
+                                                  POINTER(c_size_t)]),
         "moe_route": (c_int, [cfgp, c_int64, c_void_p, wp, op, c_void_p, c_size_t, c_void_p]),
         "moe_permute": (c_int, [cfgp, c_int64, c_void_p, op, c_void_p, c_void_p, c_size_t,
                                 c_void_p]),
@@ -147,6 +155,15 @@ def moe_workspace_region(cfg: MoeConfig, T: int, which: int) -> tuple[int, int]:
     off, n = c_size_t(0), c_size_t(0)
     _check(load().moe_workspace_region(ctypes.byref(cfg), T, which, ctypes.byref(off),
                                        ctypes.byref(n)), "moe_workspace_region")
+    return off.value, n.value
+
+
+def moe_backward_workspace_region(cfg: MoeConfig, T: int, which: int) -> tuple[int, int]:
+    """(byte offset into the backward workspace, bytes) of an intermediate region."""
+    off, n = c_size_t(0), c_size_t(0)
+    _check(load().moe_backward_workspace_region(ctypes.byref(cfg), T, which, ctypes.byref(off),
+                                                ctypes.byref(n)),
+           "moe_backward_workspace_region")
     return off.value, n.value
 
 

@@ -789,14 +789,25 @@ int layer_forward(const moe_config* c, int64_t T, const void* x, const moe_weigh
 constexpr int kRouterKChunk = 512;
 constexpr int kSharedKChunk = 4096;
 
+// bf16 layers with E a multiple of 8 (the router's gradient products read E
+// in 16-byte pieces); rank-r experts with r a multiple of 32 (a K-step of the
+// backward products) and no shared experts.
 bool backward_supported(const moe_config* c) {
-  return c->dtype == MOE_BF16 && c->rank == 0 && c->n_routed % 8 == 0;
+  if (c->dtype != MOE_BF16 || c->n_routed % 8) return false;
+  if (c->rank == 0) return true;
+  return c->rank % 32 == 0 && c->rank <= 64 && c->n_shared == 0;
 }
 
 struct BwdLayout {
-  int64_t T = 0, R = 0, nch_r = 1, nch_s = 1;
+  int64_t T = 0, R = 0, nch_r = 1, nch_s = 1, lr_tiles = 0;
   size_t dyr = 0, dysh = 0, dg = 0, dl = 0, dab = 0, dabsh = 0, xperm = 0, dxp = 0,
          dxsh = 0, part_r = 0, part_g = 0, part_u = 0, part_d = 0, total = 0;
+  // rank-r experts: the 256-row tile list, the recomputed forward chain
+  // (x U, its scaled and rounded z, the gate and up products, h, h U_d, z_d)
+  // and the backward's (dz_d, dz_d s_d rounded, dz_g | dz_u, their scaled
+  // and rounded forms)
+  size_t lr_plan = 0, ug = 0, uu = 0, dzd = 0, ud = 0, dzg = 0, dzu = 0, zgu = 0, zd = 0,
+         dud = 0, dugu = 0, ab = 0, hh = 0;
 };
 
 BwdLayout make_bwd_layout(const moe_config* c, int64_t T) {
@@ -826,6 +837,23 @@ BwdLayout make_bwd_layout(const moe_config* c, int64_t T) {
   B.part_g = take(shp);
   B.part_u = take(shp);
   B.part_d = take(shp);
+  if (c->rank > 0) {
+    const int64_t r = c->rank, R = B.R;
+    B.lr_tiles = ceil_div(R, kGemmBigBM) + E;
+    B.lr_plan = take((size_t)(1 + 2 * B.lr_tiles) * 4);
+    B.ug = take((size_t)R * r * 4);
+    B.uu = take((size_t)R * r * 4);
+    B.dzd = take((size_t)R * r * 4);
+    B.ud = take((size_t)R * r * 4);
+    B.dzg = take((size_t)R * r * 4);
+    B.dzu = take((size_t)R * r * 4);
+    B.zgu = take((size_t)R * 2 * r * 2);
+    B.zd = take((size_t)R * r * 2);
+    B.dud = take((size_t)R * r * 2);
+    B.dugu = take((size_t)R * 2 * r * 2);
+    B.ab = take((size_t)R * 2 * F * 4);
+    B.hh = take((size_t)R * F * 2);
+  }
   B.total = off;
   return B;
 }
@@ -836,6 +864,254 @@ BwdGemm bwd_problem() {
   p.G = 1;
   p.c_split = INT32_MAX;
   return p;
+}
+
+// Backward of a layer of rank-r experts (no shared experts): the upstream
+// rows, gate gradients and router gradient as for dense experts; then, per
+// dispatched row of expert e (W[in, out] = U[in, r] diag(s) V[out, r]^T),
+// the forward chain recomputed and the chain rule back through it:
+//   ug = x U_g, zg = bf16(ug s_g), a = zg V_g^T (same for up), h = bf16(SiLU(a) b),
+//   ud = h U_d, zd = bf16(ud s_d); with dY = bf16(gate dy):
+//   dzd = dY V_d, dud = bf16(dzd s_d), dh = dud U_d^T -> da, db (bf16),
+//   dzg = da V_g, dzu = db V_u, dug = bf16(dzg s_g), duu = bf16(dzu s_u),
+//   dx rows = dug U_g^T + duu U_u^T;
+//   dV_d = dY^T zd, dU_d = h^T dud, dV_g = da^T zg, dV_u = db^T zu,
+//   dU_g = x^T dug, dU_u = x^T duu (summed over the expert's rows), and
+//   ds = the row sums of dz * u.
+void lowrank_backward(Runner& Rn, const moe_config* c, int64_t T, const void* x,
+                      const moe_weights* w, const moe_outputs* o, const float* dy,
+                      float aux_grad, moe_grads* g, const Layout& L, const BwdLayout& B,
+                      void* fws, void* bws) {
+  const int64_t E = c->n_routed, d = c->hidden, F = c->ffn, k = c->top_k, r = c->rank;
+  const int64_t R = B.R;
+  uint16_t* dyr = at<uint16_t>(bws, B.dyr);
+  float* dg = at<float>(bws, B.dg);
+  uint16_t* dl = at<uint16_t>(bws, B.dl);
+  uint16_t* dab = at<uint16_t>(bws, B.dab);
+  uint16_t* xperm = at<uint16_t>(bws, B.xperm);
+  float* dxp = at<float>(bws, B.dxp);
+  int32_t* plan = at<int32_t>(bws, B.lr_plan);
+  float *ug = at<float>(bws, B.ug), *uu = at<float>(bws, B.uu), *dzd = at<float>(bws, B.dzd);
+  float *ud = at<float>(bws, B.ud), *dzg = at<float>(bws, B.dzg), *dzu = at<float>(bws, B.dzu);
+  uint16_t *zgu = at<uint16_t>(bws, B.zgu), *zd = at<uint16_t>(bws, B.zd);
+  uint16_t *dud = at<uint16_t>(bws, B.dud), *dugu = at<uint16_t>(bws, B.dugu);
+  float* ab = at<float>(bws, B.ab);
+  uint16_t* hh = at<uint16_t>(bws, B.hh);
+  const float* y_perm = at<float>(fws, L.y_perm);
+  const float* logits = at<float>(fws, L.logits);
+  const int32_t* offs = o->offsets;
+  const int32_t* rows = o->offsets + E;
+
+  // a product over the dispatched rows of each expert (the 256-row tile list)
+  auto rows_problem = [&](const void* A, int64_t lda, const void* B0, int64_t ldb, int64_t bgrp,
+                          float* C, int64_t ldc, int64_t N, int64_t K) {
+    BwdGemm p = bwd_problem();
+    p.A = A;
+    p.lda = lda;
+    p.B0 = B0;
+    p.ldb = ldb;
+    p.b_group = bgrp;
+    p.C0 = C;
+    p.ldc = ldc;
+    p.m_off = offs;
+    p.plan = plan;
+    p.N = (int32_t)N;
+    p.K = (int32_t)K;
+    p.G = (int32_t)E;
+    p.n_tiles_n = (int32_t)ceil_div(N, 128);
+    p.max_m_tiles = (int32_t)B.lr_tiles;
+    return p;
+  };
+  // a weight gradient: sum over each expert's rows of A^T B
+  auto wgrad_problem = [&](const void* A, int64_t lda, const void* B0, int64_t ldb, float* C,
+                           int64_t M, int64_t N) {
+    BwdGemm p = bwd_problem();
+    p.A = A;
+    p.lda = lda;
+    p.B0 = B0;
+    p.ldb = ldb;
+    p.C0 = C;
+    p.ldc = N;
+    p.c_group = M * N;
+    p.k_off = offs;
+    p.M = (int32_t)M;
+    p.N = (int32_t)N;
+    p.K = (int32_t)R;
+    p.G = (int32_t)E;
+    p.n_tiles_m = (int32_t)ceil_div(M, kGemmBigBM);
+    p.n_tiles_n = (int32_t)ceil_div(N, 128);
+    return p;
+  };
+  auto scale = [&](const char* name, LowRankScaleJob j0, LowRankScaleJob j1, int n) {
+    LowRankScaleJobs J{};
+    J.job[0] = j0;
+    J.job[1] = j1;
+    J.n = n;
+    J.offsets = offs;
+    J.rows = rows;
+    J.E = (int32_t)E;
+    J.r = (int32_t)r;
+    Rn.run(name, [&] { return launch_scale_round(J, R, Rn.stream); });
+  };
+  auto s16 = [](const void* p) { return static_cast<const uint16_t*>(p); };
+
+  if (T > 0) {
+    CombineBwdArgs cb{};
+    cb.dy = dy;
+    cb.x = static_cast<const uint16_t*>(x);
+    cb.x_perm = xperm;
+    cb.y_routed = y_perm;
+    cb.row_of_slot = o->row_of_slot;
+    cb.topk_gate = o->topk_gate;
+    cb.dy_routed = dyr;
+    cb.dy_shared = nullptr;
+    cb.dgate = dg;
+    cb.T = T;
+    cb.d = (int32_t)d;
+    cb.k = (int32_t)k;
+    Rn.run("combine_bwd", [&] { return launch_combine_bwd(cb, Rn.stream); });
+
+    RouterBwdArgs rb{};
+    rb.logits = logits;
+    rb.topk_idx = o->topk_idx;
+    rb.topk_gate = o->topk_gate;
+    rb.dgate = dg;
+    rb.counts = o->counts;
+    rb.dl = dl;
+    rb.T = T;
+    rb.E = (int32_t)E;
+    rb.k = (int32_t)k;
+    rb.score = c->score;
+    rb.renorm = c->renorm_topk;
+    rb.aux_scale = (float)((double)aux_grad * c->aux_coef * (double)E / (double)T);
+    Rn.run("router_bwd", [&] { return launch_router_bwd(rb, Rn.stream); });
+    Rn.run("plan", [&] { return launch_plan(offs, (int32_t)E, kGemmBigBM, plan, Rn.stream); });
+
+    {  // x U_g, x U_u and dY V_d
+      BwdLaunch BL{};
+      BL.p[0] = rows_problem(xperm, d, w->u_gate, r, d * r, ug, r, r, d);
+      BL.p[1] = rows_problem(xperm, d, w->u_up, r, d * r, uu, r, r, d);
+      BL.p[2] = rows_problem(dyr, d, w->v_down, r, d * r, dzd, r, r, d);
+      BL.n = 3;
+      Rn.run("lr_in_gemm", [&] { return launch_gemm_bwd(BL, true, false, kBwdStoreF32, Rn.stream); });
+    }
+    scale("lr_z_in", LowRankScaleJob{ug, r, s16(w->s_gate), zgu, 2 * r},
+          LowRankScaleJob{uu, r, s16(w->s_up), zgu + r, 2 * r}, 2);
+    {  // a = zg V_g^T, b = zu V_u^T
+      BwdLaunch BL{};
+      BL.p[0] = rows_problem(zgu, 2 * r, w->v_gate, r, F * r, ab, 2 * F, F, r);
+      BL.p[1] = rows_problem(zgu + r, 2 * r, w->v_up, r, F * r, ab + F, 2 * F, F, r);
+      BL.n = 2;
+      Rn.run("lr_ab_gemm", [&] { return launch_gemm_bwd(BL, true, true, kBwdStoreF32, Rn.stream); });
+    }
+    Rn.run("lr_h", [&] { return launch_swiglu_h(ab, hh, rows, R, (int)F, Rn.stream); });
+    {  // ud = h U_d
+      BwdLaunch BL{};
+      BL.p[0] = rows_problem(hh, F, w->u_down, r, F * r, ud, r, r, F);
+      BL.n = 1;
+      Rn.run("lr_ud_gemm", [&] { return launch_gemm_bwd(BL, true, false, kBwdStoreF32, Rn.stream); });
+    }
+    scale("lr_z_down", LowRankScaleJob{ud, r, s16(w->s_down), zd, r},
+          LowRankScaleJob{dzd, r, s16(w->s_down), dud, r}, 2);
+    {  // dh = dud U_d^T with the SwiGLU backward in the epilogue
+      BwdLaunch BL{};
+      BwdGemm& p = BL.p[0] = rows_problem(dud, r, w->u_down, r, F * r,
+                                          reinterpret_cast<float*>(dab), 2 * F, F, r);
+      p.ab = ab;
+      p.ab_ld = 2 * F;
+      p.half = (int32_t)F;
+      BL.n = 1;
+      Rn.run("lr_dh_gemm", [&] { return launch_gemm_bwd(BL, true, true, kBwdSwiGLU, Rn.stream); });
+    }
+    {  // dz_g = da V_g, dz_u = db V_u
+      BwdLaunch BL{};
+      BL.p[0] = rows_problem(dab, 2 * F, w->v_gate, r, F * r, dzg, r, r, F);
+      BL.p[1] = rows_problem(dab + F, 2 * F, w->v_up, r, F * r, dzu, r, r, F);
+      BL.n = 2;
+      Rn.run("lr_dz_gemm", [&] { return launch_gemm_bwd(BL, true, false, kBwdStoreF32, Rn.stream); });
+    }
+    scale("lr_du", LowRankScaleJob{dzg, r, s16(w->s_gate), dugu, 2 * r},
+          LowRankScaleJob{dzu, r, s16(w->s_up), dugu + r, 2 * r}, 2);
+    {  // input-gradient rows [dug | duu] [U_g; U_u]^T, and the router's dl W_r^T
+      BwdLaunch BL{};
+      BwdGemm& p = BL.p[0] = rows_problem(dugu, 2 * r, w->u_gate, r, d * r, dxp, d, d, 2 * r);
+      p.B1 = w->u_up;
+      p.k_seg = (int32_t)r;
+      BwdGemm& q = BL.p[1] = bwd_problem();
+      q.A = dl;
+      q.lda = E;
+      q.B0 = w->w_router;
+      q.ldb = E;
+      q.C0 = g->dx;
+      q.ldc = d;
+      q.M = (int32_t)T;
+      q.N = (int32_t)d;
+      q.K = (int32_t)E;
+      q.k_chunk = q.K;
+      q.n_tiles_m = (int32_t)ceil_div(T, kGemmBigBM);
+      q.n_tiles_n = (int32_t)ceil_div(d, 128);
+      BL.n = 2;
+      Rn.run("dgrad_gemm", [&] { return launch_gemm_bwd(BL, true, true, kBwdStoreF32, Rn.stream); });
+    }
+    DxGatherArgs dxa{};
+    dxa.dx_rows = dxp;
+    dxa.dx_shared = nullptr;
+    dxa.row_of_slot = o->row_of_slot;
+    dxa.dx = g->dx;
+    dxa.T = T;
+    dxa.d = (int32_t)d;
+    dxa.k = (int32_t)k;
+    Rn.run("dx_gather", [&] { return launch_dx_gather(dxa, Rn.stream); });
+  }
+
+  {  // factor gradients, each summed over its expert's rows
+    BwdLaunch BL{};
+    BL.p[0] = wgrad_problem(dyr, d, zd, r, g->dv_down, d, r);
+    BL.p[1] = wgrad_problem(hh, F, dud, r, g->du_down, F, r);
+    BL.p[2] = wgrad_problem(dab, 2 * F, zgu, 2 * r, g->dv_gate, F, r);
+    BL.p[3] = wgrad_problem(dab + F, 2 * F, zgu + r, 2 * r, g->dv_up, F, r);
+    BL.p[4] = wgrad_problem(xperm, d, dugu, 2 * r, g->du_gate, d, r);
+    BL.n = 5;
+    Rn.run("wgrad_gemm", [&] { return launch_gemm_bwd(BL, false, false, kBwdStoreF32, Rn.stream); });
+  }
+  {  // du_up and the router's x^T dl (split over tokens when long)
+    BwdLaunch BL{};
+    BL.p[0] = wgrad_problem(xperm, d, dugu + r, 2 * r, g->du_up, d, r);
+    BwdGemm& p = BL.p[1] = bwd_problem();
+    p.A = x;
+    p.lda = d;
+    p.B0 = dl;
+    p.ldb = E;
+    p.C0 = B.nch_r > 1 ? at<float>(bws, B.part_r) : g->dw_router;
+    p.ldc = E;
+    p.c_chunk = d * E;
+    p.M = (int32_t)d;
+    p.N = (int32_t)E;
+    p.K = (int32_t)T;
+    p.k_chunk = B.nch_r > 1 ? kRouterKChunk : (int32_t)std::max<int64_t>(T, 1);
+    p.n_chunks = (int32_t)B.nch_r;
+    p.n_tiles_m = (int32_t)ceil_div(d, kGemmBigBM);
+    p.n_tiles_n = (int32_t)ceil_div(E, 128);
+    BL.n = 2;
+    Rn.run("wgrad_gemm2", [&] { return launch_gemm_bwd(BL, false, false, kBwdStoreF32, Rn.stream); });
+    if (B.nch_r > 1) {
+      Rn.run("reduce_router", [&] {
+        return launch_reduce_chunks(at<float>(bws, B.part_r), g->dw_router, 1, B.nch_r, d * E,
+                                    Rn.stream);
+      });
+    }
+  }
+  {  // ds = row sums of dz * u per expert
+    LowRankDsJobs J{};
+    J.job[0] = LowRankDsJob{dzg, r, ug, r, g->ds_gate};
+    J.job[1] = LowRankDsJob{dzu, r, uu, r, g->ds_up};
+    J.job[2] = LowRankDsJob{dzd, r, ud, r, g->ds_down};
+    J.n = 3;
+    J.offsets = offs;
+    J.E = (int32_t)E;
+    J.r = (int32_t)r;
+    Rn.run("lr_ds", [&] { return launch_ds_sum(J, Rn.stream); });
+  }
 }
 
 int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weights* w,
@@ -851,7 +1127,10 @@ int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weig
   if (T > 0 && (!x || !dy || !o->topk_idx || !o->topk_gate || !o->row_of_slot ||
                 !o->sorted_token))
     return MOE_EINVAL;
-  if (!g || !g->dw_router || !g->dw_gate || !g->dw_up || !g->dw_down || (T > 0 && !g->dx))
+  if (!g || !g->dw_router || (T > 0 && !g->dx)) return MOE_EINVAL;
+  if (c->rank == 0 && (!g->dw_gate || !g->dw_up || !g->dw_down)) return MOE_EINVAL;
+  if (c->rank > 0 && (!g->du_gate || !g->ds_gate || !g->dv_gate || !g->du_up || !g->ds_up ||
+                      !g->dv_up || !g->du_down || !g->ds_down || !g->dv_down))
     return MOE_EINVAL;
   if (c->n_shared > 0 && (!g->dsh_gate || !g->dsh_up || !g->dsh_down)) return MOE_EINVAL;
   Layout L;
@@ -879,6 +1158,11 @@ int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weig
   const void* h = at<void>(fws, L.h);
   const void* h_sh = at<void>(fws, L.h_sh);
   const int32_t* plan256 = at<int32_t>(fws, L.plan);
+  if (c->rank > 0) {
+    lowrank_backward(Rn, c, T, x, w, o, dy, aux_grad, g, L, B, fws, bws);
+    st = finish(tl);
+    return st ? st : tl.n;
+  }
 
   if (T > 0) {
     // upstream rows of the expert products and the gate gradients
@@ -1404,6 +1688,38 @@ int moe_workspace_region(const moe_config* c, int64_t T, int32_t which, size_t* 
     case MOE_WS_HQ_SCALE: at = L.hs; n = q ? (size_t)L.R * 4 : 0; break;
     case MOE_WS_HQ_SHARED: at = L.hq_sh; n = fp8(c) ? (size_t)T * S * F : 0; break;
     case MOE_WS_HQ_SHARED_SCALE: at = L.hs_sh; n = fp8(c) && S > 0 ? (size_t)T * 4 : 0; break;
+    default: return MOE_EINVAL;
+  }
+  *offset = n ? at : 0;
+  *bytes = n;
+  return MOE_OK;
+}
+
+int moe_backward_workspace_region(const moe_config* c, int64_t T, int32_t which, size_t* offset,
+                                  size_t* bytes) {
+  if (!valid_config(c) || T < 0 || !offset || !bytes) return MOE_EINVAL;
+  const BwdLayout B = make_bwd_layout(c, T);
+  const int64_t d = c->hidden, F = c->ffn, E = c->n_routed, R = B.R;
+  const int64_t r = c->rank;
+  const bool lr = r > 0;
+  size_t at = 0, n = 0;
+  switch (which) {
+    case MOE_BWS_DY_ROUTED: at = B.dyr; n = (size_t)R * d * 2; break;
+    case MOE_BWS_X_PERM: at = B.xperm; n = (size_t)R * d * 2; break;
+    case MOE_BWS_DAB: at = B.dab; n = (size_t)R * 2 * F * 2; break;
+    case MOE_BWS_DL: at = B.dl; n = (size_t)T * E * 2; break;
+    case MOE_BWS_LR_UG: at = B.ug; n = lr ? (size_t)R * r * 4 : 0; break;
+    case MOE_BWS_LR_UU: at = B.uu; n = lr ? (size_t)R * r * 4 : 0; break;
+    case MOE_BWS_LR_Z_GU: at = B.zgu; n = lr ? (size_t)R * 2 * r * 2 : 0; break;
+    case MOE_BWS_LR_AB: at = B.ab; n = lr ? (size_t)R * 2 * F * 4 : 0; break;
+    case MOE_BWS_LR_H: at = B.hh; n = lr ? (size_t)R * F * 2 : 0; break;
+    case MOE_BWS_LR_UD: at = B.ud; n = lr ? (size_t)R * r * 4 : 0; break;
+    case MOE_BWS_LR_ZD: at = B.zd; n = lr ? (size_t)R * r * 2 : 0; break;
+    case MOE_BWS_LR_DZD: at = B.dzd; n = lr ? (size_t)R * r * 4 : 0; break;
+    case MOE_BWS_LR_DUD: at = B.dud; n = lr ? (size_t)R * r * 2 : 0; break;
+    case MOE_BWS_LR_DZG: at = B.dzg; n = lr ? (size_t)R * r * 4 : 0; break;
+    case MOE_BWS_LR_DZU: at = B.dzu; n = lr ? (size_t)R * r * 4 : 0; break;
+    case MOE_BWS_LR_DU_GU: at = B.dugu; n = lr ? (size_t)R * 2 * r * 2 : 0; break;
     default: return MOE_EINVAL;
   }
   *offset = n ? at : 0;

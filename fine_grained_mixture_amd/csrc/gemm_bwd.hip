@@ -557,7 +557,7 @@ hipError_t launch_gemm_bwd(BwdLaunch& L, bool a_kc, bool b_kc, int epi, hipStrea
   if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)total), block(kThreads);
   // the layouts the layer backward uses: dgrad and dh (k-contiguous both),
-  // wgrad (k-strided both)
+  // wgrad (k-strided both), and rows times a row-major weight
   if (epi == kBwdSwiGLU) {
     if (!a_kc || !b_kc) return hipErrorInvalidValue;
     for (int i = 0; i < L.n; ++i)
@@ -567,6 +567,9 @@ hipError_t launch_gemm_bwd(BwdLaunch& L, bool a_kc, bool b_kc, int epi, hipStrea
     hipLaunchKernelGGL((gemm_bwd_kernel<true, true, kBwdStoreF32>), grid, block, 0, s, L);
   } else if (!a_kc && !b_kc) {
     hipLaunchKernelGGL((gemm_bwd_kernel<false, false, kBwdStoreF32>), grid, block, 0, s, L);
+  } else if (a_kc && !b_kc) {
+    // rows times a row-major weight (the rank-r experts' U x and V products)
+    hipLaunchKernelGGL((gemm_bwd_kernel<true, false, kBwdStoreF32>), grid, block, 0, s, L);
   } else {
     return hipErrorInvalidValue;
   }

@@ -366,6 +366,42 @@ hipError_t launch_dx_gather(const DxGatherArgs& a, hipStream_t s);
 hipError_t launch_reduce_chunks(const float* part, float* out, int64_t groups, int64_t chunks,
                                 int64_t n, hipStream_t s);
 
+// Backward of rank-r experts: the steps between its products.
+// out[row, c] = bf16(in[row, c] s[e(row), c]) for rows < *rows, c < r.
+struct LowRankScaleJob {
+  const float* in;
+  int64_t ldi;
+  const uint16_t* s;         // [E, r] bf16
+  uint16_t* out;
+  int64_t ldo;
+};
+struct LowRankScaleJobs {
+  LowRankScaleJob job[2];
+  int32_t n;
+  const int32_t* offsets;    // [E + 1]
+  const int32_t* rows;       // &offsets[E]
+  int32_t E, r;
+};
+hipError_t launch_scale_round(const LowRankScaleJobs& J, int64_t R_max, hipStream_t s);
+// h[row, f] = bf16(SiLU(ab[row, f]) * ab[row, F + f]) for rows < *rows.
+hipError_t launch_swiglu_h(const float* ab, uint16_t* h, const int32_t* rows, int64_t R_max,
+                           int F, hipStream_t s);
+// ds[e, i] = sum over the rows of expert e, in order, of p[row, i] q[row, i].
+struct LowRankDsJob {
+  const float* p;
+  int64_t ldp;
+  const float* q;
+  int64_t ldq;
+  float* ds;                 // [E, r]
+};
+struct LowRankDsJobs {
+  LowRankDsJob job[3];
+  int32_t n;
+  const int32_t* offsets;
+  int32_t E, r;
+};
+hipError_t launch_ds_sum(const LowRankDsJobs& J, hipStream_t s);
+
 // Records a failed HIP call's text for moe_last_error(); returns MOE_EHIP.
 int report_hip_error(hipError_t e);
 // The whole layer forward on a given workspace (api.cpp), and its argument

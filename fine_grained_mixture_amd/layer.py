@@ -325,18 +325,25 @@ class Grads:
 
 
 def allocate_grads(cfg: MoeConfig, T: int, device="cuda") -> Grads:
-    E, d, F, S = cfg.n_routed, cfg.hidden, cfg.ffn, cfg.n_shared
+    """Gradient tensors of one backward call: dense experts' dW, or rank-r
+    experts' factor gradients in the factors' shapes."""
+    E, d, F, S, r = cfg.n_routed, cfg.hidden, cfg.ffn, cfg.n_shared, cfg.rank
     f32 = dict(dtype=torch.float32, device=device)
+    dense = r == 0
     t = {
         "dx": torch.empty((T, d), **f32),
         "dw_router": torch.empty((d, E), **f32),
-        "dw_gate": torch.empty((E, d, F), **f32),
-        "dw_up": torch.empty((E, d, F), **f32),
-        "dw_down": torch.empty((E, F, d), **f32),
+        "dw_gate": torch.empty((E, d, F), **f32) if dense else None,
+        "dw_up": torch.empty((E, d, F), **f32) if dense else None,
+        "dw_down": torch.empty((E, F, d), **f32) if dense else None,
         "dsh_gate": torch.empty((S, d, F), **f32) if S else None,
         "dsh_up": torch.empty((S, d, F), **f32) if S else None,
         "dsh_down": torch.empty((S, F, d), **f32) if S else None,
     }
+    for m, (din, dout) in (("gate", (d, F)), ("up", (d, F)), ("down", (F, d))):
+        t["du_" + m] = None if dense else torch.empty((E, din, r), **f32)
+        t["ds_" + m] = None if dense else torch.empty((E, r), **f32)
+        t["dv_" + m] = None if dense else torch.empty((E, dout, r), **f32)
     return Grads(t, _lib.MoeGrads(**{n: _ptr(t[n]) for n in _lib.GRAD_FIELDS}))
 
 

@@ -335,11 +335,49 @@ typedef struct {
   float *dsh_gate;    /* [S, d, F]  (NULL allowed when S == 0)               */
   float *dsh_up;      /* [S, d, F]                                           */
   float *dsh_down;    /* [S, F, d]                                           */
+  /* rank-r experts (rank > 0): the gradients of their factors, in the
+     factors' own shapes (dw_gate, dw_up, dw_down are then unused, NULL
+     allowed); the dormouse "TSCT low-rank experts" card's U diag(s) V^T      */
+  float *du_gate, *ds_gate, *dv_gate;   /* [E, d, r], [E, r], [E, F, r]      */
+  float *du_up,   *ds_up,   *dv_up;     /* [E, d, r], [E, r], [E, F, r]      */
+  float *du_down, *ds_down, *dv_down;   /* [E, F, r], [E, r], [E, d, r]      */
 } moe_grads;
 
 /* Bytes of the backward's own workspace for this config and T (0 if cfg is
    invalid). */
 size_t moe_backward_workspace_bytes(const moe_config *cfg, int64_t T);
+
+/* Intermediates that moe_layer_backward leaves in bwd_ws, for inspection after
+   the call (parity checks, debugging); valid until the next call on the same
+   bwd_ws. Rows are the dispatched rows in the forward's expert-sorted order
+   (rows at and beyond offsets[E] hold no data). moe_backward_workspace_region
+   gives the byte offset into bwd_ws and the size of region `which`; a size of
+   0 means the config has no such region. Returns MOE_EINVAL for an invalid
+   config, T < 0, NULL outputs or an unknown region.
+     MOE_BWS_DY_ROUTED   bf16 [R_max, d]: gate * dy of each row, rounded
+     MOE_BWS_X_PERM      bf16 [R_max, d]: x of each row's token
+     MOE_BWS_DAB         bf16 [R_max, 2F]: da | db of each row
+     MOE_BWS_DL          bf16 [T, E]: the router-logit gradient
+   rank-r experts (W = U diag(s) V^T of the dormouse "TSCT low-rank experts"
+   card), per row, the recomputed forward chain and the backward's:
+     MOE_BWS_LR_UG, _UU  float32 [R_max, r]: x U_gate, x U_up
+     MOE_BWS_LR_Z_GU     bf16 [R_max, 2r]: zg | zu = bf16(x U s) of gate, up
+     MOE_BWS_LR_AB       float32 [R_max, 2F]: a | b = zg V_gate^T | zu V_up^T
+     MOE_BWS_LR_H        bf16 [R_max, F]: h = bf16(SiLU(a) b)
+     MOE_BWS_LR_UD       float32 [R_max, r]: h U_down
+     MOE_BWS_LR_ZD       bf16 [R_max, r]: bf16(h U_down s_down)
+     MOE_BWS_LR_DZD      float32 [R_max, r]: (gate dy) V_down
+     MOE_BWS_LR_DUD      bf16 [R_max, r]: bf16(dzd s_down)
+     MOE_BWS_LR_DZG, _DZU float32 [R_max, r]: da V_gate, db V_up
+     MOE_BWS_LR_DU_GU    bf16 [R_max, 2r]: bf16(dzg s_gate) | bf16(dzu s_up)  */
+enum {
+  MOE_BWS_DY_ROUTED = 0, MOE_BWS_X_PERM = 1, MOE_BWS_DAB = 2, MOE_BWS_DL = 3,
+  MOE_BWS_LR_UG = 4, MOE_BWS_LR_UU = 5, MOE_BWS_LR_Z_GU = 6, MOE_BWS_LR_AB = 7,
+  MOE_BWS_LR_H = 8, MOE_BWS_LR_UD = 9, MOE_BWS_LR_ZD = 10, MOE_BWS_LR_DZD = 11,
+  MOE_BWS_LR_DUD = 12, MOE_BWS_LR_DZG = 13, MOE_BWS_LR_DZU = 14, MOE_BWS_LR_DU_GU = 15
+};
+int moe_backward_workspace_region(const moe_config *cfg, int64_t T, int32_t which,
+                                  size_t *offset, size_t *bytes);
 
 /* Layer backward. Must follow moe_layer_forward on the same stream with the
    same cfg, T, x and w; o and ws are that call's outputs and workspace, read
@@ -347,7 +385,8 @@ size_t moe_backward_workspace_bytes(const moe_config *cfg, int64_t T);
    forward live in ws). dy [T, d] float32 device: the loss gradient of o->y;
    aux_grad: the loss gradient of aux (o->aux[1]), finite. bwd_ws: device,
    256-byte aligned, at least moe_backward_workspace_bytes. This library: bf16
-   dense experts with n_routed a multiple of 8, otherwise MOE_EUNSUPPORTED.
+   layers with n_routed a multiple of 8, of dense experts, or of rank-32 or
+   rank-64 experts without shared experts; otherwise MOE_EUNSUPPORTED.
    The result does not depend on scheduling (fixed summation orders, no
    atomics).                                                                 */
 int moe_layer_backward(const moe_config *cfg, int64_t T, const void *x, const moe_weights *w,

@@ -53,6 +53,9 @@ BF16_PRODUCT_REL = 2.0 ** -14
 # RMS(y) (a float32 evaluation of the chain on the CPU gives 1.8e-4 at the
 # Dormouse widths)
 LOWRANK_ERR_RMS = 1e-3
+# rank-r experts' backward: largest RMS of (gpu - oracle) over a gradient
+# tensor, relative to its RMS
+LOWRANK_GRAD_ERR_RMS = 1e-3
 
 
 def spec_of(wl) -> oracle.LayerSpec:
@@ -258,6 +261,259 @@ def lowrank_zd_allowance(inp, spec, ref):
         ulp = np.where(zd != 0, np.ldexp(1.0, ex2 - 8), 0.0)
         np.add.at(out, ts, gates[ts, js][:, None] * (ulp @ np.abs(f["v_down"]).T))
     return out
+
+
+def backward_intermediates(cfg, T, bws, rows) -> dict:
+    """The backward's intermediates read from its workspace after a call
+    (regions from moe_backward_workspace_region), as float64 numpy, routed
+    regions up to the `rows` dispatched rows; None where the config has no
+    such region."""
+    R, d, F, E, r = _lib.moe_max_rows(cfg, T), cfg.hidden, cfg.ffn, cfg.n_routed, cfg.rank
+    f32, b16 = torch.float32, torch.bfloat16
+
+    def region(which, dtype, shape):
+        off, n = _lib.moe_backward_workspace_region(cfg, T, which)
+        if n == 0:
+            return None
+        t = bws[off:off + n].view(dtype).reshape(shape)
+        if shape[0] == R:
+            t = t[:rows]
+        return t.float().cpu().numpy().astype(np.float64)
+
+    m = _lib
+    return dict(dy=region(m.MOE_BWS_DY_ROUTED, b16, (R, d)),
+                xperm=region(m.MOE_BWS_X_PERM, b16, (R, d)),
+                dab=region(m.MOE_BWS_DAB, b16, (R, 2 * F)),
+                dl=region(m.MOE_BWS_DL, b16, (T, E)),
+                ug=region(m.MOE_BWS_LR_UG, f32, (R, r)),
+                uu=region(m.MOE_BWS_LR_UU, f32, (R, r)),
+                zgu=region(m.MOE_BWS_LR_Z_GU, b16, (R, 2 * r)),
+                ab=region(m.MOE_BWS_LR_AB, f32, (R, 2 * F)),
+                h=region(m.MOE_BWS_LR_H, b16, (R, F)),
+                ud=region(m.MOE_BWS_LR_UD, f32, (R, r)),
+                zd=region(m.MOE_BWS_LR_ZD, b16, (R, r)),
+                dzd=region(m.MOE_BWS_LR_DZD, f32, (R, r)),
+                dud=region(m.MOE_BWS_LR_DUD, b16, (R, r)),
+                dzg=region(m.MOE_BWS_LR_DZG, f32, (R, r)),
+                dzu=region(m.MOE_BWS_LR_DZU, f32, (R, r)),
+                dugu=region(m.MOE_BWS_LR_DU_GU, b16, (R, 2 * r)))
+
+
+def sum_rel(K):
+    """Bound on |fp32 result - exact| of a sum of K products (MFMA with fp32
+    accumulators: at most K/16 + 16 fp32 roundings of partial sums, each
+    within 2^-24 of the sum of the terms' magnitudes; four times that),
+    relative to that sum."""
+    return 4.0 * (np.asarray(K, np.float64) / 16.0 + 16.0) * 2.0 ** -24
+
+
+def seq_rel(K):
+    """The same for a sequential fp32 sum of K products (one rounding each)."""
+    return 4.0 * (np.asarray(K, np.float64) + 16.0) * 2.0 ** -24
+
+
+def _window_check(what, gpu, v, eps):
+    """A bf16 rounding point: the GPU's rounded value lies in
+    [rho(v - eps), rho(v + eps)] (v the unrounded value from the GPU's own
+    operands in float64, eps what the GPU's float32 evaluation of it can be
+    off by); rho is monotone, so any value the GPU could have rounded lies
+    there. Returns how many entries the GPU rounded off rho(v)."""
+    rho = oracle.round_bf16
+    eps = eps + 1e-30
+    lo, hi = rho(v - eps), rho(v + eps)
+    bad = (gpu < lo) | (gpu > hi)
+    if bad.any():
+        i = np.unravel_index(int(np.argmax(bad)), bad.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} entries outside their "
+                             f"rounding window, e.g. {i}: gpu {gpu[i]:.6e} window "
+                             f"[{lo[i]:.6e}, {hi[i]:.6e}] (v {v[i]:.6e}, eps {eps[i]:.2e})")
+    return int(np.count_nonzero(gpu != rho(v)))
+
+
+def _sum_check(what, gpu, exact, tol):
+    """An fp32 product or sum: |gpu - exact| <= tol, every entry."""
+    err = np.abs(gpu - exact)
+    bad = ~(err <= tol)
+    if bad.any():
+        i = np.unravel_index(int(np.argmax(np.where(bad, err / np.maximum(tol, 1e-300), 0))),
+                             bad.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} entries beyond their "
+                             f"summation bound, e.g. {i}: gpu {gpu[i]:.6e} exact {exact[i]:.6e} "
+                             f"tol {tol[i]:.3e}")
+    return float(np.max(err / np.maximum(tol, 1e-300))) if err.size else 0.0
+
+
+def lowrank_backward_check(inp, spec, dy, fwd, g, I, ref):
+    """The backward of rank-r experts checked link by link on every element,
+    from the GPU's own operands of each link (read from the backward's
+    workspace), then against the oracle.
+
+    Per dispatched row of expert e (fwd's expert-sorted rows):
+      x rows:    the token's x exactly; gate * dy: rounding window of the
+                 GPU gate times dy;
+      products:  ug = x U_g, uu = x U_u, a | b = z V^T, ud = h U_d,
+                 dzd = dY V_d, dzg = da V_g, dzu = db V_u within sum_rel of
+                 the sum of their terms' magnitudes from the GPU's operands;
+      roundings: zg, zu, zd, dud, dug, duu (a float32 value times s), h
+                 (SiLU(a) b), da and db (the SwiGLU backward of dh = dud U_d^T,
+                 whose float32 error is carried) each inside its window;
+      outputs:   every factor gradient, dx and dw_router are their sums over
+                 the GPU's operands within sum_rel (seq_rel for ds);
+    then each gradient's error RMS against the oracle's is at most
+    LOWRANK_GRAD_ERR_RMS of its RMS, and dx and dw_router are within
+    2^-5 B + 2^-16 S of the oracle's (the dense experts' bound).
+
+    The chain itself is not compared with the oracle element by element:
+    its fp32 sums tip some bf16 roundings the other way than the oracle's
+    float64 sums, and a tipped da entry moves a cancelled dz = da V sum (and
+    the du built from it) by many of its own ulps; each link above holds
+    regardless, and the error RMS bounds how much of that reaches a
+    gradient. Returns a report."""
+    rho = oracle.round_bf16
+    ex = oracle.Experts(inp, spec)
+    x = np.asarray(inp["x"], np.float64)
+    dy = np.asarray(dy, np.float64)
+    T, d = x.shape
+    E, F, r, k = spec.n_routed, spec.ffn, spec.rank, spec.top_k
+    offs = np.asarray(fwd["offsets"][:E + 1], np.int64)
+    R = int(offs[-1])
+    row_of_slot = np.asarray(fwd["row_of_slot"], np.int64)
+    st = np.asarray(fwd["sorted_token"][:R], np.int64)
+    tok_of_row = np.zeros(R, np.int64)
+    slot_of_row = np.zeros(R, np.int64)
+    ts, js = np.nonzero(row_of_slot >= 0)
+    tok_of_row[row_of_slot[ts, js]] = ts
+    slot_of_row[row_of_slot[ts, js]] = js
+    assert np.array_equal(tok_of_row, st), "row_of_slot and sorted_token disagree"
+    gate = np.asarray(fwd["topk_gate"], np.float64)[tok_of_row, slot_of_row]
+    e_of_row = np.repeat(np.arange(E), np.diff(offs))
+    sg, su, sd = (np.stack([np.asarray(ex.lr[n][e], np.float64) for e in range(E)])[e_of_row]
+                  for n in ("s_gate", "s_up", "s_down"))
+    rep = {"tipped": {}}
+    tip = rep["tipped"]
+    cut = {n: (v[:R] if v is not None and n != "dl" else v) for n, v in I.items()}
+    X, DY = cut["xperm"], cut["dy"]
+    ZG, ZU = cut["zgu"][:, :r], cut["zgu"][:, r:]
+    A, Bv = cut["ab"][:, :F], cut["ab"][:, F:]
+    H, ZD, DUD = cut["h"], cut["zd"], cut["dud"]
+    DA, DB = cut["dab"][:, :F], cut["dab"][:, F:]
+    DUG, DUU = cut["dugu"][:, :r], cut["dugu"][:, r:]
+    UG, UU, UD = cut["ug"], cut["uu"], cut["ud"]
+    DZD, DZG, DZU = cut["dzd"], cut["dzg"], cut["dzu"]
+
+    # rows in and the routed upstream
+    assert np.array_equal(X, x[tok_of_row]), "x rows"
+    v = gate[:, None] * dy[tok_of_row]
+    tip["dY"] = _window_check("gate * dy", DY, v, 2.0 ** -23 * np.abs(v))
+
+    # products over the rows of each expert
+    def per_expert(fn, shape):
+        ex_, mag = np.zeros(shape), np.zeros(shape)
+        for e in range(E):
+            a, b = int(offs[e]), int(offs[e + 1])
+            if a < b:
+                f = {n: np.asarray(bk[e], np.float64) for n, bk in ex.lr.items()}
+                ex_[a:b], mag[a:b] = fn(a, b, f)
+        return ex_, mag
+
+    def prod(P, Q):
+        return P @ Q, np.abs(P) @ np.abs(Q)
+
+    worst = rep.setdefault("worst_sum", {})
+    for what, gpu, fn, K in (
+            ("x U_gate", UG, lambda a, b, f: prod(X[a:b], f["u_gate"]), d),
+            ("x U_up", UU, lambda a, b, f: prod(X[a:b], f["u_up"]), d),
+            ("dY V_down", DZD, lambda a, b, f: prod(DY[a:b], f["v_down"]), d),
+            ("zg V_gate^T", A, lambda a, b, f: prod(ZG[a:b], f["v_gate"].T), r),
+            ("zu V_up^T", Bv, lambda a, b, f: prod(ZU[a:b], f["v_up"].T), r),
+            ("h U_down", UD, lambda a, b, f: prod(H[a:b], f["u_down"]), F),
+            ("da V_gate", DZG, lambda a, b, f: prod(DA[a:b], f["v_gate"]), F),
+            ("db V_up", DZU, lambda a, b, f: prod(DB[a:b], f["v_up"]), F)):
+        exact, mag = per_expert(fn, gpu.shape)
+        worst[what] = _sum_check(what, gpu, exact,
+                                 sum_rel(K) * mag + 2.0 ** -24 * np.abs(exact) + 1e-30)
+
+    # rounding points fed by those products
+    for what, gpu, val, s_ in (("zg", ZG, UG, sg), ("zu", ZU, UU, su), ("zd", ZD, UD, sd),
+                               ("dud", DUD, DZD, sd), ("dug", DUG, DZG, sg),
+                               ("duu", DUU, DZU, su)):
+        v = val * s_
+        tip[what] = _window_check(what, gpu, v, 2.0 ** -23 * np.abs(v))
+    sA = oracle.silu(A)
+    v = sA * Bv
+    tip["h"] = _window_check("h", H, v, 2.0 ** -20 * np.abs(v))
+    dh, dh_mag = per_expert(lambda a, b, f: prod(DUD[a:b], f["u_down"].T), A.shape)
+    e_dh = sum_rel(r) * dh_mag + 2.0 ** -24 * np.abs(dh)
+    sig = oracle.sigmoid(A)
+    dsA = oracle.dsilu(A)
+    e_ds = 2.0 ** -21 * (sig * (1.0 + np.abs(A)) + np.abs(dsA))
+    va = dh * Bv * dsA
+    tip["da"] = _window_check("da", DA, va, np.abs(Bv * dsA) * e_dh + np.abs(dh * Bv) * e_ds +
+                              2.0 ** -22 * np.abs(va))
+    vb = dh * sA
+    tip["db"] = _window_check("db", DB, vb, np.abs(sA) * e_dh + 2.0 ** -21 * np.abs(vb) +
+                              2.0 ** -22 * np.abs(vb))
+
+    # outputs from the GPU's operands
+    n_e = np.diff(offs)
+    outs = {}
+    for n, P, Q in (("dv_down", DY, ZD), ("du_down", H, DUD), ("dv_gate", DA, ZG),
+                    ("dv_up", DB, ZU), ("du_gate", X, DUG), ("du_up", X, DUU)):
+        ex_ = np.zeros(g[n].shape)
+        mag = np.zeros(g[n].shape)
+        for e in range(E):
+            a, b = int(offs[e]), int(offs[e + 1])
+            if a < b:
+                ex_[e], mag[e] = prod(P[a:b].T, Q[a:b])
+        outs[n] = (ex_, sum_rel(n_e)[:, None, None] * mag + 2.0 ** -24 * np.abs(ex_))
+    for n, P, Q in (("ds_gate", DZG, UG), ("ds_up", DZU, UU), ("ds_down", DZD, UD)):
+        t_ = P * Q
+        ex_, mag = np.zeros((E, r)), np.zeros((E, r))
+        for e in range(E):
+            ex_[e] = t_[offs[e]:offs[e + 1]].sum(axis=0)
+            mag[e] = np.abs(t_[offs[e]:offs[e + 1]]).sum(axis=0)
+        outs[n] = (ex_, seq_rel(n_e)[:, None] * mag + 2.0 ** -24 * np.abs(ex_))
+    dl = I["dl"]
+    wr = np.asarray(inp["w_router"], np.float64)
+    dxr, dxr_mag = np.zeros((T, d)), np.zeros((T, d))
+    dxe, dxe_mag = np.zeros((R, d)), np.zeros((R, d))
+    for e in range(E):
+        a, b = int(offs[e]), int(offs[e + 1])
+        if a < b:
+            f = {n: np.asarray(bk[e], np.float64) for n, bk in ex.lr.items()}
+            p1, m1 = prod(DUG[a:b], f["u_gate"].T)
+            p2, m2 = prod(DUU[a:b], f["u_up"].T)
+            dxe[a:b], dxe_mag[a:b] = p1 + p2, m1 + m2
+    if T:
+        dxr, dxr_mag = prod(dl, wr.T)
+    dx_ex = dxr.copy()
+    dx_tol = sum_rel(E) * dxr_mag + 2.0 ** -24 * np.abs(dxr)
+    for j in range(k):
+        rr = row_of_slot[:, j]
+        m = rr >= 0
+        dx_ex[m] += dxe[rr[m]]
+        dx_tol[m] += sum_rel(2 * r) * dxe_mag[rr[m]]
+    dx_tol += (k + 1) * 2.0 ** -24 * (dxr_mag + np.abs(dx_ex))
+    outs["dx"] = (dx_ex, dx_tol)
+    dwr, dwr_mag = prod(x.T, dl) if T else (np.zeros((d, E)), np.zeros((d, E)))
+    outs["dw_router"] = (dwr, sum_rel(T) * dwr_mag + 2.0 ** -24 * np.abs(dwr))
+    for n, (ex_, tol) in outs.items():
+        worst[n] = _sum_check(n + " from the GPU's operands", g[n].astype(np.float64), ex_, tol)
+
+    # against the oracle
+    rep["err_rms"] = {}
+    for n in ("dx", "dw_router", *oracle.LOWRANK_GRADS):
+        rv, gv = ref[n], g[n].astype(np.float64)
+        assert gv.shape == rv.shape and np.all(np.isfinite(gv)), n
+        rms = float(np.sqrt(np.mean(rv ** 2))) if rv.size else 0.0
+        err = float(np.sqrt(np.mean((gv - rv) ** 2))) if rv.size else 0.0
+        rep["err_rms"][n] = err / rms if rms else err
+        assert err <= LOWRANK_GRAD_ERR_RMS * rms, (
+            f"{n}: error RMS {err:.3e} is {err / rms:.2e} of its RMS {rms:.3e}")
+        if n in ("dx", "dw_router"):
+            tol = 2.0 ** -5 * ref["B_" + n] + 2.0 ** -16 * ref["S_" + n]
+            _sum_check(n + " against the oracle", gv, rv, tol)
+    return rep
 
 
 def _worst(diff, tol, what):

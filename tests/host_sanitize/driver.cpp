@@ -138,13 +138,34 @@ static void backward_cases() {
     EXPECT(moe_layer_backward(&c, T, fake(50), &w, &o, static_cast<float*>(fake(70)), 1.0f, &g,
                               ws_addr(), need, fake(8192), bneed, nullptr) == MOE_OK);
   }
-  moe_config r = cfg(768, 1024, 2, 0, 512, 64);
+  // rank-64 experts without shared experts: the factor-gradient path
   moe_weights w = weights();
   moe_outputs o = outputs();
   moe_grads g = grads();
-  EXPECT(moe_layer_backward(&r, 64, fake(50), &w, &o, static_cast<float*>(fake(70)), 1.0f, &g,
-                            ws_addr(), moe_workspace_bytes(&r, 64), fake(8192),
-                            moe_backward_workspace_bytes(&r, 64), nullptr) == MOE_EUNSUPPORTED);
+  for (int64_t T : {4096, 1, 0, 3000}) {
+    moe_config r = cfg(768, 1024, 2, 0, 512, 64);
+    const int before = g_launches;
+    EXPECT(moe_layer_backward(&r, T, fake(50), &w, &o, static_cast<float*>(fake(70)), 1.0f, &g,
+                              ws_addr(), moe_workspace_bytes(&r, T), fake(8192),
+                              moe_backward_workspace_bytes(&r, T), nullptr) == MOE_OK);
+    EXPECT(g_launches > before);
+    for (int q = MOE_BWS_DY_ROUTED; q <= MOE_BWS_LR_DU_GU; ++q) {
+      size_t off = 1, n = 1;
+      EXPECT(moe_backward_workspace_region(&r, T, q, &off, &n) == MOE_OK);
+      EXPECT(off + n <= moe_backward_workspace_bytes(&r, T));
+    }
+    moe_grads g2 = g;
+    g2.dv_up = nullptr;
+    EXPECT(moe_layer_backward(&r, T, fake(50), &w, &o, static_cast<float*>(fake(70)), 1.0f, &g2,
+                              ws_addr(), moe_workspace_bytes(&r, T), fake(8192),
+                              moe_backward_workspace_bytes(&r, T), nullptr) == MOE_EINVAL);
+  }
+  // rank-64 experts beside shared experts, and rank 16: legal, no backward here
+  moe_config r1 = cfg(768, 1024, 2, 1, 512, 64), r2 = cfg(768, 1024, 2, 0, 512, 16);
+  for (moe_config* r : {&r1, &r2})
+    EXPECT(moe_layer_backward(r, 64, fake(50), &w, &o, static_cast<float*>(fake(70)), 1.0f, &g,
+                              ws_addr(), moe_workspace_bytes(r, 64), fake(8192),
+                              moe_backward_workspace_bytes(r, 64), nullptr) == MOE_EUNSUPPORTED);
 }
 
 static void invalid_cases() {

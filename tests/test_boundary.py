@@ -147,6 +147,40 @@ def test_workspace_regions(lib):
         _lib.moe_workspace_region(_cfg(), 64, 99)
 
 
+def test_backward_workspace_regions(lib):
+    """The backward's intermediate regions lie inside its workspace, do not
+    overlap, and have the documented sizes; rank-r regions are empty for
+    dense experts."""
+    from fine_grained_mixture_amd.layer import config_from_workload
+    for wl in (WORKLOADS["quartz"], WORKLOADS["dormouse"], WORKLOADS["dormouse"].replace(T=1),
+               WORKLOADS["dormouse"].replace(rank=32, T=777)):
+        cfg = config_from_workload(wl)
+        T, R = wl.T, _lib.moe_max_rows(cfg, wl.T)
+        total = _lib.moe_backward_workspace_bytes(cfg, T)
+        d, F, E, r = wl.hidden, wl.ffn, wl.n_routed, wl.rank
+        lr = r > 0
+        m = _lib
+        want = {m.MOE_BWS_DY_ROUTED: R * d * 2, m.MOE_BWS_X_PERM: R * d * 2,
+                m.MOE_BWS_DAB: R * 2 * F * 2, m.MOE_BWS_DL: T * E * 2,
+                m.MOE_BWS_LR_UG: R * r * 4 * lr, m.MOE_BWS_LR_UU: R * r * 4 * lr,
+                m.MOE_BWS_LR_Z_GU: R * 2 * r * 2 * lr, m.MOE_BWS_LR_AB: R * 2 * F * 4 * lr,
+                m.MOE_BWS_LR_H: R * F * 2 * lr, m.MOE_BWS_LR_UD: R * r * 4 * lr,
+                m.MOE_BWS_LR_ZD: R * r * 2 * lr, m.MOE_BWS_LR_DZD: R * r * 4 * lr,
+                m.MOE_BWS_LR_DUD: R * r * 2 * lr, m.MOE_BWS_LR_DZG: R * r * 4 * lr,
+                m.MOE_BWS_LR_DZU: R * r * 4 * lr, m.MOE_BWS_LR_DU_GU: R * 2 * r * 2 * lr}
+        spans = []
+        for which, n in want.items():
+            off, got = _lib.moe_backward_workspace_region(cfg, T, which)
+            assert got == n, (wl.name, which)
+            assert off % 256 == 0 and off + got <= total
+            if got:
+                spans.append((off, off + got))
+        spans.sort()
+        assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+    with pytest.raises(_lib.MoeError):
+        _lib.moe_backward_workspace_region(_cfg(), 64, 16)
+
+
 @pytest.mark.parametrize("rank,dtype", [(8, "bf16"), (40, "bf16"), (80, "bf16"), (128, "bf16"),
                                         (32, "fp8"), (64, "f32")])
 def test_unsupported_rank_rejected_before_any_launch(lib, rank, dtype):

@@ -5,6 +5,9 @@ oracle's backward then takes the GPU's expert selection for every token (it is
 the oracle's own for tokens away from near-ties, and either choice is correct
 within them) and the same upstream gradient.
 
+Dense experts give dW of every expert matrix; rank-r experts give the
+gradients of their factors U, s and V (no shared experts beside them).
+
 Tolerance, per element of every gradient tensor. Each element is a sum of
 products whose bf16 operands both sides round at the same points; the GPU
 forms the unrounded operand in float32, the oracle in float64, so an operand
@@ -27,7 +30,8 @@ from tests import _parity as P
 
 pytestmark = pytest.mark.gpu
 
-NAMES = ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dsh_gate", "dsh_up", "dsh_down")
+NAMES = ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dsh_gate", "dsh_up", "dsh_down",
+         *oracle.LOWRANK_GRADS)
 
 
 def _gpu_fwd_bwd(wl, inp, dy, aux_grad, saved=False):
@@ -228,3 +232,82 @@ def test_full_size_backward(name):
         assert not bad.any(), f"{n}: {int(bad.sum())} elements beyond 2^-5 B + 2^-16 S"
     print(f"[report] {name}: " + ", ".join(
         f"{k}: {a:.2e} rms, {b:.2f} tol" for k, (a, b) in rep.items()), flush=True)
+
+
+# Rank-64 (and rank-32) experts: the factor gradients of U diag(s) V^T,
+# checked link by link on every element from the GPU's own intermediates (the
+# backward workspace) and then against the per-expert batched oracle
+# (_parity.lowrank_backward_check).
+def _check_lowrank(wl, aux_grad=1.0):
+    print(f"\n[case] low-rank backward {wl}", flush=True)
+    inp = synth.make_inputs(wl)
+    dy = synth.make_upstream(wl)
+    cfg, x, w = P.upload(wl, inp)
+    out = L.allocate_outputs(cfg, wl.T, x.device)
+    ws = L.allocate_workspace(cfg, wl.T, x.device)
+    L.layer_forward(cfg, x, w, out, ws)
+    bws = L.allocate_backward_workspace(cfg, wl.T, x.device)
+    g = L.layer_backward(cfg, x, w, out, ws, torch.from_numpy(dy).to(x.device), aux_grad,
+                         bws=bws)
+    torch.cuda.synchronize()
+    fwd = P.to_numpy(out)
+    grads = {n: v.cpu().numpy() for n, v in g.t.items() if v is not None}
+    rows = int(fwd["offsets"][wl.n_routed])
+    I = P.backward_intermediates(cfg, wl.T, bws, rows)
+    P.check_parity(wl, inp, fwd, check_y=False)
+    spec = P.spec_of(wl)
+    gi = fwd["topk_idx"].astype(np.int64)
+    ref_f = oracle.layer_forward(inp["x"], inp, spec, tokens=[], override_idx=gi,
+                                 override_mask=np.ones(wl.T, bool))
+    ref = oracle.layer_backward_batched(inp["x"], inp, spec, dy, aux_grad=aux_grad, fwd=ref_f)
+    rep = P.lowrank_backward_check(inp, spec, dy, fwd, grads, I, ref)
+    print(f"[report] low-rank {wl.name} T={wl.T}: tipped {rep['tipped']}; "
+          f"worst sum/bound {max(rep['worst_sum'].values()):.3f}; error RMS " +
+          ", ".join(f"{k}: {v:.1e}" for k, v in rep["err_rms"].items()), flush=True)
+    return rep
+
+
+LOWRANK = {
+    "dormouse_small": synth.DORMOUSE.replace(T=600, hidden=256, ffn=128),
+    "dormouse_small_renorm": synth.DORMOUSE.replace(T=500, hidden=256, ffn=192, renorm=1,
+                                                    seed=3),
+    "rank32": synth.DORMOUSE.replace(T=420, hidden=256, ffn=128, rank=32, n_routed=64, seed=4),
+    "capacity": synth.DORMOUSE.replace(T=900, hidden=128, ffn=128, n_routed=64,
+                                       capacity_factor="3/2", logit_offset_std=0.5, seed=13),
+    "sigmoid": synth.DORMOUSE.replace(T=333, hidden=192, ffn=128, n_routed=200, score="sigmoid",
+                                      renorm=1, select_bias_std=0.1, seed=14),
+    "zipf_skew": synth.DORMOUSE.replace(T=1500, hidden=256, ffn=128, n_routed=64, zipf_s=1.1,
+                                        seed=11),
+    "one_token": synth.DORMOUSE.replace(T=1, hidden=128, ffn=64, seed=2),
+    "full_dormouse": synth.DORMOUSE,
+}
+
+
+@pytest.mark.parametrize("name", list(LOWRANK))
+def test_lowrank_backward_parity(name):
+    _check_lowrank(LOWRANK[name])
+
+
+def test_lowrank_backward_deterministic_and_empty_batch():
+    wl = LOWRANK["dormouse_small"]
+    inp = synth.make_inputs(wl)
+    dy = synth.make_upstream(wl)
+    _, g1 = _gpu_fwd_bwd(wl, inp, dy, 1.0)
+    _, g2 = _gpu_fwd_bwd(wl, inp, dy, 1.0)
+    for n in g1:
+        assert np.array_equal(g1[n], g2[n]), n
+    wl0 = wl.replace(T=0)
+    cfg, x, w = P.upload(wl0, synth.make_inputs(wl0))
+    out = L.allocate_outputs(cfg, 0, x.device)
+    ws = L.allocate_workspace(cfg, 0, x.device)
+    L.layer_forward(cfg, x, w, out, ws)
+    grads = L.allocate_grads(cfg, 0, x.device)
+    for v in grads.t.values():
+        if v is not None:
+            v.fill_(7.0)
+    L.layer_backward(cfg, x, w, out, ws, torch.zeros((0, wl.hidden), device=x.device), 1.0,
+                     grads)
+    torch.cuda.synchronize()
+    for n, v in grads.t.items():
+        if v is not None and v.numel():
+            assert float(v.abs().max()) == 0.0, n

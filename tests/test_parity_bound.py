@@ -144,3 +144,138 @@ def test_lowrank_allowance_covers_a_float32_chain_and_catches_a_slip(dtype):
     bad["s_down"] = (np.asarray(inp["s_down"], np.float64) * (1 + 2.0 ** -6)).astype(np.float32)
     dev = np.abs(_float32_lowrank_y(bad, spec, ref) - y)
     assert np.sqrt(np.mean(dev ** 2)) / rms > P.LOWRANK_ERR_RMS
+
+
+def _emulate_lowrank_backward(inp, spec, ref, dy, dl, s_gate_scale=1.0, dsilu=None):
+    """A GPU-like evaluation of the rank-r experts' backward on the CPU: the
+    forward chain recomputed and the chain rule back through it, products in
+    float32 (NumPy's own summation order), bf16 rounding at the layer's
+    points, laid out as the GPU leaves it: the forward's routing (fwd), the
+    gradients (g) and the backward workspace's intermediates (I, rows in
+    expert-sorted order). dl is the router-logit gradient taken as given.
+    s_gate_scale and dsilu plant mistakes."""
+    f32 = np.float32
+    ex = oracle.Experts(inp, spec)
+
+    def r32(v):
+        return oracle.round_bf16(np.asarray(v, np.float64)).astype(f32)
+
+    x = np.asarray(inp["x"], f32)
+    dy = np.asarray(dy, f32)
+    T, d = x.shape
+    E, F, r, k = spec.n_routed, spec.ffn, spec.rank, spec.top_k
+    offs = np.asarray(ref["offsets"][:E + 1], np.int64)
+    R = int(offs[-1])
+    rows = np.asarray(ref["row_of_slot"], np.int64)
+    tok = np.zeros(R, np.int64)
+    slot = np.zeros(R, np.int64)
+    ts, js = np.nonzero(rows >= 0)
+    tok[rows[ts, js]], slot[rows[ts, js]] = ts, js
+    gate32 = np.asarray(ref["gates"], f32)
+    shapes = dict(dy=d, xperm=d, dab=2 * F, ug=r, uu=r, zgu=2 * r, ab=2 * F, h=F, ud=r, zd=r,
+                  dzd=r, dud=r, dzg=r, dzu=r, dugu=2 * r)
+    I = {n: np.zeros((R, w), f32) for n, w in shapes.items()}
+    g = {n: np.zeros((E,) + np.shape(ex.lr[n[1:]][0]), f32) for n in oracle.LOWRANK_GRADS}
+    dxe = np.zeros((R, d), f32)
+    for e in range(E):
+        a, b = int(offs[e]), int(offs[e + 1])
+        if a == b:
+            continue
+        f = {n: np.asarray(bk[e], f32) for n, bk in ex.lr.items()}
+        sg = (f["s_gate"] * f32(s_gate_scale)).astype(f32)
+        X = x[tok[a:b]]
+        UG, UU = X @ f["u_gate"], X @ f["u_up"]
+        ZG, ZU = r32(UG * sg), r32(UU * f["s_up"])
+        A, B = ZG @ f["v_gate"].T, ZU @ f["v_up"].T
+        sgm = f32(1) / (f32(1) + np.exp(-A))
+        H = r32(A * sgm * B)
+        UD = H @ f["u_down"]
+        ZD = r32(UD * f["s_down"])
+        DY = r32(gate32[tok[a:b], slot[a:b]][:, None] * dy[tok[a:b]])
+        DZD = DY @ f["v_down"]
+        DUD = r32(DZD * f["s_down"])
+        DH = DUD @ f["u_down"].T
+        dsA = sgm * (f32(1) + A * (f32(1) - sgm)) if dsilu is None else dsilu(A)
+        DA, DB = r32(DH * B * dsA), r32(DH * (A * sgm))
+        DZG, DZU = DA @ f["v_gate"], DB @ f["v_up"]
+        DUG, DUU = r32(DZG * sg), r32(DZU * f["s_up"])
+        for n, v in (("dy", DY), ("xperm", X), ("dab", np.concatenate([DA, DB], 1)),
+                     ("ug", UG), ("uu", UU), ("zgu", np.concatenate([ZG, ZU], 1)),
+                     ("ab", np.concatenate([A, B], 1)), ("h", H), ("ud", UD), ("zd", ZD),
+                     ("dzd", DZD), ("dud", DUD), ("dzg", DZG), ("dzu", DZU),
+                     ("dugu", np.concatenate([DUG, DUU], 1))):
+            I[n][a:b] = v
+        g["dv_down"][e], g["du_down"][e] = DY.T @ ZD, H.T @ DUD
+        g["dv_gate"][e], g["dv_up"][e] = DA.T @ ZG, DB.T @ ZU
+        g["du_gate"][e], g["du_up"][e] = X.T @ DUG, X.T @ DUU
+        g["ds_gate"][e] = (DZG * UG).sum(axis=0)
+        g["ds_up"][e] = (DZU * UU).sum(axis=0)
+        g["ds_down"][e] = (DZD * UD).sum(axis=0)
+        dxe[a:b] = DUG @ f["u_gate"].T + DUU @ f["u_up"].T
+    dl32 = np.asarray(dl, f32)
+    dx = dl32 @ np.asarray(inp["w_router"], f32).T
+    for j in range(k):
+        m = rows[:, j] >= 0
+        dx[m] += dxe[rows[m, j]]
+    g["dx"], g["dw_router"] = dx, x.T @ dl32
+    I = {n: v.astype(np.float64) for n, v in I.items()}
+    I["dl"] = dl32.astype(np.float64)
+    fwd = dict(offsets=offs, row_of_slot=rows, sorted_token=np.asarray(ref["sorted_token"]),
+               topk_gate=gate32)
+    return fwd, g, I
+
+
+def _lowrank_bwd_case():
+    wl = synth.DORMOUSE.replace(T=1500, hidden=384, ffn=256, seed=5)
+    inp = synth.make_inputs(wl)
+    dy = synth.make_upstream(wl)
+    spec = P.spec_of(wl)
+    ref = oracle.layer_forward(inp["x"], inp, spec, tokens=[])
+    orc = oracle.layer_backward_batched(inp["x"], inp, spec, dy, aux_grad=1.0, fwd=ref)
+    return inp, spec, dy, ref, orc
+
+
+def test_lowrank_backward_check_accepts_a_float32_chain_and_rejects_planted_mistakes():
+    """A float32 evaluation of the rank-r backward, laid out as the GPU leaves
+    it, passes lowrank_backward_check (its fp32 sums tip bf16 roundings all
+    along the chain, which the oracle comparison tolerates); each planted
+    mistake fails it: an intermediate two ulps off its rounding, one gradient
+    element 2^-10 off its sum, a SwiGLU derivative that drops a term, s_gate
+    2^-6 off, two x rows swapped, a router-logit gradient entry changed after
+    use, the router's share of dx left out."""
+    inp, spec, dy, ref, orc = _lowrank_bwd_case()
+    fwd, g, I = _emulate_lowrank_backward(inp, spec, ref, dy, orc["dl"])
+    rep = P.lowrank_backward_check(inp, spec, dy, fwd, g, I, orc)
+    print(rep)
+    assert sum(rep["tipped"].values()) > 0                 # the orders differ
+
+    def fails(fwd2, g2, I2, what):
+        with pytest.raises(AssertionError):
+            P.lowrank_backward_check(inp, spec, dy, fwd2, g2, I2, orc)
+
+    r = spec.rank
+    I2 = {n: v.copy() for n, v in I.items()}
+    i = int(np.argmax(np.abs(I2["dugu"][:, 3])))
+    v = I2["dugu"][i, 3]
+    I2["dugu"][i, 3] = v + 2 * np.ldexp(1.0, int(np.frexp(abs(v))[1]) - 8) * np.sign(v)
+    fails(fwd, g, I2, "dug two ulps off")
+    g2 = {n: v.copy() for n, v in g.items()}
+    e = int(np.argmax(np.diff(fwd["offsets"])))
+    g2["du_gate"][e, 5, 7] *= 1 + 2.0 ** -10
+    fails(fwd, g2, I, "du_gate element")
+    fails(*_emulate_lowrank_backward(inp, spec, ref, dy, orc["dl"],
+                                     dsilu=lambda A: 1 / (1 + np.exp(-A))), "dsilu")
+    fails(*_emulate_lowrank_backward(inp, spec, ref, dy, orc["dl"], s_gate_scale=1 + 2.0 ** -6),
+          "s_gate")
+    I2 = {n: v.copy() for n, v in I.items()}
+    I2["xperm"][[0, 1]] = I2["xperm"][[1, 0]]
+    fails(fwd, g, I2, "x rows")
+    I2 = {n: v.copy() for n, v in I.items()}
+    t = int(np.argmax(np.abs(I2["dl"]).max(axis=1)))
+    I2["dl"][t] *= 1.5
+    fails(fwd, g, I2, "dl")
+    g2 = {n: v.copy() for n, v in g.items()}
+    g2["dx"] = g2["dx"] - (np.asarray(orc["dl"], np.float32) @
+                           np.asarray(inp["w_router"], np.float32).T)
+    fails(fwd, g2, I, "router share of dx")
+    assert r == 64
