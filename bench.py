@@ -105,6 +105,31 @@ def backward_flops(wl, rows):
                 wgrad_gemm=6.0 * d * F * ex + 2.0 * d * E * T)
 
 
+def lowrank_backward_work(wl, rows, used):
+    """Algorithmic FLOPs and HBM bytes of each product kernel of the rank-r
+    experts' backward, for `rows` dispatched rows and `used` experts with
+    rows: each operand read once, each result written once (bf16 operands and
+    factors, fp32 products and gradients)."""
+    T, d, E, F, r = wl.T, wl.hidden, wl.n_routed, wl.ffn, wl.rank
+    R, fac = rows, used * r * 2            # one factor column set of `used` experts, bf16
+    flops = dict(lr_in_gemm=6.0 * R * d * r, lr_ab_gemm=4.0 * R * r * F,
+                 lr_ud_gemm=2.0 * R * F * r, lr_dh_gemm=2.0 * R * r * F,
+                 lr_dz_gemm=4.0 * R * F * r, dgrad_gemm=4.0 * R * r * d + 2.0 * T * E * d,
+                 wgrad_gemm=4.0 * R * d * r + 6.0 * R * F * r,
+                 wgrad_gemm2=2.0 * R * d * r + 2.0 * d * E * T)
+    nbytes = dict(
+        lr_in_gemm=4 * R * d + 3 * d * fac + 12 * R * r,
+        lr_ab_gemm=4 * R * r + 2 * F * fac + 8 * R * F,
+        lr_ud_gemm=2 * R * F + F * fac + 4 * R * r,
+        lr_dh_gemm=2 * R * r + F * fac + 8 * R * F + 4 * R * F,
+        lr_dz_gemm=4 * R * F + 2 * F * fac + 8 * R * r,
+        dgrad_gemm=4 * R * r + 2 * d * fac + 4 * R * d + 2 * T * E + 2 * d * E + 4 * T * d,
+        wgrad_gemm=(2 * R * d + 2 * R * r + 2 * R * F + 2 * R * r + 4 * R * F + 4 * R * r +
+                    2 * R * d + 2 * R * r + 4 * E * r * (2 * d + 3 * F)),
+        wgrad_gemm2=2 * R * d + 2 * R * r + 4 * E * d * r + 2 * T * d + 2 * T * E + 4 * d * E)
+    return flops, nbytes
+
+
 def time_backward(wl, cfg, x, w, steps, warmup, stream):
     """The training pair: mean time of moe_layer_forward keeping its gate and
     up products (saved_ab), and of moe_layer_backward after it (reading that
@@ -119,7 +144,7 @@ def time_backward(wl, cfg, x, w, steps, warmup, stream):
 
     dev = x.device
     dy = torch.from_numpy(synth.make_upstream(wl)).to(dev)
-    out = allocate_outputs(cfg, wl.T, dev, saved_ab=True)
+    out = allocate_outputs(cfg, wl.T, dev, saved_ab=wl.rank == 0)
     ws = allocate_workspace(cfg, wl.T, dev)
     g = allocate_grads(cfg, wl.T, dev)
     bws = allocate_backward_workspace(cfg, wl.T, dev)
@@ -159,7 +184,7 @@ def time_backward(wl, cfg, x, w, steps, warmup, stream):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    n_ev = 32
+    n_ev = 64
     sets = []
     for _ in range(steps):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
@@ -171,7 +196,7 @@ def time_backward(wl, cfg, x, w, steps, warmup, stream):
     for evs in sets:
         n_k = bstep(evs)
     torch.cuda.synchronize()
-    names = [_lib.moe_stage_name(i) for i in range(n_k)]
+    names = [_lib.moe_stage_name(i) for i in range(min(n_k, n_ev // 2))]
     dur = {n: [] for n in names}
     for evs in sets:
         for i, n in enumerate(names):
@@ -593,7 +618,7 @@ def main():
     for evs in ev_sets:
         n_k = step(evs)
     torch.cuda.synchronize()
-    names = [_lib.moe_stage_name(i) for i in range(n_k)]
+    names = [_lib.moe_stage_name(i) for i in range(min(n_k, n_ev // 2))]
     dur = {n: [] for n in names}
     for evs in ev_sets:
         for i, n in enumerate(names):
@@ -763,6 +788,21 @@ def main():
             "lowrank_experts_gbs": b8 / (us8 * 1e-6) / 1e9,
             "lowrank_experts_frac_of_hbm_peak": b8 / (us8 * 1e-6) / 1e9 / PEAK_HBM_GBS,
         }
+    if (wl.dtype == "bf16" and wl.rank in (32, 64) and wl.n_shared == 0 and wl.n_routed % 8 == 0
+            and not args.no_backward):
+        # rank-r experts: the backward recomputes the forward chain per row
+        fms, bms, bst = time_backward(wl, cfg, x, w, args.steps, args.warmup, stream)
+        used = int((out["kept"].cpu().numpy() > 0).sum())
+        bfl, bby = lowrank_backward_work(wl, rows, used)
+        bwd = {"ms_per_step": bms, "tokens_per_s": wl.T / (bms * 1e-3),
+               "forward_ms": fms, "fwd_plus_bwd_tokens_per_s": wl.T / ((bms + fms) * 1e-3),
+               "flops": sum(bfl.values()), "product_bytes": sum(bby.values()),
+               "stage_us_mean": bst}
+        for n in bfl:
+            if n in bst:
+                bwd[n + "_tflops"] = bfl[n] / (bst[n] * 1e-6) / 1e12
+                bwd[n + "_gbs"] = bby[n] / (bst[n] * 1e-6) / 1e9
+        result["backward"] = bwd
     if wl.dtype == "bf16" and wl.rank == 0 and not args.no_fp8:
         fms8, st8 = time_fp8(wl, inp, x, args.steps, args.warmup, stream)
         gu8 = alg["gate_up_flops"] + alg["shared_gate_up_flops"]
