@@ -942,18 +942,13 @@ void lowrank_backward(Runner& Rn, const moe_config* c, int64_t T, const void* x,
     p.n_tiles_n = (int32_t)ceil_div(N, 128);
     return p;
   };
-  auto scale = [&](const char* name, LowRankScaleJob j0, LowRankScaleJob j1, int n) {
-    LowRankScaleJobs J{};
-    J.job[0] = j0;
-    J.job[1] = j1;
-    J.n = n;
-    J.offsets = offs;
-    J.rows = rows;
-    J.E = (int32_t)E;
-    J.r = (int32_t)r;
-    Rn.run(name, [&] { return launch_scale_round(J, R, Rn.stream); });
+  // the product's bf16 copy scaled by s of the row's expert (its rounding point)
+  auto scaled = [&](BwdGemm& p, uint16_t* out, int64_t ldo, const void* s_vec) {
+    p.C2 = out;
+    p.ldc2 = ldo;
+    p.c2_scale = static_cast<const uint16_t*>(s_vec);
+    p.c2_scale_group = r;
   };
-  auto s16 = [](const void* p) { return static_cast<const uint16_t*>(p); };
 
   if (T > 0) {
     CombineBwdArgs cb{};
@@ -987,16 +982,17 @@ void lowrank_backward(Runner& Rn, const moe_config* c, int64_t T, const void* x,
     Rn.run("router_bwd", [&] { return launch_router_bwd(rb, Rn.stream); });
     Rn.run("plan", [&] { return launch_plan(offs, (int32_t)E, kGemmBigBM, plan, Rn.stream); });
 
-    {  // x U_g, x U_u and dY V_d
+    {  // x U_g, x U_u and dY V_d, with zg = bf16(x U_g s_g), zu and dud = bf16(dzd s_d)
       BwdLaunch BL{};
       BL.p[0] = rows_problem(xperm, d, w->u_gate, r, d * r, ug, r, r, d);
+      scaled(BL.p[0], zgu, 2 * r, w->s_gate);
       BL.p[1] = rows_problem(xperm, d, w->u_up, r, d * r, uu, r, r, d);
+      scaled(BL.p[1], zgu + r, 2 * r, w->s_up);
       BL.p[2] = rows_problem(dyr, d, w->v_down, r, d * r, dzd, r, r, d);
+      scaled(BL.p[2], dud, r, w->s_down);
       BL.n = 3;
       Rn.run("lr_in_gemm", [&] { return launch_gemm_bwd(BL, true, false, kBwdStoreF32, Rn.stream); });
     }
-    scale("lr_z_in", LowRankScaleJob{ug, r, s16(w->s_gate), zgu, 2 * r},
-          LowRankScaleJob{uu, r, s16(w->s_up), zgu + r, 2 * r}, 2);
     {  // a = zg V_g^T, b = zu V_u^T
       BwdLaunch BL{};
       BL.p[0] = rows_problem(zgu, 2 * r, w->v_gate, r, F * r, ab, 2 * F, F, r);
@@ -1005,14 +1001,13 @@ void lowrank_backward(Runner& Rn, const moe_config* c, int64_t T, const void* x,
       Rn.run("lr_ab_gemm", [&] { return launch_gemm_bwd(BL, true, true, kBwdStoreF32, Rn.stream); });
     }
     Rn.run("lr_h", [&] { return launch_swiglu_h(ab, hh, rows, R, (int)F, Rn.stream); });
-    {  // ud = h U_d
+    {  // ud = h U_d, with zd = bf16(ud s_d)
       BwdLaunch BL{};
       BL.p[0] = rows_problem(hh, F, w->u_down, r, F * r, ud, r, r, F);
+      scaled(BL.p[0], zd, r, w->s_down);
       BL.n = 1;
       Rn.run("lr_ud_gemm", [&] { return launch_gemm_bwd(BL, true, false, kBwdStoreF32, Rn.stream); });
     }
-    scale("lr_z_down", LowRankScaleJob{ud, r, s16(w->s_down), zd, r},
-          LowRankScaleJob{dzd, r, s16(w->s_down), dud, r}, 2);
     {  // dh = dud U_d^T with the SwiGLU backward in the epilogue
       BwdLaunch BL{};
       BwdGemm& p = BL.p[0] = rows_problem(dud, r, w->u_down, r, F * r,
@@ -1023,15 +1018,15 @@ void lowrank_backward(Runner& Rn, const moe_config* c, int64_t T, const void* x,
       BL.n = 1;
       Rn.run("lr_dh_gemm", [&] { return launch_gemm_bwd(BL, true, true, kBwdSwiGLU, Rn.stream); });
     }
-    {  // dz_g = da V_g, dz_u = db V_u
+    {  // dz_g = da V_g, dz_u = db V_u, with dug = bf16(dz_g s_g) and duu
       BwdLaunch BL{};
       BL.p[0] = rows_problem(dab, 2 * F, w->v_gate, r, F * r, dzg, r, r, F);
+      scaled(BL.p[0], dugu, 2 * r, w->s_gate);
       BL.p[1] = rows_problem(dab + F, 2 * F, w->v_up, r, F * r, dzu, r, r, F);
+      scaled(BL.p[1], dugu + r, 2 * r, w->s_up);
       BL.n = 2;
       Rn.run("lr_dz_gemm", [&] { return launch_gemm_bwd(BL, true, false, kBwdStoreF32, Rn.stream); });
     }
-    scale("lr_du", LowRankScaleJob{dzg, r, s16(w->s_gate), dugu, 2 * r},
-          LowRankScaleJob{dzu, r, s16(w->s_up), dugu + r, 2 * r}, 2);
     {  // input-gradient rows [dug | duu] [U_g; U_u]^T, and the router's dl W_r^T
       BwdLaunch BL{};
       BwdGemm& p = BL.p[0] = rows_problem(dugu, 2 * r, w->u_gate, r, d * r, dxp, d, d, 2 * r);

@@ -308,6 +308,13 @@ gemm_bwd_kernel(BwdLaunch L) {
       cbase = (col < P.c_split ? P.C0 + col : P.C1 + (col - P.c_split)) + s * P.c_group +
               (int64_t)c * P.c_chunk;
     }
+    // the scaled bf16 copy: this lane's four column scales
+    uint16_t* c2base = P.C2 && col < N ? P.C2 + col : nullptr;
+    float sc[4] = {0.f, 0.f, 0.f, 0.f};
+    if (c2base) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[e] = bf16_to_f32(P.c2_scale[s * P.c2_scale_group + col + e]);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       stage_block(i);
@@ -318,6 +325,12 @@ gemm_bwd_kernel(BwdLaunch L) {
         const int row = row_base + 32 * i + r;
         const floatx4 v = *reinterpret_cast<const floatx4*>(&st[r * 72 + 4 * (lane & 15)]);
         if (row < r_end && cbase) *reinterpret_cast<floatx4*>(cbase + (int64_t)row * P.ldc) = v;
+        if (row < r_end && c2base) {
+          u32x2 q;
+          q[0] = (uint32_t)f32_to_bf16(v[0] * sc[0]) | ((uint32_t)f32_to_bf16(v[1] * sc[1]) << 16);
+          q[1] = (uint32_t)f32_to_bf16(v[2] * sc[2]) | ((uint32_t)f32_to_bf16(v[3] * sc[3]) << 16);
+          *reinterpret_cast<u32x2*>(c2base + (int64_t)row * P.ldc2) = q;
+        }
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -549,6 +562,11 @@ hipError_t launch_gemm_bwd(BwdLaunch& L, bool a_kc, bool b_kc, int epi, hipStrea
     if ((a_kc || b_kc) && P.K % 8) return hipErrorInvalidValue;
     if (b_kc && P.k_seg % kBK) return hipErrorInvalidValue;
     if (!P.plan && (P.n_tiles_m < 1 || P.n_chunks < 1)) return hipErrorInvalidValue;
+    // the scaled copy: one fp32 result per element (no column split, no
+    // K chunks), and its scale vector
+    if (P.C2 && (epi != kBwdStoreF32 || !P.c2_scale || P.c_split < P.N || P.n_chunks != 1 ||
+                 P.N % 4))
+      return hipErrorInvalidValue;
     L.start[i] = (int32_t)total;
     total += bwd_tiles(P);
   }

@@ -1,12 +1,9 @@
 // Elementwise and per-expert steps of the backward of rank-r experts (each
 // matrix W[in, out] = U[in, r] diag(s) V[out, r]^T, dormouse "TSCT low-rank
 // experts" card). The products between them run on the backward GEMM
-// (gemm_bwd.hip); these kernels scale by s, round to bf16 where a product
-// takes the result as an operand, and reduce the s gradients.
+// (gemm_bwd.hip), whose epilogue also writes the s-scaled bf16 copies; these
+// kernels form h and reduce the s gradients.
 //
-//   scale_round: out[row, c] = bf16(in[row, c] * s[e(row), c % r]) for the
-//     dispatched rows, e(row) the expert whose rows [offsets[e],
-//     offsets[e+1]) hold row; up to two (in, s, out) jobs per launch.
 //   swiglu_h:    h[row, f] = bf16(SiLU(a) * b) from the recomputed a, b.
 //   ds_sum:      ds[e, i] = sum over the expert's rows, in row order, of
 //     p[row, i] * q[row, i]; up to three jobs per launch, one workgroup per
@@ -17,32 +14,6 @@
 
 namespace moe {
 namespace {
-
-// The expert whose row range holds `row` (offsets ascending, E + 1 entries).
-__device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int row) {
-  int lo = 0, hi = E;   // offsets[lo] <= row < offsets[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (offsets[mid] <= row) lo = mid;
-    else hi = mid;
-  }
-  return lo;
-}
-
-__global__ void __launch_bounds__(256) scale_round_kernel(LowRankScaleJobs J) {
-  const int64_t R = *J.rows;
-  const int r = J.r;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // one element
-  const int job = blockIdx.y;
-  if (job >= J.n) return;
-  const LowRankScaleJob& jb = J.job[job];
-  const int64_t row = i / r;
-  const int c = (int)(i - row * r);
-  if (row >= R) return;
-  const int e = expert_of_row(J.offsets, J.E, (int)row);
-  const float s = bf16_to_f32(jb.s[(int64_t)e * r + c]);
-  jb.out[row * jb.ldo + c] = f32_to_bf16(jb.in[row * jb.ldi + c] * s);
-}
 
 __global__ void __launch_bounds__(256) swiglu_h_kernel(const float* ab, bf16_t* h,
                                                        const int32_t* rows, int F) {
@@ -77,15 +48,6 @@ __global__ void __launch_bounds__(256) ds_sum_kernel(LowRankDsJobs J) {
 }
 
 }  // namespace
-
-hipError_t launch_scale_round(const LowRankScaleJobs& J, int64_t R_max, hipStream_t s) {
-  if (J.n < 1 || J.n > 2 || J.r < 1 || J.r > 64) return hipErrorInvalidValue;
-  const int64_t n = R_max * J.r;
-  if (n == 0) return hipSuccess;
-  const dim3 grid((unsigned)((n + 255) / 256), (unsigned)J.n);
-  hipLaunchKernelGGL(scale_round_kernel, grid, dim3(256), 0, s, J);
-  return hipGetLastError();
-}
 
 hipError_t launch_swiglu_h(const float* ab, bf16_t* h, const int32_t* rows, int64_t R_max, int F,
                            hipStream_t s) {

@@ -272,6 +272,12 @@ struct BwdGemm {
   const float* ab;           // kBwdSwiGLU only
   int64_t ab_ld, ab_group;
   int32_t half;
+  // kBwdStoreF32, optional: also C2[row, col] = bf16(C[row, col] *
+  // c2_scale[s * c2_scale_group + col]) (a per-group column scale)
+  uint16_t* C2;
+  int64_t ldc2;
+  const uint16_t* c2_scale;
+  int64_t c2_scale_group;
 };
 constexpr int kBwdMaxProblems = 5;
 // Problems of one launch share the operand layouts; tiles of p[i] are
@@ -367,22 +373,6 @@ hipError_t launch_reduce_chunks(const float* part, float* out, int64_t groups, i
                                 int64_t n, hipStream_t s);
 
 // Backward of rank-r experts: the steps between its products.
-// out[row, c] = bf16(in[row, c] s[e(row), c]) for rows < *rows, c < r.
-struct LowRankScaleJob {
-  const float* in;
-  int64_t ldi;
-  const uint16_t* s;         // [E, r] bf16
-  uint16_t* out;
-  int64_t ldo;
-};
-struct LowRankScaleJobs {
-  LowRankScaleJob job[2];
-  int32_t n;
-  const int32_t* offsets;    // [E + 1]
-  const int32_t* rows;       // &offsets[E]
-  int32_t E, r;
-};
-hipError_t launch_scale_round(const LowRankScaleJobs& J, int64_t R_max, hipStream_t s);
 // h[row, f] = bf16(SiLU(ab[row, f]) * ab[row, F + f]) for rows < *rows.
 hipError_t launch_swiglu_h(const float* ab, uint16_t* h, const int32_t* rows, int64_t R_max,
                            int F, hipStream_t s);
