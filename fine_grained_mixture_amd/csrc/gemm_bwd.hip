@@ -29,6 +29,8 @@
 // so the epilogue forms da and db without writing dh or the recomputed gate
 // and up values to memory.
 
+#include <type_traits>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -239,7 +241,13 @@ gemm_bwd_kernel(BwdLaunch L) {
   const int bk_lane = 8 * (g16 >> 1) + (s16 >> 2);
   const int bn_lane = 16 * (g16 & 1) + 4 * (s16 & 3);
 
-  auto step = [&](int st, int kt_next) {
+  // NI, NJ: how many of the wave's four 32-row and two 32-column blocks hold
+  // output of the work item (an expert's last rows, or columns past N); the
+  // others skip their fragment reads and MFMAs, which frees the SIMD for the
+  // co-resident workgroup's wave. The loads and barriers are the same for
+  // every wave.
+  auto step = [&](int st, int kt_next, auto ni, auto nj) {
+    constexpr int NI = decltype(ni)::value, NJ = decltype(nj)::value;
     const unsigned char* As = smem + st * kStageBytes;
     const unsigned char* Bs = As + kAStageBytes;
     const uint32_t Asn = smem_base + (kt_next % kStages) * kStageBytes;
@@ -250,20 +258,25 @@ gemm_bwd_kernel(BwdLaunch L) {
     bf16x8 a[2][4], b[2][2];
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
+      if (NJ > 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[ks][i] = A_KC ? frag_kc(As, 128 * wm + 32 * i + l32, 2 * ks + lhi)
-                        : frag_ks<kBM>(As, 16 * ks + bk_lane, 128 * wm + 32 * i + bn_lane);
+        for (int i = 0; i < NI; ++i)
+          a[ks][i] = A_KC ? frag_kc(As, 128 * wm + 32 * i + l32, 2 * ks + lhi)
+                          : frag_ks<kBM>(As, 16 * ks + bk_lane, 128 * wm + 32 * i + bn_lane);
+      }
+      if (NI > 0) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[ks][j] = B_KC ? frag_kc(Bs, 64 * wn + 32 * j + l32, 2 * ks + lhi)
-                        : frag_ks<kBN>(Bs, 16 * ks + bk_lane, 64 * wn + 32 * j + bn_lane);
+        for (int j = 0; j < NJ; ++j)
+          b[ks][j] = B_KC ? frag_kc(Bs, 64 * wn + 32 * j + l32, 2 * ks + lhi)
+                          : frag_ks<kBN>(Bs, 16 * ks + bk_lane, 64 * wn + 32 * j + bn_lane);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int ks = q >> 3, i = (q >> 1) & 3, j = q & 1;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0);
+      if (i < NI && j < NJ)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0);
       if (do_issue && q < 6) {
         __builtin_amdgcn_sched_barrier(0);
         if (q < 4) dma16(a_ptr(q, k0n), Asn + (4 * wave_u + q) * 1024);
@@ -275,16 +288,48 @@ gemm_bwd_kernel(BwdLaunch L) {
 
   constexpr int kWaitVm6 = 6 | (7 << 4) | (15 << 8);
   constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
-  if (nk > 0) issue(0);
-  if (nk > 1) issue(1);
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(kWaitVm6);   // step kt landed
-    else __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();   // stage kt published; stage (kt - 1) % 3 released
-    __builtin_amdgcn_sched_barrier(0);
-    step(kt % kStages, kt + 2);
-    __builtin_amdgcn_sched_barrier(0);
+  auto main_loop = [&](auto ni, auto nj) {
+    if (nk > 0) issue(0);
+    if (nk > 1) issue(1);
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(kWaitVm6);   // step kt landed
+      else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();   // stage kt published; stage (kt - 1) % 3 released
+      __builtin_amdgcn_sched_barrier(0);
+      step(kt % kStages, kt + 2, ni, nj);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  if constexpr (EPI == kBwdSwiGLU || !A_KC) {
+    // every block runs: the SwiGLU epilogue's operand prefetch leaves no
+    // registers for the skipping variants (they spill), and the weight
+    // gradients' tiles are whole in M (the k range is what is ragged there),
+    // where the extra variants cost 7% at the Quartz shape
+    main_loop(std::integral_constant<int, 4>(), std::integral_constant<int, 2>());
+  } else {
+    using std::integral_constant;
+    const int rows_here = r_end - r0 - 128 * wm;
+    const int cols_here = N - n0 - 64 * wn;
+    const int nib = __builtin_amdgcn_readfirstlane(min(4, max(0, (rows_here + 31) / 32)));
+    const int njb = __builtin_amdgcn_readfirstlane(min(2, max(0, (cols_here + 31) / 32)));
+    if (nib == 0 || njb == 0) {
+      main_loop(integral_constant<int, 0>(), integral_constant<int, 0>());
+    } else if (njb == 2) {
+      switch (nib) {
+        case 4: main_loop(integral_constant<int, 4>(), integral_constant<int, 2>()); break;
+        case 3: main_loop(integral_constant<int, 3>(), integral_constant<int, 2>()); break;
+        case 2: main_loop(integral_constant<int, 2>(), integral_constant<int, 2>()); break;
+        default: main_loop(integral_constant<int, 1>(), integral_constant<int, 2>()); break;
+      }
+    } else {
+      switch (nib) {
+        case 4: main_loop(integral_constant<int, 4>(), integral_constant<int, 1>()); break;
+        case 3: main_loop(integral_constant<int, 3>(), integral_constant<int, 1>()); break;
+        case 2: main_loop(integral_constant<int, 2>(), integral_constant<int, 1>()); break;
+        default: main_loop(integral_constant<int, 1>(), integral_constant<int, 1>()); break;
+      }
+    }
   }
 
   // ---- epilogue through a private 18 KiB LDS slice per wave: each 32-row

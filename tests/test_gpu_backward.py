@@ -102,6 +102,11 @@ CASES = {
     "odd_widths": synth.Workload("ow", T=257, hidden=192, n_routed=16, top_k=3, n_shared=3,
                                  ffn=192, logit_offset_std=0.3, seed=11),
     "three_tokens": synth.QUARTZ.replace(T=3, hidden=256, ffn=128, seed=12),
+    # many experts: the router backward holding a token's logits in registers
+    # (E >= 256), raw softmax gates, the last lanes partly filled
+    "many_experts_raw_softmax": synth.Workload("me", T=300, hidden=128, n_routed=264, top_k=4,
+                                               n_shared=1, ffn=64, renorm=0,
+                                               logit_offset_std=0.3, seed=21),
 }
 
 
@@ -276,6 +281,9 @@ LOWRANK = {
                                        capacity_factor="3/2", logit_offset_std=0.5, seed=13),
     "sigmoid": synth.DORMOUSE.replace(T=333, hidden=192, ffn=128, n_routed=200, score="sigmoid",
                                       renorm=1, select_bias_std=0.1, seed=14),
+    "sigmoid_many": synth.DORMOUSE.replace(T=700, hidden=128, ffn=64, n_routed=520,
+                                           score="sigmoid", renorm=1, select_bias_std=0.1,
+                                           seed=15),
     "zipf_skew": synth.DORMOUSE.replace(T=1500, hidden=256, ffn=128, n_routed=64, zipf_s=1.1,
                                         seed=11),
     "one_token": synth.DORMOUSE.replace(T=1, hidden=128, ffn=64, seed=2),
