@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "gemm.hip", "gemm_big.hip", "skinny.hip", "route.hip", "route_small.hip",
-           "combine.hip", "lowrank.hip", "gemm_bwd.hip", "backward.hip", "lowrank_bwd.hip",
+           "combine.hip", "lowrank.hip", "gemm_bwd.hip", "gemm_bwd_f32.hip", "backward.hip", "lowrank_bwd.hip",
            "fp8.hip", "noalloc.hip"]
 
 # -packed-fp32-ops: no packed fp32 VALU instructions in the device code.

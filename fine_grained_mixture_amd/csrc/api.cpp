@@ -793,6 +793,7 @@ constexpr int kSharedKChunk = 4096;
 // in 16-byte pieces); rank-r experts with r a multiple of 32 (a K-step of the
 // backward products) and no shared experts.
 bool backward_supported(const moe_config* c) {
+  if (c->dtype == MOE_F32) return c->rank == 0;   // the fp32 FMA products
   if (c->dtype != MOE_BF16 || c->n_routed % 8) return false;
   if (c->rank == 0) return true;
   return c->rank % 32 == 0 && c->rank <= 64 && c->n_shared == 0;
@@ -802,6 +803,8 @@ struct BwdLayout {
   int64_t T = 0, R = 0, nch_r = 1, nch_s = 1, lr_tiles = 0;
   size_t dyr = 0, dysh = 0, dg = 0, dl = 0, dab = 0, dabsh = 0, xperm = 0, dxp = 0,
          dxsh = 0, part_r = 0, part_g = 0, part_u = 0, part_d = 0, total = 0;
+  // float32 layers: the recomputed gate and up products (routed, shared)
+  size_t ab32 = 0, absh32 = 0;
   // rank-r experts: the 256-row tile list, the recomputed forward chain
   // (x U, its scaled and rounded z, the gate and up products, h, h U_d, z_d)
   // and the backward's (dz_d, dz_d s_d rounded, dz_g | dz_u, their scaled
@@ -823,13 +826,17 @@ BwdLayout make_bwd_layout(const moe_config* c, int64_t T) {
     off = align_up(off + bytes);
     return at;
   };
-  B.dyr = take((size_t)B.R * d * 2);
-  B.dysh = take((size_t)T * d * 2 * (S > 0));
+  // operands of the backward products in the activation type (bf16, or
+  // float32 for float32 layers, whose shared upstream rows are dy itself)
+  const bool f32 = c->dtype == MOE_F32;
+  const size_t es = f32 ? 4 : 2;
+  B.dyr = take((size_t)B.R * d * es);
+  B.dysh = take((size_t)T * d * 2 * (S > 0 && !f32));
   B.dg = take((size_t)T * k * 4);
-  B.dl = take((size_t)T * E * 2);
-  B.dab = take((size_t)B.R * 2 * F * 2);
-  B.dabsh = take((size_t)T * S * 2 * F * 2);
-  B.xperm = take((size_t)B.R * d * 2);
+  B.dl = take((size_t)T * E * es);
+  B.dab = take((size_t)B.R * 2 * F * es);
+  B.dabsh = take((size_t)T * S * 2 * F * es);
+  B.xperm = take((size_t)B.R * d * es);
   B.dxp = take((size_t)B.R * d * 4);
   B.dxsh = take((size_t)T * d * 4 * (S > 0));
   B.part_r = take(B.nch_r > 1 ? (size_t)B.nch_r * d * E * 4 : 0);
@@ -837,6 +844,10 @@ BwdLayout make_bwd_layout(const moe_config* c, int64_t T) {
   B.part_g = take(shp);
   B.part_u = take(shp);
   B.part_d = take(shp);
+  if (f32) {
+    B.ab32 = take((size_t)B.R * 2 * F * 4);
+    B.absh32 = take((size_t)T * S * 2 * F * 4);
+  }
   if (c->rank > 0) {
     const int64_t r = c->rank, R = B.R;
     B.lr_tiles = ceil_div(R, kGemmBigBM) + E;
@@ -1139,11 +1150,18 @@ int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weig
   const int64_t R = B.R;
   Timeline tl{events, n_events};
   Runner Rn{static_cast<hipStream_t>(stream), &tl};
-  uint16_t* dyr = at<uint16_t>(bws, B.dyr);
-  uint16_t* dysh = S > 0 ? at<uint16_t>(bws, B.dysh) : nullptr;
+  const bool f32 = c->dtype == MOE_F32;
+  void* dyr = at<void>(bws, B.dyr);
+  // shared upstream rows: bf16(dy), or dy itself in a float32 layer
+  void* dysh = S > 0 ? (f32 ? const_cast<float*>(dy) : at<void>(bws, B.dysh)) : nullptr;
   float* dg = at<float>(bws, B.dg);
   const float* logits = at<float>(fws, L.logits);   // the forward router's
-  uint16_t* dl = at<uint16_t>(bws, B.dl);
+  void* dl = at<void>(bws, B.dl);
+  // the products: MFMA on bf16 operands, or fp32 FMA for float32 layers
+  auto gemm = [&](BwdLaunch& BL, bool akc, bool bkc, int epi) {
+    return f32 ? launch_gemm_bwd_f32(BL, akc, bkc, epi, Rn.stream)
+               : launch_gemm_bwd(BL, akc, bkc, epi, Rn.stream);
+  };
   void* dab = at<void>(bws, B.dab);
   void* dabsh = at<void>(bws, B.dabsh);
   void* xperm = at<void>(bws, B.xperm);
@@ -1163,17 +1181,18 @@ int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weig
     // upstream rows of the expert products and the gate gradients
     CombineBwdArgs cb{};
     cb.dy = dy;
-    cb.x = static_cast<const uint16_t*>(x);
-    cb.x_perm = static_cast<uint16_t*>(xperm);
+    cb.x = x;
+    cb.x_perm = xperm;
     cb.y_routed = y_perm;
     cb.row_of_slot = o->row_of_slot;
     cb.topk_gate = o->topk_gate;
     cb.dy_routed = dyr;
-    cb.dy_shared = dysh;
+    cb.dy_shared = f32 ? nullptr : static_cast<uint16_t*>(dysh);
     cb.dgate = dg;
     cb.T = T;
     cb.d = (int32_t)d;
     cb.k = (int32_t)k;
+    cb.f32 = f32;
     Rn.run("combine_bwd", [&] { return launch_combine_bwd(cb, Rn.stream); });
 
     RouterBwdArgs rb{};
@@ -1189,9 +1208,61 @@ int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weig
     rb.score = c->score;
     rb.renorm = c->renorm_topk;
     rb.aux_scale = (float)((double)aux_grad * c->aux_coef * (double)E / (double)T);
+    rb.f32_out = f32;
     Rn.run("router_bwd", [&] { return launch_router_bwd(rb, Rn.stream); });
 
-    if (o->saved_ab) {
+    // float32 layers (the forward keeps no products): a | b recomputed, x W_gate
+    // and x W_up as one problem per weight (routed rows, then the shared
+    // experts over all tokens)
+    float* ab32 = f32 ? at<float>(bws, B.ab32) : nullptr;
+    float* absh32 = f32 ? at<float>(bws, B.absh32) : nullptr;
+    if (f32) {
+      BwdLaunch BL{};
+      int np = 0;
+      for (int half = 0; half < 2; ++half) {
+        {
+          BwdGemm& p = BL.p[np++] = bwd_problem();
+          p.A = xperm;
+          p.lda = d;
+          p.B0 = half ? w->w_up : w->w_gate;
+          p.ldb = F;
+          p.b_group = d * F;
+          p.C0 = ab32 + half * F;
+          p.ldc = 2 * F;
+          p.m_off = o->offsets;
+          p.plan = plan256;
+          p.N = (int32_t)F;
+          p.K = (int32_t)d;
+          p.G = (int32_t)E;
+          p.n_tiles_n = (int32_t)ceil_div(F, 128);
+          p.max_m_tiles = (int32_t)L.max_tiles;
+        }
+        if (S > 0) {
+          BwdGemm& p = BL.p[np++] = bwd_problem();
+          p.A = x;
+          p.lda = d;
+          p.B0 = half ? w->sh_up : w->sh_gate;
+          p.ldb = F;
+          p.b_group = d * F;
+          p.C0 = absh32 + half * F;
+          p.ldc = S * 2 * F;
+          p.c_group = 2 * F;
+          p.M = (int32_t)T;
+          p.N = (int32_t)F;
+          p.K = (int32_t)d;
+          p.G = (int32_t)S;
+          p.k_chunk = p.K;
+          p.n_tiles_m = (int32_t)ceil_div(T, kGemmBigBM);
+          p.n_tiles_n = (int32_t)ceil_div(F, 128);
+        }
+      }
+      BL.n = np;
+      Rn.run("ab_gemm", [&] { return gemm(BL, true, false, kBwdStoreF32); });
+    }
+    const float* ab_routed = f32 ? ab32 : o->saved_ab;
+    const float* ab_shared = f32 ? absh32 : (o->saved_ab ? o->saved_ab + R * 2 * F : nullptr);
+
+    if (ab_routed) {
       // dh = dy W_down^T with the SwiGLU backward in the epilogue, on the
       // forward's saved gate and up products (shared experts, then routed)
       BwdLaunch BL{};
@@ -1203,10 +1274,10 @@ int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weig
         p.B0 = w->sh_down;
         p.ldb = d;
         p.b_group = F * d;
-        p.C0 = static_cast<float*>(dabsh);   // bf16 output
+        p.C0 = static_cast<float*>(dabsh);   // output in the activation type
         p.ldc = S * 2 * F;
         p.c_group = 2 * F;
-        p.ab = o->saved_ab + R * 2 * F;
+        p.ab = ab_shared;
         p.ab_ld = S * 2 * F;
         p.ab_group = 2 * F;
         p.half = (int32_t)F;
@@ -1225,9 +1296,9 @@ int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weig
         p.B0 = w->w_down;
         p.ldb = d;
         p.b_group = F * d;
-        p.C0 = static_cast<float*>(dab);     // bf16 output
+        p.C0 = static_cast<float*>(dab);     // output in the activation type
         p.ldc = 2 * F;
-        p.ab = o->saved_ab;
+        p.ab = ab_routed;
         p.ab_ld = 2 * F;
         p.half = (int32_t)F;
         p.m_off = o->offsets;
@@ -1239,7 +1310,7 @@ int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weig
         p.max_m_tiles = (int32_t)L.max_tiles;
       }
       BL.n = np;
-      Rn.run("dh_gemm", [&] { return launch_gemm_bwd(BL, true, true, kBwdSwiGLU, Rn.stream); });
+      Rn.run("dh_gemm", [&] { return gemm(BL, true, true, kBwdSwiGLU); });
     } else {
     // SwiGLU backward with the gate and up products recomputed (shared
     // experts, then routed)
@@ -1349,9 +1420,7 @@ int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weig
         p.max_m_tiles = (int32_t)L.max_tiles;
       }
       BL.n = np;
-      Rn.run("dgrad_gemm", [&] {
-        return launch_gemm_bwd(BL, true, true, kBwdStoreF32, Rn.stream);
-      });
+      Rn.run("dgrad_gemm", [&] { return gemm(BL, true, true, kBwdStoreF32); });
     }
     DxGatherArgs dx{};
     dx.dx_rows = dxp;
@@ -1467,9 +1536,7 @@ int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weig
       p.n_tiles_n = (int32_t)ceil_div(E, 128);
     }
     BL.n = np;
-    Rn.run("wgrad_gemm", [&] {
-      return launch_gemm_bwd(BL, false, false, kBwdStoreF32, Rn.stream);
-    });
+    Rn.run("wgrad_gemm", [&] { return gemm(BL, false, false, kBwdStoreF32); });
     if (B.nch_r > 1) {
       Rn.run("reduce_router", [&] {
         return launch_reduce_chunks(at<float>(bws, B.part_r), g->dw_router, 1, B.nch_r, d * E,
@@ -1697,12 +1764,13 @@ int moe_backward_workspace_region(const moe_config* c, int64_t T, int32_t which,
   const int64_t d = c->hidden, F = c->ffn, E = c->n_routed, R = B.R;
   const int64_t r = c->rank;
   const bool lr = r > 0;
+  const size_t es = c->dtype == MOE_F32 ? 4 : 2;
   size_t at = 0, n = 0;
   switch (which) {
-    case MOE_BWS_DY_ROUTED: at = B.dyr; n = (size_t)R * d * 2; break;
-    case MOE_BWS_X_PERM: at = B.xperm; n = (size_t)R * d * 2; break;
-    case MOE_BWS_DAB: at = B.dab; n = (size_t)R * 2 * F * 2; break;
-    case MOE_BWS_DL: at = B.dl; n = (size_t)T * E * 2; break;
+    case MOE_BWS_DY_ROUTED: at = B.dyr; n = (size_t)R * d * es; break;
+    case MOE_BWS_X_PERM: at = B.xperm; n = (size_t)R * d * es; break;
+    case MOE_BWS_DAB: at = B.dab; n = (size_t)R * 2 * F * es; break;
+    case MOE_BWS_DL: at = B.dl; n = (size_t)T * E * es; break;
     case MOE_BWS_LR_UG: at = B.ug; n = lr ? (size_t)R * r * 4 : 0; break;
     case MOE_BWS_LR_UU: at = B.uu; n = lr ? (size_t)R * r * 4 : 0; break;
     case MOE_BWS_LR_Z_GU: at = B.zgu; n = lr ? (size_t)R * 2 * r * 2 : 0; break;

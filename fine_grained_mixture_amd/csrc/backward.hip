@@ -17,6 +17,8 @@
 //   from its router part, its shared-expert part and its kept slots' rows.
 // reduce_chunks_kernel: fixed-order sums of split-K partial products.
 
+#include <type_traits>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -32,7 +34,7 @@ __device__ __forceinline__ u32x2 pack_bf16x4(float a, float b, float c, float d)
   return p;
 }
 
-template <int KMAX>
+template <int KMAX, bool F32>
 __global__ void __launch_bounds__(256) combine_bwd_kernel(CombineBwdArgs a) {
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -59,21 +61,25 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(CombineBwdArgs a) {
       part[j] = 0.f;
     }
     const floatx4* dyt = reinterpret_cast<const floatx4*>(a.dy + t * a.d);
-    const u32x2* xt = reinterpret_cast<const u32x2*>(a.x + t * a.d);
+    // activation-type rows: 4 values are 8 bytes (bf16) or 16 (float32)
+    typedef typename std::conditional<F32, floatx4, u32x2>::type act4;
+    const act4* xt = static_cast<const act4*>(a.x) + t * d4;
+    act4* xp = static_cast<act4*>(a.x_perm);
+    act4* dyr = static_cast<act4*>(a.dy_routed);
     for (int c = lane; c < d4; c += 64) {
       const floatx4 g = dyt[c];
-      u32x2 xv = {0u, 0u};
-      if (a.x_perm) xv = xt[c];
+      act4 xv{};
+      if (xp) xv = xt[c];
       floatx4 v[KMAX];
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
         if (kept[j]) v[j] = yr[(int64_t)row[j] * d4 + c];
-      if (a.x_perm) {
+      if (xp) {
 #pragma unroll
         for (int j = 0; j < KMAX; ++j)
-          if (kept[j]) reinterpret_cast<u32x2*>(a.x_perm + (int64_t)row[j] * a.d)[c] = xv;
+          if (kept[j]) xp[(int64_t)row[j] * d4 + c] = xv;
       }
-      if (a.dy_shared)
+      if (!F32 && a.dy_shared)
         reinterpret_cast<u32x2*>(a.dy_shared + t * a.d)[c] = pack_bf16x4(g[0], g[1], g[2], g[3]);
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) {
@@ -82,8 +88,9 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(CombineBwdArgs a) {
           part[j] = fmaf(g[1], v[j][1], part[j]);
           part[j] = fmaf(g[2], v[j][2], part[j]);
           part[j] = fmaf(g[3], v[j][3], part[j]);
-          reinterpret_cast<u32x2*>(a.dy_routed + (int64_t)row[j] * a.d)[c] =
-              pack_bf16x4(gate[j] * g[0], gate[j] * g[1], gate[j] * g[2], gate[j] * g[3]);
+          const floatx4 gy = {gate[j] * g[0], gate[j] * g[1], gate[j] * g[2], gate[j] * g[3]};
+          if constexpr (F32) dyr[(int64_t)row[j] * d4 + c] = gy;
+          else dyr[(int64_t)row[j] * d4 + c] = pack_bf16x4(gy[0], gy[1], gy[2], gy[3]);
         }
       }
     }
@@ -97,6 +104,11 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(CombineBwdArgs a) {
     }
     if (lane < k) a.dgate[t * k + lane] = mine;
   }
+}
+
+__device__ __forceinline__ void store_dl(void* dl, int64_t i, float v, bool f32) {
+  if (f32) static_cast<float*>(dl)[i] = v;
+  else static_cast<uint16_t*>(dl)[i] = f32_to_bf16(v);
 }
 
 // One wave per token; lane e (+ 64 c) holds expert e's logit.
@@ -171,7 +183,7 @@ __global__ void __launch_bounds__(256) router_bwd_kernel(RouterBwdArgs a) {
         const float vj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vsel), j));
         if (sj == e) dl += vj;
       }
-      a.dl[t * E + e] = f32_to_bf16(dl);
+      store_dl(a.dl, t * E + e, dl, a.f32_out);
     }
   }
 }
@@ -278,7 +290,12 @@ __global__ void __launch_bounds__(256) router_bwd_vec_kernel(RouterBwdArgs a) {
         const float vj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vsel), j));
         if ((sj >> 2) == idx) dl[sj & 3] += vj;
       }
-      reinterpret_cast<u32x2*>(a.dl + t * E)[idx] = pack_bf16x4(dl[0], dl[1], dl[2], dl[3]);
+      if (a.f32_out)
+        reinterpret_cast<floatx4*>(static_cast<float*>(a.dl) + t * E)[idx] =
+            floatx4{dl[0], dl[1], dl[2], dl[3]};
+      else
+        reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.dl) + t * E)[idx] =
+            pack_bf16x4(dl[0], dl[1], dl[2], dl[3]);
     }
   }
 }
@@ -345,10 +362,16 @@ hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   if (a.k < 1 || a.k > 16 || a.d % 4) return hipErrorInvalidValue;
   const unsigned grid = wave_grid(a.T);
-  if (a.k <= 2) hipLaunchKernelGGL((combine_bwd_kernel<2>), dim3(grid), dim3(256), 0, s, a);
-  else if (a.k <= 4) hipLaunchKernelGGL((combine_bwd_kernel<4>), dim3(grid), dim3(256), 0, s, a);
-  else if (a.k <= 8) hipLaunchKernelGGL((combine_bwd_kernel<8>), dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((combine_bwd_kernel<16>), dim3(grid), dim3(256), 0, s, a);
+#define MOE_CB(F32)                                                                       \
+  do {                                                                                    \
+    if (a.k <= 2) hipLaunchKernelGGL((combine_bwd_kernel<2, F32>), dim3(grid), dim3(256), 0, s, a); \
+    else if (a.k <= 4) hipLaunchKernelGGL((combine_bwd_kernel<4, F32>), dim3(grid), dim3(256), 0, s, a); \
+    else if (a.k <= 8) hipLaunchKernelGGL((combine_bwd_kernel<8, F32>), dim3(grid), dim3(256), 0, s, a); \
+    else hipLaunchKernelGGL((combine_bwd_kernel<16, F32>), dim3(grid), dim3(256), 0, s, a); \
+  } while (0)
+  if (a.f32) MOE_CB(true);
+  else MOE_CB(false);
+#undef MOE_CB
   return hipGetLastError();
 }
 
@@ -359,7 +382,7 @@ hipError_t launch_router_bwd(const RouterBwdArgs& a, hipStream_t s) {
   // E = 24 the plain one is faster)
   const bool vec = a.E >= 256 && a.E % 4 == 0 && a.E <= 4096 &&
                    reinterpret_cast<uintptr_t>(a.logits) % 16 == 0 &&
-                   reinterpret_cast<uintptr_t>(a.dl) % 8 == 0;
+                   reinterpret_cast<uintptr_t>(a.dl) % 16 == 0;
   const dim3 grid(wave_grid(a.T)), block(256);
   if (!vec) hipLaunchKernelGGL(router_bwd_kernel, grid, block, 0, s, a);
   else if (a.E <= 512) hipLaunchKernelGGL(router_bwd_vec_kernel<2>, grid, block, 0, s, a);

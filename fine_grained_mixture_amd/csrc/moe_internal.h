@@ -291,6 +291,10 @@ struct BwdLaunch {
 int64_t bwd_tiles(const BwdGemm& P);
 hipError_t launch_gemm_bwd(BwdLaunch& L, bool a_kcontig, bool b_kcontig, int epilogue,
                            hipStream_t s);
+// The same work items with float32 operands and outputs (the SwiGLU epilogue
+// writes float32 da, db); no scaled copy (C2).
+hipError_t launch_gemm_bwd_f32(BwdLaunch& L, bool a_kcontig, bool b_kcontig, int epilogue,
+                               hipStream_t s);
 
 // SwiGLU backward of one expert group, fused with the recomputation of its
 // gate and up products: for rows r of group s and columns f < F
@@ -328,30 +332,33 @@ hipError_t launch_swiglu_bwd(const SwigluBwdLaunch& L, hipStream_t s);
 // the token rows of the expert products x_perm[row] = x[t] when non-null.
 struct CombineBwdArgs {
   const float* dy;
-  const uint16_t* x;         // [T, d] bf16
-  uint16_t* x_perm;          // [R_max, d] bf16 or null
+  const void* x;             // [T, d] in the activation type
+  void* x_perm;              // [R_max, d] in the activation type, or null
   const float* y_routed;
   const int32_t* row_of_slot;
   const float* topk_gate;
-  uint16_t* dy_routed;
-  uint16_t* dy_shared;
+  void* dy_routed;           // [R_max, d]: bf16, or float32 when f32
+  uint16_t* dy_shared;       // bf16 layers only, or null
   float* dgate;
   int64_t T;
   int32_t d, k;
+  int32_t f32;               // float32 layer: no rounding of the routed rows
 };
 hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t s);
 
-// Gradient of the router logits, one token per wave, rounded to bf16.
+// Gradient of the router logits, one token per wave, rounded to bf16 (or kept
+// in float32 for float32 layers).
 struct RouterBwdArgs {
   const float* logits;       // [T, E], logit_bias included
   const int32_t* topk_idx;   // [T, k]
   const float* topk_gate;    // [T, k]
   const float* dgate;        // [T, k]
   const int32_t* counts;     // [E] pre-drop slot counts
-  uint16_t* dl;            // [T, E] out
+  void* dl;                  // [T, E] out: bf16, or float32 when f32_out
   int64_t T;
   int32_t E, k, score, renorm;
   float aux_scale;           // d(loss)/d(aux) * aux_coef * E / T
+  int32_t f32_out;
 };
 hipError_t launch_router_bwd(const RouterBwdArgs& a, hipStream_t s);
 

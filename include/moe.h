@@ -354,10 +354,11 @@ size_t moe_backward_workspace_bytes(const moe_config *cfg, int64_t T);
    gives the byte offset into bwd_ws and the size of region `which`; a size of
    0 means the config has no such region. Returns MOE_EINVAL for an invalid
    config, T < 0, NULL outputs or an unknown region.
-     MOE_BWS_DY_ROUTED   bf16 [R_max, d]: gate * dy of each row, rounded
-     MOE_BWS_X_PERM      bf16 [R_max, d]: x of each row's token
-     MOE_BWS_DAB         bf16 [R_max, 2F]: da | db of each row
-     MOE_BWS_DL          bf16 [T, E]: the router-logit gradient
+     MOE_BWS_DY_ROUTED   [R_max, d]: gate * dy of each row (bf16, rounded; float32
+                         in a MOE_F32 layer, as the next three)
+     MOE_BWS_X_PERM      [R_max, d]: x of each row's token
+     MOE_BWS_DAB         [R_max, 2F]: da | db of each row
+     MOE_BWS_DL          [T, E]: the router-logit gradient
    rank-r experts (W = U diag(s) V^T of the dormouse "TSCT low-rank experts"
    card), per row, the recomputed forward chain and the backward's:
      MOE_BWS_LR_UG, _UU  float32 [R_max, r]: x U_gate, x U_up
@@ -386,7 +387,9 @@ int moe_backward_workspace_region(const moe_config *cfg, int64_t T, int32_t whic
    aux_grad: the loss gradient of aux (o->aux[1]), finite. bwd_ws: device,
    256-byte aligned, at least moe_backward_workspace_bytes. This library: bf16
    layers with n_routed a multiple of 8, of dense experts, or of rank-32 or
-   rank-64 experts without shared experts; otherwise MOE_EUNSUPPORTED.
+   rank-64 experts without shared experts; MOE_F32 layers of dense experts
+   (every operand and sum in float32, no rounding points); otherwise
+   MOE_EUNSUPPORTED.
    The result does not depend on scheduling (fixed summation orders, no
    atomics).                                                                 */
 int moe_layer_backward(const moe_config *cfg, int64_t T, const void *x, const moe_weights *w,

@@ -138,6 +138,18 @@ static void backward_cases() {
     EXPECT(moe_layer_backward(&c, T, fake(50), &w, &o, static_cast<float*>(fake(70)), 1.0f, &g,
                               ws_addr(), need, fake(8192), bneed, nullptr) == MOE_OK);
   }
+  // float32 dense experts: the fp32 FMA products, a | b recomputed
+  for (int64_t T : {64, 1, 0, 3000}) {
+    moe_config f = cfg(128, 8, 2, 1, 64, 0, MOE_F32);
+    moe_weights w = weights();
+    moe_outputs o = outputs();
+    moe_grads g = grads();
+    const int before = g_launches;
+    EXPECT(moe_layer_backward(&f, T, fake(50), &w, &o, static_cast<float*>(fake(70)), 1.0f, &g,
+                              ws_addr(), moe_workspace_bytes(&f, T), fake(8192),
+                              moe_backward_workspace_bytes(&f, T), nullptr) == MOE_OK);
+    EXPECT(g_launches > before);
+  }
   // rank-64 experts without shared experts: the factor-gradient path
   moe_weights w = weights();
   moe_outputs o = outputs();

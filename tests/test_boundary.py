@@ -153,15 +153,16 @@ def test_backward_workspace_regions(lib):
     dense experts."""
     from fine_grained_mixture_amd.layer import config_from_workload
     for wl in (WORKLOADS["quartz"], WORKLOADS["dormouse"], WORKLOADS["dormouse"].replace(T=1),
-               WORKLOADS["dormouse"].replace(rank=32, T=777)):
+               WORKLOADS["dormouse"].replace(rank=32, T=777), WORKLOADS["tiny"]):
         cfg = config_from_workload(wl)
         T, R = wl.T, _lib.moe_max_rows(cfg, wl.T)
         total = _lib.moe_backward_workspace_bytes(cfg, T)
         d, F, E, r = wl.hidden, wl.ffn, wl.n_routed, wl.rank
         lr = r > 0
+        es = 4 if wl.dtype == "f32" else 2
         m = _lib
-        want = {m.MOE_BWS_DY_ROUTED: R * d * 2, m.MOE_BWS_X_PERM: R * d * 2,
-                m.MOE_BWS_DAB: R * 2 * F * 2, m.MOE_BWS_DL: T * E * 2,
+        want = {m.MOE_BWS_DY_ROUTED: R * d * es, m.MOE_BWS_X_PERM: R * d * es,
+                m.MOE_BWS_DAB: R * 2 * F * es, m.MOE_BWS_DL: T * E * es,
                 m.MOE_BWS_LR_UG: R * r * 4 * lr, m.MOE_BWS_LR_UU: R * r * 4 * lr,
                 m.MOE_BWS_LR_Z_GU: R * 2 * r * 2 * lr, m.MOE_BWS_LR_AB: R * 2 * F * 4 * lr,
                 m.MOE_BWS_LR_H: R * F * 2 * lr, m.MOE_BWS_LR_UD: R * r * 4 * lr,
@@ -285,8 +286,9 @@ def test_backward_validation(lib):
     assert call(bws=0) == _lib.MOE_EWORKSPACE
     assert call(bws=0x1001) == _lib.MOE_EWORKSPACE
     assert call(T=-1) == _lib.MOE_EINVAL
-    # the library's backward: bf16 dense experts, expert count a multiple of 8
-    for bad in (_cfg(dtype="f32"), _cfg(n_routed=12), _cfg(rank=64)):
+    # the library's backward: bf16 dense experts (expert count a multiple of 8)
+    # or rank-32/64 experts without shared ones, and float32 dense experts
+    for bad in (_cfg(dtype="fp8"), _cfg(n_routed=12), _cfg(rank=64), _cfg(dtype="f32", rank=64)):
         nb = _lib.moe_backward_workspace_bytes(bad, T)
         st = call(c=bad, nbytes=_lib.moe_workspace_bytes(bad, T), bbytes=nb)
         assert st == _lib.MOE_EUNSUPPORTED

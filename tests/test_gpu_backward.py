@@ -76,10 +76,19 @@ def _check(wl, *, aux_grad=1.0, zero_dy=False, saved=False):
             i = np.unravel_index(int(np.argmax(err - tol)), err.shape)
             raise AssertionError(f"{n}: {int(bad.sum())} elements beyond 2^-5 M + 2^-16 S, "
                                  f"e.g. {i}: gpu {v[i]:.6e} oracle {r[i]:.6e} tol {tol[i]:.3e}")
+        if wl.dtype == "f32" and rms > 0:
+            # no rounding points: only fp32 sums separate the two sides (a bf16
+            # rounding anywhere would leave about 1e-3 of the RMS)
+            e_rms = float(np.sqrt(np.mean(err ** 2))) / rms
+            assert e_rms <= F32_ERR_RMS, f"{n}: error RMS {e_rms:.2e} of its RMS"
     print(f"[report] {wl.name} T={wl.T}: " + ", ".join(
         f"{k}: {a:.2e} rms, {b:.2f} tol" for k, (a, b) in rep.items()), flush=True)
     return rep
 
+
+# float32 layers: largest RMS of (gpu - oracle) over a gradient tensor,
+# relative to its RMS
+F32_ERR_RMS = 1e-5
 
 CASES = {
     "quartz_small": synth.QUARTZ.replace(T=517, hidden=256, ffn=128),
@@ -102,6 +111,18 @@ CASES = {
     "odd_widths": synth.Workload("ow", T=257, hidden=192, n_routed=16, top_k=3, n_shared=3,
                                  ffn=192, logit_offset_std=0.3, seed=11),
     "three_tokens": synth.QUARTZ.replace(T=3, hidden=256, ffn=128, seed=12),
+    # float32 layers (the fp32 FMA products, a | b recomputed): the Tiny layer
+    # and wider ones with capacity drops, sigmoid gates, no or three shared
+    # experts, top-1, and more rows than one tile per expert
+    "tiny_f32": synth.TINY,
+    "f32_rows": synth.TINY.replace(T=1500, hidden=192, ffn=128, n_routed=12, top_k=3,
+                                   n_shared=2, seed=31),
+    "f32_capacity_sigmoid": synth.Workload("fc", T=600, hidden=128, n_routed=16, top_k=2,
+                                           n_shared=0, ffn=64, score="sigmoid", renorm=1,
+                                           select_bias_std=0.1, capacity_factor="1/2",
+                                           dtype="f32", seed=32),
+    "f32_k1_three_shared": synth.Workload("f1", T=257, hidden=128, n_routed=8, top_k=1,
+                                          n_shared=3, ffn=192, dtype="f32", seed=33),
     # many experts: the router backward holding a token's logits in registers
     # (E >= 256), raw softmax gates, the last lanes partly filled
     "many_experts_raw_softmax": synth.Workload("me", T=300, hidden=128, n_routed=264, top_k=4,
