@@ -93,22 +93,32 @@ def test_forward_writes_stay_inside_their_buffers(name):
     P.check_parity(wl, inp, P.with_intermediates(wl, cfg, P.to_numpy(out), ws), no_rho=False)
 
 
-def test_backward_writes_stay_inside_their_buffers():
-    wl = synth.QUARTZ.replace(T=300, hidden=256, ffn=128)
-    print("\n[case] guard backward", flush=True)
+@pytest.mark.parametrize("kind", ["dense", "rank64", "f32"])
+def test_backward_writes_stay_inside_their_buffers(kind):
+    wl = {"dense": synth.QUARTZ.replace(T=300, hidden=256, ffn=128),
+          "rank64": synth.DORMOUSE.replace(T=300, hidden=256, ffn=128),
+          "f32": synth.TINY.replace(T=200)}[kind]
+    print(f"\n[case] guard backward {kind}", flush=True)
     inp = synth.make_inputs(wl)
     cfg, x, w = P.upload(wl, inp)
-    out = L.allocate_outputs(cfg, wl.T, x.device, saved_ab=True)
+    out = L.allocate_outputs(cfg, wl.T, x.device, saved_ab=kind == "dense")
     ws = L.allocate_workspace(cfg, wl.T, x.device)
     L.layer_forward(cfg, x, w, out, ws)
     g = Guarded(x.device)
-    E, d, F, S = cfg.n_routed, cfg.hidden, cfg.ffn, cfg.n_shared
+    E, d, F, S, r = cfg.n_routed, cfg.hidden, cfg.ffn, cfg.n_shared, cfg.rank
     f32 = torch.float32
-    t = {"dx": g.alloc((wl.T, d), f32), "dw_router": g.alloc((d, E), f32),
-         "dw_gate": g.alloc((E, d, F), f32), "dw_up": g.alloc((E, d, F), f32),
-         "dw_down": g.alloc((E, F, d), f32), "dsh_gate": g.alloc((S, d, F), f32),
-         "dsh_up": g.alloc((S, d, F), f32), "dsh_down": g.alloc((S, F, d), f32)}
-    grads = L.Grads(t, _lib.MoeGrads(**{n: L._ptr(t[n]) for n in _lib.GRAD_FIELDS}))
+    t = {"dx": g.alloc((wl.T, d), f32), "dw_router": g.alloc((d, E), f32)}
+    if r == 0:
+        t.update({"dw_gate": g.alloc((E, d, F), f32), "dw_up": g.alloc((E, d, F), f32),
+                  "dw_down": g.alloc((E, F, d), f32)})
+    else:
+        for m, (din, dout) in (("gate", (d, F)), ("up", (d, F)), ("down", (F, d))):
+            t.update({"du_" + m: g.alloc((E, din, r), f32), "ds_" + m: g.alloc((E, r), f32),
+                      "dv_" + m: g.alloc((E, dout, r), f32)})
+    if S:
+        t.update({"dsh_gate": g.alloc((S, d, F), f32), "dsh_up": g.alloc((S, d, F), f32),
+                  "dsh_down": g.alloc((S, F, d), f32)})
+    grads = L.Grads(t, _lib.MoeGrads(**{n: L._ptr(t.get(n)) for n in _lib.GRAD_FIELDS}))
     bws = g.alloc((_lib.moe_backward_workspace_bytes(cfg, wl.T),), torch.uint8)
     dy = torch.from_numpy(synth.make_upstream(wl)).to(x.device)
     _lib.moe_layer_backward(cfg, wl.T, x.data_ptr(), w.struct, out.struct, dy.data_ptr(), 1.0,

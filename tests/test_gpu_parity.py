@@ -72,6 +72,18 @@ EDGE = {
     # 3000 experts: the top-k workgroup's probability sums take the one-row LDS path
     "experts_3000": synth.Workload("e3000", T=100, hidden=128, n_routed=3000, top_k=4,
                                    n_shared=0, ffn=64, seed=14),
+    # 520 to 1,000 experts (the top-k kernel with 16 experts per lane, the
+    # last lanes partly past E): sigmoid keys with a selection bias beside a
+    # shared expert; k = 15 with capacity drops and a last routing block of
+    # one token; a single token at the Dormouse expert count
+    "experts_1000_sigmoid_k7": synth.Workload("w7", T=300, hidden=128, n_routed=1000, top_k=7,
+                                             n_shared=1, ffn=64, score="sigmoid", renorm=1,
+                                             select_bias_std=0.1, seed=15),
+    "experts_520_k15_capacity": synth.Workload("w15", T=129, hidden=192, n_routed=520,
+                                               top_k=15, n_shared=0, ffn=64, renorm=0,
+                                               capacity_factor="1", logit_offset_std=0.3,
+                                               seed=16),
+    "experts_1024_one_token": synth.DORMOUSE.replace(T=1, hidden=256, ffn=128, seed=17),
     # many experts, two active: routing blocks of one 64-slot chunk, with drops
     "many_experts_k2_capacity": synth.Workload("mc", T=333, hidden=128, n_routed=128, top_k=2,
                                                n_shared=0, ffn=64, capacity_factor="3/2",
@@ -93,6 +105,11 @@ TIES = {
                                    n_shared=0, ffn=64, score="sigmoid", renorm=1),
     "few_softmax": synth.Workload("tie_f", T=150, hidden=128, n_routed=24, top_k=6,
                                   n_shared=0, ffn=64, renorm=1),
+    # 600 and 1,024 experts
+    "wide_softmax": synth.Workload("tie_w", T=100, hidden=128, n_routed=1024, top_k=4,
+                                   n_shared=0, ffn=64, renorm=1),
+    "wide_sigmoid_k15": synth.Workload("tie_ws", T=70, hidden=128, n_routed=600, top_k=15,
+                                       n_shared=0, ffn=64, score="sigmoid", renorm=1),
 }
 
 
