@@ -763,7 +763,8 @@ def main():
         torch.cuda.synchronize()
         result["bias_update_us"] = e0.elapsed_time(e1) * 1e3 / args.steps
         sb.copy_(saved)
-    if wl.dtype == "bf16" and wl.rank == 0 and wl.n_routed % 8 == 0 and not args.no_backward:
+    if ((wl.dtype == "bf16" and wl.n_routed % 8 == 0) or wl.dtype == "f32") and wl.rank == 0 \
+            and not args.no_backward:
         fms, bms, bst = time_backward(wl, cfg, x, w, args.steps, args.warmup, stream)
         bfl = backward_flops(wl, rows)
         gemm = {n: f for n, f in bfl.items() if n in bst}
