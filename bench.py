@@ -51,6 +51,9 @@ def parse():
                     help="tokens of the workload the CPU oracle processes (0: all of them)")
     ap.add_argument("--tokens", type=int, default=0,
                     help="override the workload's token count T (e.g. decode-sized batches)")
+    ap.add_argument("--blas-reference", action="store_true",
+                    help="also time the platform BLAS (torch.bmm / matmul, hipBLASLt) on "
+                         "uniform stand-ins for the workload's expert products, for context")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the layer, run 3 plain device copies of this many MiB "
                          "(calibrates the HBM byte counters of a profiler run)")
@@ -128,6 +131,57 @@ def lowrank_backward_work(wl, rows, used):
                     2 * R * d + 2 * R * r + 4 * E * r * (2 * d + 3 * F)),
         wgrad_gemm2=2 * R * d + 2 * R * r + 4 * E * d * r + 2 * T * d + 2 * T * E + 4 * d * E)
     return flops, nbytes
+
+
+def blas_reference(wl, steps):
+    """The platform BLAS (torch.bmm and matmul, i.e. hipBLASLt) on uniform stand-ins for the
+    dense expert products of this workload: every routed expert given T k / E rows, the
+    gate and up products as one [rows, d] x [d, 2F] product per expert, the down product
+    [rows, F] x [F, d] with a bf16 output, the shared experts as one product over all T
+    tokens (K = S F for down). Context only: no gather, no ragged groups, no fused
+    epilogue, no fp32 output. Also an 8192^3 product, the library's ceiling."""
+    import torch
+
+    T, d, E, k, S, F = wl.T, wl.hidden, wl.n_routed, wl.top_k, wl.n_shared, wl.ffn
+    dev, bf = "cuda", torch.bfloat16
+    g = torch.Generator(device=dev).manual_seed(0)
+
+    def rnd(*shape):
+        return torch.randn(*shape, device=dev, dtype=bf, generator=g).contiguous()
+
+    def us_of(fn, n):
+        for _ in range(max(2, n // 5)):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    rows = max(1, T * k // E)
+    out = {"rows_per_expert": rows}
+    parts = {"gate_up": [(rnd(E, rows, d), rnd(E, d, 2 * F))],
+             "down": [(rnd(E, rows, F), rnd(E, F, d))]}
+    if S:
+        parts["gate_up"].append((rnd(T, d), rnd(d, S * 2 * F)))
+        parts["down"].append((rnd(T, S * F), rnd(S * F, d)))
+    for name, prods in parts.items():
+        us = flops = 0.0
+        for a, b in prods:
+            us += us_of(lambda a=a, b=b: torch.matmul(a, b), steps)
+            flops += 2.0 * a.numel() * b.shape[-1]
+        out[name] = {"us": us, "tflops": flops / (us * 1e-6) / 1e12,
+                     "frac_of_bf16_peak": flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS}
+    n = 8192
+    a, b = rnd(n, n), rnd(n, n)
+    us = us_of(lambda: torch.matmul(a, b), 20)
+    out["square_8192"] = {"us": us, "tflops": 2.0 * n ** 3 / (us * 1e-6) / 1e12,
+                          "frac_of_bf16_peak": 2.0 * n ** 3 / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS}
+    return out
 
 
 def time_backward(wl, cfg, x, w, steps, warmup, stream):
@@ -815,6 +869,8 @@ def main():
             "expert_gemm_tflops": (gu8 + dn8) / ((st8["gate_up_gemm"] + st8["down_gemm"]) * 1e-6)
             / 1e12,
         }
+    if args.blas_reference and wl.dtype == "bf16" and wl.rank == 0:
+        result["blas_reference"] = blas_reference(wl, args.steps)
     if cpu is not None:
         result["cpu_baseline"] = cpu
     print(json.dumps(result))
