@@ -24,6 +24,7 @@ MOE_BWS_DY_ROUTED, MOE_BWS_X_PERM, MOE_BWS_DAB, MOE_BWS_DL = 0, 1, 2, 3
 (MOE_BWS_LR_UG, MOE_BWS_LR_UU, MOE_BWS_LR_Z_GU, MOE_BWS_LR_AB, MOE_BWS_LR_H, MOE_BWS_LR_UD,
  MOE_BWS_LR_ZD, MOE_BWS_LR_DZD, MOE_BWS_LR_DUD, MOE_BWS_LR_DZG, MOE_BWS_LR_DZU,
  MOE_BWS_LR_DU_GU) = range(4, 16)
+MOE_BWS_DAB_SHARED = 16
 
 EXPORTED = ("moe_capacity", "moe_max_rows", "moe_workspace_bytes", "moe_workspace_region",
             "moe_route", "moe_permute",

@@ -796,7 +796,7 @@ bool backward_supported(const moe_config* c) {
   if (c->dtype == MOE_F32) return c->rank == 0;   // the fp32 FMA products
   if (c->dtype != MOE_BF16 || c->n_routed % 8) return false;
   if (c->rank == 0) return true;
-  return c->rank % 32 == 0 && c->rank <= 64 && c->n_shared == 0;
+  return c->rank % 32 == 0 && c->rank <= 64;
 }
 
 struct BwdLayout {
@@ -894,8 +894,15 @@ void lowrank_backward(Runner& Rn, const moe_config* c, int64_t T, const void* x,
                       float aux_grad, moe_grads* g, const Layout& L, const BwdLayout& B,
                       void* fws, void* bws) {
   const int64_t E = c->n_routed, d = c->hidden, F = c->ffn, k = c->top_k, r = c->rank;
+  const int64_t S = c->n_shared;
   const int64_t R = B.R;
   uint16_t* dyr = at<uint16_t>(bws, B.dyr);
+  // shared experts (dense, beside the rank-r ones): their upstream rows bf16(dy),
+  // da | db, input-gradient rows, and the forward's h of theirs
+  uint16_t* dysh = S > 0 ? at<uint16_t>(bws, B.dysh) : nullptr;
+  void* dabsh = at<void>(bws, B.dabsh);
+  float* dxsh = S > 0 ? at<float>(bws, B.dxsh) : nullptr;
+  const void* h_sh = at<void>(fws, L.h_sh);
   float* dg = at<float>(bws, B.dg);
   uint16_t* dl = at<uint16_t>(bws, B.dl);
   uint16_t* dab = at<uint16_t>(bws, B.dab);
@@ -970,12 +977,37 @@ void lowrank_backward(Runner& Rn, const moe_config* c, int64_t T, const void* x,
     cb.row_of_slot = o->row_of_slot;
     cb.topk_gate = o->topk_gate;
     cb.dy_routed = dyr;
-    cb.dy_shared = nullptr;
+    cb.dy_shared = dysh;
     cb.dgate = dg;
     cb.T = T;
     cb.d = (int32_t)d;
     cb.k = (int32_t)k;
     Rn.run("combine_bwd", [&] { return launch_combine_bwd(cb, Rn.stream); });
+
+    if (S > 0) {
+      // the shared experts' SwiGLU backward, their gate and up products recomputed
+      SwigluBwdLaunch SL{};
+      SwigluBwdProblem& p = SL.p[0];
+      p.X = x;
+      p.ldx = d;
+      p.DY = dysh;
+      p.ldy = d;
+      p.Wg = w->sh_gate;
+      p.Wu = w->sh_up;
+      p.Wd = w->sh_down;
+      p.w_group = d * F;
+      p.DAB = dabsh;
+      p.ldab = S * 2 * F;
+      p.ab_group = 2 * F;
+      p.M = (int32_t)T;
+      p.d = (int32_t)d;
+      p.F = (int32_t)F;
+      p.G = (int32_t)S;
+      p.n_tiles_n = (int32_t)(F / 64);
+      SL.n = 1;
+      SL.tiles0 = p.G * (int32_t)ceil_div(p.M, kSwigluBwdBM) * p.n_tiles_n;
+      Rn.run("swiglu_bwd", [&] { return launch_swiglu_bwd(SL, Rn.stream); });
+    }
 
     RouterBwdArgs rb{};
     rb.logits = logits;
@@ -1057,11 +1089,29 @@ void lowrank_backward(Runner& Rn, const moe_config* c, int64_t T, const void* x,
       q.n_tiles_m = (int32_t)ceil_div(T, kGemmBigBM);
       q.n_tiles_n = (int32_t)ceil_div(d, 128);
       BL.n = 2;
+      if (S > 0) {   // the shared experts' [da | db] [W_gate; W_up]^T
+        BwdGemm& u = BL.p[BL.n++] = bwd_problem();
+        u.A = dabsh;
+        u.lda = S * 2 * F;
+        u.B0 = w->sh_gate;
+        u.B1 = w->sh_up;
+        u.ldb = F;
+        u.k_seg = (int32_t)F;
+        u.b_seg = d * F;
+        u.C0 = dxsh;
+        u.ldc = d;
+        u.M = (int32_t)T;
+        u.N = (int32_t)d;
+        u.K = (int32_t)(S * 2 * F);
+        u.k_chunk = u.K;
+        u.n_tiles_m = (int32_t)ceil_div(T, kGemmBigBM);
+        u.n_tiles_n = (int32_t)ceil_div(d, 128);
+      }
       Rn.run("dgrad_gemm", [&] { return launch_gemm_bwd(BL, true, true, kBwdStoreF32, Rn.stream); });
     }
     DxGatherArgs dxa{};
     dxa.dx_rows = dxp;
-    dxa.dx_shared = nullptr;
+    dxa.dx_shared = dxsh;
     dxa.row_of_slot = o->row_of_slot;
     dxa.dx = g->dx;
     dxa.T = T;
@@ -1099,11 +1149,67 @@ void lowrank_backward(Runner& Rn, const moe_config* c, int64_t T, const void* x,
     p.n_tiles_m = (int32_t)ceil_div(d, kGemmBigBM);
     p.n_tiles_n = (int32_t)ceil_div(E, 128);
     BL.n = 2;
+    // the shared experts over all tokens (split over tokens when long)
+    const bool split_s = S > 0 && B.nch_s > 1;
+    const int32_t kch_s = (int32_t)(split_s ? kSharedKChunk : std::max<int64_t>(T, 1));
+    if (S > 0) {
+      BwdGemm& u = BL.p[BL.n++] = bwd_problem();
+      u.A = h_sh;
+      u.lda = S * F;
+      u.a_group = F;
+      u.B0 = dysh;
+      u.ldb = d;
+      u.C0 = split_s ? at<float>(bws, B.part_d) : g->dsh_down;
+      u.ldc = d;
+      u.c_group = (int64_t)B.nch_s * F * d;
+      u.c_chunk = F * d;
+      u.M = (int32_t)F;
+      u.N = (int32_t)d;
+      u.K = (int32_t)T;
+      u.G = (int32_t)S;
+      u.k_chunk = kch_s;
+      u.n_chunks = (int32_t)B.nch_s;
+      u.n_tiles_m = (int32_t)ceil_div(F, kGemmBigBM);
+      u.n_tiles_n = (int32_t)ceil_div(d, 128);
+      BwdGemm& v = BL.p[BL.n++] = bwd_problem();
+      v.A = x;
+      v.lda = d;
+      v.B0 = dabsh;
+      v.ldb = S * 2 * F;
+      v.b_group = 2 * F;
+      v.C0 = split_s ? at<float>(bws, B.part_g) : g->dsh_gate;
+      v.C1 = split_s ? at<float>(bws, B.part_u) : g->dsh_up;
+      v.c_split = (int32_t)F;
+      v.ldc = F;
+      v.c_group = (int64_t)B.nch_s * d * F;
+      v.c_chunk = d * F;
+      v.M = (int32_t)d;
+      v.N = (int32_t)(2 * F);
+      v.K = (int32_t)T;
+      v.G = (int32_t)S;
+      v.k_chunk = kch_s;
+      v.n_chunks = (int32_t)B.nch_s;
+      v.n_tiles_m = (int32_t)ceil_div(d, kGemmBigBM);
+      v.n_tiles_n = (int32_t)ceil_div(2 * F, 128);
+    }
     Rn.run("wgrad_gemm2", [&] { return launch_gemm_bwd(BL, false, false, kBwdStoreF32, Rn.stream); });
     if (B.nch_r > 1) {
       Rn.run("reduce_router", [&] {
         return launch_reduce_chunks(at<float>(bws, B.part_r), g->dw_router, 1, B.nch_r, d * E,
                                     Rn.stream);
+      });
+    }
+    if (split_s) {
+      Rn.run("reduce_shared", [&] {
+        hipError_t e = launch_reduce_chunks(at<float>(bws, B.part_g), g->dsh_gate, S, B.nch_s,
+                                            d * F, Rn.stream);
+        if (e == hipSuccess)
+          e = launch_reduce_chunks(at<float>(bws, B.part_u), g->dsh_up, S, B.nch_s, d * F,
+                                   Rn.stream);
+        if (e == hipSuccess)
+          e = launch_reduce_chunks(at<float>(bws, B.part_d), g->dsh_down, S, B.nch_s, F * d,
+                                   Rn.stream);
+        return e;
       });
     }
   }
@@ -1771,6 +1877,7 @@ int moe_backward_workspace_region(const moe_config* c, int64_t T, int32_t which,
     case MOE_BWS_X_PERM: at = B.xperm; n = (size_t)R * d * es; break;
     case MOE_BWS_DAB: at = B.dab; n = (size_t)R * 2 * F * es; break;
     case MOE_BWS_DL: at = B.dl; n = (size_t)T * E * es; break;
+    case MOE_BWS_DAB_SHARED: at = B.dabsh; n = (size_t)T * c->n_shared * 2 * F * es; break;
     case MOE_BWS_LR_UG: at = B.ug; n = lr ? (size_t)R * r * 4 : 0; break;
     case MOE_BWS_LR_UU: at = B.uu; n = lr ? (size_t)R * r * 4 : 0; break;
     case MOE_BWS_LR_Z_GU: at = B.zgu; n = lr ? (size_t)R * 2 * r * 2 : 0; break;

@@ -359,6 +359,7 @@ size_t moe_backward_workspace_bytes(const moe_config *cfg, int64_t T);
      MOE_BWS_X_PERM      [R_max, d]: x of each row's token
      MOE_BWS_DAB         [R_max, 2F]: da | db of each row
      MOE_BWS_DL          [T, E]: the router-logit gradient
+     MOE_BWS_DAB_SHARED  [T, S*2F]: the shared experts' da | db of each token
    rank-r experts (W = U diag(s) V^T of the dormouse "TSCT low-rank experts"
    card), per row, the recomputed forward chain and the backward's:
      MOE_BWS_LR_UG, _UU  float32 [R_max, r]: x U_gate, x U_up
@@ -375,7 +376,8 @@ enum {
   MOE_BWS_DY_ROUTED = 0, MOE_BWS_X_PERM = 1, MOE_BWS_DAB = 2, MOE_BWS_DL = 3,
   MOE_BWS_LR_UG = 4, MOE_BWS_LR_UU = 5, MOE_BWS_LR_Z_GU = 6, MOE_BWS_LR_AB = 7,
   MOE_BWS_LR_H = 8, MOE_BWS_LR_UD = 9, MOE_BWS_LR_ZD = 10, MOE_BWS_LR_DZD = 11,
-  MOE_BWS_LR_DUD = 12, MOE_BWS_LR_DZG = 13, MOE_BWS_LR_DZU = 14, MOE_BWS_LR_DU_GU = 15
+  MOE_BWS_LR_DUD = 12, MOE_BWS_LR_DZG = 13, MOE_BWS_LR_DZU = 14, MOE_BWS_LR_DU_GU = 15,
+  MOE_BWS_DAB_SHARED = 16
 };
 int moe_backward_workspace_region(const moe_config *cfg, int64_t T, int32_t which,
                                   size_t *offset, size_t *bytes);
@@ -387,7 +389,7 @@ int moe_backward_workspace_region(const moe_config *cfg, int64_t T, int32_t whic
    aux_grad: the loss gradient of aux (o->aux[1]), finite. bwd_ws: device,
    256-byte aligned, at least moe_backward_workspace_bytes. This library: bf16
    layers with n_routed a multiple of 8, of dense experts, or of rank-32 or
-   rank-64 experts without shared experts; MOE_F32 layers of dense experts
+   rank-64 experts (beside dense shared experts or none); MOE_F32 layers of dense experts
    (every operand and sum in float32, no rounding points); otherwise
    MOE_EUNSUPPORTED.
    The result does not depend on scheduling (fixed summation orders, no

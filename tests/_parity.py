@@ -296,7 +296,8 @@ def backward_intermediates(cfg, T, bws, rows) -> dict:
                 dud=region(m.MOE_BWS_LR_DUD, b16, (R, r)),
                 dzg=region(m.MOE_BWS_LR_DZG, f32, (R, r)),
                 dzu=region(m.MOE_BWS_LR_DZU, f32, (R, r)),
-                dugu=region(m.MOE_BWS_LR_DU_GU, b16, (R, 2 * r)))
+                dugu=region(m.MOE_BWS_LR_DU_GU, b16, (R, 2 * r)),
+                dab_sh=region(m.MOE_BWS_DAB_SHARED, b16, (T, cfg.n_shared * 2 * F)))
 
 
 def sum_rel(K):
@@ -310,6 +311,12 @@ def sum_rel(K):
 def seq_rel(K):
     """The same for a sequential fp32 sum of K products (one rounding each)."""
     return 4.0 * (np.asarray(K, np.float64) + 16.0) * 2.0 ** -24
+
+
+def _dsilu2(z):
+    """Second derivative of z sigmoid(z): s (1 - s) (2 + z (1 - 2 s))."""
+    sg = oracle.sigmoid(z)
+    return sg * (1.0 - sg) * (2.0 + z * (1.0 - 2.0 * sg))
 
 
 def _window_check(what, gpu, v, eps):
@@ -362,6 +369,11 @@ def lowrank_backward_check(inp, spec, dy, fwd, g, I, ref):
     then each gradient's error RMS against the oracle's is at most
     LOWRANK_GRAD_ERR_RMS of its RMS, and dx and dw_router are within
     2^-5 B + 2^-16 S of the oracle's (the dense experts' bound).
+    Dense shared experts beside them (I["dab_sh"], and I["h_sh"] from the
+    forward's workspace): their da | db inside the windows of the exact a, b
+    and dh carried through the SwiGLU backward, their share of dx, their
+    weight gradients from the GPU's operands and, against the oracle, within
+    the dense bound.
 
     The chain itself is not compared with the oracle element by element:
     its fp32 sums tip some bf16 roundings the other way than the oracle's
@@ -488,6 +500,51 @@ def lowrank_backward_check(inp, spec, dy, fwd, g, I, ref):
         dxr, dxr_mag = prod(dl, wr.T)
     dx_ex = dxr.copy()
     dx_tol = sum_rel(E) * dxr_mag + 2.0 ** -24 * np.abs(dxr)
+    S = spec.n_shared
+    if S:
+        # dense shared experts beside the rank-r ones: their da | db (GPU,
+        # recomputed a, b and dh in fp32) inside the rounding windows of the
+        # exact a, b, dh carried through the SwiGLU backward, their share of dx,
+        # and their weight gradients from the GPU's operands
+        xs = x
+        dysh = rho(dy)
+        dab_sh = I["dab_sh"]
+        h_sh = I["h_sh"]
+        for e in range(S):
+            wg = np.asarray(ex.sh[0][e], np.float64)
+            wu = np.asarray(ex.sh[1][e], np.float64)
+            wd = np.asarray(ex.sh[2][e], np.float64)
+            A_, mA = prod(xs, wg)
+            B_, mB = prod(xs, wu)
+            dh_, mdh = prod(dysh, wd.T)
+            eA = sum_rel(d) * mA + 2.0 ** -24 * np.abs(A_)
+            eB = sum_rel(d) * mB + 2.0 ** -24 * np.abs(B_)
+            edh = sum_rel(d) * mdh + 2.0 ** -24 * np.abs(dh_)
+            sA_, dA_ = oracle.silu(A_), oracle.dsilu(A_)
+            sig_ = oracle.sigmoid(A_)
+            e_ds = 2.0 ** -21 * (sig_ * (1.0 + np.abs(A_)) + np.abs(dA_)) + np.abs(_dsilu2(A_)) * eA
+            va_ = dh_ * B_ * dA_
+            vb_ = dh_ * sA_
+            DAs = dab_sh[:, e * 2 * F:e * 2 * F + F]
+            DBs = dab_sh[:, e * 2 * F + F:(e + 1) * 2 * F]
+            tip[f"da_shared{e}"] = _window_check(
+                f"shared expert {e} da", DAs, va_,
+                np.abs(B_ * dA_) * edh + np.abs(dh_ * dA_) * eB + np.abs(dh_ * B_) * e_ds +
+                2.0 ** -22 * np.abs(va_))
+            tip[f"db_shared{e}"] = _window_check(
+                f"shared expert {e} db", DBs, vb_,
+                np.abs(sA_) * edh + np.abs(dh_ * dA_) * eA + 2.0 ** -21 * np.abs(vb_) +
+                2.0 ** -22 * np.abs(vb_))
+            p1, m1 = prod(DAs, wg.T)
+            p2, m2 = prod(DBs, wu.T)
+            dx_ex += p1 + p2
+            dx_tol += sum_rel(2 * F * S) * (m1 + m2)
+            hs = h_sh[:, e * F:(e + 1) * F]
+            for n, P_, Q_ in (("dsh_down", hs, dysh), ("dsh_gate", xs, DAs), ("dsh_up", xs, DBs)):
+                ex_, mag = prod(P_.T, Q_)
+                worst[f"{n}[{e}]"] = _sum_check(
+                    f"{n}[{e}] from the GPU's operands", g[n][e].astype(np.float64), ex_,
+                    sum_rel(T) * mag + 2.0 ** -24 * np.abs(ex_))
     for j in range(k):
         rr = row_of_slot[:, j]
         m = rr >= 0
@@ -502,7 +559,8 @@ def lowrank_backward_check(inp, spec, dy, fwd, g, I, ref):
 
     # against the oracle
     rep["err_rms"] = {}
-    for n in ("dx", "dw_router", *oracle.LOWRANK_GRADS):
+    for n in ("dx", "dw_router", *oracle.LOWRANK_GRADS,
+              *(("dsh_gate", "dsh_up", "dsh_down") if S else ())):
         rv, gv = ref[n], g[n].astype(np.float64)
         assert gv.shape == rv.shape and np.all(np.isfinite(gv)), n
         rms = float(np.sqrt(np.mean(rv ** 2))) if rv.size else 0.0
@@ -510,7 +568,7 @@ def lowrank_backward_check(inp, spec, dy, fwd, g, I, ref):
         rep["err_rms"][n] = err / rms if rms else err
         assert err <= LOWRANK_GRAD_ERR_RMS * rms, (
             f"{n}: error RMS {err:.3e} is {err / rms:.2e} of its RMS {rms:.3e}")
-        if n in ("dx", "dw_router"):
+        if n in ("dx", "dw_router", "dsh_gate", "dsh_up", "dsh_down"):
             tol = 2.0 ** -5 * ref["B_" + n] + 2.0 ** -16 * ref["S_" + n]
             _sum_check(n + " against the oracle", gv, rv, tol)
     return rep

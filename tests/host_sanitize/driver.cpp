@@ -161,7 +161,7 @@ static void backward_cases() {
                               ws_addr(), moe_workspace_bytes(&r, T), fake(8192),
                               moe_backward_workspace_bytes(&r, T), nullptr) == MOE_OK);
     EXPECT(g_launches > before);
-    for (int q = MOE_BWS_DY_ROUTED; q <= MOE_BWS_LR_DU_GU; ++q) {
+    for (int q = MOE_BWS_DY_ROUTED; q <= MOE_BWS_DAB_SHARED; ++q) {
       size_t off = 1, n = 1;
       EXPECT(moe_backward_workspace_region(&r, T, q, &off, &n) == MOE_OK);
       EXPECT(off + n <= moe_backward_workspace_bytes(&r, T));
@@ -172,12 +172,19 @@ static void backward_cases() {
                               ws_addr(), moe_workspace_bytes(&r, T), fake(8192),
                               moe_backward_workspace_bytes(&r, T), nullptr) == MOE_EINVAL);
   }
-  // rank-64 experts beside shared experts, and rank 16: legal, no backward here
-  moe_config r1 = cfg(768, 1024, 2, 1, 512, 64), r2 = cfg(768, 1024, 2, 0, 512, 16);
-  for (moe_config* r : {&r1, &r2})
-    EXPECT(moe_layer_backward(r, 64, fake(50), &w, &o, static_cast<float*>(fake(70)), 1.0f, &g,
-                              ws_addr(), moe_workspace_bytes(r, 64), fake(8192),
-                              moe_backward_workspace_bytes(r, 64), nullptr) == MOE_EUNSUPPORTED);
+  // rank-64 experts beside a shared expert (its dense backward in the same
+  // call, split over tokens past 4096)
+  for (int64_t T : {64, 5000}) {
+    moe_config r1 = cfg(768, 1024, 2, 1, 512, 64);
+    EXPECT(moe_layer_backward(&r1, T, fake(50), &w, &o, static_cast<float*>(fake(70)), 1.0f, &g,
+                              ws_addr(), moe_workspace_bytes(&r1, T), fake(8192),
+                              moe_backward_workspace_bytes(&r1, T), nullptr) == MOE_OK);
+  }
+  // rank 16: legal, no backward here
+  moe_config r2 = cfg(768, 1024, 2, 0, 512, 16);
+  EXPECT(moe_layer_backward(&r2, 64, fake(50), &w, &o, static_cast<float*>(fake(70)), 1.0f, &g,
+                            ws_addr(), moe_workspace_bytes(&r2, 64), fake(8192),
+                            moe_backward_workspace_bytes(&r2, 64), nullptr) == MOE_EUNSUPPORTED);
 }
 
 static void invalid_cases() {

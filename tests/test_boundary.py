@@ -168,7 +168,8 @@ def test_backward_workspace_regions(lib):
                 m.MOE_BWS_LR_H: R * F * 2 * lr, m.MOE_BWS_LR_UD: R * r * 4 * lr,
                 m.MOE_BWS_LR_ZD: R * r * 2 * lr, m.MOE_BWS_LR_DZD: R * r * 4 * lr,
                 m.MOE_BWS_LR_DUD: R * r * 2 * lr, m.MOE_BWS_LR_DZG: R * r * 4 * lr,
-                m.MOE_BWS_LR_DZU: R * r * 4 * lr, m.MOE_BWS_LR_DU_GU: R * 2 * r * 2 * lr}
+                m.MOE_BWS_LR_DZU: R * r * 4 * lr, m.MOE_BWS_LR_DU_GU: R * 2 * r * 2 * lr,
+                m.MOE_BWS_DAB_SHARED: T * wl.n_shared * 2 * F * es}
         spans = []
         for which, n in want.items():
             off, got = _lib.moe_backward_workspace_region(cfg, T, which)
@@ -179,7 +180,7 @@ def test_backward_workspace_regions(lib):
         spans.sort()
         assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
     with pytest.raises(_lib.MoeError):
-        _lib.moe_backward_workspace_region(_cfg(), 64, 16)
+        _lib.moe_backward_workspace_region(_cfg(), 64, 17)
 
 
 @pytest.mark.parametrize("rank,dtype", [(8, "bf16"), (40, "bf16"), (80, "bf16"), (128, "bf16"),
@@ -287,8 +288,8 @@ def test_backward_validation(lib):
     assert call(bws=0x1001) == _lib.MOE_EWORKSPACE
     assert call(T=-1) == _lib.MOE_EINVAL
     # the library's backward: bf16 dense experts (expert count a multiple of 8)
-    # or rank-32/64 experts without shared ones, and float32 dense experts
-    for bad in (_cfg(dtype="fp8"), _cfg(n_routed=12), _cfg(rank=64), _cfg(dtype="f32", rank=64)):
+    # or rank-32/64 experts, and float32 dense experts
+    for bad in (_cfg(dtype="fp8"), _cfg(n_routed=12), _cfg(rank=16), _cfg(dtype="f32", rank=64)):
         nb = _lib.moe_backward_workspace_bytes(bad, T)
         st = call(c=bad, nbytes=_lib.moe_workspace_bytes(bad, T), bbytes=nb)
         assert st == _lib.MOE_EUNSUPPORTED

@@ -6,7 +6,8 @@ the oracle's own for tokens away from near-ties, and either choice is correct
 within them) and the same upstream gradient.
 
 Dense experts give dW of every expert matrix; rank-r experts give the
-gradients of their factors U, s and V (no shared experts beside them).
+gradients of their factors U, s and V (and dW of dense shared experts beside
+them).
 
 Tolerance, per element of every gradient tensor. Each element is a sum of
 products whose bf16 operands both sides round at the same points; the GPU
@@ -280,6 +281,7 @@ def _check_lowrank(wl, aux_grad=1.0):
     grads = {n: v.cpu().numpy() for n, v in g.t.items() if v is not None}
     rows = int(fwd["offsets"][wl.n_routed])
     I = P.backward_intermediates(cfg, wl.T, bws, rows)
+    I["h_sh"] = P.workspace_intermediates(cfg, wl.T, ws, rows)["h_sh"]
     P.check_parity(wl, inp, fwd, check_y=False)
     spec = P.spec_of(wl)
     gi = fwd["topk_idx"].astype(np.int64)
@@ -308,6 +310,14 @@ LOWRANK = {
     "zipf_skew": synth.DORMOUSE.replace(T=1500, hidden=256, ffn=128, n_routed=64, zipf_s=1.1,
                                         seed=11),
     "one_token": synth.DORMOUSE.replace(T=1, hidden=128, ffn=64, seed=2),
+    # dense shared experts beside the rank-r ones: one, two with r = 32 and
+    # renormalised gates, and one over more tokens than a shared-expert chunk
+    # (4096: the weight gradients split over tokens and reduced in order)
+    "shared": synth.DORMOUSE.replace(T=500, hidden=256, ffn=128, n_shared=1, seed=21),
+    "rank32_two_shared": synth.DORMOUSE.replace(T=700, hidden=192, ffn=128, rank=32,
+                                                n_routed=64, n_shared=2, renorm=1, seed=22),
+    "shared_split": synth.DORMOUSE.replace(T=5000, hidden=128, ffn=64, n_routed=64, n_shared=1,
+                                           seed=23),
     "full_dormouse": synth.DORMOUSE,
 }
 

@@ -217,6 +217,27 @@ def _emulate_lowrank_backward(inp, spec, ref, dy, dl, s_gate_scale=1.0, dsilu=No
     for j in range(k):
         m = rows[:, j] >= 0
         dx[m] += dxe[rows[m, j]]
+    S = spec.n_shared
+    if S:
+        # dense shared experts over all tokens, as the GPU runs them
+        dysh = r32(dy)
+        dab_sh = np.zeros((T, S * 2 * F), f32)
+        h_sh = np.zeros((T, S * F), f32)
+        for n in ("dsh_gate", "dsh_up", "dsh_down"):
+            g[n] = np.zeros((S, F, d) if n == "dsh_down" else (S, d, F), f32)
+        for e in range(S):
+            wg, wu, wd = (np.asarray(ex.sh[i][e], f32) for i in range(3))
+            A, B = x @ wg, x @ wu
+            sgm = f32(1) / (f32(1) + np.exp(-A))
+            h_sh[:, e * F:(e + 1) * F] = r32(A * sgm * B)
+            dh = dysh @ wd.T
+            DA = r32(dh * B * (sgm * (f32(1) + A * (f32(1) - sgm))))
+            DB = r32(dh * (A * sgm))
+            dab_sh[:, e * 2 * F:e * 2 * F + F], dab_sh[:, e * 2 * F + F:(e + 1) * 2 * F] = DA, DB
+            dx += DA @ wg.T + DB @ wu.T
+            g["dsh_down"][e] = h_sh[:, e * F:(e + 1) * F].T @ dysh
+            g["dsh_gate"][e], g["dsh_up"][e] = x.T @ DA, x.T @ DB
+        I["dab_sh"], I["h_sh"] = dab_sh, h_sh
     g["dx"], g["dw_router"] = dx, x.T @ dl32
     I = {n: v.astype(np.float64) for n, v in I.items()}
     I["dl"] = dl32.astype(np.float64)
@@ -279,3 +300,42 @@ def test_lowrank_backward_check_accepts_a_float32_chain_and_rejects_planted_mist
                            np.asarray(inp["w_router"], np.float32).T)
     fails(fwd, g2, I, "router share of dx")
     assert r == 64
+
+
+def test_lowrank_backward_check_covers_shared_experts():
+    """With dense shared experts beside the rank-r ones, the float32
+    evaluation still passes the check, and mistakes planted in the shared
+    part fail it: a shared da entry two ulps off its rounding, a shared down
+    gradient element 2^-10 off its sum, the shared experts' share of dx left
+    out."""
+    wl = synth.DORMOUSE.replace(T=700, hidden=192, ffn=128, rank=32, n_routed=64, n_shared=2,
+                                renorm=1, seed=22)
+    inp = synth.make_inputs(wl)
+    dy = synth.make_upstream(wl)
+    spec = P.spec_of(wl)
+    ref = oracle.layer_forward(inp["x"], inp, spec, tokens=[])
+    orc = oracle.layer_backward_batched(inp["x"], inp, spec, dy, aux_grad=1.0, fwd=ref)
+    fwd, g, I = _emulate_lowrank_backward(inp, spec, ref, dy, orc["dl"])
+    rep = P.lowrank_backward_check(inp, spec, dy, fwd, g, I, orc)
+    assert "da_shared1" in rep["tipped"] and "dsh_down[1]" in rep["worst_sum"]
+
+    def fails(g2, I2):
+        with pytest.raises(AssertionError):
+            P.lowrank_backward_check(inp, spec, dy, fwd, g2, I2, orc)
+
+    I2 = {n: v.copy() for n, v in I.items()}
+    t, c = np.unravel_index(int(np.argmax(np.abs(I2["dab_sh"][:, 5:6]))), (wl.T, 1))
+    v = I2["dab_sh"][t, 5]
+    I2["dab_sh"][t, 5] = v + 2 * np.ldexp(1.0, int(np.frexp(abs(v))[1]) - 8) * np.sign(v)
+    fails(g, I2)
+    g2 = {n: v.copy() for n, v in g.items()}
+    g2["dsh_down"][1, 3, 4] *= 1 + 2.0 ** -10
+    fails(g2, I)
+    g2 = {n: v.copy() for n, v in g.items()}
+    F = wl.ffn
+    for e in range(wl.n_shared):
+        wg, wu = (np.asarray(oracle.Experts(inp, spec).sh[i][e], np.float32) for i in range(2))
+        g2["dx"] = g2["dx"] - (I["dab_sh"][:, e * 2 * F:e * 2 * F + F].astype(np.float32) @ wg.T +
+                               I["dab_sh"][:, e * 2 * F + F:(e + 1) * 2 * F].astype(np.float32)
+                               @ wu.T)
+    fails(g2, I)
