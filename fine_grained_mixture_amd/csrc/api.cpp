@@ -801,6 +801,7 @@ bool backward_supported(const moe_config* c) {
 
 struct BwdLayout {
   int64_t T = 0, R = 0, nch_r = 1, nch_s = 1, lr_tiles = 0;
+  int32_t kch_r = 1;   // tokens per chunk of the router's weight gradient
   size_t dyr = 0, dysh = 0, dg = 0, dl = 0, dab = 0, dabsh = 0, xperm = 0, dxp = 0,
          dxsh = 0, part_r = 0, part_g = 0, part_u = 0, part_d = 0, total = 0;
   // float32 layers: the recomputed gate and up products (routed, shared)
@@ -818,7 +819,16 @@ BwdLayout make_bwd_layout(const moe_config* c, int64_t T) {
   const int64_t E = c->n_routed, d = c->hidden, F = c->ffn, S = c->n_shared, k = c->top_k;
   B.T = T;
   B.R = max_rows(c, T);
-  B.nch_r = std::max<int64_t>(1, ceil_div(T, kRouterKChunk));
+  // the router's weight gradient x^T dl: its (d / 256) x (E / 128) tiles split
+  // over token chunks of at least kRouterKChunk, about one round of
+  // workgroups in all (fewer chunks, fewer partials to write and reduce)
+  {
+    const int64_t tiles = ceil_div(d, kGemmBigBM) * ceil_div(E, 128);
+    const int64_t most = std::max<int64_t>(1, ceil_div(T, kRouterKChunk));
+    const int64_t want = std::min<int64_t>(most, std::max<int64_t>(1, ceil_div(512, tiles)));
+    B.kch_r = (int32_t)(ceil_div(ceil_div(std::max<int64_t>(T, 1), want), 32) * 32);
+    B.nch_r = std::max<int64_t>(1, ceil_div(T, B.kch_r));
+  }
   B.nch_s = std::max<int64_t>(1, ceil_div(T, kSharedKChunk));
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -1144,7 +1154,7 @@ void lowrank_backward(Runner& Rn, const moe_config* c, int64_t T, const void* x,
     p.M = (int32_t)d;
     p.N = (int32_t)E;
     p.K = (int32_t)T;
-    p.k_chunk = B.nch_r > 1 ? kRouterKChunk : (int32_t)std::max<int64_t>(T, 1);
+    p.k_chunk = B.nch_r > 1 ? B.kch_r : (int32_t)std::max<int64_t>(T, 1);
     p.n_chunks = (int32_t)B.nch_r;
     p.n_tiles_m = (int32_t)ceil_div(d, kGemmBigBM);
     p.n_tiles_n = (int32_t)ceil_div(E, 128);
@@ -1636,7 +1646,7 @@ int layer_backward(const moe_config* c, int64_t T, const void* x, const moe_weig
       p.M = (int32_t)d;
       p.N = (int32_t)E;
       p.K = (int32_t)T;
-      p.k_chunk = B.nch_r > 1 ? kRouterKChunk : (int32_t)std::max<int64_t>(T, 1);
+      p.k_chunk = B.nch_r > 1 ? B.kch_r : (int32_t)std::max<int64_t>(T, 1);
       p.n_chunks = (int32_t)B.nch_r;
       p.n_tiles_m = (int32_t)ceil_div(d, kGemmBigBM);
       p.n_tiles_n = (int32_t)ceil_div(E, 128);
