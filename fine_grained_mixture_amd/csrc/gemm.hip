@@ -345,22 +345,11 @@ gemm_f32_kernel(GemmLaunch L) {
 // ---------------------------------------------------------------------------
 __device__ int block_exclusive_scan(int v, int* smem, int& total) {
   const int lane = lane_id(), wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int n = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += n;
-  }
+  const int incl = wave_incl_scan_i32(v);
   if (lane == 63) smem[wave] = incl;
   __syncthreads();
   if (wave == 0) {
-    int w = lane < nw ? smem[lane] : 0;
-    int wi = w;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      int n = __shfl_up(wi, o, 64);
-      if (lane >= o) wi += n;
-    }
+    const int wi = wave_incl_scan_i32(lane < nw ? smem[lane] : 0);
     if (lane < nw) smem[lane] = wi;
   }
   __syncthreads();

@@ -109,6 +109,59 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// Inclusive prefix sums over the 64 lanes of a wave in lane order, on the DPP
+// path (no LDS round trips): row_shr:1, 2, 4, 8 scan each row of 16 lanes,
+// then row_bcast:15 adds row 0's total to row 1 and row 2's to row 3
+// (row_mask 0xA), and row_bcast:31 adds lane 31's running total to rows 2 and
+// 3 (row_mask 0xC). Lanes whose DPP source does not exist, and rows the mask
+// leaves out, add 0. The additions run in one fixed order.
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_or0_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_or0_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROW_MASK,
+                                                            0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL,
+                                                            ROW_MASK, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ int wave_incl_scan_i32(int v) {
+  v += dpp_or0_i32<kDppRowShr1, 0xF>(v);
+  v += dpp_or0_i32<kDppRowShr2, 0xF>(v);
+  v += dpp_or0_i32<kDppRowShr4, 0xF>(v);
+  v += dpp_or0_i32<kDppRowShr8, 0xF>(v);
+  v += dpp_or0_i32<kDppRowBcast15, 0xA>(v);
+  v += dpp_or0_i32<kDppRowBcast31, 0xC>(v);
+  return v;
+}
+__device__ __forceinline__ double wave_incl_scan_f64(double v) {
+  v += dpp_or0_f64<kDppRowShr1, 0xF>(v);
+  v += dpp_or0_f64<kDppRowShr2, 0xF>(v);
+  v += dpp_or0_f64<kDppRowShr4, 0xF>(v);
+  v += dpp_or0_f64<kDppRowShr8, 0xF>(v);
+  v += dpp_or0_f64<kDppRowBcast15, 0xA>(v);
+  v += dpp_or0_f64<kDppRowBcast31, 0xC>(v);
+  return v;
+}
+// lane 63's value in every lane (a scalar read)
+__device__ __forceinline__ int lane63_i32(int v) { return __builtin_amdgcn_readlane(v, 63); }
+__device__ __forceinline__ double lane63_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 // Bits of a wave ballot below this lane.
 __device__ __forceinline__ uint64_t lanemask_lt() {
   int l = lane_id();

@@ -177,22 +177,11 @@ __global__ void __launch_bounds__((topk_threads<EPL, R>())) topk_kernel(TopkArgs
 // ---------------------------------------------------------------------------
 __device__ int block_scan_excl(int v, int* smem, int& total) {
   const int lane = lane_id(), wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += n;
-  }
+  const int incl = wave_incl_scan_i32(v);
   if (lane == 63) smem[wave] = incl;
   __syncthreads();
   if (wave == 0) {
-    const int w = lane < nw ? smem[lane] : 0;
-    int wi = w;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int n = __shfl_up(wi, o, 64);
-      if (lane >= o) wi += n;
-    }
+    const int wi = wave_incl_scan_i32(lane < nw ? smem[lane] : 0);
     if (lane < nw) smem[lane] = wi;
   }
   __syncthreads();
@@ -202,11 +191,11 @@ __device__ int block_scan_excl(int v, int* smem, int& total) {
   return base + incl - v;
 }
 
-// Sum over the workgroup in a fixed order (lane butterfly, then waves in order).
+// Sum over the workgroup in a fixed order (a wave's prefix sum, then waves in
+// order).
 __device__ double block_sum_fixed(double v, double* smem) {
   const int lane = lane_id(), wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  v = lane63_f64(wave_incl_scan_f64(v));
   if (lane == 0) smem[wave] = v;
   __syncthreads();
   double tot = 0.0;
@@ -604,13 +593,7 @@ __global__ void __launch_bounds__(1024) scan_rank_small_kernel(ScanArgs a, RankA
       excl = scan_outputs(a, c, P);
     } else {
       const int kp = ve ? (a.capacity > 0 ? min(c, a.capacity) : c) : 0;
-      int incl = kp;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int n = __shfl_up(incl, o, 64);
-        if (e >= o) incl += n;
-      }
-      excl = incl - kp;
+      excl = wave_incl_scan_i32(kp) - kp;
     }
     s_off[e] = excl;
   }

@@ -234,10 +234,10 @@ __global__ void __launch_bounds__(256) route_small_kernel(RouteSmallArgs a, int 
       for (int i = 0; i < 4; ++i)
         s_part[(wave * kTB + 4 * g + i) * (EP + 1) + 16 * j + l16] = acc[j][i];
     // next group's fragments travel while this group is scored (rows are
-    // clamped to the last token, so the load after the last group is a
-    // harmless re-read; no data-dependent branch around the loads keeps them
-    // back to back)
-    if (RES) {
+    // clamped to the last token, so a load past the batch's end is a harmless
+    // re-read; the launch's last group loads nothing, and the branch is
+    // uniform, so the loads still go out back to back)
+    if (RES && grp + 1 < groups) {
       __builtin_amdgcn_sched_barrier(0);
       load_x(x_row(t0 + kTB), s_lo, s_hi - s_lo);
       __builtin_amdgcn_sched_barrier(0);

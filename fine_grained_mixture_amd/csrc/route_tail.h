@@ -16,17 +16,10 @@ __device__ inline int scan_outputs(const ScanArgs& a, int c, float P) {
   const int e = lane_id();
   const bool ve = e < E;
   const int kp = ve ? (a.capacity > 0 ? min(c, a.capacity) : c) : 0;
-  int incl = kp;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(incl, o, 64);
-    if (e >= o) incl += n;
-  }
+  const int incl = wave_incl_scan_i32(kp);
   const int excl = incl - kp;
-  const int total_kept = __shfl(incl, 63, 64);
-  int drop = ve ? c - kp : 0;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) drop += __shfl_xor(drop, m, 64);
+  const int total_kept = lane63_i32(incl);
+  const int drop = lane63_i32(wave_incl_scan_i32(ve ? c - kp : 0));
   if (ve) {
     a.counts[e] = c;
     a.kept[e] = kp;
@@ -42,9 +35,7 @@ __device__ inline int scan_outputs(const ScanArgs& a, int c, float P) {
   const double Pe = ve && a.T > 0 ? (double)P / (double)a.T : 0.0;
   if (ve && a.f) a.f[e] = (float)fe;
   if (ve && a.P) a.P[e] = (float)Pe;
-  double prod = fe * Pe;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) prod += __shfl_xor(prod, m, 64);
+  const double prod = lane63_f64(wave_incl_scan_f64(fe * Pe));
   if (e == 0) {
     const double raw = (double)E * prod;
     a.aux[0] = (float)raw;
@@ -54,13 +45,8 @@ __device__ inline int scan_outputs(const ScanArgs& a, int c, float P) {
   // tile list of the routed grouped GEMM, (expert, first row) in expert order
   if (a.plan) {
     const int nt = (kp + a.plan_bm - 1) / a.plan_bm;
-    int ti = nt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int n = __shfl_up(ti, o, 64);
-      if (e >= o) ti += n;
-    }
-    const int total = __shfl(ti, 63, 64);
+    const int ti = wave_incl_scan_i32(nt);
+    const int total = lane63_i32(ti);
     int tp = ti - nt;
     for (int r = 0; r < kp; r += a.plan_bm, ++tp) {
       a.plan[1 + 2 * tp] = e;
