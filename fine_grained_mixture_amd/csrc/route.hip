@@ -539,6 +539,9 @@ __global__ void __launch_bounds__(1024) scan_rank_small_kernel(ScanArgs a, RankA
   const int e = lane_id(), part = threadIdx.x >> 6;
   const bool ve = e < E;
   const bool lead = blockIdx.x == 0;
+  // the launch's last workgroup only sums the probabilities and writes the
+  // aux statistic, off the ranking workgroups' path
+  const bool aux = blockIdx.x == gridDim.x - 1;
   const int g0 = kScanParts * blockIdx.x;
   const int rb = g0 + part;   // the block this wave ranks
   BlockIds B;
@@ -552,7 +555,7 @@ __global__ void __launch_bounds__(1024) scan_rank_small_kernel(ScanArgs a, RankA
   for (int i = 0; i < kScanReg; ++i)
     creg[i] = ve && b0 + i < b1 ? a.blk_counts[(int64_t)(b0 + i) * E + e] : 0;
   float ps = 0.f;
-  if (lead) {
+  if (aux) {
     float preg[kScanReg];
 #pragma unroll
     for (int i = 0; i < kScanReg; ++i)
@@ -566,6 +569,20 @@ __global__ void __launch_bounds__(1024) scan_rank_small_kernel(ScanArgs a, RankA
   s_c[part][e] = cs;
   s_p[part][e] = ps;
   __syncthreads();
+  if (aux) {
+    if (part == 0) {
+      int c = 0;
+      float P = 0.f;
+      if (ve) {
+        for (int q = 0; q < kScanParts; ++q) {
+          c += s_c[q][e];
+          P += s_p[q][e];
+        }
+      }
+      scan_outputs_aux(a, c, P);
+    }
+    return;
+  }
 
   // 2) the bases of this workgroup's blocks, written by the wave holding each
   //    block's part, and the experts' first rows
@@ -579,18 +596,13 @@ __global__ void __launch_bounds__(1024) scan_rank_small_kernel(ScanArgs a, RankA
   }
   if (part == 0) {
     int c = 0;
-    float P = 0.f;
-    if (ve) {
-      for (int q = 0; q < kScanParts; ++q) {
-        c += s_c[q][e];
-        P += s_p[q][e];
-      }
-    }
+    if (ve)
+      for (int q = 0; q < kScanParts; ++q) c += s_c[q][e];
     // 3) workgroup 0 writes the per-expert outputs; every workgroup keeps
     //    the first rows
     int excl;
     if (lead) {
-      excl = scan_outputs(a, c, P);
+      excl = scan_outputs_rows(a, c);
     } else {
       const int kp = ve ? (a.capacity > 0 ? min(c, a.capacity) : c) : 0;
       excl = wave_incl_scan_i32(kp) - kp;
@@ -700,7 +712,8 @@ hipError_t launch_scan_rank(const ScanArgs& a, const RankArgs& r, hipStream_t s)
   if (a.E > 64 || a.nblk > kScanParts * kScanReg || (int64_t)r.tb * r.k > 64 * kMaxChunks ||
       r.nblk != a.nblk)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(scan_rank_small_kernel, dim3((a.nblk + kScanParts - 1) / kScanParts),
+  // the ranking workgroups, then one for the aux statistic
+  hipLaunchKernelGGL(scan_rank_small_kernel, dim3((a.nblk + kScanParts - 1) / kScanParts + 1),
                      dim3(1024), 0, s, a, r);
   return hipGetLastError();
 }

@@ -8,10 +8,9 @@
 namespace moe {
 
 // One wave, lane e = expert e (E <= 64), given expert e's pre-drop slot count
-// c and probability sum P: capacity, counts, kept, offsets, drops, the aux
-// statistic and the tile list of the routed grouped GEMM. Returns expert e's
-// first row.
-__device__ inline int scan_outputs(const ScanArgs& a, int c, float P) {
+// c: capacity, counts, kept, offsets, drops and the tile list of the routed
+// grouped GEMM. Returns expert e's first row.
+__device__ inline int scan_outputs_rows(const ScanArgs& a, int c) {
   const int E = a.E;
   const int e = lane_id();
   const bool ve = e < E;
@@ -30,18 +29,6 @@ __device__ inline int scan_outputs(const ScanArgs& a, int c, float P) {
     a.n_dropped[0] = drop;
   }
 
-  // aux statistic: f_e = counts_e / (T k), P_e = psum_e / T
-  const double fe = ve && a.T > 0 ? (double)c / ((double)a.T * a.k) : 0.0;
-  const double Pe = ve && a.T > 0 ? (double)P / (double)a.T : 0.0;
-  if (ve && a.f) a.f[e] = (float)fe;
-  if (ve && a.P) a.P[e] = (float)Pe;
-  const double prod = lane63_f64(wave_incl_scan_f64(fe * Pe));
-  if (e == 0) {
-    const double raw = (double)E * prod;
-    a.aux[0] = (float)raw;
-    a.aux[1] = (float)(a.aux_coef * raw);
-  }
-
   // tile list of the routed grouped GEMM, (expert, first row) in expert order
   if (a.plan) {
     const int nt = (kp + a.plan_bm - 1) / a.plan_bm;
@@ -55,6 +42,30 @@ __device__ inline int scan_outputs(const ScanArgs& a, int c, float P) {
     if (e == 0) a.plan[0] = total;
   }
   return excl;
+}
+
+// One wave, lane e = expert e: the aux statistic from expert e's pre-drop
+// slot count c and probability sum P: f_e = c / (T k), P_e = P / T.
+__device__ inline void scan_outputs_aux(const ScanArgs& a, int c, float P) {
+  const int E = a.E;
+  const int e = lane_id();
+  const bool ve = e < E;
+  const double fe = ve && a.T > 0 ? (double)c / ((double)a.T * a.k) : 0.0;
+  const double Pe = ve && a.T > 0 ? (double)P / (double)a.T : 0.0;
+  if (ve && a.f) a.f[e] = (float)fe;
+  if (ve && a.P) a.P[e] = (float)Pe;
+  const double prod = lane63_f64(wave_incl_scan_f64(fe * Pe));
+  if (e == 0) {
+    const double raw = (double)E * prod;
+    a.aux[0] = (float)raw;
+    a.aux[1] = (float)(a.aux_coef * raw);
+  }
+}
+
+// Both of the above. Returns expert e's first row.
+__device__ inline int scan_outputs(const ScanArgs& a, int c, float P) {
+  scan_outputs_aux(a, c, P);
+  return scan_outputs_rows(a, c);
 }
 
 constexpr int kMaxChunks = 15;   // tb * k / 64 slots of a block, tb * k <= 960
