@@ -88,7 +88,10 @@ __global__ void __launch_bounds__(256) route_small_kernel(RouteSmallArgs a, int 
   constexpr int EP = 16 * NS;
   constexpr int ws_slice = slice_bytes<NS>();
   __shared__ __attribute__((aligned(16))) unsigned char s_w[kWaves][ws_slice + kWsPad];
-  __shared__ float s_part[kWaves * kTB * (EP + 1)];   // [wave][token][expert] partial logits
+  // [wave][token][expert] partial logits; after a group's logits are summed,
+  // each wave's slice holds its top-k exchange (4 tokens' pairs and picks)
+  __shared__ __attribute__((aligned(16))) float s_part[kWaves * kTB * (EP + 1)];
+  static_assert(4 * (EP + KMAX) * 8 <= kTB * (EP + 1) * 4, "top-k exchange fits a slice");
   __shared__ float s_ps[kWaves][EP];
   __shared__ int s_ct[kWaves][EP];
 
@@ -261,22 +264,60 @@ __global__ void __launch_bounds__(256) route_small_kernel(RouteSmallArgs a, int 
     }
     __syncthreads();   // s_part is free for the next group
 
+    // Top-(k+1). One group per workgroup (the chain of one group is the
+    // launch's latency): each (key, id) pair's place among the token's
+    // pairs, all counted at once. The row's pairs go through this wave's own
+    // slice of s_part (no other wave touches it until this wave's next
+    // partials); LDS operations of one wave run in order. Unused slots hold 0,
+    // below every pair. Several groups (throughput): k + 1 rounds of a
+    // row-wide maximum, the winner removed after each; fewer instructions.
+    // Either way sel[r] is the r-th largest pair for r < rounds, else 0.
     const int rounds = min(k + 1, E);
     uint64_t sel[KMAX];
+    if (groups == 1) {
+      uint64_t pk[NS];
 #pragma unroll
-    for (int r = 0; r < KMAX; ++r) sel[r] = 0;
+      for (int j = 0; j < NS; ++j) pk[j] = eid[j] < E ? pack_key_id(key[j], eid[j]) : 0;
+      uint64_t* s_pk = reinterpret_cast<uint64_t*>(s_part + wave * kTB * (EP + 1)) + g * EP;
+      uint64_t* s_sel = reinterpret_cast<uint64_t*>(s_part + wave * kTB * (EP + 1)) + 4 * EP +
+                        g * KMAX;
 #pragma unroll
-    for (int r = 0; r < KMAX; ++r) {
-      if (r >= rounds) break;
-      uint64_t best = 0;
+      for (int j = 0; j < NS; ++j) s_pk[16 * j + l16] = pk[j];
+      __builtin_amdgcn_wave_barrier();
+      int place[NS];
 #pragma unroll
-      for (int j = 0; j < NS; ++j) best = max_u64(best, pack_key_id(key[j], eid[j]));
-      best = row_max_u64(best);
-      sel[r] = best;
-      const int id = packed_id(best);
+      for (int j = 0; j < NS; ++j) place[j] = 0;
+#pragma unroll
+      for (int q = 0; q < EP; q += 2) {
+        const uint64_t v0 = s_pk[q], v1 = s_pk[q + 1];
+#pragma unroll
+        for (int j = 0; j < NS; ++j) place[j] += (v0 > pk[j]) + (v1 > pk[j]);
+      }
+#pragma unroll
+      for (int r = 0; r < KMAX; ++r) s_sel[r] = 0;
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int j = 0; j < NS; ++j)
-        if (eid[j] == id) key[j] = -INFINITY;
+        if (eid[j] < E && place[j] < rounds) s_sel[place[j]] = pk[j];
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int r = 0; r < KMAX; ++r) sel[r] = s_sel[r];
+    } else {
+#pragma unroll
+      for (int r = 0; r < KMAX; ++r) sel[r] = 0;
+#pragma unroll
+      for (int r = 0; r < KMAX; ++r) {
+        if (r >= rounds) break;
+        uint64_t best = 0;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) best = max_u64(best, pack_key_id(key[j], eid[j]));
+        best = row_max_u64(best);
+        sel[r] = best;
+        const int id = packed_id(best);
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+          if (eid[j] == id) key[j] = -INFINITY;
+      }
     }
 
     float gate[KMAX], prob[NS];
