@@ -64,6 +64,7 @@ CASES = {
     "dormouse_lowrank": synth.DORMOUSE.replace(T=300, hidden=256, ffn=128),
     "quartz_fp8": synth.QUARTZ.replace(T=333, hidden=256, ffn=128, dtype="fp8"),
     "quartz_decode": synth.QUARTZ.replace(T=3),
+    "quartz_small_batch": synth.QUARTZ.replace(T=50),
     "tiny_f32": synth.TINY.replace(T=77),
 }
 

@@ -145,6 +145,9 @@ DECODE = {
     "quartz_t33": synth.QUARTZ.replace(T=33, seed=14),
     "quartz_t17": synth.QUARTZ.replace(T=17, seed=6),
     "quartz_t64": synth.QUARTZ.replace(T=64, seed=7),
+    # tens of rows per expert, softmax and sigmoid
+    "quartz_t256": synth.QUARTZ.replace(T=256, seed=15),
+    "sutra_t200": synth.SUTRA.replace(T=200, seed=16),
     "sutra_t3": synth.SUTRA.replace(T=3, seed=8),
     "sutra_t9": synth.SUTRA.replace(T=9, seed=8),
     "moonfrost_t40_capacity": synth.MOONFROST.replace(T=40, seed=9),
