@@ -527,8 +527,9 @@ __global__ void __launch_bounds__(256) rank_one_chunk_kernel(RankArgs a) {
 // 16 waves summing one part of the blocks each as scan_small_kernel does
 // (nblk * E * 4 bytes read from L2 per workgroup, less than the cost of a
 // second launch and its wait); workgroup 0 also writes the per-expert
-// outputs, the aux statistic and the tile list; then wave w of workgroup g
-// ranks block 16 g + w from the bases and offsets kept in LDS.
+// outputs and the tile list; then wave w of workgroup g ranks block 16 g + w
+// from the bases and offsets kept in LDS. One more workgroup, the launch's
+// last, sums the routing probabilities and writes the aux statistic.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(1024) scan_rank_small_kernel(ScanArgs a, RankArgs r) {
   __shared__ int s_c[kScanParts][64];

@@ -16,10 +16,11 @@
 //   2. The four partial sums meet in LDS and are added in wave order, plus
 //      logit_bias. Wave w then scores tokens 4w .. 4w+3, one per 16-lane DPP
 //      row, lane l holding experts 16 j + l%16.
-//   3. Top-(k+1) by k+1 rounds of a row-wide maximum of (key, id) packed so
-//      that equal keys resolve to the lower expert id, the winner's entry
-//      removed after each round; gates and routing probabilities with sums
-//      over the row in a fixed order.
+//   3. Top-(k+1) of the (key, id) pairs, packed so that equal keys resolve to
+//      the lower expert id: with one group per workgroup, each pair's place
+//      among the token's pairs, counted at once; with several, k+1 rounds of
+//      a row-wide maximum, the winner's entry removed after each round. Gates
+//      and routing probabilities with sums over the row in a fixed order.
 //   4. The workgroup's per-expert slot counts and probability sums, summed
 //      over its rows and waves in a fixed order.
 #include <float.h>
