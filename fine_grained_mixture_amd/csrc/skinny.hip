@@ -25,7 +25,6 @@ namespace {
 constexpr int kCols = 64;      // output columns per workgroup (whole 128-byte lines)
 constexpr int kCG = kCols / 8; // column groups of 8 columns
 constexpr int kRows = 4;       // rows per pass
-constexpr int kKG = 256 / kCG; // K groups
 
 __device__ __forceinline__ void unpack8(const u32x4 v, float* f) {
 #pragma unroll
@@ -35,9 +34,13 @@ __device__ __forceinline__ void unpack8(const u32x4 v, float* f) {
   }
 }
 
-template <int EPI, bool DUAL>
-__global__ void __launch_bounds__(256) skinny_kernel(GemmLaunch L, int nch0, int nch1) {
+// THREADS / 8 K groups (256 threads: 32; 512: 64, for one or two rows per
+// group, where the loads in flight per workgroup are what bounds the kernel:
+// the down projection at Quartz T = 1 takes 9.8 against 12.0 us)
+template <int EPI, bool DUAL, int THREADS>
+__global__ void __launch_bounds__(THREADS) skinny_kernel(GemmLaunch L, int nch0, int nch1) {
   constexpr int NB = DUAL ? 2 : 1;
+  constexpr int kKG = THREADS / kCG;   // K groups
   __shared__ float s_part[NB][kKG][kRows][kCols];
 
   int bid = blockIdx.x, prob = 0;
@@ -131,7 +134,8 @@ __global__ void __launch_bounds__(256) skinny_kernel(GemmLaunch L, int nch0, int
               floatx4{acc[b][r][c], acc[b][r][c + 1], acc[b][r][c + 2], acc[b][r][c + 3]};
     __syncthreads();
 
-    // thread -> (row, column); K groups added in order
+    // thread -> (row, column); K groups added in order (threads past the
+    // kRows rows idle)
     const int col = tid % kCols, r = tid / kCols;
     if (r < nr) {
       float v0 = 0.f, v1 = 0.f;
@@ -159,7 +163,7 @@ __global__ void __launch_bounds__(256) skinny_kernel(GemmLaunch L, int nch0, int
 
 }  // namespace
 
-hipError_t launch_gemm_skinny(const GemmLaunch& L, int epilogue, hipStream_t s) {
+hipError_t launch_gemm_skinny(const GemmLaunch& L, int epilogue, hipStream_t s, bool wide) {
   int nch[2] = {0, 0}, blocks = 0;
   for (int i = 0; i < L.n_problems; ++i) {
     const GemmProblem& P = L.p[i];
@@ -168,12 +172,17 @@ hipError_t launch_gemm_skinny(const GemmLaunch& L, int epilogue, hipStream_t s) 
     blocks += P.G * nch[i];
   }
   if (blocks == 0) return hipSuccess;
+  // 64 K groups pay off where K holds more than one 8-row chunk per group
+  for (int i = 0; i < L.n_problems; ++i) wide = wide && L.p[i].K > 8 * 64;
   if (epilogue == kEpiSwiGLU)
-    hipLaunchKernelGGL((skinny_kernel<kEpiSwiGLU, true>), dim3(blocks), dim3(256), 0, s, L, nch[0],
-                       nch[1]);
-  else
-    hipLaunchKernelGGL((skinny_kernel<kEpiStoreF32, false>), dim3(blocks), dim3(256), 0, s, L,
+    hipLaunchKernelGGL((skinny_kernel<kEpiSwiGLU, true, 256>), dim3(blocks), dim3(256), 0, s, L,
                        nch[0], nch[1]);
+  else if (wide)
+    hipLaunchKernelGGL((skinny_kernel<kEpiStoreF32, false, 512>), dim3(blocks), dim3(512), 0, s,
+                       L, nch[0], nch[1]);
+  else
+    hipLaunchKernelGGL((skinny_kernel<kEpiStoreF32, false, 256>), dim3(blocks), dim3(256), 0, s,
+                       L, nch[0], nch[1]);
   return hipGetLastError();
 }
 
