@@ -584,7 +584,7 @@ void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool 
   const bool skinny = bf && T <= kSkinnyMaxT;
   auto launch = [&](const GemmLaunch& G, int epi, const char* name) {
     R.run(name, [&] {
-      if (skinny) return launch_gemm_skinny(G, epi, R.stream, T <= 2);
+      if (skinny) return launch_gemm_skinny(G, epi, R.stream, T <= 2, (int)T);
       return bf ? launch_gemm_big(G, epi, R.stream) : launch_gemm_f32(G, epi, R.stream);
     });
   };

@@ -97,9 +97,11 @@ hipError_t launch_quant_cols(const uint16_t* w, int64_t G, int32_t K, int32_t N,
 // Tile list of a row_off problem from offsets[0..G] (one workgroup).
 // Few rows per group (bf16): one workgroup per (group, 64 columns), weights
 // streamed once per pass of 4 rows; row_off groups or uniform groups of M rows.
-// wide: the fp32-store epilogue with 512 threads (64 K groups), for one or
-// two rows per group; taken where every problem's K exceeds 512.
-hipError_t launch_gemm_skinny(const GemmLaunch& L, int epilogue, hipStream_t s, bool wide = false);
+// wide: 512 threads (64 K groups), for one or two rows per group, taken
+// where every problem's K exceeds 512: the fp32-store epilogue, and the fused
+// SwiGLU with passes of `rows` rows (1 or 2, the most a group holds).
+hipError_t launch_gemm_skinny(const GemmLaunch& L, int epilogue, hipStream_t s, bool wide = false,
+                              int rows = kSkinnyMaxT);
 hipError_t launch_plan(const int32_t* offsets, int32_t G, int32_t bm, int32_t* plan,
                        hipStream_t s);
 

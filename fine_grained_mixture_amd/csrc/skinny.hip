@@ -24,7 +24,7 @@ namespace {
 
 constexpr int kCols = 64;      // output columns per workgroup (whole 128-byte lines)
 constexpr int kCG = kCols / 8; // column groups of 8 columns
-constexpr int kRows = 4;       // rows per pass
+constexpr int kRows = 4;       // rows per pass (ROWS = 1 for single-row groups)
 
 __device__ __forceinline__ void unpack8(const u32x4 v, float* f) {
 #pragma unroll
@@ -36,11 +36,13 @@ __device__ __forceinline__ void unpack8(const u32x4 v, float* f) {
 
 // THREADS / 8 K groups (256 threads: 32; 512: 64, for one or two rows per
 // group, where the loads in flight per workgroup are what bounds the kernel:
-// the down projection at Quartz T = 1 takes 9.8 against 12.0 us)
-template <int EPI, bool DUAL, int THREADS>
+// the down projection at Quartz T = 1 takes 9.8 against 12.0 us). ROWS rows
+// per pass: 1 or 2 keep the fused gate/up's registers within 512 threads.
+template <int EPI, bool DUAL, int THREADS, int ROWS>
 __global__ void __launch_bounds__(THREADS) skinny_kernel(GemmLaunch L, int nch0, int nch1) {
   constexpr int NB = DUAL ? 2 : 1;
   constexpr int kKG = THREADS / kCG;   // K groups
+  constexpr int kRows = ROWS;
   __shared__ float s_part[NB][kKG][kRows][kCols];
 
   int bid = blockIdx.x, prob = 0;
@@ -163,7 +165,8 @@ __global__ void __launch_bounds__(THREADS) skinny_kernel(GemmLaunch L, int nch0,
 
 }  // namespace
 
-hipError_t launch_gemm_skinny(const GemmLaunch& L, int epilogue, hipStream_t s, bool wide) {
+hipError_t launch_gemm_skinny(const GemmLaunch& L, int epilogue, hipStream_t s, bool wide,
+                              int rows) {
   int nch[2] = {0, 0}, blocks = 0;
   for (int i = 0; i < L.n_problems; ++i) {
     const GemmProblem& P = L.p[i];
@@ -174,15 +177,21 @@ hipError_t launch_gemm_skinny(const GemmLaunch& L, int epilogue, hipStream_t s, 
   if (blocks == 0) return hipSuccess;
   // 64 K groups pay off where K holds more than one 8-row chunk per group
   for (int i = 0; i < L.n_problems; ++i) wide = wide && L.p[i].K > 8 * 64;
-  if (epilogue == kEpiSwiGLU)
-    hipLaunchKernelGGL((skinny_kernel<kEpiSwiGLU, true, 256>), dim3(blocks), dim3(256), 0, s, L,
-                       nch[0], nch[1]);
+  if (epilogue == kEpiSwiGLU && wide && rows <= 1)
+    hipLaunchKernelGGL((skinny_kernel<kEpiSwiGLU, true, 512, 1>), dim3(blocks), dim3(512), 0, s,
+                       L, nch[0], nch[1]);
+  else if (epilogue == kEpiSwiGLU && wide && rows == 2)
+    hipLaunchKernelGGL((skinny_kernel<kEpiSwiGLU, true, 512, 2>), dim3(blocks), dim3(512), 0, s,
+                       L, nch[0], nch[1]);
+  else if (epilogue == kEpiSwiGLU)
+    hipLaunchKernelGGL((skinny_kernel<kEpiSwiGLU, true, 256, kRows>), dim3(blocks), dim3(256), 0,
+                       s, L, nch[0], nch[1]);
   else if (wide)
-    hipLaunchKernelGGL((skinny_kernel<kEpiStoreF32, false, 512>), dim3(blocks), dim3(512), 0, s,
-                       L, nch[0], nch[1]);
+    hipLaunchKernelGGL((skinny_kernel<kEpiStoreF32, false, 512, kRows>), dim3(blocks), dim3(512),
+                       0, s, L, nch[0], nch[1]);
   else
-    hipLaunchKernelGGL((skinny_kernel<kEpiStoreF32, false, 256>), dim3(blocks), dim3(256), 0, s,
-                       L, nch[0], nch[1]);
+    hipLaunchKernelGGL((skinny_kernel<kEpiStoreF32, false, 256, kRows>), dim3(blocks), dim3(256),
+                       0, s, L, nch[0], nch[1]);
   return hipGetLastError();
 }
 
