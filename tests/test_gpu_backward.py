@@ -112,6 +112,10 @@ CASES = {
     "odd_widths": synth.Workload("ow", T=257, hidden=192, n_routed=16, top_k=3, n_shared=3,
                                  ffn=192, logit_offset_std=0.3, seed=11),
     "three_tokens": synth.QUARTZ.replace(T=3, hidden=256, ffn=128, seed=12),
+    # Quartz widths at T = 1 and 2: the forward keeps its products from the
+    # 512-thread decode kernels
+    "quartz_widths_t1": synth.QUARTZ.replace(T=1, seed=21),
+    "quartz_widths_t2": synth.QUARTZ.replace(T=2, seed=22),
     # float32 layers (the fp32 FMA products, a | b recomputed): the Tiny layer
     # and wider ones with capacity drops, sigmoid gates, no or three shared
     # experts, top-1, and more rows than one tile per expert
@@ -139,7 +143,7 @@ def test_backward_parity(name):
 
 # the forward keeps its gate and up products; the backward then runs dh alone
 SAVED = ["quartz_small", "moonfrost_small_capacity", "sutra_small_sigmoid", "quartz_no_shared",
-         "one_token", "wide_ffn_k1"]
+         "one_token", "wide_ffn_k1", "quartz_widths_t1", "quartz_widths_t2"]
 
 
 @pytest.mark.parametrize("name", SAVED)
@@ -151,7 +155,8 @@ def test_saving_products_leaves_forward_unchanged():
     """y and the routing are bitwise the same with saved_ab; the saved gate and
     up products match the oracle's x W_gate and x W_up on sampled rows."""
     for wl in (synth.QUARTZ.replace(T=300, hidden=256, ffn=128, seed=12),
-               synth.QUARTZ.replace(T=3, hidden=256, ffn=128, seed=13)):
+               synth.QUARTZ.replace(T=3, hidden=256, ffn=128, seed=13),
+               synth.QUARTZ.replace(T=2, seed=14)):
         inp = synth.make_inputs(wl)
         cfg, x, w = P.upload(wl, inp)
         outs = []

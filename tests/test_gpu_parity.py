@@ -134,11 +134,15 @@ def test_exact_ties_take_lower_ids(name):
 
 
 # decode-sized batches (T <= 4 take the weight-streaming skinny expert kernel,
-# T = 1 with only k + S experts busy; the larger ones check the tile kernel at
-# few rows per expert)
+# T = 1 with only k + S experts busy, T <= 2 with 512 threads where K > 512;
+# the larger ones check the tile kernel at few rows per expert)
 DECODE = {
     "quartz_t1": synth.QUARTZ.replace(T=1, seed=4),
     "quartz_t2": synth.QUARTZ.replace(T=2, seed=5),
+    "sutra_t1": synth.SUTRA.replace(T=1, seed=17),
+    "sutra_t2": synth.SUTRA.replace(T=2, seed=18),
+    # K = 512 for the down product: its 256-thread kernel beside the 512-thread gate/up
+    "moonfrost_t2": synth.MOONFROST.replace(T=2, seed=19),
     "quartz_t4": synth.QUARTZ.replace(T=4, seed=10),
     # the first batch past the skinny kernel, and the first with two routing blocks
     "quartz_t5": synth.QUARTZ.replace(T=5, seed=13),
