@@ -3,15 +3,15 @@
 // reading the weights once, so the layout serves bandwidth rather than MFMA:
 //
 //   one workgroup per (group, 64-column chunk), so each weight row is read
-//   as whole 128-byte lines; its 256 threads split the chunk into 8 column
+//   as whole 128-byte lines; its threads split the chunk into 8 column
 //   groups of 8 consecutive columns (one 16-byte load per weight row) and the
-//   K dimension into 32 interleaved groups of 8-row chunks, taken two chunks
-//   at a time so that every load of both is in flight before the first FMA;
-//   the weight slice B[K, 64] (and B1's for the fused SwiGLU) streams through
-//   once per pass of up to kRows rows; each thread keeps kRows x 8 partial
-//   sums (x2 for gate and up) in registers, and the 32 K-group partials are
-//   added through LDS in K-group order, so the result does not depend on
-//   scheduling.
+//   K dimension into interleaved groups of 8-row chunks (32 groups with 256
+//   threads, 64 with 512), taken two chunks at a time so that every load of
+//   both is in flight before the first FMA; the weight slice B[K, 64] (and
+//   B1's for the fused SwiGLU) streams through once per pass of up to ROWS
+//   rows; each thread keeps ROWS x 8 partial sums (x2 for gate and up) in
+//   registers, and the K-group partials are added through LDS in K-group
+//   order, so the result does not depend on scheduling.
 //
 // Epilogues as in the large-tile kernel: fp32 rows (+ column bias), or
 // bf16 h = SiLU(gate) * up.
