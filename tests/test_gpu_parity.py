@@ -257,6 +257,40 @@ def test_stage_entry_points_match_layer(base):
     np.testing.assert_array_equal(whole["y_lowp"], yl)
 
 
+
+# one case per shape of the stand-alone gather: 16-byte pieces per row 96 (bf16
+# d = 768), 192 (1536), 512 (fp32 2048) and 1024 (bf16 8192, two passes per
+# row), and a capacity that drops slots
+GATHER = {
+    "d768": synth.QUARTZ.replace(T=400, hidden=768, ffn=64, seed=21),
+    "d1536_sigmoid": synth.SUTRA.replace(T=333, ffn=64, seed=22),
+    "f32_d2048": synth.TINY.replace(T=257, hidden=2048, dtype="f32", seed=23),
+    "d8192": synth.QUARTZ.replace(T=129, hidden=8192, ffn=64, seed=24),
+    "capacity_drops": synth.MOONFROST.replace(T=600, ffn=64, seed=25),
+}
+
+
+@pytest.mark.parametrize("base", list(GATHER))
+def test_permute_gathers_token_rows(base):
+    """moe_permute's x_perm holds x[sorted_token[row]] for every kept row, bit
+    for bit, and leaves the rows past offsets[E] as they were."""
+    wl = GATHER[base]
+    inp = synth.make_inputs(wl)
+    cfg, x, w = P.upload(wl, inp)
+    T = wl.T
+    out = L.allocate_outputs(cfg, T, x.device)
+    ws = L.allocate_workspace(cfg, T, x.device)
+    R = max(1, int(L._lib.moe_max_rows(cfg, T)))
+    x_perm = torch.full((R + 3, wl.hidden), 7.0, dtype=x.dtype, device=x.device)
+    L.route(cfg, x, w, out, ws)
+    L.permute(cfg, x, out, ws, x_perm)
+    torch.cuda.synchronize()
+    rows = int(out["offsets"][-1].item())
+    assert 0 < rows <= R
+    st = out["sorted_token"][:rows].long()
+    assert torch.equal(x_perm[:rows], x[st])
+    assert bool((x_perm[rows:] == 7).all())
+
 def test_bias_update_matches_oracle():
     """moe_bias_update against the oracle, bit for bit: counts from a real
     routing call on the GPU (Sutra-shaped skew), then hand-made patterns with
