@@ -721,6 +721,11 @@ void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool 
       p.G = c->n_routed;
       p.n_tiles_n = (int32_t)ceil_div(d, bn);
       p.max_m_tiles = (int32_t)L.max_tiles;
+      // the routed rows (k fp32 rows per token, read once by the combine)
+      // bypass the L2 with streaming stores: at the Quartz shape the down
+      // product drops from 77 to 63-65 us while the combine, now reading
+      // them from HBM, gains 4.5 us (Sutra -2% per call, Moonfrost +1%)
+      p.c_stream = bf ? 1 : 0;
     }
     G.n_problems = np;
     G.tiles0 = G.p[0].max_m_tiles * G.p[0].n_tiles_n;

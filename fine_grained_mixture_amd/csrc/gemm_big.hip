@@ -44,6 +44,11 @@ constexpr int kAStage = kBM * kBK;     // elements
 constexpr int kBStage = kBK * kBNT;
 constexpr int kStageBytes = (kAStage + kBStage) * 2;   // 24 KiB
 
+// raw buffer descriptor word 3 (32-bit data format) and the cache-policy bit of
+// a non-temporal (streaming) store
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kCpolNT = 2;
+
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
@@ -283,6 +288,9 @@ gemm_big_kernel(GemmLaunch L) {
   if (EPI == kEpiStoreF32) {
     float* C = static_cast<float*>(P.C);
     float* st = reinterpret_cast<float*>(stage);
+    // the tile's rows of C as a raw buffer (stores past its range are dropped)
+    const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+        C + (int64_t)tile.r0 * P.ldc + ccol0, 0, 0x7fffffff, kBufferRsrcWord3);
     const int col0 = tile.n0 + 64 * wn;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -302,8 +310,14 @@ gemm_big_kernel(GemmLaunch L) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] += col + e < N ? P.col_bias[col + e] : 0.f;
         }
-        if (row < tile.r_end && col < N)
-          *reinterpret_cast<floatx4*>(C + (int64_t)row * P.ldc + ccol0 + col) = v;
+        if (row < tile.r_end && col < N) {
+          // byte offset from the tile's first row: below 2^31 while 256 ldc < 2^29
+          const int off = (int)(((int64_t)(row - tile.r0) * P.ldc + col) * 4);
+          if (P.c_stream)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), crs, off, 0, kCpolNT);
+          else
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), crs, off, 0, 0);
+        }
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -366,6 +380,9 @@ int grid_of(const GemmLaunch& L) {
 hipError_t launch_gemm_big(const GemmLaunch& L, int epilogue, hipStream_t s) {
   const int grid = grid_of(L);
   if (grid <= 0) return hipSuccess;
+  // the fp32 epilogue addresses a tile's rows of C with 32-bit byte offsets
+  for (int i = 0; i < L.n_problems; ++i)
+    if (epilogue == kEpiStoreF32 && L.p[i].ldc >= ((int64_t)1 << 21)) return hipErrorInvalidValue;
   if (epilogue == kEpiSwiGLU)
     hipLaunchKernelGGL((gemm_big_kernel<kEpiSwiGLU, true>), dim3(grid), dim3(kThreads), 0, s, L);
   else

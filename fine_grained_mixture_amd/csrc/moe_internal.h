@@ -57,6 +57,8 @@ struct GemmProblem {
   int32_t M, N, K, G;
   int32_t n_tiles_n;         // N-tiles per M-tile
   int32_t max_m_tiles;       // upper bound of M-tiles (grid sizing)
+  int32_t c_stream;          // fp32 epilogue of the bf16 tile kernel: store C with
+                             // non-temporal (streaming) stores
 };
 
 enum GemmEpilogue : int {
