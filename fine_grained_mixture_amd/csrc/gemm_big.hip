@@ -325,7 +325,9 @@ gemm_big_kernel(GemmLaunch L) {
     if (P.ab) {
       // the gate and up sums themselves, for the backward: each of the two is
       // staged as the wave's 128 rows x 32 columns (row pitch 36 floats), then
-      // written as 16-byte pieces, 8 per row
+      // written as 16-byte pieces, 8 per row, with streaming stores: nothing
+      // reads them before the backward (Quartz forward keeping them 0.285 ->
+      // 0.25-0.26 ms, forward + backward about 1% faster)
       float* sf = reinterpret_cast<float*>(stage);
       float* abp = P.ab + tile.g * P.ab_group_col + tile.n0 + 32 * wn + 4 * (lane & 7);
 #pragma unroll
@@ -342,7 +344,7 @@ gemm_big_kernel(GemmLaunch L) {
           const int row = row_base + r;
           const floatx4 v = *reinterpret_cast<const floatx4*>(&sf[r * 36 + 4 * (lane & 7)]);
           if (row < tile.r_end)
-            *reinterpret_cast<floatx4*>(abp + (int64_t)row * P.ab_ld + half * N) = v;
+            __builtin_nontemporal_store(v, reinterpret_cast<floatx4*>(abp + (int64_t)row * P.ab_ld + half * N));
         }
         __builtin_amdgcn_wave_barrier();
       }
