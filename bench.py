@@ -526,7 +526,21 @@ def run_metadata(wl):
                              text=True, timeout=10).stdout.strip() or None
     except (OSError, subprocess.SubprocessError):
         sha = None
-    return {"source_sha256": h.hexdigest(), "git_sha": sha,
+    sha_from = "git" if sha else None
+    if not sha:
+        # a copy of the tree without its history: the commit recorded when the
+        # library was built, if its sources are the ones here
+        from fine_grained_mixture_amd import build as _build
+        try:
+            with open(_build.INFO) as f:
+                info = json.load(f)
+            if info.get("source_sha256") == _build.source_digest() and info.get("git_sha"):
+                sha = info["git_sha"]
+                sha_from = ("build (sources modified since that commit)"
+                            if info.get("sources_modified_since_commit") else "build")
+        except (OSError, ValueError):
+            pass
+    return {"source_sha256": h.hexdigest(), "git_sha": sha, "git_sha_from": sha_from,
             "input_seed": wl.seed, "upstream_seed": wl.seed + 1000,
             "date_utc": time.strftime("%Y-%m-%dT%H:%M:%SZ", time.gmtime())}
 

@@ -48,6 +48,42 @@ def _compile(src: str) -> str:
     return obj
 
 
+INFO = os.path.join(PKG, "build_info.json")
+
+
+def source_digest() -> str:
+    """sha256 over the library's sources (csrc and include), file names included."""
+    import hashlib
+    h = hashlib.sha256()
+    for dname in (CSRC, os.path.join(ROOT, "include")):
+        for name in sorted(os.listdir(dname)):
+            if name.endswith((".hip", ".cpp", ".h")):
+                h.update(name.encode())
+                with open(os.path.join(dname, name), "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()
+
+
+def _write_info() -> None:
+    """Record the commit the library was built from, so that a copy of the
+    tree without its git history can still name it."""
+    import json
+    import time
+    try:
+        sha = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                             text=True, timeout=10).stdout.strip() or None
+        dirty = bool(subprocess.run(["git", "-C", ROOT, "status", "--porcelain", "--",
+                                     "fine_grained_mixture_amd/csrc", "include"],
+                                    capture_output=True, text=True, timeout=10).stdout.strip())
+    except (OSError, subprocess.SubprocessError):
+        sha, dirty = None, None
+    info = {"git_sha": sha, "sources_modified_since_commit": dirty,
+            "source_sha256": source_digest(),
+            "built_utc": time.strftime("%Y-%m-%dT%H:%M:%SZ", time.gmtime())}
+    with open(INFO, "w") as f:
+        json.dump(info, f)
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link the shared library. Returns its path."""
     os.makedirs(BUILD, exist_ok=True)
@@ -60,6 +96,7 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    _write_info()
     if verbose:
         print(f"built {LIB}")
     return LIB
