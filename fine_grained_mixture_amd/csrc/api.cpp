@@ -52,6 +52,9 @@ bool supported_config(const moe_config* c) {
   // the products' tiles: d and F whole 64-column chunks; the top-k keeps at
   // most 15 selections per token in registers
   if (c->hidden % 64 || c->ffn % 64 || c->top_k > 15) return false;
+  // the bf16 tile kernel's fp32 epilogue addresses a tile's 256 output rows
+  // of pitch d with 32-bit byte offsets
+  if (c->dtype != MOE_F32 && c->hidden >= (1 << 21)) return false;
   // low-rank experts: bf16 with rank 16, 32, 48 or 64; fp8 factors with rank 64
   if (c->rank != 0 && (c->rank > 64 || c->rank % 16 || c->dtype == MOE_F32 ||
                        (c->dtype == MOE_FP8 && c->rank != 64)))

@@ -98,7 +98,7 @@ def test_invalid_config_rejected(lib, bad):
 
 @pytest.mark.parametrize("legal", [
     dict(hidden=104), dict(ffn=48), dict(hidden=136, ffn=200), dict(top_k=16, n_routed=32),
-    dict(top_k=32, n_routed=32),
+    dict(top_k=32, n_routed=32), dict(hidden=1 << 21),
 ])
 def test_legal_but_unimplemented_layer_is_unsupported(lib, legal):
     """Layers the layer's definition allows (d, F multiples of 8; k <= E) but
