@@ -38,7 +38,8 @@
  *     multiples of 8; 0 <= S <= 64; T*k < 2^31; sigmoid scoring requires
  *     renorm_topk == 1.
  *   - Legal layers outside this library's kernels return MOE_EUNSUPPORTED:
- *     k > 15; d or F not a multiple of 64; rank other than 0, 16, 32, 48 or 64
+ *     k > 15; d or F not a multiple of 64; d >= 2^21 with bf16 or fp8
+ *     activations; rank other than 0, 16, 32, 48 or 64
  *     with bf16, or 64 with fp8 (low-rank float32 experts are unsupported);
  *     MOE_FP8 with d, F or S*F above 4096. MOE_FP8 runs in moe_layer_forward
  *     and moe_grouped_ffn.
