@@ -724,19 +724,14 @@ void run_ffn(Runner& R, const moe_config* c, const Layout& L, bool routed, bool 
       p.G = c->n_routed;
       p.n_tiles_n = (int32_t)ceil_div(d, bn);
       p.max_m_tiles = (int32_t)L.max_tiles;
-      // the routed rows (k fp32 rows per token, read once by the combine)
-      // bypass the L2 with streaming stores: at the Quartz shape the down
-      // product drops from 77 to 63-65 us while the combine, now reading
-      // them from HBM, gains 4.5 us (Sutra -2% per call; Moonfrost +1% with
-      // the shared tiles first)
-      p.c_stream = bf ? 1 : 0;
+      // the routed rows (k fp32 rows per token, read once by the combine) go
+      // out as streaming stores when they cannot stay in the 256 MiB Infinity
+      // Cache anyway (Sutra: 805 MB, -2% per call with warm or cold weights).
+      // Rows that fit are stored normally, for the combine to find there:
+      // streaming them made the Quartz layer 4% faster while its weights sat
+      // in that cache, but 3-7% slower once they had been evicted.
+      p.c_stream = bf && L.R * d * 4 > kInfinityCacheBytes ? 1 : 0;
     }
-    // longest tiles first: the shared experts' tiles lead when their K = S F
-    // exceeds the routed F (Quartz, S = 2; routed first there: down 66 -> 85
-    // us). With equal K the routed tiles lead, so that their streamed rows
-    // drain to memory while the shared tiles compute (Moonfrost, S = 1: down
-    // 105 -> 99 us, step -3%; Sutra unchanged)
-    if (np == 2 && S == 1) std::swap(G.p[0], G.p[1]);
     G.n_problems = np;
     G.tiles0 = G.p[0].max_m_tiles * G.p[0].n_tiles_n;
     launch(G, kEpiStoreF32, both || routed ? "down_gemm" : "shared_down_gemm");

@@ -20,6 +20,8 @@ constexpr int kRouteSmallMaxE = 64;
 constexpr int kGemmBM = 128;
 // Rows per tile of the large-tile expert GEMM (256 x 128 output tiles).
 constexpr int kGemmBigBM = 256;
+// MI355X's Infinity Cache (the memory-side cache in front of HBM), bytes
+constexpr int64_t kInfinityCacheBytes = (int64_t)256 << 20;
 constexpr int kGemmBM_F32 = 64;
 // Rows per workgroup of the fused low-rank expert kernel.
 constexpr int kLowRankBM = 64;
