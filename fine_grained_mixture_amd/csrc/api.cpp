@@ -557,6 +557,9 @@ void run_ffn_fp8(Runner& R, const moe_config* c, const Layout& L, bool routed, b
       p.G = (int32_t)E;
       p.n_tiles_n = (int32_t)ceil_div(d, 128);
       p.max_m_tiles = (int32_t)L.max_tiles;
+      // streaming stores for routed rows that cannot stay in the Infinity
+      // Cache, as in the bf16 down product
+      p.c_stream = L.R * d * 4 > kInfinityCacheBytes ? 1 : 0;
     }
     G.n_problems = np;
     G.tiles0 = G.p[0].max_m_tiles * G.p[0].n_tiles_n;

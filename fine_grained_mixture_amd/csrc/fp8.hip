@@ -254,6 +254,10 @@ gemm_fp8_kernel(GemmLaunch L) {
   if (EPI == kEpiStoreF32) {
     float* C = static_cast<float*>(P.C);
     float* st = reinterpret_cast<float*>(stage);
+    // the tile's rows of C as a raw buffer; the cache policy of its stores is
+    // an immediate, so each policy is a store of its own
+    const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+        C + (int64_t)tile.r0 * P.ldc + ccol0, 0, 0x7fffffff, kBufferRsrcWord3);
     const int col = tile.n0 + 64 * wn + 4 * (lane & 15);
     floatx4 cs = {0.f, 0.f, 0.f, 0.f};
     if (col < N) cs = *reinterpret_cast<const floatx4*>(P.b_scale0 + tile.g * P.b_scale_group + col);
@@ -273,8 +277,14 @@ gemm_fp8_kernel(GemmLaunch L) {
         floatx4 v = *reinterpret_cast<const floatx4*>(&st[r * 72 + 4 * (lane & 15)]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = v[e] * rs * cs[e];
-        if (row < tile.r_end && col < N)
-          *reinterpret_cast<floatx4*>(C + (int64_t)row * P.ldc + ccol0 + col) = v;
+        if (row < tile.r_end && col < N) {
+          // byte offset from the tile's first row: below 2^31 while 256 ldc < 2^29
+          const int off = (int)(((int64_t)(row - tile.r0) * P.ldc + col) * 4);
+          if (P.c_stream)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), crs, off, 0, kCpolNT);
+          else
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), crs, off, 0, 0);
+        }
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -405,6 +415,8 @@ int grid_of(const GemmLaunch& L) {
 hipError_t launch_gemm_fp8(const GemmLaunch& L, int epilogue, hipStream_t s) {
   for (int i = 0; i < L.n_problems; ++i) {
     const GemmProblem& P = L.p[i];
+    // the fp32 epilogue addresses a tile's rows of C with 32-bit byte offsets
+    if (epilogue == kEpiStoreF32 && P.ldc >= ((int64_t)1 << 21)) return hipErrorInvalidValue;
     if (P.K % kBK || P.N % 64 || P.lda % 16 || P.ldb % 16 || !P.a_scale || !P.b_scale0)
       return hipErrorInvalidValue;
     if (epilogue == kEpiSwiGLU && !P.b_scale1) return hipErrorInvalidValue;

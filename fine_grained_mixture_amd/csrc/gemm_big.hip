@@ -44,11 +44,6 @@ constexpr int kAStage = kBM * kBK;     // elements
 constexpr int kBStage = kBK * kBNT;
 constexpr int kStageBytes = (kAStage + kBStage) * 2;   // 24 KiB
 
-// raw buffer descriptor word 3 (32-bit data format) and the cache-policy bit of
-// a non-temporal (streaming) store
-constexpr int kBufferRsrcWord3 = 0x00020000;
-constexpr int kCpolNT = 2;
-
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 

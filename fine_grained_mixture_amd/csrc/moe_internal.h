@@ -22,6 +22,10 @@ constexpr int kGemmBM = 128;
 constexpr int kGemmBigBM = 256;
 // MI355X's Infinity Cache (the memory-side cache in front of HBM), bytes
 constexpr int64_t kInfinityCacheBytes = (int64_t)256 << 20;
+// Raw buffer descriptor word 3 (32-bit data format), and the cache-policy bit
+// of a non-temporal (streaming) buffer store.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kCpolNT = 2;
 constexpr int kGemmBM_F32 = 64;
 // Rows per workgroup of the fused low-rank expert kernel.
 constexpr int kLowRankBM = 64;
